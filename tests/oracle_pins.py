@@ -1,0 +1,490 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` takes an oracle module and raises AssertionError when the oracle
+disagrees with a fact that the pages or plain mathematics fix: a pure-Python
+brute force written from the definition, torch's CPU scaled-dot-product attention
+(a library routine that computes the same textbook operation), closed forms,
+invariants, exact rational arithmetic, and hand-worked examples.
+
+The same pins run against mutated copies of the oracle in test_oracle_mutants.py
+to show that a plausible slip (a dropped scale, a wrong group index, a flipped
+tie rule...) fails at least one of them.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+import workloads
+
+TOL = 1e-12
+
+
+def _dec(bits):
+    """bf16 bits -> Python floats, via struct-free integer arithmetic."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def _tiny_cases():
+    cases = [workloads.make(1)]
+    cases.append(workloads.random_case(11, batch=3, num_q_heads=6, num_kv_heads=2, head_dim=64,
+                                       block_size=16, context_lens=[1, 17, 50]))
+    cases.append(workloads.random_case(12, batch=2, num_q_heads=8, num_kv_heads=4, head_dim=64,
+                                       block_size=32, context_lens=[33, 64]))
+    return cases
+
+
+# ---------------------------------------------------------------------------
+# ReshapeAndCache
+# ---------------------------------------------------------------------------
+
+def pin_write_hand_worked(orc):
+    """Slots worked out by hand with block_size 4: 5 -> (1,1), 0 -> (0,0), 15 -> (3,3)."""
+    NB, bs, H, D = 4, 4, 1, 2
+    kc = np.zeros((NB, bs, H, D), np.uint16)
+    vc = np.zeros((NB, bs, H, D), np.uint16)
+    key = np.array([[[1, 2]], [[3, 4]], [[5, 6]], [[7, 8]]], np.uint16)
+    val = key + 100
+    slots = np.array([5, -1, 0, 15], np.int64)
+    k2, v2 = orc.reshape_and_cache(kc, vc, key, val, slots, bs)
+    ek = np.zeros_like(kc)
+    ek[1, 1, 0] = [1, 2]
+    ek[0, 0, 0] = [5, 6]
+    ek[3, 3, 0] = [7, 8]
+    ev = np.zeros_like(vc)
+    ev[1, 1, 0] = [101, 102]
+    ev[0, 0, 0] = [105, 106]
+    ev[3, 3, 0] = [107, 108]
+    assert np.array_equal(k2, ek), "key cache after hand-worked write"
+    assert np.array_equal(v2, ev), "value cache after hand-worked write"
+    assert not kc.any() and not vc.any(), "inputs must not be modified"
+
+
+def pin_write_config1(orc):
+    """Config 1: token 0 goes to (seq 0, position 36) -> logical block 2, row 4;
+    token 1 has slot -1 and changes nothing. Every other byte is untouched."""
+    w = workloads.make(1)
+    k2, v2 = orc.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                   w.slot_mapping, w.block_size)
+    pb = int(w.block_tables[0, 36 // 16])
+    assert int(w.slot_mapping[0]) == pb * 16 + 4
+    ek = w.key_cache.copy()
+    ek[pb, 4] = w.new_key[0]
+    ev = w.value_cache.copy()
+    ev[pb, 4] = w.new_value[0]
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+
+
+def pin_write_negative_skips(orc):
+    w = workloads.make(1)
+    slots = np.array([-1, -7], np.int64)
+    k2, v2 = orc.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value, slots, 16)
+    assert np.array_equal(k2, w.key_cache) and np.array_equal(v2, w.value_cache)
+
+
+# ---------------------------------------------------------------------------
+# Dense attention
+# ---------------------------------------------------------------------------
+
+def _brute_dense_row(w, b, h):
+    """Pure-Python definition: walk the block table token by token."""
+    G = w.num_q_heads // w.num_kv_heads
+    g = h // G
+    bs = w.block_size
+    scale = float(w.scale)
+    q = _dec(w.query[b, h]).tolist()
+    L = int(w.context_lens[b])
+    if L == 0:
+        return [0.0] * w.head_dim
+    scores, vals = [], []
+    for t in range(L):
+        pb = int(w.block_tables[b][t // bs])
+        k = _dec(w.key_cache[pb, t % bs, g]).tolist()
+        vals.append(_dec(w.value_cache[pb, t % bs, g]).tolist())
+        scores.append(scale * math.fsum(qi * ki for qi, ki in zip(q, k)))
+    m = max(scores)
+    e = [math.exp(s - m) for s in scores]
+    z = math.fsum(e)
+    return [math.fsum(e[t] * vals[t][c] for t in range(L)) / z for c in range(w.head_dim)]
+
+
+def pin_dense_brute_force(orc):
+    for w in _tiny_cases():
+        out = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                         w.context_lens, w.scale)
+        for b in range(w.batch):
+            for h in range(w.num_q_heads):
+                ref = np.array(_brute_dense_row(w, b, h))
+                err = np.abs(out[b, h] - ref).max()
+                assert err <= TOL, f"{w.name} b={b} h={h} err={err}"
+
+
+def pin_dense_torch_sdpa(orc):
+    """torch CPU scaled_dot_product_attention in float64 with enable_gqa (head h
+    reads KV head h // G) on the K/V gathered into contiguous order."""
+    import torch
+    import torch.nn.functional as F
+    for w in _tiny_cases():
+        out = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                         w.context_lens, w.scale)
+        for b in range(w.batch):
+            L = int(w.context_lens[b])
+            if L == 0:
+                continue
+            k = np.stack([_dec(w.key_cache[int(w.block_tables[b][t // w.block_size]), t % w.block_size])
+                          for t in range(L)])                  # [L, Hkv, D]
+            v = np.stack([_dec(w.value_cache[int(w.block_tables[b][t // w.block_size]), t % w.block_size])
+                          for t in range(L)])
+            qt = torch.from_numpy(_dec(w.query[b]))[None, :, None, :]       # [1,Hq,1,D]
+            kt = torch.from_numpy(k).permute(1, 0, 2)[None].contiguous()    # [1,Hkv,L,D]
+            vt = torch.from_numpy(v).permute(1, 0, 2)[None].contiguous()
+            ref = F.scaled_dot_product_attention(qt, kt, vt, scale=float(w.scale), enable_gqa=True)
+            err = np.abs(out[b] - ref[0, :, 0].numpy()).max()
+            assert err <= TOL, f"{w.name} b={b} sdpa err={err}"
+
+
+def pin_dense_closed_forms(orc):
+    w = workloads.random_case(21, batch=3, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                              block_size=16, context_lens=[1, 40, 23])
+    # ctx = 1: the output is the single value row, exactly.
+    out = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                     w.context_lens, w.scale)
+    pb = int(w.block_tables[0, 0])
+    for h in range(4):
+        assert np.array_equal(out[0, h], _dec(w.value_cache[pb, 0, h // 2])), "ctx=1 -> v_0"
+    # all keys of a sequence equal -> uniform weights -> mean of V.
+    kc = w.key_cache.copy()
+    for t in range(40):
+        kc[int(w.block_tables[1, t // 16]), t % 16] = w.key_cache[int(w.block_tables[1, 0]), 0]
+    out = orc.paged_attention_decode(w.query, kc, w.value_cache, w.block_tables, w.context_lens, w.scale)
+    for h in range(4):
+        vs = [_dec(w.value_cache[int(w.block_tables[1, t // 16]), t % 16, h // 2]) for t in range(40)]
+        ref = np.array([math.fsum(v[c] for v in vs) / 40 for c in range(64)])
+        assert np.abs(out[1, h] - ref).max() <= TOL, "equal keys -> mean(v)"
+    # constant V -> output equals that constant.
+    vc = np.full_like(w.value_cache, 0x3FC0)        # bf16 1.5
+    out = orc.paged_attention_decode(w.query, w.key_cache, vc, w.block_tables, w.context_lens, w.scale)
+    assert np.abs(out - 1.5).max() <= TOL, "constant V"
+
+
+def pin_dense_scale_and_group(orc):
+    """Doubling the query equals doubling the scale (scores are linear in scale*q),
+    and moving KV head 1's data onto head 0 only changes the second group's heads."""
+    w = workloads.random_case(22, batch=2, num_q_heads=6, num_kv_heads=3, head_dim=64,
+                              block_size=16, context_lens=[29, 45])
+    out1 = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                      w.context_lens, w.scale)
+    ref = np.zeros_like(out1)
+    for b in range(2):
+        for h in range(6):
+            ref[b, h] = _brute_dense_row(w, b, h)
+    assert np.abs(out1 - ref).max() <= TOL
+    kc = w.key_cache.copy()
+    kc[:, :, 1] = kc[:, :, 0]
+    vc = w.value_cache.copy()
+    vc[:, :, 1] = vc[:, :, 0]
+    out2 = orc.paged_attention_decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale)
+    assert np.array_equal(out2[:, [0, 1, 4, 5]], out1[:, [0, 1, 4, 5]]), "heads of groups 0, 2 unchanged"
+    assert not np.allclose(out2[:, [2, 3]], out1[:, [2, 3]]), "heads of group 1 read KV head 1"
+
+
+def _permuted_pool(w, seed):
+    """Move every physical block to a new id (data copied along)."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(w.num_blocks)            # new id of old block i
+    kc = np.empty_like(w.key_cache)
+    vc = np.empty_like(w.value_cache)
+    kc[perm] = w.key_cache
+    vc[perm] = w.value_cache
+    bt = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    return kc, vc, bt
+
+
+def pin_dense_permuted_table(orc):
+    for w in _tiny_cases():
+        out = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                         w.context_lens, w.scale)
+        kc, vc, bt = _permuted_pool(w, 5)
+        out2 = orc.paged_attention_decode(w.query, kc, vc, bt, w.context_lens, w.scale)
+        assert np.array_equal(out, out2), "permuted block table"
+
+
+def _poison(w, value=0x7FC0):
+    """Fill every slot outside some sequence's context with ``value`` bits (NaN)."""
+    kc = w.key_cache.copy()
+    vc = w.value_cache.copy()
+    live = np.zeros(w.key_cache.shape[:2], dtype=bool)
+    for b in range(w.batch):
+        for t in range(int(w.context_lens[b])):
+            live[int(w.block_tables[b, t // w.block_size]), t % w.block_size] = True
+    kc[~live] = value
+    vc[~live] = value
+    return kc, vc
+
+
+def pin_dense_nan_poison(orc):
+    for w in _tiny_cases():
+        out = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                         w.context_lens, w.scale)
+        kc, vc = _poison(w)
+        out2 = orc.paged_attention_decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale)
+        assert np.array_equal(out, out2), "NaN outside the context changed the output"
+
+
+def pin_dense_empty_context(orc):
+    w = workloads.random_case(23, batch=2, num_q_heads=2, num_kv_heads=1, head_dim=64,
+                              block_size=16, context_lens=[0, 5])
+    out = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                     w.context_lens, w.scale)
+    assert np.array_equal(out[0], np.zeros((2, 64))), "ctx = 0 -> zeros"
+
+
+# ---------------------------------------------------------------------------
+# Split-KV combine
+# ---------------------------------------------------------------------------
+
+def pin_split_combine_equals_dense(orc):
+    w = workloads.random_case(31, batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                              block_size=16, context_lens=[200])
+    dense = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                       w.context_lens, w.scale)[0]
+    pos = np.arange(200)
+    k = orc.bf16_to_f64(orc.gather_sequence(w.key_cache, w.block_tables, 0, pos, 16))[:, 0]
+    v = orc.bf16_to_f64(orc.gather_sequence(w.value_cache, w.block_tables, 0, pos, 16))[:, 0]
+    q = orc.bf16_to_f64(w.query[0])
+    sc = float(w.scale) * 8.0      # sharpen the softmax so the splits' maxima differ a lot
+    dense_sharp = orc.split_kv_combine(*orc.split_kv_partials(q, k, v, sc, [(0, 200)]))
+    ref = np.array([[_ref_row(q[h], k, v, sc)] for h in range(4)])[:, 0]
+    assert np.abs(dense_sharp - ref).max() <= TOL
+    for S in (1, 2, 3, 7, 64):
+        prop = [(200 * s // S, 200 * (s + 1) // S) for s in range(S)]
+        fixed = [(min(200, 32 * s), min(200, 32 * (s + 1))) for s in range(S)] + [(32 * S, 200)]
+        for bounds in (prop, fixed):
+            got = orc.split_kv_combine(*orc.split_kv_partials(q, k, v, sc, bounds))
+            assert np.abs(got - ref).max() <= TOL, f"S={S} split combine"
+    got = orc.split_kv_combine(*orc.split_kv_partials(q, k, v, float(w.scale), [(0, 0), (0, 77), (77, 77), (77, 200)]))
+    assert np.abs(got - dense).max() <= TOL, "empty splits carry weight 0"
+
+
+def _ref_row(qh, k, v, sc):
+    s = [sc * math.fsum(a * b for a, b in zip(qh, kt)) for kt in k]
+    m = max(s)
+    e = [math.exp(x - m) for x in s]
+    z = math.fsum(e)
+    return [math.fsum(e[t] * v[t][c] for t in range(len(e))) / z for c in range(v.shape[1])]
+
+
+# ---------------------------------------------------------------------------
+# Quest metadata
+# ---------------------------------------------------------------------------
+
+def _brute_meta(w):
+    NB, bs, H, D = w.key_cache.shape
+    kmin = {}
+    kmax = {}
+    for b in range(w.batch):
+        L = int(w.context_lens[b])
+        for lb in range(-(-L // bs)):
+            pb = int(w.block_tables[b, lb])
+            n = min(bs, L - lb * bs)
+            for g in range(H):
+                for c in range(D):
+                    vals = [float(_dec(w.key_cache[pb, t, g, c])) for t in range(n)]
+                    kmin[(pb, g, c)] = min(vals)
+                    kmax[(pb, g, c)] = max(vals)
+    return kmin, kmax
+
+
+def pin_meta_brute_force(orc):
+    for w in _tiny_cases()[:2]:
+        kmin, kmax = orc.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, w.block_size)
+        bmin, bmax = _brute_meta(w)
+        dmin, dmax = _dec(kmin), _dec(kmax)
+        for (pb, g, c), v in bmin.items():
+            assert dmin[pb, g, c] == v and dmax[pb, g, c] == bmax[(pb, g, c)], (pb, g, c)
+
+
+def pin_meta_poison_and_step(orc):
+    w = workloads.make(1)
+    kc = w.key_cache.copy()
+    # +-1e4 in the invalid rows of each sequence's last block must not show up.
+    for b in range(2):
+        L = int(w.context_lens[b])
+        pb = int(w.block_tables[b, (L - 1) // 16])
+        kc[pb, L % 16 or 16:, :, ::2] = 0x461C      # bf16 10000
+        kc[pb, L % 16 or 16:, :, 1::2] = 0xC61C     # bf16 -10000
+    kmin, kmax = orc.quest_block_metadata(kc, w.block_tables, w.context_lens, 16)
+    assert np.abs(_dec(kmin)).max() < 1e4 and np.abs(_dec(kmax)).max() < 1e4
+    # step mode writes only each sequence's last block.
+    base = np.full_like(kmin, 0x1234)
+    smin, smax = orc.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16,
+                                          last_block_only=True, key_min=base, key_max=base)
+    fmin, fmax = orc.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+    last = {int(w.block_tables[0, 2]), int(w.block_tables[1, 4])}
+    for pb in range(16):
+        if pb in last:
+            assert np.array_equal(smin[pb], fmin[pb]) and np.array_equal(smax[pb], fmax[pb])
+        else:
+            assert (smin[pb] == 0x1234).all() and (smax[pb] == 0x1234).all()
+
+
+# ---------------------------------------------------------------------------
+# Quest score and Top-K
+# ---------------------------------------------------------------------------
+
+def _frac_score(w, kmin, kmax, b, g, lb):
+    G = w.group
+    pb = int(w.block_tables[b, lb])
+    tot = Fraction(0)
+    for h in range(g * G, (g + 1) * G):
+        q = _dec(w.query[b, h])
+        lo = _dec(kmin[pb, g])
+        hi = _dec(kmax[pb, g])
+        for c in range(w.head_dim):
+            tot += max(Fraction(q[c]) * Fraction(lo[c]), Fraction(q[c]) * Fraction(hi[c]))
+    return tot
+
+
+def pin_score_exact_rational(orc):
+    w = workloads.make(1)
+    kmin, kmax = orc.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+    for b in range(2):
+        s = orc.quest_block_scores(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, b, 0)
+        nb = -(-int(w.context_lens[b]) // 16)
+        assert s.size == nb
+        for lb in range(nb):
+            assert s[lb] == float(_frac_score(w, kmin, kmax, b, 0, lb)), (b, lb)
+
+
+def pin_score_upper_bound_and_single_token(orc):
+    w = workloads.random_case(41, batch=2, num_q_heads=6, num_kv_heads=2, head_dim=64,
+                              block_size=16, context_lens=[33, 48])   # seq 0: last block has 1 token
+    kmin, kmax = orc.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+    G = 3
+    for b in range(2):
+        L = int(w.context_lens[b])
+        for g in range(2):
+            s = orc.quest_block_scores(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, b, g)
+            for lb in range(-(-L // 16)):
+                pb = int(w.block_tables[b, lb])
+                n = min(16, L - lb * 16)
+                dots = []
+                for t in range(n):
+                    k = _dec(w.key_cache[pb, t, g])
+                    dots.append(sum(Fraction(float(x)) * Fraction(float(y))
+                                    for h in range(g * G, (g + 1) * G)
+                                    for x, y in zip(_dec(w.query[b, h]), k)))
+                assert Fraction(float(s[lb])) >= max(dots) - Fraction(1, 10**9), "upper bound"
+                if n == 1:
+                    assert s[lb] == float(dots[0]), "single-token block score = sum_h q.k"
+
+
+def _rank_select(scores, k):
+    """Independent Top-K: a block is kept iff fewer than k blocks beat it
+    (higher score, or equal score and lower index)."""
+    n = len(scores)
+    keep = []
+    for i in range(n):
+        beat = sum(1 for j in range(n) if scores[j] > scores[i] or (scores[j] == scores[i] and j < i))
+        if beat < k:
+            keep.append(i)
+    return keep
+
+
+def pin_topk_rank_and_all(orc):
+    w = workloads.random_case(42, batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                              block_size=16, context_lens=[100, 16, 77])
+    kmin, kmax = orc.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+    for K in (1, 3, 7, 20):
+        sel = orc.quest_select_topk(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, K)
+        assert sel.shape == (3, 2, K) and sel.dtype == np.int32
+        for b in range(3):
+            nb = -(-int(w.context_lens[b]) // 16)
+            for g in range(2):
+                s = orc.quest_block_scores(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, b, g)
+                exp = _rank_select(s.tolist(), K)
+                row = sel[b, g].tolist()
+                assert row[:len(exp)] == exp and all(x == -1 for x in row[len(exp):]), (K, b, g)
+                if K >= nb:
+                    assert exp == list(range(nb))
+
+
+def pin_topk_tie_lower_index(orc):
+    """Copy block A's rows into a later block B: equal metadata, equal score.
+    With room for one of the two, the lower logical index wins."""
+    w = workloads.random_case(43, batch=1, num_q_heads=2, num_kv_heads=1, head_dim=64,
+                              block_size=16, context_lens=[64])
+    kmin, kmax = orc.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+    s = orc.quest_block_scores(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, 0, 0)
+    best = int(np.argmax(s))
+    kc = w.key_cache.copy()
+    others = [lb for lb in range(4) if lb != best]
+    later = max(others)
+    kc[int(w.block_tables[0, later])] = kc[int(w.block_tables[0, best])]
+    a, c = min(best, later), max(best, later)
+    kmin, kmax = orc.quest_block_metadata(kc, w.block_tables, w.context_lens, 16)
+    s2 = orc.quest_block_scores(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, 0, 0)
+    assert s2[a] == s2[c]
+    sel = orc.quest_select_topk(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, 1)
+    assert sel[0, 0, 0] == a, "tie goes to the lower logical block"
+
+
+# ---------------------------------------------------------------------------
+# Sparse attention
+# ---------------------------------------------------------------------------
+
+def pin_sparse_all_equals_dense(orc):
+    for w in _tiny_cases():
+        nbmax = int(w.nblocks().max())
+        sel = np.full((w.batch, w.num_kv_heads, nbmax + 2), -1, np.int32)
+        for b, nb in enumerate(w.nblocks().tolist()):
+            sel[b, :, :nb] = np.arange(nb)
+        d = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                       w.context_lens, w.scale)
+        s = orc.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                              w.context_lens, sel, w.scale)
+        assert np.abs(d - s).max() <= TOL
+
+
+def pin_sparse_equals_dense_on_dropped_context(orc):
+    """Sparse attention == dense attention on a table that lists only the selected
+    blocks (ascending, so a partial last block stays last)."""
+    w = workloads.random_case(51, batch=2, num_q_heads=3, num_kv_heads=1, head_dim=64,
+                              block_size=16, context_lens=[90, 64])
+    sel = np.array([[[0, 2, 5, -1]], [[1, 3, -1, -1]]], np.int32)
+    s = orc.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                          w.context_lens, sel, w.scale)
+    bt2 = np.full_like(w.block_tables, -1)
+    ctx2 = np.zeros(2, np.int32)
+    for b in range(2):
+        ids = [x for x in sel[b, 0].tolist() if x >= 0]
+        bt2[b, :len(ids)] = w.block_tables[b, ids]
+        L = int(w.context_lens[b])
+        ctx2[b] = sum(min(16, L - lb * 16) for lb in ids)
+    d = orc.paged_attention_decode(w.query, w.key_cache, w.value_cache, bt2, ctx2, w.scale)
+    assert np.abs(d - s).max() <= TOL
+
+
+def pin_sparse_brute_force(orc):
+    w = workloads.random_case(52, batch=2, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                              block_size=16, context_lens=[70, 35])
+    sel = np.array([[[4, 1, -1], [0, 2, 3]], [[2, -1, -1], [1, 0, -1]]], np.int32)
+    s = orc.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                          w.context_lens, sel, w.scale)
+    for b in range(2):
+        L = int(w.context_lens[b])
+        for h in range(4):
+            g = h // 2
+            ids = sorted(x for x in sel[b, g].tolist() if x >= 0)
+            pos = [t for lb in ids for t in range(lb * 16, min(lb * 16 + 16, L))]
+            q = _dec(w.query[b, h])
+            k = np.stack([_dec(w.key_cache[int(w.block_tables[b, t // 16]), t % 16, g]) for t in pos])
+            v = np.stack([_dec(w.value_cache[int(w.block_tables[b, t // 16]), t % 16, g]) for t in pos])
+            ref = np.array(_ref_row(q, k, v, float(w.scale)))
+            assert np.abs(s[b, h] - ref).max() <= TOL, (b, h)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
