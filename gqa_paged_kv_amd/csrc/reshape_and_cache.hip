@@ -1,0 +1,56 @@
+// ReshapeAndCache: scatter new tokens' K/V rows into the paged cache.
+//
+// ["Ascend Kernel-to-Serving Pipeline", section "ReshapeAndCache"]: the physical
+// block of a token is slot // block_size and its row inside the block is
+// slot % block_size; a negative slot means the token is not written.
+//
+// With the cache laid out [num_blocks, block_size, H_kv, D], one token's K (or V)
+// for all KV heads is a single contiguous row of H_kv * D bf16, so the write is a
+// 16-byte-per-lane row copy. One wave per token: T is small (one new token per
+// sequence), so the kernel is launch-bound and its only job is to move whole
+// rows with full-width stores.
+#include "gpkv_internal.h"
+
+namespace gpkv {
+
+__global__ __launch_bounds__(64) void reshape_and_cache_kernel(
+    const u32x4* __restrict__ key, const u32x4* __restrict__ value, u32x4* __restrict__ key_cache,
+    u32x4* __restrict__ value_cache, const int64_t* __restrict__ slot_mapping, int row_vec,
+    int block_size, long long num_slots) {
+  const int i = blockIdx.x;
+  const long long s = slot_mapping[i];
+  if (s < 0 || s >= num_slots) return;  // negative: skip; past the pool: tolerated, skipped
+  const long long blk = s / block_size;
+  const long long off = s - blk * block_size;
+  const size_t dst = (size_t)(blk * block_size + off) * (size_t)row_vec;
+  const size_t src = (size_t)i * (size_t)row_vec;
+  for (int c = threadIdx.x; c < row_vec; c += 64) {
+    key_cache[dst + c] = key[src + c];
+    value_cache[dst + c] = value[src + c];
+  }
+}
+
+}  // namespace gpkv
+
+extern "C" int gpkv_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                                      void* value_cache, const int64_t* slot_mapping,
+                                      int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int64_t num_blocks, void* stream) {
+  using namespace gpkv;
+  clear_error();
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
+    return fail(GPKV_ERR_SHAPE, "reshape_and_cache: num_tokens=%d num_kv_heads=%d num_blocks=%lld",
+                num_tokens, num_kv_heads, (long long)num_blocks);
+  if (!supported_head_dim(head_dim))
+    return fail(GPKV_ERR_UNSUPPORTED, "reshape_and_cache: head_dim=%d (64 or 128)", head_dim);
+  if (!supported_block_size(block_size))
+    return fail(GPKV_ERR_UNSUPPORTED, "reshape_and_cache: block_size=%d (16/32/64/128)", block_size);
+  if (num_tokens == 0) return GPKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(GPKV_ERR_NULL, "reshape_and_cache: null pointer argument");
+  const int row_vec = num_kv_heads * head_dim * 2 / 16;
+  reshape_and_cache_kernel<<<dim3(num_tokens), dim3(64), 0, (hipStream_t)stream>>>(
+      (const u32x4*)key, (const u32x4*)value, (u32x4*)key_cache, (u32x4*)value_cache,
+      slot_mapping, row_vec, block_size, (long long)num_blocks * block_size);
+  return check_launch("reshape_and_cache");
+}

@@ -1,0 +1,204 @@
+"""torch-tensor front end of the gpkv C ABI (names follow include/gpkv.h).
+
+Tensors must live on the GPU and be contiguous. bf16 tensors are torch.bfloat16;
+block_tables / context_lens / topk indices are int32, slot_mapping is int64 and
+attention outputs are float32. Every call is asynchronous on
+torch.cuda.current_stream() (or the ``stream`` given).
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import lib
+
+__all__ = [
+    "GpkvError", "reshape_and_cache", "paged_attention_decode", "quest_block_metadata",
+    "quest_select_topk", "sparse_paged_attention_decode", "paged_attention_workspace_bytes",
+    "quest_select_workspace_bytes", "sparse_attention_workspace_bytes", "split_tokens",
+]
+
+
+class GpkvError(RuntimeError):
+    """A gpkv call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.message = message
+        name = lib().gpkv_status_string(status).decode()
+        super().__init__(f"gpkv status {status} ({name}): {message}")
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise GpkvError(status, lib().gpkv_last_error_message().decode())
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int | None = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {tuple(t.shape)})")
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace: torch.Tensor | None) -> torch.Tensor:
+    if workspace is not None:
+        _dev("workspace", workspace, torch.uint8)
+        return workspace
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _cache_dims(key_cache: torch.Tensor):
+    NB, bs, Hkv, D = key_cache.shape
+    return int(NB), int(bs), int(Hkv), int(D)
+
+
+def split_tokens(batch: int, num_kv_heads: int, span_tokens: int) -> int:
+    return int(lib().gpkv_split_tokens(batch, num_kv_heads, span_tokens))
+
+
+def paged_attention_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    max_context_len) -> int:
+    return int(lib().gpkv_paged_attention_workspace_bytes(
+        batch, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len))
+
+
+def quest_select_workspace_bytes(batch, num_kv_heads, max_blocks_per_seq) -> int:
+    return int(lib().gpkv_quest_select_workspace_bytes(batch, num_kv_heads, max_blocks_per_seq))
+
+
+def sparse_attention_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     topk_blocks) -> int:
+    return int(lib().gpkv_sparse_attention_workspace_bytes(
+        batch, num_q_heads, num_kv_heads, head_dim, block_size, topk_blocks))
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, stream=None) -> None:
+    """Write key[i] / value[i] to the cache slot slot_mapping[i] (negative: skip)."""
+    _dev("key_cache", key_cache, torch.bfloat16, 4)
+    _dev("value_cache", value_cache, torch.bfloat16, 4)
+    _dev("key", key, torch.bfloat16, 3)
+    _dev("value", value, torch.bfloat16, 3)
+    _dev("slot_mapping", slot_mapping, torch.int64, 1)
+    NB, bs, Hkv, D = _cache_dims(key_cache)
+    T = key.shape[0]
+    if value_cache.shape != key_cache.shape or key.shape != (T, Hkv, D) or value.shape != key.shape \
+            or slot_mapping.shape[0] != T:
+        raise ValueError("reshape_and_cache: inconsistent shapes")
+    _check(lib().gpkv_reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T, Hkv, D,
+        bs, NB, _stream(stream)))
+
+
+def _attn_checks(query, key_cache, value_cache, block_tables, context_lens):
+    _dev("query", query, torch.bfloat16, 3)
+    _dev("key_cache", key_cache, torch.bfloat16, 4)
+    _dev("value_cache", value_cache, torch.bfloat16, 4)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    NB, bs, Hkv, D = _cache_dims(key_cache)
+    B, Hq, Dq = query.shape
+    if value_cache.shape != key_cache.shape or Dq != D or block_tables.shape[0] != B \
+            or context_lens.shape[0] != B:
+        raise ValueError("inconsistent shapes between query, caches, block_tables, context_lens")
+    return B, Hq, Hkv, D, bs, NB, int(block_tables.shape[1])
+
+
+def paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens, *,
+                           max_context_len: int, scale: float, out=None, workspace=None,
+                           stream=None) -> torch.Tensor:
+    """Dense GQA paged decode attention; returns out [B, H_q, D] float32."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks(query, key_cache, value_cache, block_tables,
+                                             context_lens)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    need = paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_paged_attention_decode(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), B, Hq, Hkv, D, bs, NB, MB, int(max_context_len), float(scale),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def quest_block_metadata(key_cache, block_tables, context_lens, key_min, key_max, *,
+                         max_context_len: int, last_block_only: bool = False,
+                         stream=None) -> None:
+    """Refresh per-block key min / max (all referenced blocks, or each last block)."""
+    _dev("key_cache", key_cache, torch.bfloat16, 4)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    _dev("key_min", key_min, torch.bfloat16, 3)
+    _dev("key_max", key_max, torch.bfloat16, 3)
+    NB, bs, Hkv, D = _cache_dims(key_cache)
+    B = int(context_lens.shape[0])
+    if key_min.shape != (NB, Hkv, D) or key_max.shape != (NB, Hkv, D) \
+            or block_tables.shape[0] != B:
+        raise ValueError("quest_block_metadata: inconsistent shapes")
+    _check(lib().gpkv_quest_block_metadata(
+        _ptr(key_min), _ptr(key_max), _ptr(key_cache), _ptr(block_tables), _ptr(context_lens), B,
+        Hkv, D, bs, NB, int(block_tables.shape[1]), int(max_context_len),
+        1 if last_block_only else 0, _stream(stream)))
+
+
+def quest_select_topk(query, key_min, key_max, block_tables, context_lens, *, block_size: int,
+                      topk_blocks: int, max_context_len: int, out=None, workspace=None,
+                      stream=None) -> torch.Tensor:
+    """Quest block scores + Top-K; returns [B, H_kv, topk_blocks] int32 (ascending, -1 pad)."""
+    _dev("query", query, torch.bfloat16, 3)
+    _dev("key_min", key_min, torch.bfloat16, 3)
+    _dev("key_max", key_max, torch.bfloat16, 3)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    NB, Hkv, D = (int(x) for x in key_min.shape)
+    B, Hq, Dq = query.shape
+    MB = int(block_tables.shape[1])
+    if key_max.shape != key_min.shape or Dq != D or block_tables.shape[0] != B \
+            or context_lens.shape[0] != B:
+        raise ValueError("quest_select_topk: inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, Hkv, int(topk_blocks)), dtype=torch.int32, device=query.device)
+    _dev("out", out, torch.int32, 3)
+    ws = _workspace(quest_select_workspace_bytes(B, Hkv, MB), query.device, workspace)
+    _check(lib().gpkv_quest_select_topk(
+        _ptr(out), _ptr(query), _ptr(key_min), _ptr(key_max), _ptr(block_tables),
+        _ptr(context_lens), B, Hq, Hkv, D, int(block_size), NB, MB, int(max_context_len),
+        int(topk_blocks), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def sparse_paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens,
+                                  topk_indices, *, max_context_len: int, scale: float, out=None,
+                                  workspace=None, stream=None) -> torch.Tensor:
+    """Exact attention over the selected logical blocks; returns [B, H_q, D] float32."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks(query, key_cache, value_cache, block_tables,
+                                             context_lens)
+    _dev("topk_indices", topk_indices, torch.int32, 3)
+    if topk_indices.shape[0] != B or topk_indices.shape[1] != Hkv:
+        raise ValueError("sparse_paged_attention_decode: topk_indices must be [B, H_kv, K]")
+    K = int(topk_indices.shape[2])
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    need = sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_sparse_paged_attention_decode(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(topk_indices), B, Hq, Hkv, D, bs, NB, MB, int(max_context_len),
+        K, float(scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return out

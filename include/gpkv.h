@@ -1,0 +1,193 @@
+/*
+ * gpkv.h -- C ABI of the paged GQA decode-attention library for AMD MI355X (gfx950).
+ *
+ * Single-token decode attention over a paged KV cache, its write path and the
+ * Quest long-context variant. Five operations:
+ *
+ *   gpkv_reshape_and_cache           write new tokens' K/V rows into the cache
+ *   gpkv_paged_attention_decode      dense GQA paged attention (split-KV + combine)
+ *   gpkv_quest_block_metadata        per-block, per-channel key min / max
+ *   gpkv_quest_select_topk           Quest block scores + Top-K per KV head
+ *   gpkv_sparse_paged_attention_decode  exact attention over the selected blocks
+ *
+ * Sources, by page title and section:
+ *   [ASC]  "Ascend Kernel-to-Serving Pipeline": sections "ReshapeAndCache",
+ *          "GQA Paged Attention", "Quest Sparse Attention", "single-operator
+ *          correctness", "Sparse precision", "memory optimisation".
+ *   [TL18] TileLang tutorial, chapter 18 (end-to-end inference serving):
+ *          2.4 KV-cache structure, 2.6 paged KV, 4.1 split-KV decode attention,
+ *          6.1 kernels on the framework's current stream, 6.2 graph capture.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - bf16 tensors are passed as `const void*` / `void*` to raw bfloat16 bits.
+ *    Every tensor is contiguous, row-major, in device memory (HBM), except where
+ *    a comment says otherwise.
+ *  - KV cache layout ([TL18] 2.6): key_cache and value_cache are each
+ *    [num_blocks, block_size, num_kv_heads, head_dim] bf16. Token t of sequence b
+ *    lives in physical block block_tables[b * max_blocks_per_seq + t / block_size],
+ *    row t % block_size.
+ *  - block_tables: [batch, max_blocks_per_seq] int32; entries at logical index
+ *    >= ceil(context_lens[b] / block_size) are never read.
+ *  - context_lens: [batch] int32, each in [0, max_context_len]. It includes the
+ *    token written by this step's reshape_and_cache.
+ *  - GQA ([ASC] "GQA Paged Attention"): num_q_heads is a multiple of
+ *    num_kv_heads; query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *  - Supported shapes: head_dim in {64, 128}; block_size in {16, 32, 64, 128};
+ *    group size num_q_heads / num_kv_heads in [1, 16].
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on it: no allocation, no host<->device copy, no
+ *    synchronisation ([TL18] 6.1). Grids depend only on host scalars, so the
+ *    calls can be captured into a HIP graph ([TL18] 6.2).
+ *  - Ownership: the caller owns every buffer (caches, metadata, outputs and
+ *    workspaces); the library keeps no pointer after a call returns.
+ *  - Errors: arguments are checked on the host before any launch. A failing
+ *    check returns a negative gpkv_status, launches nothing, and stores a
+ *    message readable with gpkv_last_error_message() (per thread). A launch
+ *    failure reported by the HIP runtime returns GPKV_ERR_HIP. Device-side
+ *    contents (block ids, lengths, slots, selected ids) are preconditions and
+ *    are not checked; kernels still skip out-of-range slots and selected ids.
+ */
+#ifndef GPKV_H_
+#define GPKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPKV_OK = 0,
+  GPKV_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  GPKV_ERR_SHAPE = -2,       /* inconsistent or negative sizes                    */
+  GPKV_ERR_UNSUPPORTED = -3, /* head_dim / block_size / group size not supported  */
+  GPKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
+  GPKV_ERR_HIP = -5          /* the HIP runtime reported an error at launch       */
+} gpkv_status;
+
+/* ReshapeAndCache ([ASC] "ReshapeAndCache").
+ * For each new token i < num_tokens with s = slot_mapping[i]:
+ *   s < 0                 -> the token is skipped;
+ *   otherwise block = s / block_size, row = s % block_size, and
+ *   key_cache[block, row, :, :] = key[i], value_cache[block, row, :, :] = value[i].
+ * key, value: [num_tokens, num_kv_heads, head_dim] bf16 (read).
+ * key_cache, value_cache: [num_blocks, block_size, num_kv_heads, head_dim] bf16,
+ *   modified in place; rows not named by a slot are left untouched.
+ * slot_mapping: [num_tokens] int64. Slots >= num_blocks * block_size are skipped
+ *   (precondition violation, tolerated for memory safety); two tokens naming the
+ *   same slot is a precondition violation with an unspecified winner.
+ * num_tokens == 0 is a no-op. */
+int gpkv_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                           void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, void* stream);
+
+/* Bytes of workspace gpkv_paged_attention_decode needs for these sizes (0 if the
+ * sizes are invalid). The workspace holds split-KV partial outputs and their
+ * log-sum-exp ([TL18] 4.1). */
+size_t gpkv_paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int32_t max_context_len);
+
+/* Dense GQA paged decode attention ([ASC] "GQA Paged Attention"; [TL18] 2.6, 4.1).
+ * out[b, h, :] = sum_t p_t V_t with p = softmax_t(scale * q[b, h, :] . K_t) over the
+ * tokens t < context_lens[b] of sequence b (ragged last block masked; a
+ * sequence with context 0 gets a zero row). K_t, V_t are KV head h / G of the
+ * token's cache row.
+ * out: [batch, num_q_heads, head_dim] float32 (written).
+ * query: [batch, num_q_heads, head_dim] bf16.
+ * max_context_len: a host-side upper bound of context_lens (sizes the grid and
+ *   the workspace); must be <= max_blocks_per_seq * block_size.
+ * scale: the softmax scale (typically 1/sqrt(head_dim)).
+ * workspace: device memory of at least gpkv_paged_attention_workspace_bytes(...)
+ *   bytes; its contents on entry are ignored and on exit are unspecified. */
+int gpkv_paged_attention_decode(float* out, const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, int32_t batch,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len,
+                                float scale, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Quest block metadata ([ASC] "Quest Sparse Attention": blocks are scored at low
+ * cost; tokens past the context are skipped). For every sequence b and logical
+ * block lb < ceil(context_lens[b] / block_size) -- only the last one when
+ * last_block_only != 0 -- with pb = block_tables[b, lb] and
+ * n = min(block_size, context_lens[b] - lb * block_size) valid rows:
+ *   key_min[pb, g, c] = min over rows t < n of key_cache[pb, t, g, c]
+ *   key_max[pb, g, c] = max over rows t < n of key_cache[pb, t, g, c]
+ * key_min, key_max: [num_blocks, num_kv_heads, head_dim] bf16, written only at
+ *   referenced blocks (the rest keep their contents). Results are exact (they are
+ *   input values). A physical block referenced by two sequences is a
+ *   precondition violation. */
+int gpkv_quest_block_metadata(void* key_min, void* key_max, const void* key_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t batch, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                              int32_t last_block_only, void* stream);
+
+/* Bytes of workspace gpkv_quest_select_topk needs (per-block scores in float64). */
+size_t gpkv_quest_select_workspace_bytes(int32_t batch, int32_t num_kv_heads,
+                                         int32_t max_blocks_per_seq);
+
+/* Quest block scoring and Top-K selection ([ASC] "Quest Sparse Attention").
+ * For each (b, KV head g) and each logical block lb < nb_b = ceil(ctx_b / bs):
+ *   score(lb) = sum over the group's query heads h and channels c of
+ *               max(q[b,h,c] * key_min[pb,g,c], q[b,h,c] * key_max[pb,g,c])
+ * computed in float64 (bf16 products are exact; the sum is rounded in float64).
+ * The min(topk_blocks, nb_b) highest-scoring blocks are kept (equal scores: the
+ * lower logical index wins) and written in ascending order of logical index,
+ * padded with -1 up to topk_blocks.
+ * topk_indices: [batch, num_kv_heads, topk_blocks] int32 (written).
+ * key_min, key_max: as produced by gpkv_quest_block_metadata.
+ * topk_blocks >= 1. */
+int gpkv_quest_select_topk(int32_t* topk_indices, const void* query, const void* key_min,
+                           const void* key_max, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, int32_t topk_blocks, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gpkv_sparse_paged_attention_decode needs. */
+size_t gpkv_sparse_attention_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t topk_blocks);
+
+/* Quest sparse paged attention ([ASC] "Quest Sparse Attention", "Sparse precision").
+ * Exact softmax attention of every query head of group g over only the tokens of
+ * the logical blocks listed in topk_indices[b, g, :] (tokens >= context_lens[b]
+ * masked). Entries equal to -1 (or outside [0, nb_b)) are ignored; listing a
+ * block twice is a precondition violation. Output as in
+ * gpkv_paged_attention_decode (zero row when no token is selected).
+ * topk_indices: [batch, num_kv_heads, topk_blocks] int32 logical block ids. */
+int gpkv_sparse_paged_attention_decode(float* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens,
+                                       const int32_t* topk_indices, int32_t batch,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int64_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_context_len, int32_t topk_blocks,
+                                       float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* Static description of a status code. */
+const char* gpkv_status_string(int status);
+
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char* gpkv_last_error_message(void);
+
+/* Tokens per split-KV work unit the attention calls pick for these sizes
+ * (reported by benchmarks; the same value sizes the workspace). */
+int32_t gpkv_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t span_tokens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPKV_H_ */

@@ -1,0 +1,98 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host-side argument checks return the documented status without launching."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from gqa_paged_kv_amd import _lib
+    from gqa_paged_kv_amd import build as b
+    srcs = [os.path.join(b.CSRC, s) for s in b.SOURCES] + [os.path.join(b.CSRC, "gpkv_internal.h"),
+                                                          os.path.join(b.INCLUDE, "gpkv.h")]
+    if not os.path.exists(_lib.LIB_PATH) or os.path.getmtime(_lib.LIB_PATH) < max(map(os.path.getmtime, srcs)):
+        b.build()
+    return _lib.lib()
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "gpkv.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(gpkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    from gqa_paged_kv_amd._lib import SIGNATURES
+    names = declared_symbols()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(SIGNATURES) == names
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert L.gpkv_status_string(st)
+    assert L.gpkv_status_string(7) == b"unknown status"
+
+
+ARGS = dict(B=2, Hq=4, Hkv=1, D=64, bs=16, NB=16, MB=5, mcl=80)
+
+
+def _dense(L, **o):
+    a = {**ARGS, **o}
+    ws = o.get("ws", 1 << 40)
+    return L.gpkv_paged_attention_decode(
+        o.get("out", 8), 8, 8, 8, 8, 8, a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"],
+        a["MB"], a["mcl"], 0.125, o.get("wsp", 8), ws, None)
+
+
+@pytest.mark.parametrize("override,status", [
+    (dict(out=None), -1),
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(Hq=34, Hkv=2), -3),       # group 17 > 16
+    (dict(D=96), -3),
+    (dict(bs=8), -3),
+    (dict(bs=24), -3),
+    (dict(mcl=81), -2),             # > max_blocks * block_size
+    (dict(B=-1), -2),
+    (dict(ws=16), -4),
+    (dict(wsp=None), -4),
+])
+def test_dense_argument_checks(L, override, status):
+    assert _dense(L, **override) == status
+    assert L.gpkv_last_error_message()
+
+
+def test_other_entry_points_checks(L):
+    # reshape_and_cache: null pointers, bad head_dim; zero tokens is a no-op.
+    assert L.gpkv_reshape_and_cache(None, 8, 8, 8, 8, 2, 1, 64, 16, 16, None) == -1
+    assert L.gpkv_reshape_and_cache(8, 8, 8, 8, 8, 2, 1, 80, 16, 16, None) == -3
+    assert L.gpkv_reshape_and_cache(None, None, None, None, None, 0, 1, 64, 16, 16, None) == 0
+    # metadata
+    assert L.gpkv_quest_block_metadata(None, 8, 8, 8, 8, 2, 1, 64, 16, 16, 5, 80, 0, None) == -1
+    assert L.gpkv_quest_block_metadata(8, 8, 8, 8, 8, 2, 1, 64, 16, 16, 4, 80, 0, None) == -2
+    # top-k: topk_blocks < 1, workspace too small, group too large
+    assert L.gpkv_quest_select_topk(8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 0, 8, 1 << 30, None) == -2
+    assert L.gpkv_quest_select_topk(8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 3, 8, 8, None) == -4
+    assert L.gpkv_quest_select_topk(8, 8, 8, 8, 8, 8, 2, 40, 2, 64, 16, 16, 5, 80, 3, 8, 1 << 30, None) == -3
+    # sparse: null topk, topk_blocks < 1
+    assert L.gpkv_sparse_paged_attention_decode(8, 8, 8, 8, 8, 8, None, 2, 4, 1, 64, 16, 16, 5, 80, 3,
+                                                0.1, 8, 1 << 30, None) == -1
+    assert L.gpkv_sparse_paged_attention_decode(8, 8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 0,
+                                                0.1, 8, 1 << 30, None) == -2
+
+
+def test_workspace_queries(L):
+    assert L.gpkv_paged_attention_workspace_bytes(2, 4, 1, 64, 16, 80) > 0
+    assert L.gpkv_paged_attention_workspace_bytes(2, 4, 1, 96, 16, 80) == 0
+    assert L.gpkv_sparse_attention_workspace_bytes(2, 4, 1, 64, 16, 0) == 0
+    assert L.gpkv_quest_select_workspace_bytes(64, 4, 1024) == 64 * 4 * 1024 * 8
+    # split size: a multiple of 128 in [128, 1024]; enough units for the 8K-average workload
+    t = L.gpkv_split_tokens(64, 4, 14998)
+    assert t % 128 == 0 and 128 <= t <= 1024
+    assert 64 * 4 * -(-14998 // t) >= 4096

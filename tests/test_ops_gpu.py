@@ -1,0 +1,360 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded inputs.
+
+Bars: cache writes, Quest metadata and Top-K indices bit-exact; attention outputs
+within max-abs 2e-3 of the float64 oracle (bf16 inputs, fp32 accumulation).
+Full-size configs compare every output of the cheap ops and a sample of
+sequences (longest, shortest, seeded random) for attention, in the launch
+configuration the benchmark uses.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_paged_kv_amd as gp
+import oracle
+import workloads
+from gpu_util import BF, Dev, bits, max_abs, sample_seqs, to_dev, workload
+
+pytestmark = pytest.mark.gpu
+ATOL = 2e-3
+
+
+# ---------------------------------------------------------------------------
+# ReshapeAndCache
+# ---------------------------------------------------------------------------
+
+def _check_write(w):
+    d = Dev(w)
+    gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
+    torch.cuda.synchronize()
+    ek, ev = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                      w.slot_mapping, w.block_size)
+    assert np.array_equal(bits(d.kc), ek), "key cache differs from the oracle"
+    assert np.array_equal(bits(d.vc), ev), "value cache differs from the oracle"
+    return d
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 5])
+def test_reshape_and_cache_config(config):
+    _check_write(workload(config))
+
+
+@pytest.mark.parametrize("seed,Hkv,D,bs", [(101, 1, 64, 16), (102, 4, 128, 32), (103, 8, 128, 128),
+                                           (104, 2, 64, 64)])
+def test_reshape_and_cache_random(seed, Hkv, D, bs):
+    w = workloads.random_case(seed, batch=9, num_q_heads=Hkv * 2, num_kv_heads=Hkv, head_dim=D,
+                              block_size=bs, context_lens=[1, 5, 16, 17, 40, 64, 100, 129, 300],
+                              num_tokens=9, neg_slots=3)
+    _check_write(w)
+
+
+def test_reshape_and_cache_all_negative_and_empty():
+    w = workloads.make(1)
+    d = Dev(w)
+    before_k, before_v = bits(d.kc), bits(d.vc)
+    gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, torch.full_like(d.slots, -1))
+    empty_k = torch.empty((0, 1, 64), dtype=BF, device="cuda")
+    gp.reshape_and_cache(empty_k, empty_k, d.kc, d.vc, torch.empty((0,), dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d.kc), before_k) and np.array_equal(bits(d.vc), before_v)
+
+
+# ---------------------------------------------------------------------------
+# Dense attention
+# ---------------------------------------------------------------------------
+
+def _dense(d, w, **kw):
+    return gp.paged_attention_decode(d.q, d.kc, d.vc, d.bt, d.ctx, max_context_len=w.max_context_len,
+                                     scale=float(w.scale), **kw)
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+def test_dense_config(config):
+    w = workload(config)
+    d = Dev(w)
+    if w.num_tokens:   # the step writes the new token first (context_lens include it)
+        gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
+        kc, vc = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                          w.slot_mapping, w.block_size)
+    else:
+        kc, vc = w.key_cache, w.value_cache
+    out = _dense(d, w).cpu().numpy()
+    seqs = list(range(w.batch)) if w.batch <= 4 else sample_seqs(w)
+    ref = oracle.paged_attention_decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                        seqs=seqs)
+    err = max_abs(out[seqs], ref[seqs])
+    print(f"config {config}: dense max-abs {err:.3e} over sequences {seqs}")
+    assert err <= ATOL
+    assert np.isfinite(out).all()
+
+
+DENSE_CASES = [
+    # seed, Hq, Hkv, D, bs, context lengths
+    (201, 4, 1, 64, 16, [0, 1, 15, 16, 17, 33]),
+    (202, 28, 4, 128, 16, [31, 32, 33, 500, 1023, 1025]),
+    (203, 16, 16, 128, 32, [7, 64, 65, 300]),             # G = 1 (MHA)
+    (204, 16, 1, 128, 64, [129, 2047, 4100]),              # G = 16 (largest group)
+    (205, 64, 8, 128, 128, [1, 127, 128, 129, 3000, 5000]),
+    (206, 14, 2, 64, 128, [250, 1, 700]),
+    (207, 12, 3, 64, 32, [513, 514, 96]),
+]
+
+
+@pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx", DENSE_CASES)
+def test_dense_random(seed, Hq, Hkv, D, bs, ctx):
+    w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                              block_size=bs, context_lens=ctx)
+    d = Dev(w)
+    out = _dense(d, w).cpu().numpy()
+    ref = oracle.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                        w.context_lens, w.scale)
+    err = max_abs(out, ref)
+    print(f"seed {seed}: max-abs {err:.3e}")
+    assert err <= ATOL
+    for b, L in enumerate(ctx):
+        if L == 0:
+            assert (out[b] == 0).all(), "empty context -> zero row"
+
+
+@pytest.mark.parametrize("split", [128, 256, 512, 1024, 2048])
+def test_dense_split_sizes_agree(split, monkeypatch):
+    """Any split partition gives the same attention (the combine identity)."""
+    monkeypatch.setenv("GPKV_SPLIT_TOKENS", str(split))
+    assert gp.split_tokens(3, 4, 4000) == split
+    w = workloads.random_case(210, batch=3, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                              block_size=16, context_lens=[4000, 2500, 129])
+    d = Dev(w)
+    ref = oracle.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                        w.context_lens, w.scale)
+    out = _dense(d, w).cpu().numpy()
+    assert max_abs(out, ref) <= ATOL
+    sel = np.full((3, 4, 250), -1, np.int32)
+    for b, nb in enumerate(w.nblocks().tolist()):
+        sel[b, :, :nb] = np.arange(nb)
+    sp = _sparse(d, w, to_dev(sel, torch.int32)).cpu().numpy()
+    assert max_abs(sp, ref) <= ATOL
+
+
+def test_dense_invariants_permuted_poison_deterministic():
+    w = workloads.random_case(220, batch=4, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                              block_size=16, context_lens=[700, 37, 1600, 16], slack=9)
+    d = Dev(w)
+    out1 = _dense(d, w)
+    out2 = _dense(d, w)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2), "two runs differ bitwise"
+    # NaN in every row outside the contexts (incl. unreferenced blocks) changes nothing.
+    kc = w.key_cache.copy()
+    vc = w.value_cache.copy()
+    live = np.zeros(kc.shape[:2], dtype=bool)
+    for b in range(w.batch):
+        for t in range(int(w.context_lens[b])):
+            live[int(w.block_tables[b, t // 16]), t % 16] = True
+    kc[~live] = 0x7FC0
+    vc[~live] = 0x7FC0
+    d2 = Dev(w)
+    d2.kc, d2.vc = to_dev(kc, BF), to_dev(vc, BF)
+    out3 = _dense(d2, w)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out3), "NaN outside the context leaked into the output"
+    # Moving every physical block (data copied along) leaves the output unchanged.
+    perm = np.random.default_rng(7).permutation(w.num_blocks)
+    kp = np.empty_like(w.key_cache)
+    vp = np.empty_like(w.value_cache)
+    kp[perm] = w.key_cache
+    vp[perm] = w.value_cache
+    btp = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    d3 = Dev(w)
+    d3.kc, d3.vc, d3.bt = to_dev(kp, BF), to_dev(vp, BF), to_dev(btp, torch.int32)
+    out4 = _dense(d3, w)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out4), "permuted block table changed the output"
+
+
+# ---------------------------------------------------------------------------
+# Quest metadata, Top-K, sparse attention
+# ---------------------------------------------------------------------------
+
+SENTINEL = 0x1234
+
+
+def _meta(d, w, last_only=False, kmin=None, kmax=None):
+    if kmin is None:
+        kmin = to_dev(np.full((w.num_blocks, w.num_kv_heads, w.head_dim), SENTINEL, np.uint16), BF)
+        kmax = to_dev(np.full((w.num_blocks, w.num_kv_heads, w.head_dim), SENTINEL, np.uint16), BF)
+    gp.quest_block_metadata(d.kc, d.bt, d.ctx, kmin, kmax, max_context_len=w.max_context_len,
+                            last_block_only=last_only)
+    return kmin, kmax
+
+
+def _meta_equal(got, exp):
+    """Bitwise, except +0 and -0 count as equal."""
+    g = got.copy()
+    e = exp.copy()
+    g[g == 0x8000] = 0
+    e[e == 0x8000] = 0
+    return np.array_equal(g, e)
+
+
+@pytest.mark.parametrize("config", [1, 3, 4, 5])
+def test_quest_metadata_config(config):
+    w = workload(config)
+    d = Dev(w)
+    kmin, kmax = _meta(d, w)
+    torch.cuda.synchronize()
+    base = np.full((w.num_blocks, w.num_kv_heads, w.head_dim), SENTINEL, np.uint16)
+    emin, emax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens,
+                                             w.block_size, key_min=base, key_max=base)
+    assert _meta_equal(bits(kmin), emin) and _meta_equal(bits(kmax), emax)
+
+
+def test_quest_metadata_step_after_write():
+    """Write the new tokens, refresh only each sequence's last block."""
+    w = workloads.random_case(301, batch=6, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                              block_size=16, context_lens=[1, 16, 17, 100, 250, 33],
+                              num_tokens=6, neg_slots=1)
+    d = Dev(w)
+    base = np.full((w.num_blocks, w.num_kv_heads, w.head_dim), SENTINEL, np.uint16)
+    kmin, kmax = to_dev(base, BF), to_dev(base, BF)
+    gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
+    _meta(d, w, last_only=True, kmin=kmin, kmax=kmax)
+    torch.cuda.synchronize()
+    kc, _ = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                     w.slot_mapping, w.block_size)
+    emin, emax = oracle.quest_block_metadata(kc, w.block_tables, w.context_lens, w.block_size,
+                                             last_block_only=True, key_min=base, key_max=base)
+    assert _meta_equal(bits(kmin), emin) and _meta_equal(bits(kmax), emax)
+
+
+def _topk_case(w, K):
+    d = Dev(w)
+    kmin, kmax = _meta(d, w)
+    sel = gp.quest_select_topk(d.q, kmin, kmax, d.bt, d.ctx, block_size=w.block_size,
+                               topk_blocks=K, max_context_len=w.max_context_len)
+    torch.cuda.synchronize()
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, w.block_size)
+    exp = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens,
+                                   w.block_size, K)
+    return d, sel.cpu().numpy(), exp
+
+
+@pytest.mark.parametrize("config,K", [(1, 3), (1, 5), (3, 64), (4, 256), (5, 32)])
+def test_quest_topk_config(config, K):
+    w = workload(config)
+    _, got, exp = _topk_case(w, K)
+    mism = int((got != exp).any(axis=2).sum())
+    assert mism == 0, f"{mism} (b, g) rows differ from the oracle"
+
+
+@pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx,K", [
+    (311, 8, 2, 64, 16, [1, 100, 16, 1000, 4000], 7),
+    (312, 28, 4, 128, 32, [2000, 33, 640], 1),
+    (313, 64, 8, 128, 128, [129, 9000, 256], 5),
+    (314, 16, 16, 128, 64, [3000], 40),
+])
+def test_quest_topk_random(seed, Hq, Hkv, D, bs, ctx, K):
+    w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                              block_size=bs, context_lens=ctx)
+    _, got, exp = _topk_case(w, K)
+    assert np.array_equal(got, exp)
+
+
+def test_quest_topk_tie_goes_to_lower_block():
+    w = workloads.random_case(320, batch=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
+                              block_size=16, context_lens=[640])
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+    s = oracle.quest_block_scores(w.query, omin, omax, w.block_tables, w.context_lens, 16, 0, 0)
+    order = np.argsort(-s, kind="stable")
+    a = int(order[0])
+    later = max(lb for lb in range(40) if lb != a)
+    kc = w.key_cache.copy()
+    kc[int(w.block_tables[0, later])] = kc[int(w.block_tables[0, a])]
+    w.key_cache = kc
+    for K in (1, 2, 3):
+        _, got, exp = _topk_case(w, K)
+        assert np.array_equal(got, exp), K
+        assert min(a, later) in got[0, 0].tolist()
+
+
+def _sparse(d, w, sel):
+    return gp.sparse_paged_attention_decode(d.q, d.kc, d.vc, d.bt, d.ctx, sel,
+                                            max_context_len=w.max_context_len,
+                                            scale=float(w.scale))
+
+
+@pytest.mark.parametrize("config,K", [(1, 3), (1, 5), (3, 64), (4, 256), (5, 32)])
+def test_sparse_config_fixed_selection(config, K):
+    """Sparse kernel judged with the selection fixed to the oracle's Top-K."""
+    w = workload(config)
+    d = Dev(w)
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, w.block_size)
+    sel = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens,
+                                   w.block_size, K)
+    out = _sparse(d, w, to_dev(sel, torch.int32)).cpu().numpy()
+    seqs = list(range(w.batch)) if w.batch <= 4 else sample_seqs(w)
+    ref = oracle.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                               w.context_lens, sel, w.scale, seqs=seqs)
+    err = max_abs(out[seqs], ref[seqs])
+    print(f"config {config} K={K}: sparse max-abs {err:.3e}")
+    assert err <= ATOL
+
+
+def test_sparse_all_blocks_equals_dense_and_handles_holes():
+    w = workloads.random_case(330, batch=3, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                              block_size=16, context_lens=[300, 17, 1000])
+    d = Dev(w)
+    nb = w.nblocks()
+    K = int(nb.max()) + 3
+    sel = np.full((3, 4, K), -1, np.int32)
+    for b in range(3):
+        sel[b, :, :nb[b]] = np.arange(nb[b])
+    dense = _dense(d, w).cpu().numpy()
+    sp = _sparse(d, w, to_dev(sel, torch.int32)).cpu().numpy()
+    ref = oracle.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                        w.context_lens, w.scale)
+    assert max_abs(sp, ref) <= ATOL and max_abs(dense, ref) <= ATOL
+    # -1 holes and unsorted ids in the middle of the list, per KV head.
+    sel2 = np.full((3, 4, 6), -1, np.int32)
+    sel2[0, 0] = [5, -1, 2, 18, -1, 0]
+    sel2[0, 1] = [-1, -1, -1, -1, -1, 1]
+    sel2[1, 2] = [1, 0, -1, -1, -1, -1]
+    sel2[2, 3] = [62, 61, 3, -1, 9, 10]
+    out = _sparse(d, w, to_dev(sel2, torch.int32)).cpu().numpy()
+    ref2 = oracle.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache,
+                                                w.block_tables, w.context_lens, sel2, w.scale)
+    assert max_abs(out, ref2) <= ATOL
+    assert (out[1, :8] == 0).all(), "no block selected -> zero rows"
+
+
+# ---------------------------------------------------------------------------
+# Composed Quest step, one stage swapped at a time
+# ---------------------------------------------------------------------------
+
+def test_composed_quest_step_matches_oracle_chain():
+    w = workloads.random_case(340, batch=5, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                              block_size=16, context_lens=[2000, 700, 16, 1234, 3001],
+                              num_tokens=5, neg_slots=1)
+    K = 24
+    d = Dev(w)
+    base = np.zeros((w.num_blocks, 4, 128), np.uint16)
+    kmin, kmax = to_dev(base, BF), to_dev(base, BF)
+    _meta(d, w, kmin=kmin, kmax=kmax)                       # prefill-time full build
+    gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)  # decode step: write
+    _meta(d, w, last_only=True, kmin=kmin, kmax=kmax)      # refresh the last blocks
+    sel = gp.quest_select_topk(d.q, kmin, kmax, d.bt, d.ctx, block_size=16, topk_blocks=K,
+                               max_context_len=w.max_context_len)
+    out = _sparse(d, w, sel)
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                      w.slot_mapping, 16)
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16,
+                                             key_min=base, key_max=base)
+    omin, omax = oracle.quest_block_metadata(kc, w.block_tables, w.context_lens, 16,
+                                             last_block_only=True, key_min=omin, key_max=omax)
+    osel = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens, 16, K)
+    assert np.array_equal(sel.cpu().numpy(), osel)
+    ref = oracle.sparse_paged_attention_decode(w.query, kc, vc, w.block_tables, w.context_lens,
+                                               osel, w.scale)
+    assert max_abs(out.cpu().numpy(), ref) <= ATOL
