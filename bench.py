@@ -1,0 +1,333 @@
+"""Decode-step benchmark of the paged GQA attention library on one MI355X.
+
+One step = the whole hot path once over one batch of synthetic input:
+  reshape_and_cache (one new token per sequence)
+  -> paged_attention_decode (dense, split-KV + combine)
+  -> quest_block_metadata (last block of each sequence)
+  -> quest_select_topk -> sparse_paged_attention_decode.
+Inputs are resident in HBM before timing. Before every timed step a 1 GiB buffer
+is written so that no KV bytes survive in the 256 MB Infinity Cache; the
+per-call durations come from HIP events on the launch stream and exclude that
+flush. The value reported is the step's algorithmic KV/metadata bytes divided by
+the step time (GB/s). The full metadata rebuild is a prefill-time cost and is
+reported separately, outside the step.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT_CONFIG = 3
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = "attn_split_dense_long8k_traffic.md"
+DOMINANT_KERNEL = "attn_split_kernel<128, false>"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for PMC byte calibration)")
+    ap.add_argument("--details", action="store_true", help="print per-call timings to stderr")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("paged_attention.hip", "gpkv_internal.h"):
+        with open(os.path.join(ROOT, "gqa_paged_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(cfg: int):
+    """HBM bytes per launch of the dominant kernel from the committed PMC summary,
+    or None when the summary is missing, for another workload, or the kernel source
+    changed since the counters were taken."""
+    path = os.path.join(PROFILES, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_cfg = re.search(r"workload_config:\s*(\d+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_cfg and m_bytes):
+        return None
+    if m_hash.group(1) != kernel_source_hash() or int(m_cfg.group(1)) != cfg:
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, target_s: float):
+    """Time the CPU oracle on the first sequences of the same workload until about
+    target_s seconds of work; report algorithmic GB/s of that sample."""
+    import numpy as np
+    import oracle
+    from gqa_paged_kv_amd import roofline as R
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    K = w.topk_list[0] if w.topk_list else None
+    kc, vc = w.key_cache, w.value_cache
+    kmin = kmax = None
+    if K:   # prefill-time metadata of every block (outside the step, as on the GPU)
+        kmin, kmax = oracle.quest_block_metadata(kc, w.block_tables, w.context_lens, w.block_size)
+    t0 = time.perf_counter()
+    total_bytes = 0
+    seqs_done = 0
+    if w.num_tokens:
+        kc, vc = oracle.reshape_and_cache(kc, vc, w.new_key, w.new_value, w.slot_mapping, w.block_size)
+        total_bytes += R.write_bytes(w.slot_mapping, w.num_blocks, w.block_size, w.num_kv_heads,
+                                     w.head_dim)
+    for b in range(w.batch):
+        ctx1 = w.context_lens[b:b + 1]
+        bt1 = w.block_tables[b:b + 1]
+        oracle.paged_attention_decode(w.query[b:b + 1], kc, vc, bt1, ctx1, w.scale)
+        total_bytes += R.dense_attention_bytes(ctx1, w.num_kv_heads, w.head_dim)
+        if K:
+            kmin, kmax = oracle.quest_block_metadata(kc, bt1, ctx1, w.block_size,
+                                                     last_block_only=True, key_min=kmin, key_max=kmax)
+            sel = oracle.quest_select_topk(w.query[b:b + 1], kmin, kmax, bt1, ctx1, w.block_size, K)
+            oracle.sparse_paged_attention_decode(w.query[b:b + 1], kc, vc, bt1, ctx1, sel, w.scale)
+            total_bytes += (R.metadata_step_bytes(ctx1, w.block_size, w.num_kv_heads, w.head_dim)
+                            + R.select_bytes(ctx1, w.block_size, w.num_kv_heads, w.head_dim)
+                            + R.sparse_attention_bytes(sel, ctx1, w.block_size, w.head_dim))
+        seqs_done += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"full decode step (write + dense + Quest) of the first {seqs_done} of "
+                      f"{w.batch} sequences of the same workload, float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (got --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gqa_paged_kv_amd as gp
+    import workloads
+    from gqa_paged_kv_amd import roofline as R
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = workloads.make(args.config)
+    print(f"[bench] workload {w.name}: {workloads.shape_summary(w)}", file=sys.stderr, flush=True)
+
+    def dev(a, dtype):
+        a = np.ascontiguousarray(a)
+        if dtype == torch.bfloat16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).to(dtype).cuda()
+
+    bf = torch.bfloat16
+    kc, vc = dev(w.key_cache, bf), dev(w.value_cache, bf)
+    q = dev(w.query, bf)
+    bt, ctx = dev(w.block_tables, torch.int32), dev(w.context_lens, torch.int32)
+    nk, nv = dev(w.new_key, bf), dev(w.new_value, bf)
+    slots = dev(w.slot_mapping, torch.int64)
+    B, Hq, Hkv, D, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    mcl = w.max_context_len
+    K = w.topk_list[0] if w.topk_list else 0
+    scale = float(w.scale)
+
+    out_d = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    out_s = torch.empty_like(out_d)
+    ws_d = torch.empty(gp.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl), dtype=torch.uint8,
+                       device="cuda")
+    kmin = torch.zeros((w.num_blocks, Hkv, D), dtype=bf, device="cuda")
+    kmax = torch.zeros_like(kmin)
+    if K:
+        ws_sel = torch.empty(gp.quest_select_workspace_bytes(B, Hkv, w.max_blocks_per_seq),
+                             dtype=torch.uint8, device="cuda")
+        ws_sp = torch.empty(gp.sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K),
+                            dtype=torch.uint8, device="cuda")
+        sel = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda")
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    calls = ["reshape_and_cache", "paged_attention_decode"]
+    if K:
+        calls += ["quest_block_metadata", "quest_select_topk", "sparse_paged_attention_decode"]
+
+    def run_call(name):
+        if name == "reshape_and_cache":
+            if w.num_tokens:
+                gp.reshape_and_cache(nk, nv, kc, vc, slots)
+        elif name == "paged_attention_decode":
+            gp.paged_attention_decode(q, kc, vc, bt, ctx, max_context_len=mcl, scale=scale,
+                                      out=out_d, workspace=ws_d)
+        elif name == "quest_block_metadata":
+            gp.quest_block_metadata(kc, bt, ctx, kmin, kmax, max_context_len=mcl, last_block_only=True)
+        elif name == "quest_select_topk":
+            gp.quest_select_topk(q, kmin, kmax, bt, ctx, block_size=bs, topk_blocks=K,
+                                 max_context_len=mcl, out=sel, workspace=ws_sel)
+        elif name == "sparse_paged_attention_decode":
+            gp.sparse_paged_attention_decode(q, kc, vc, bt, ctx, sel, max_context_len=mcl,
+                                             scale=scale, out=out_s, workspace=ws_sp)
+
+    def step(events=None):
+        for i, name in enumerate(calls):
+            if events is not None:
+                events[i].record(stream)
+            run_call(name)
+        if events is not None:
+            events[len(calls)].record(stream)
+
+    # Prefill-time work: full metadata build (timed once, outside the step).
+    t_full = None
+    if K:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        flush.fill_(1)
+        e0.record(stream)
+        gp.quest_block_metadata(kc, bt, ctx, kmin, kmax, max_context_len=mcl, last_block_only=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_full = e0.elapsed_time(e1) * 1e3
+
+    # Warm-up: at least `warmup` steps and at least 25 ms of work.
+    torch.cuda.synchronize()
+    tw = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or (time.perf_counter() - tw) < 0.025:
+        step()
+        n_warm += 1
+        if n_warm % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    print(f"[bench] warm-up done: {n_warm} steps", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(3)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        flush.fill_(k & 0xFF)
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    per_call = {name: np.array([evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)])
+                for i, name in enumerate(calls)}
+    step_us = np.array([evs[k][0].elapsed_time(evs[k][len(calls)]) * 1e3 for k in range(args.steps)])
+
+    # Algorithmic bytes of one step.
+    sel_host = sel.cpu().numpy() if K else None
+    by = {
+        "reshape_and_cache": R.write_bytes(w.slot_mapping, w.num_blocks, bs, Hkv, D),
+        "paged_attention_decode": R.dense_attention_bytes(w.context_lens, Hkv, D),
+    }
+    if K:
+        by["quest_block_metadata"] = R.metadata_step_bytes(w.context_lens, bs, Hkv, D)
+        by["quest_select_topk"] = R.select_bytes(w.context_lens, bs, Hkv, D)
+        by["sparse_paged_attention_decode"] = R.sparse_attention_bytes(sel_host, w.context_lens, bs, D)
+    step_bytes = sum(by.values())
+    mean_step = float(step_us.mean())
+    value = step_bytes / (mean_step * 1e-6) / 1e9
+
+    calls_out = {}
+    for name in calls:
+        t = per_call[name]
+        calls_out[name] = {
+            "us_mean": round(float(t.mean()), 2), "us_median": round(float(np.median(t)), 2),
+            "us_min": round(float(t.min()), 2), "algorithmic_bytes": int(by[name]),
+            "gbps": round(by[name] / (t.mean() * 1e-6) / 1e9, 1) if by[name] else 0.0,
+        }
+        calls_out[name]["pct_of_peak"] = round(100 * calls_out[name]["gbps"] / R.MI355X_HBM_GBPS, 1)
+
+    dense_t = per_call["paged_attention_decode"].mean()
+    achieved = by["paged_attention_decode"] / (dense_t * 1e-6) / 1e9
+    traffic = committed_traffic(args.config)
+    quest_us = sum(calls_out[n]["us_mean"] for n in calls[2:]) if K else None
+
+    line = {
+        "metric": "paged decode attention KV-read HBM GB/s over one decode step (write + dense + Quest)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_step / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": bs, "sum_context": int(w.context_lens.sum()),
+                   "max_context_len": mcl, "topk_blocks": K, "parallelism": "single-gpu",
+                   "split_tokens_dense": gp.split_tokens(B, Hkv, mcl)},
+        "pct_of_peak": round(100 * value / R.MI355X_HBM_GBPS, 1),
+        "us_per_step": round(mean_step, 2),
+        "us_per_step_median": round(float(np.median(step_us)), 2),
+        "dense_step_us": round(calls_out["reshape_and_cache"]["us_mean"]
+                               + calls_out["paged_attention_decode"]["us_mean"], 2),
+        "quest_step_us": round(quest_us, 2) if quest_us is not None else None,
+        "quest_full_metadata_rebuild_us": round(t_full, 2) if t_full is not None else None,
+        "calls": calls_out,
+        "step_algorithmic_bytes": int(step_bytes),
+        "wall_s_timed_region_incl_flush": round(wall, 4),
+        "flush_mib_between_steps": args.flush_mib,
+        "roofline": {
+            "bound": "hbm", "kernel": f"paged_attention_decode ({DOMINANT_KERNEL} + combine)",
+            "achieved": round(achieved, 1), "peak": R.MI355X_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / R.MI355X_HBM_GBPS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(by["paged_attention_decode"]),
+            "launch_us_mean": round(float(dense_t), 2),
+        },
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "gpu": torch.cuda.get_device_name(0),
+        "torch": torch.__version__, "hip": torch.version.hip,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    if args.details:
+        print(json.dumps(calls_out, indent=1), file=sys.stderr)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
