@@ -43,12 +43,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
 }
 
+// Cache-policy bits of a buffer load on gfx950: NT (non-temporal) marks data that
+// is streamed once. The KV cache is read exactly once per decode step, and NT loads
+// sustain far more HBM bandwidth than default-policy loads on MI355X.
+constexpr int kLoadNT = 2;
+
 // Buffer loads: an offset at or past `bytes` of the descriptor returns zeros.
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadNT);
 }
 __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLoadNT);
 }
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
