@@ -11,12 +11,15 @@
 //
 // Work decomposition (MI355X-first)
 // ---------------------------------
-// A workgroup of 4 waves owns one (sequence b, KV head g, split) unit: a range of
-// `split_tokens` tokens (dense) or of selected-block tokens (sparse). Its waves
-// take interleaved 32-token tiles; each tile is two 16-token sub-tiles, and a
-// 16-token sub-tile always lies inside one physical block (block_size is a
-// multiple of 16), so its block id is wave-uniform and the KV rows it needs come
-// from one contiguous region.
+// A workgroup owns one (sequence b, split) unit: a range of `split_tokens` tokens
+// (dense) or of selected-block tokens (sparse), for every KV head. Its waves each
+// take one KV head (wave w: heads w, w + W, ...), so the waves stream the same
+// token rows at the same time: on MI355X whole cache rows (all KV heads of a
+// token) then come from HBM together, which sustains more bandwidth than
+// scattering the heads of a row over different workgroups. A wave walks the
+// split's 32-token tiles; each tile is two 16-token sub-tiles, and a 16-token
+// sub-tile always lies inside one physical block (block_size is a multiple of
+// 16), so its block id is wave-uniform and its rows are one contiguous region.
 //
 // The group's G query heads are padded to 16 and both contractions run on MFMA
 // (v_mfma_f32_16x16x32_bf16) with fp32 accumulation:
@@ -35,17 +38,17 @@
 // weights is the ~2^-16 relative truncation of the low part.
 // Masking uses raw buffer loads whose descriptor ends after the sub-tile's valid
 // rows: rows past the context read as zeros (never NaN), and their scores are
-// set to -inf. The KV stream never goes through LDS; LDS holds only the split's
-// block-table entries and the 4-wave merge at the end.
+// set to -inf. KV loads are non-temporal (each byte is read once per step) and
+// never pass through LDS; LDS holds only the split's block-table entries.
 #include <math.h>
 
 #include "gpkv_internal.h"
 
 namespace gpkv {
 
-constexpr int kWaves = 4;
+constexpr int kMaxWaves = 8;            // waves per workgroup (KV heads processed at once)
 constexpr int kMaxSplitTokens = 2048;
-constexpr int kMaxEntries = kMaxSplitTokens / 16;
+constexpr int kMaxTable = 2048;         // block-table entries staged in LDS per workgroup
 
 struct SplitParams {
   float* part_o;             // [B, H_kv, S, G, D] fp32, each split's normalised output
@@ -81,21 +84,25 @@ struct VecT<64> {
 };
 
 template <int D, bool SPARSE>
-__global__ __launch_bounds__(256) void attn_split_kernel(const SplitParams p) {
+__global__ __launch_bounds__(kMaxWaves * 64) void attn_split_kernel(const SplitParams p) {
   constexpr int KSTEPS = D / 32;  // k-steps of the q.k contraction
   constexpr int CPL = D / 16;     // channels per lane in the V^T operand / O^T tiles
   constexpr int VBYTES = CPL * 2;
   typedef typename VecT<D>::type vvec;
 
-  extern __shared__ float smem[];
-  __shared__ int s_pb[kMaxEntries];
-  __shared__ int s_tok0[kMaxEntries];
+  // Block-table entries of the split: entry e covers virtual tokens
+  // [t0 + e*bs, t0 + (e+1)*bs). s_tok0 = logical position of the block's row 0,
+  // or a huge value when the entry selects nothing. Dense: one table shared by all
+  // KV heads; sparse: one table per KV head (the selection is per head).
+  __shared__ int s_pb[kMaxTable];
+  __shared__ int s_tok0[kMaxTable];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int W = blockDim.x >> 6;
   const int wave = uniform(tid >> 6);  // tell the compiler the tile loop is wave-uniform
   const int r = lane & 15, qd = lane >> 4;
-  const int G = p.G, bs = p.bs;
+  const int G = p.G, bs = p.bs, Hkv = p.Hkv;
   int ctx = p.ctx[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);  // memory safety only
   const int nb = (ctx + bs - 1) / bs;
@@ -104,181 +111,204 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const SplitParams p) {
   const int t0 = split * T;
   if (t0 >= span) return;  // dense: past this sequence's context (the combine skips it)
 
-  // Block-table entries of this split: entry e covers virtual tokens
-  // [t0 + e*bs, t0 + (e+1)*bs). s_tok0 = logical position of the block's row 0,
-  // or a huge value when the entry selects nothing.
   const int n_ent = T / bs;
   const int e0 = t0 / bs;
-  for (int e = tid; e < n_ent; e += 256) {
+  const int n_tab = SPARSE ? Hkv * n_ent : n_ent;
+  for (int i = tid; i < n_tab; i += blockDim.x) {
+    const int e = SPARSE ? i % n_ent : i;
     const int ve = e0 + e;
     int lb;
-    if (SPARSE)
-      lb = ve < p.topk_blocks ? p.topk[((size_t)b * p.Hkv + g) * p.topk_blocks + ve] : -1;
-    else
+    if (SPARSE) {
+      const int gh = i / n_ent;
+      lb = ve < p.topk_blocks ? p.topk[((size_t)b * Hkv + gh) * p.topk_blocks + ve] : -1;
+    } else {
       lb = ve;
-    int pb = (lb >= 0 && lb < nb) ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
+    }
+    const int pb = (lb >= 0 && lb < nb) ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
     const bool ok = pb >= 0 && pb < p.NB;
-    s_pb[e] = ok ? pb : 0;
-    s_tok0[e] = ok ? lb * bs : 0x3fffffff;
+    s_pb[i] = ok ? pb : 0;
+    s_tok0[i] = ok ? lb * bs : 0x3fffffff;
   }
   __syncthreads();
 
-  // Q^T operand: lane holds head r's channels 32s + 8qd .. +8 (zero rows past G).
-  u32x4 qf[KSTEPS];
-  if (r < G) {
-    const unsigned short* qrow = p.q + ((size_t)b * p.Hq + (size_t)g * G + r) * D;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qrow + 32 * s + 8 * qd);
-  } else {
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
-  }
-
-  f32x4 oacc[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of head r (base 2), same in its 4 lanes
-  float l_run = 0.f;        // this lane's share of the normaliser
-
-  const unsigned off_k = (unsigned)(r * p.row_bytes + g * D * 2 + qd * 16);
-  const unsigned off_v = (unsigned)(4 * qd * p.row_bytes + g * D * 2 + r * VBYTES);
   const int n_tiles = T / 32;
+  for (int g = wave; g < Hkv; g += W) {
+    const int* tab_pb = s_pb + (SPARSE ? g * n_ent : 0);
+    const int* tab_t0 = s_tok0 + (SPARSE ? g * n_ent : 0);
 
-  for (int k = wave; k < n_tiles; k += kWaves) {
-    int pb[2], nv[2], row0[2];
+    // Q^T operand: lane holds head r's channels 32s + 8qd .. +8 (zero rows past G).
+    u32x4 qf[KSTEPS];
+    if (r < G) {
+      const unsigned short* qrow = p.q + ((size_t)b * p.Hq + (size_t)g * G + r) * D;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int u16 = 16 * (2 * k + sub);
-      const int e = u16 / bs;
-      row0[sub] = u16 & (bs - 1);
-      int n = ctx - (s_tok0[e] + row0[sub]);
-      n = n < 0 ? 0 : (n > 16 ? 16 : n);
-      nv[sub] = uniform(n);
-      pb[sub] = uniform(s_pb[e]);
+      for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qrow + 32 * s + 8 * qd);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
     }
-    if (nv[0] == 0 && nv[1] == 0) {
-      if (SPARSE) continue;  // an unselected / padded entry; later ones may be valid
-      break;                 // dense: everything after this is past the context
-    }
+
+    f32x4 oacc[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;  // running max of head r (base 2), same in its 4 lanes
+    float l_run = 0.f;        // this lane's share of the normaliser
+
+    const unsigned off_k = (unsigned)(r * p.row_bytes + g * D * 2 + qd * 16);
+    const unsigned off_v = (unsigned)(4 * qd * p.row_bytes + g * D * 2 + r * VBYTES);
+
+    // Tile k covers sub-tiles 2k and 2k+1. For each sub-tile: physical block,
+    // first row inside it, number of valid rows (all wave-uniform).
+    auto describe = [&](int k, int* pb, int* row0, int* nv) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int u16 = 16 * (2 * k + sub);
+        const int e = u16 / bs;
+        row0[sub] = u16 & (bs - 1);
+        int n = ctx - (tab_t0[e] + row0[sub]);
+        n = n < 0 ? 0 : (n > 16 ? 16 : n);
+        nv[sub] = uniform(n);
+        pb[sub] = uniform(tab_pb[e]);
+      }
+    };
+    // The next tile with at least one valid row, or n_tiles. Dense tiles are
+    // contiguous from the split start, so the first empty one ends the split;
+    // a sparse list may have unselected entries anywhere.
+    auto next_tile = [&](int k, int* pb, int* row0, int* nv) {
+      for (; k < n_tiles; ++k) {
+        describe(k, pb, row0, nv);
+        if ((nv[0] | nv[1]) != 0) return k;
+        if (!SPARSE) return n_tiles;
+      }
+      return n_tiles;
+    };
 
     u32x4 kf[2][KSTEPS];
     vvec vf[2][4];
+    auto issue_k = [&](const int* pb, const int* row0, const int* nv) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const size_t base = (size_t)pb[sub] * (size_t)p.block_bytes + (size_t)row0[sub] * p.row_bytes;
-      const unsigned bytes = (unsigned)(nv[sub] * p.row_bytes);
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.kc + base, bytes);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vc + base, bytes);
+      for (int sub = 0; sub < 2; ++sub) {
+        const size_t base = (size_t)pb[sub] * (size_t)p.block_bytes + (size_t)row0[sub] * p.row_bytes;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.kc + base, (unsigned)(nv[sub] * p.row_bytes));
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) kf[sub][s] = buf_load16(rk, off_k + 64 * s);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vf[sub][i] = VecT<D>::load(rv, off_v + i * p.row_bytes);
-    }
-
-    // S^T for both sub-tiles.
-    f32x4 sacc[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) sacc[sub] = mfma16x16x32(kf[sub][s], qf[s], sacc[sub]);
-    }
-
-    // Online softmax over this tile for head r (base 2).
-    float sv[8];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = sacc[sub][i] * p.qk_scale_log2;
-        sv[sub * 4 + i] = (4 * qd + i < nv[sub]) ? x : -INFINITY;
+        for (int s = 0; s < KSTEPS; ++s) kf[sub][s] = buf_load16(rk, off_k + 64 * s);
       }
-    float mx = sv[0];
+    };
+    auto issue_v = [&](const int* pb, const int* row0, const int* nv) {
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    float pv[8];
-    float psum = 0.f;
+      for (int sub = 0; sub < 2; ++sub) {
+        const size_t base = (size_t)pb[sub] * (size_t)p.block_bytes + (size_t)row0[sub] * p.row_bytes;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vc + base, (unsigned)(nv[sub] * p.row_bytes));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
-      psum += pv[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) oacc[j] *= alpha;
-    }
+        for (int i = 0; i < 4; ++i) vf[sub][i] = VecT<D>::load(rv, off_v + i * p.row_bytes);
+      }
+    };
 
-    // P^T operand as bf16 hi + lo parts.
-    u32x4 phi, plo;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const unsigned a = __float_as_uint(pv[2 * d]), c = __float_as_uint(pv[2 * d + 1]);
-      phi[d] = pack_hi16(a, c);
-      const float ra = pv[2 * d] - __uint_as_float(a & 0xffff0000u);
-      const float rc = pv[2 * d + 1] - __uint_as_float(c & 0xffff0000u);
-      plo[d] = pack_hi16(__float_as_uint(ra), __float_as_uint(rc));
+    // Rolling prefetch: the next tile's K is requested as soon as the current K
+    // has fed the q.k MFMAs, and its V right after the P.V MFMAs, so the wave
+    // keeps KV bytes in flight while it computes.
+    int pb[2], row0[2], nv[2];
+    int k = next_tile(0, pb, row0, nv);
+    if (k < n_tiles) {
+      issue_k(pb, row0, nv);
+      issue_v(pb, row0, nv);
     }
-
-    // O^T += V^T P^T, one 16-channel tile j at a time.
+    while (k < n_tiles) {
+      // S^T for both sub-tiles.
+      f32x4 sacc[2];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      u32x4 va;
+      for (int sub = 0; sub < 2; ++sub) {
+        sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) sacc[sub] = mfma16x16x32(kf[sub][s], qf[s], sacc[sub]);
+      }
+      int pbn[2], row0n[2], nvn[2];
+      const int kn = next_tile(k + 1, pbn, row0n, nvn);
+      if (kn < n_tiles) issue_k(pbn, row0n, nvn);
+
+      // Online softmax over this tile for head r (base 2).
+      float sv[8];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = sacc[sub][i] * p.qk_scale_log2;
+          sv[sub * 4 + i] = (4 * qd + i < nv[sub]) ? x : -INFINITY;
+        }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      float pv[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+        psum += pv[i];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) oacc[j] *= alpha;
+      }
+
+      // P^T operand as bf16 hi + lo parts.
+      u32x4 phi, plo;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const int sub = d >> 1, i0 = (d & 1) * 2;
-        const unsigned w0 = vf[sub][i0][j >> 1], w1 = vf[sub][i0 + 1][j >> 1];
-        va[d] = (j & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
+        const unsigned a = __float_as_uint(pv[2 * d]), c = __float_as_uint(pv[2 * d + 1]);
+        phi[d] = pack_hi16(a, c);
+        const float ra = pv[2 * d] - __uint_as_float(a & 0xffff0000u);
+        const float rc = pv[2 * d + 1] - __uint_as_float(c & 0xffff0000u);
+        plo[d] = pack_hi16(__float_as_uint(ra), __float_as_uint(rc));
       }
-      oacc[j] = mfma16x16x32(va, phi, oacc[j]);
-      oacc[j] = mfma16x16x32(va, plo, oacc[j]);
+
+      // O^T += V^T P^T, one 16-channel tile j at a time.
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        u32x4 va;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int sub = d >> 1, i0 = (d & 1) * 2;
+          const unsigned w0 = vf[sub][i0][j >> 1], w1 = vf[sub][i0 + 1][j >> 1];
+          va[d] = (j & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
+        }
+        oacc[j] = mfma16x16x32(va, phi, oacc[j]);
+        oacc[j] = mfma16x16x32(va, plo, oacc[j]);
+      }
+      if (kn < n_tiles) issue_v(pbn, row0n, nvn);
+      k = kn;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        pb[sub] = pbn[sub];
+        row0[sub] = row0n[sub];
+        nv[sub] = nvn[sub];
+      }
     }
-  }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-
-  // Merge the 4 waves' (max, normaliser, accumulator) and write the split's
-  // normalised output and base-2 log-sum-exp.
-  float* s_o = smem;                               // [kWaves][G][D + 4]
-  float* s_m = smem + kWaves * G * (D + 4);        // [kWaves][16]
-  float* s_l = s_m + kWaves * 16;
-  if (r < G) {
-    float* dst = s_o + (wave * G + r) * (D + 4) + CPL * 4 * qd;
+    // This head's split result: normalised output and base-2 log-sum-exp.
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const size_t unit = ((size_t)b * Hkv + g) * p.num_splits + split;
+    if (r < G) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* dst = p.part_o + (unit * G + r) * D + CPL * 4 * qd;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) dst[CPL * i + j] = oacc[j][i];
-  }
-  if (qd == 0) {
-    s_m[wave * 16 + r] = m_run;
-    s_l[wave * 16 + r] = l_tot;
-  }
-  __syncthreads();
-
-  const size_t unit = ((size_t)b * p.Hkv + g) * p.num_splits + split;
-  float* po = p.part_o + unit * (size_t)G * D;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int hh = idx / D, c = idx % D;
-    float M = -INFINITY;
+        for (int j0 = 0; j0 < CPL; j0 += 4) {
+          f32x4 v;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + hh]);
-    const float Mr = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = __builtin_amdgcn_exp2f(s_m[w * 16 + hh] - Mr);
-      L += sc * s_l[w * 16 + hh];
-      o += sc * s_o[(w * G + hh) * (D + 4) + c];
+          for (int jj = 0; jj < 4; ++jj) v[jj] = oacc[j0 + jj][i] * inv;
+          *(f32x4*)(dst + CPL * i + j0) = v;
+        }
+      }
+      if (qd == 0) p.part_lse[unit * G + r] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
     }
-    po[idx] = (L > 0.f) ? o / L : 0.f;
-    if (c == 0) p.part_lse[unit * G + hh] = (L > 0.f) ? M + log2f(L) : -INFINITY;
   }
 }
 
@@ -335,10 +365,16 @@ struct Plan {
   size_t o_bytes, lse_bytes;
 };
 
-static Plan make_plan(int B, int Hq, int Hkv, int D, int span) {
+static int waves_per_wg(int Hkv) { return Hkv < kMaxWaves ? Hkv : kMaxWaves; }
+
+static Plan make_plan(bool sparse, int B, int Hq, int Hkv, int D, int bs, int span) {
   Plan pl;
   const int G = Hq / Hkv;
   pl.split_tokens = split_tokens_for(B, Hkv, span);
+  // The split's block-table entries (per KV head when sparse) must fit in LDS.
+  const int per_token_entries = sparse ? Hkv : 1;
+  while (pl.split_tokens > 128 && (pl.split_tokens / bs) * per_token_entries > kMaxTable)
+    pl.split_tokens >>= 1;
   pl.num_splits = (span + pl.split_tokens - 1) / pl.split_tokens;
   if (pl.num_splits < 1) pl.num_splits = 1;
   const size_t units = (size_t)B * Hkv * pl.num_splits;
@@ -384,7 +420,9 @@ static int attn_run(bool sparse, float* out, const void* query, const void* kc, 
     return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
   const long long span_ll = sparse ? (long long)K * bs : (long long)max_ctx;
   if (span_ll > (1LL << 30)) return fail(GPKV_ERR_SHAPE, "%s: token span too large", fn);
-  const Plan pl = make_plan(B, Hq, Hkv, D, (int)span_ll);
+  if (sparse && (128 / bs) * Hkv > kMaxTable)
+    return fail(GPKV_ERR_UNSUPPORTED, "%s: num_kv_heads=%d too large for block_size %d", fn, Hkv, bs);
+  const Plan pl = make_plan(sparse, B, Hq, Hkv, D, bs, (int)span_ll);
   const size_t need = pl.o_bytes + pl.lse_bytes;
   if (!ws || ws_bytes < need)
     return fail(GPKV_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn,
@@ -414,18 +452,17 @@ static int attn_run(bool sparse, float* out, const void* query, const void* kc, 
   sp.topk_blocks = sparse ? K : 0;
   sp.qk_scale_log2 = scale * 1.4426950408889634f;
 
-  const size_t lds = (size_t)(kWaves * G * (D + 4) + 2 * kWaves * 16) * sizeof(float);
-  const dim3 grid(pl.num_splits, Hkv, B), block(256);
+  const dim3 grid(pl.num_splits, B), block(64 * waves_per_wg(Hkv));
   if (D == 128) {
     if (sparse)
-      attn_split_kernel<128, true><<<grid, block, lds, stream>>>(sp);
+      attn_split_kernel<128, true><<<grid, block, 0, stream>>>(sp);
     else
-      attn_split_kernel<128, false><<<grid, block, lds, stream>>>(sp);
+      attn_split_kernel<128, false><<<grid, block, 0, stream>>>(sp);
   } else {
     if (sparse)
-      attn_split_kernel<64, true><<<grid, block, lds, stream>>>(sp);
+      attn_split_kernel<64, true><<<grid, block, 0, stream>>>(sp);
     else
-      attn_split_kernel<64, false><<<grid, block, lds, stream>>>(sp);
+      attn_split_kernel<64, false><<<grid, block, 0, stream>>>(sp);
   }
   st = check_launch(fn);
   if (st) return st;
@@ -461,7 +498,8 @@ extern "C" size_t gpkv_paged_attention_workspace_bytes(int32_t batch, int32_t nu
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
       !supported_head_dim(head_dim) || !supported_block_size(block_size) || max_context_len < 0)
     return 0;
-  const Plan pl = make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_context_len);
+  const Plan pl = make_plan(false, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                            max_context_len);
   return pl.o_bytes + pl.lse_bytes;
 }
 
@@ -472,7 +510,8 @@ extern "C" size_t gpkv_sparse_attention_workspace_bytes(int32_t batch, int32_t n
       !supported_head_dim(head_dim) || !supported_block_size(block_size) || topk_blocks < 1 ||
       (long long)topk_blocks * block_size > (1LL << 30))
     return 0;
-  const Plan pl = make_plan(batch, num_q_heads, num_kv_heads, head_dim, topk_blocks * block_size);
+  const Plan pl = make_plan(true, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                            topk_blocks * block_size);
   return pl.o_bytes + pl.lse_bytes;
 }
 

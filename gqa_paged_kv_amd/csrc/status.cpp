@@ -9,6 +9,9 @@
 
 namespace gpkv {
 
+// Waves the split heuristic aims for (several times what the GPU holds at once).
+constexpr long long kSplitTargetWaves = 8192;
+
 static thread_local char g_msg[512];
 
 int fail(int status, const char* fmt, ...) {
@@ -28,11 +31,12 @@ int check_launch(const char* what) {
 }
 
 // Split-KV sizing ([TL18] 4.1 and 8(5): too few splits starve the GPU, too many
-// make the partial outputs and the extra combine launch dominate). A work unit
-// is (sequence, KV head, split); 256 CUs hold about 1024 four-wave workgroups at
-// once, so aim for several times that many units while keeping each split long
-// enough that its partial output stays a few percent of the KV bytes it reads.
-// The grid may only depend on host scalars, so the estimate uses the span
+// make the partial outputs and the extra combine launch dominate). A workgroup
+// owns one (sequence, split) with one wave per KV head (at most 8), and MI355X
+// keeps about 2048 such waves resident (256 CUs x 2 per SIMD at this kernel's
+// register use). Take the longest split that still yields a few times that many
+// waves, so each split's partial output stays a small fraction of the KV bytes it
+// reads. The grid may only depend on host scalars, so the estimate uses the span
 // (max_context_len, or topk_blocks * block_size for the sparse path).
 // GPKV_SPLIT_TOKENS (a multiple of 128 in [128, 2048]) overrides the choice; it is
 // read on every call so the workspace query and the launch always agree.
@@ -47,9 +51,9 @@ static int env_split_tokens() {
 int split_tokens_for(int batch, int num_kv_heads, int span_tokens) {
   int forced = env_split_tokens();
   if (forced) return forced;
-  const long long units = (long long)batch * num_kv_heads;
-  int t = 1024;
-  while (t > 128 && units * ((span_tokens + t - 1) / t) < 4096) t >>= 1;
+  const long long waves = (long long)batch * (num_kv_heads < 8 ? num_kv_heads : 8);
+  int t = 2048;
+  while (t > 128 && waves * ((span_tokens + t - 1) / t) < kSplitTargetWaves) t >>= 1;
   return t;
 }
 
