@@ -6,23 +6,16 @@
 // or only those in the selected logical blocks), reading K/V of KV head
 // h / G through block_tables, the ragged last block masked. The running max /
 // normaliser / rescaled accumulator (online softmax) and the split + weighted
-// combine ([TL18] = TileLang tutorial ch. 18, section 4.1) are how the kernel
-// reaches that result; they are not a different definition.
+// combine ([TL18] = TileLang tutorial ch. 18, section 4.1) are how the kernels
+// reach that result; they are not a different definition.
 //
-// Work decomposition (MI355X-first)
+// Per-head inner loop (attend_head)
 // ---------------------------------
-// A workgroup owns one (sequence b, split) unit: a range of `split_tokens` tokens
-// (dense) or of selected-block tokens (sparse), for every KV head. Its waves each
-// take one KV head (wave w: heads w, w + W, ...), so the waves stream the same
-// token rows at the same time: on MI355X whole cache rows (all KV heads of a
-// token) then come from HBM together, which sustains more bandwidth than
-// scattering the heads of a row over different workgroups. A wave walks the
-// split's 32-token tiles; each tile is two 16-token sub-tiles, and a 16-token
-// sub-tile always lies inside one physical block (block_size is a multiple of
-// 16), so its block id is wave-uniform and its rows are one contiguous region.
-//
-// The group's G query heads are padded to 16 and both contractions run on MFMA
-// (v_mfma_f32_16x16x32_bf16) with fp32 accumulation:
+// A wave handles one KV head g over a run of 16-token sub-tiles, two at a time
+// (a 32-token tile). A sub-tile always lies inside one physical block
+// (block_size is a multiple of 16), so its block id is wave-uniform and its rows
+// are one contiguous region. The group's G query heads are padded to 16 and both
+// contractions run on MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation:
 //   S^T[t, h] = sum_c K[t, c] Q[h, c]          A = K rows, B = Q^T
 //   O^T[c, h] += sum_t V^T[c, t] P^T[t, h]      A = V^T,   B = P^T
 // Lane (r = lane % 16, qd = lane / 16) supplies A/B row or column r and the
@@ -39,30 +32,46 @@
 // Masking uses raw buffer loads whose descriptor ends after the sub-tile's valid
 // rows: rows past the context read as zeros (never NaN), and their scores are
 // set to -inf. KV loads are non-temporal (each byte is read once per step) and
-// never pass through LDS; LDS holds only the split's block-table entries.
+// never pass through LDS. Rolling prefetch: the next tile's K is requested as
+// soon as the current K has fed the q.k MFMAs, and its V right after the P.V
+// MFMAs, so a wave keeps KV bytes in flight while it computes.
+//
+// Work decomposition (MI355X-first)
+// ---------------------------------
+// Workgroups hold 4 waves; the waves of a workgroup take different KV heads of
+// the same tokens, so whole cache rows (every KV head of a token) stream from
+// HBM together.
+//  - Dense (balanced): the grid is exactly as many workgroups as the GPU holds at
+//    once. Each workgroup computes the prefix sums of the sequences' 16-token
+//    sub-tile counts and takes an equal share of the flattened (sequence,
+//    sub-tile) space, so ragged batches cost no tail: every workgroup moves the
+//    same number of KV bytes. A workgroup writes one partial per sequence it
+//    touches into slot (workgroup + sequence), which is unique because shares are
+//    ordered; the combine recomputes which workgroups covered a sequence.
+//  - Sparse, and dense batches too large for the balanced table: a workgroup per
+//    (sequence, split of `split_tokens` virtual tokens), the split's block-table
+//    entries (per KV head when sparse) staged in LDS.
+#include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <mutex>
 
 #include "gpkv_internal.h"
 
 namespace gpkv {
 
-constexpr int kMaxWaves = 8;            // waves per workgroup (KV heads processed at once)
-constexpr int kMaxSplitTokens = 2048;
-constexpr int kMaxTable = 2048;         // block-table entries staged in LDS per workgroup
+constexpr int kWaves = 4;               // waves per workgroup
+constexpr int kMaxTable = 2048;         // split path: block-table entries staged in LDS
+constexpr int kMaxBalBatch = 4096;      // balanced path: largest batch (prefix in LDS)
+constexpr int kMaxSubPerWG = 2048;      // balanced path: most sub-tiles per workgroup
 
-struct SplitParams {
-  float* part_o;             // [B, H_kv, S, G, D] fp32, each split's normalised output
-  float* part_lse;           // [B, H_kv, S, G] fp32, base-2 log-sum-exp of the split
+struct AttnCommon {
   const unsigned short* q;   // [B, H_q, D] bf16
   const unsigned char* kc;   // [NB, bs, H_kv, D] bf16
   const unsigned char* vc;
-  const int* block_tables;   // [B, max_blocks]
-  const int* ctx;            // [B]
-  const int* topk;           // [B, H_kv, K] (sparse only)
   long long block_bytes;     // bs * H_kv * D * 2
   int row_bytes;             // H_kv * D * 2
-  long long NB;              // pool size; block ids outside [0, NB) select nothing
-  int Hq, Hkv, G, bs, max_blocks, max_ctx, num_splits, split_tokens, topk_blocks;
+  int Hq, Hkv, G, bs;
   float qk_scale_log2;       // softmax scale * log2(e)
 };
 
@@ -83,28 +92,221 @@ struct VecT<64> {
   }
 };
 
-template <int D, bool SPARSE>
-__global__ __launch_bounds__(kMaxWaves * 64) void attn_split_kernel(const SplitParams p) {
+// Attention of the G query heads of KV head g over sub-tiles [0, n_sub) of one
+// unit; `desc(u, pb, row0, nv)` names sub-tile u's physical block, first row and
+// valid rows (nv = 0: nothing selected). Writes the unit's normalised output
+// o_dst[h][D] and base-2 log-sum-exp lse_dst[h] for h < G.
+template <int D, class Desc>
+__device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, int n_sub,
+                                            const Desc& desc, float* o_dst, float* lse_dst) {
   constexpr int KSTEPS = D / 32;  // k-steps of the q.k contraction
   constexpr int CPL = D / 16;     // channels per lane in the V^T operand / O^T tiles
   constexpr int VBYTES = CPL * 2;
   typedef typename VecT<D>::type vvec;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, qd = lane >> 4;
+  const int G = c.G;
 
-  // Block-table entries of the split: entry e covers virtual tokens
-  // [t0 + e*bs, t0 + (e+1)*bs). s_tok0 = logical position of the block's row 0,
-  // or a huge value when the entry selects nothing. Dense: one table shared by all
-  // KV heads; sparse: one table per KV head (the selection is per head).
+  // Q^T operand: lane holds head r's channels 32s + 8qd .. +8 (zero rows past G).
+  u32x4 qf[KSTEPS];
+  if (r < G) {
+    const unsigned short* qrow = c.q + ((size_t)b * c.Hq + (size_t)g * G + r) * D;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qrow + 32 * s + 8 * qd);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x4 oacc[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max of head r (base 2), same in its 4 lanes
+  float l_run = 0.f;        // this lane's share of the normaliser
+
+  const unsigned off_k = (unsigned)(r * c.row_bytes + g * D * 2 + qd * 16);
+  const unsigned off_v = (unsigned)(4 * qd * c.row_bytes + g * D * 2 + r * VBYTES);
+  const int n_tiles = (n_sub + 1) >> 1;
+
+  auto describe = [&](int k, int* pb, int* row0, int* nv) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int u = 2 * k + sub;
+      if (u < n_sub) {
+        desc(u, pb[sub], row0[sub], nv[sub]);
+      } else {
+        pb[sub] = 0;
+        row0[sub] = 0;
+        nv[sub] = 0;
+      }
+    }
+  };
+  // The next tile with at least one valid row, or n_tiles.
+  auto next_tile = [&](int k, int* pb, int* row0, int* nv) {
+    for (; k < n_tiles; ++k) {
+      describe(k, pb, row0, nv);
+      if ((nv[0] | nv[1]) != 0) return k;
+    }
+    return n_tiles;
+  };
+
+  u32x4 kf[2][KSTEPS];
+  vvec vf[2][4];
+  auto issue_k = [&](const int* pb, const int* row0, const int* nv) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const size_t base = (size_t)pb[sub] * (size_t)c.block_bytes + (size_t)row0[sub] * c.row_bytes;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(c.kc + base, (unsigned)(nv[sub] * c.row_bytes));
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) kf[sub][s] = buf_load16(rk, off_k + 64 * s);
+    }
+  };
+  auto issue_v = [&](const int* pb, const int* row0, const int* nv) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const size_t base = (size_t)pb[sub] * (size_t)c.block_bytes + (size_t)row0[sub] * c.row_bytes;
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(c.vc + base, (unsigned)(nv[sub] * c.row_bytes));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vf[sub][i] = VecT<D>::load(rv, off_v + i * c.row_bytes);
+    }
+  };
+
+  int pb[2], row0[2], nv[2];
+  int k = next_tile(0, pb, row0, nv);
+  if (k < n_tiles) {
+    issue_k(pb, row0, nv);
+    issue_v(pb, row0, nv);
+  }
+  while (k < n_tiles) {
+    // S^T for both sub-tiles.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) sacc[sub] = mfma16x16x32(kf[sub][s], qf[s], sacc[sub]);
+    }
+    int pbn[2], row0n[2], nvn[2];
+    const int kn = next_tile(k + 1, pbn, row0n, nvn);
+    if (kn < n_tiles) issue_k(pbn, row0n, nvn);
+
+    // Online softmax over this tile for head r (base 2).
+    float sv[8];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = sacc[sub][i] * c.qk_scale_log2;
+        sv[sub * 4 + i] = (4 * qd + i < nv[sub]) ? x : -INFINITY;
+      }
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    float pv[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+      psum += pv[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) oacc[j] *= alpha;
+    }
+
+    // P^T operand as bf16 hi + lo parts.
+    u32x4 phi, plo;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const unsigned a = __float_as_uint(pv[2 * d]), cc = __float_as_uint(pv[2 * d + 1]);
+      phi[d] = pack_hi16(a, cc);
+      const float ra = pv[2 * d] - __uint_as_float(a & 0xffff0000u);
+      const float rc = pv[2 * d + 1] - __uint_as_float(cc & 0xffff0000u);
+      plo[d] = pack_hi16(__float_as_uint(ra), __float_as_uint(rc));
+    }
+
+    // O^T += V^T P^T, one 16-channel tile j at a time.
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      u32x4 va;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int sub = d >> 1, i0 = (d & 1) * 2;
+        const unsigned w0 = vf[sub][i0][j >> 1], w1 = vf[sub][i0 + 1][j >> 1];
+        va[d] = (j & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
+      }
+      oacc[j] = mfma16x16x32(va, phi, oacc[j]);
+      oacc[j] = mfma16x16x32(va, plo, oacc[j]);
+    }
+    if (kn < n_tiles) issue_v(pbn, row0n, nvn);
+    k = kn;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      pb[sub] = pbn[sub];
+      row0[sub] = row0n[sub];
+      nv[sub] = nvn[sub];
+    }
+  }
+
+  // The unit's result: normalised output and base-2 log-sum-exp.
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (r < G) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* dst = o_dst + (size_t)r * D + CPL * 4 * qd;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j0 = 0; j0 < CPL; j0 += 4) {
+        f32x4 v;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = oacc[j0 + jj][i] * inv;
+        *(f32x4*)(dst + CPL * i + j0) = v;
+      }
+    }
+    if (qd == 0) lse_dst[r] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+  }
+}
+
+__device__ __forceinline__ int clamp_ctx(int v, int max_ctx) {
+  return v < 0 ? 0 : (v > max_ctx ? max_ctx : v);
+}
+
+// ---------------------------------------------------------------------------
+// Split path: a workgroup per (sequence, split)
+// ---------------------------------------------------------------------------
+
+struct SplitParams {
+  AttnCommon c;
+  float* part_o;             // [B, H_kv, S, G, D] fp32
+  float* part_lse;           // [B, H_kv, S, G] fp32 (base 2)
+  const int* block_tables;   // [B, max_blocks]
+  const int* ctx;            // [B]
+  const int* topk;           // [B, H_kv, K] (sparse only)
+  long long NB;              // pool size; block ids outside [0, NB) select nothing
+  int max_blocks, max_ctx, num_splits, split_tokens, topk_blocks;
+};
+
+template <int D, bool SPARSE>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_split_kernel(const SplitParams p) {
+  // Entry e covers virtual tokens [t0 + e*bs, t0 + (e+1)*bs): s_pb = physical
+  // block (-1: nothing selected), s_tok0 = logical position of the block's row 0.
+  // Dense: one table for all KV heads; sparse: one table per KV head.
   __shared__ int s_pb[kMaxTable];
   __shared__ int s_tok0[kMaxTable];
 
   const int split = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int W = blockDim.x >> 6;
+  const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);  // tell the compiler the tile loop is wave-uniform
-  const int r = lane & 15, qd = lane >> 4;
-  const int G = p.G, bs = p.bs, Hkv = p.Hkv;
-  int ctx = p.ctx[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);  // memory safety only
+  const int bs = p.c.bs, Hkv = p.c.Hkv;
+  const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
   const int nb = (ctx + bs - 1) / bs;
   const int T = p.split_tokens;
   const int span = SPARSE ? p.topk_blocks * bs : ctx;
@@ -126,260 +328,405 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_split_kernel(const SplitP
     }
     const int pb = (lb >= 0 && lb < nb) ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
     const bool ok = pb >= 0 && pb < p.NB;
-    s_pb[i] = ok ? pb : 0;
-    s_tok0[i] = ok ? lb * bs : 0x3fffffff;
+    s_pb[i] = ok ? pb : -1;
+    s_tok0[i] = ok ? lb * bs : 0;
   }
   __syncthreads();
 
-  const int n_tiles = T / 32;
-  for (int g = wave; g < Hkv; g += W) {
+  const int G = p.c.G;
+  for (int g = wave; g < Hkv; g += kWaves) {
     const int* tab_pb = s_pb + (SPARSE ? g * n_ent : 0);
     const int* tab_t0 = s_tok0 + (SPARSE ? g * n_ent : 0);
-
-    // Q^T operand: lane holds head r's channels 32s + 8qd .. +8 (zero rows past G).
-    u32x4 qf[KSTEPS];
-    if (r < G) {
-      const unsigned short* qrow = p.q + ((size_t)b * p.Hq + (size_t)g * G + r) * D;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qrow + 32 * s + 8 * qd);
-    } else {
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
-    }
-
-    f32x4 oacc[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;  // running max of head r (base 2), same in its 4 lanes
-    float l_run = 0.f;        // this lane's share of the normaliser
-
-    const unsigned off_k = (unsigned)(r * p.row_bytes + g * D * 2 + qd * 16);
-    const unsigned off_v = (unsigned)(4 * qd * p.row_bytes + g * D * 2 + r * VBYTES);
-
-    // Tile k covers sub-tiles 2k and 2k+1. For each sub-tile: physical block,
-    // first row inside it, number of valid rows (all wave-uniform).
-    auto describe = [&](int k, int* pb, int* row0, int* nv) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int u16 = 16 * (2 * k + sub);
-        const int e = u16 / bs;
-        row0[sub] = u16 & (bs - 1);
-        int n = ctx - (tab_t0[e] + row0[sub]);
-        n = n < 0 ? 0 : (n > 16 ? 16 : n);
-        nv[sub] = uniform(n);
-        pb[sub] = uniform(tab_pb[e]);
-      }
+    auto desc = [&](int u, int& pb, int& row0, int& nv) {
+      const int e = (16 * u) / bs;
+      row0 = (16 * u) & (bs - 1);
+      const int x = tab_pb[e];
+      int n = ctx - (tab_t0[e] + row0);
+      n = n < 0 ? 0 : (n > 16 ? 16 : n);
+      if (x < 0) n = 0;
+      nv = uniform(n);
+      pb = uniform(x < 0 ? 0 : x);
     };
-    // The next tile with at least one valid row, or n_tiles. Dense tiles are
-    // contiguous from the split start, so the first empty one ends the split;
-    // a sparse list may have unselected entries anywhere.
-    auto next_tile = [&](int k, int* pb, int* row0, int* nv) {
-      for (; k < n_tiles; ++k) {
-        describe(k, pb, row0, nv);
-        if ((nv[0] | nv[1]) != 0) return k;
-        if (!SPARSE) return n_tiles;
-      }
-      return n_tiles;
-    };
-
-    u32x4 kf[2][KSTEPS];
-    vvec vf[2][4];
-    auto issue_k = [&](const int* pb, const int* row0, const int* nv) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const size_t base = (size_t)pb[sub] * (size_t)p.block_bytes + (size_t)row0[sub] * p.row_bytes;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.kc + base, (unsigned)(nv[sub] * p.row_bytes));
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) kf[sub][s] = buf_load16(rk, off_k + 64 * s);
-      }
-    };
-    auto issue_v = [&](const int* pb, const int* row0, const int* nv) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const size_t base = (size_t)pb[sub] * (size_t)p.block_bytes + (size_t)row0[sub] * p.row_bytes;
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vc + base, (unsigned)(nv[sub] * p.row_bytes));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vf[sub][i] = VecT<D>::load(rv, off_v + i * p.row_bytes);
-      }
-    };
-
-    // Rolling prefetch: the next tile's K is requested as soon as the current K
-    // has fed the q.k MFMAs, and its V right after the P.V MFMAs, so the wave
-    // keeps KV bytes in flight while it computes.
-    int pb[2], row0[2], nv[2];
-    int k = next_tile(0, pb, row0, nv);
-    if (k < n_tiles) {
-      issue_k(pb, row0, nv);
-      issue_v(pb, row0, nv);
-    }
-    while (k < n_tiles) {
-      // S^T for both sub-tiles.
-      f32x4 sacc[2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) sacc[sub] = mfma16x16x32(kf[sub][s], qf[s], sacc[sub]);
-      }
-      int pbn[2], row0n[2], nvn[2];
-      const int kn = next_tile(k + 1, pbn, row0n, nvn);
-      if (kn < n_tiles) issue_k(pbn, row0n, nvn);
-
-      // Online softmax over this tile for head r (base 2).
-      float sv[8];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = sacc[sub][i] * p.qk_scale_log2;
-          sv[sub * 4 + i] = (4 * qd + i < nv[sub]) ? x : -INFINITY;
-        }
-      float mx = sv[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-      float pv[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
-        psum += pv[i];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) oacc[j] *= alpha;
-      }
-
-      // P^T operand as bf16 hi + lo parts.
-      u32x4 phi, plo;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const unsigned a = __float_as_uint(pv[2 * d]), c = __float_as_uint(pv[2 * d + 1]);
-        phi[d] = pack_hi16(a, c);
-        const float ra = pv[2 * d] - __uint_as_float(a & 0xffff0000u);
-        const float rc = pv[2 * d + 1] - __uint_as_float(c & 0xffff0000u);
-        plo[d] = pack_hi16(__float_as_uint(ra), __float_as_uint(rc));
-      }
-
-      // O^T += V^T P^T, one 16-channel tile j at a time.
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        u32x4 va;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int sub = d >> 1, i0 = (d & 1) * 2;
-          const unsigned w0 = vf[sub][i0][j >> 1], w1 = vf[sub][i0 + 1][j >> 1];
-          va[d] = (j & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
-        }
-        oacc[j] = mfma16x16x32(va, phi, oacc[j]);
-        oacc[j] = mfma16x16x32(va, plo, oacc[j]);
-      }
-      if (kn < n_tiles) issue_v(pbn, row0n, nvn);
-      k = kn;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        pb[sub] = pbn[sub];
-        row0[sub] = row0n[sub];
-        nv[sub] = nvn[sub];
-      }
-    }
-
-    // This head's split result: normalised output and base-2 log-sum-exp.
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
     const size_t unit = ((size_t)b * Hkv + g) * p.num_splits + split;
-    if (r < G) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float* dst = p.part_o + (unit * G + r) * D + CPL * 4 * qd;
+    attend_head<D>(p.c, b, g, T / 16, desc, p.part_o + unit * G * D, p.part_lse + unit * G);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Balanced dense path: equal shares of the flattened (sequence, sub-tile) space
+// ---------------------------------------------------------------------------
+
+struct BalParams {
+  AttnCommon c;
+  float* part_o;             // [N + B, H_kv, G, D] fp32, slot = workgroup + sequence
+  float* part_lse;           // [N + B, H_kv, G] fp32 (base 2)
+  int* prefix;               // [B + 1] sub-tile prefix sums, written by workgroup 0
+  const int* block_tables;
+  const int* ctx;
+  long long NB;
+  int B, max_blocks, max_ctx, nwg;
+};
+
+// Exclusive prefix sum over the workgroup's 256 threads; *total gets the sum.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
 #pragma unroll
-        for (int j0 = 0; j0 < CPL; j0 += 4) {
-          f32x4 v;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) v[jj] = oacc[j0 + jj][i] * inv;
-          *(f32x4*)(dst + CPL * i + j0) = v;
-        }
-      }
-      if (qd == 0) p.part_lse[unit * G + r] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+  for (int w = 0; w < kWaves; ++w) {
+    const int x = s_wave[w];
+    off += w < wave ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + inc - v;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_balanced_kernel(const BalParams p) {
+  __shared__ int s_pref[kMaxBalBatch + 1];
+  __shared__ int s_pb[kMaxSubPerWG + 8];
+  __shared__ int s_wave[kWaves];
+  const int wg = blockIdx.x, tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int B = p.B, bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
+
+  // Sub-tile counts of every sequence, and their prefix sums (all workgroups
+  // compute the same values; workgroup 0 also hands them to the combine).
+  int carry = 0;
+  for (int base = 0; base < B; base += kWaves * 64) {
+    const int bb = base + tid;
+    const int n = bb < B ? (clamp_ctx(p.ctx[bb], p.max_ctx) + 15) >> 4 : 0;
+    int tot;
+    const int ex = wg_exclusive_scan(n, s_wave, &tot);
+    if (bb < B) s_pref[bb + 1] = carry + ex + n;
+    carry += tot;
+  }
+  if (tid == 0) s_pref[0] = 0;
+  __syncthreads();
+  if (wg == 0)
+    for (int i = tid; i <= B; i += kWaves * 64) p.prefix[i] = s_pref[i];
+  const long long S = s_pref[B];
+  const int s0 = (int)((long long)wg * S / p.nwg);
+  const int s1 = (int)((long long)(wg + 1) * S / p.nwg);
+  if (s0 >= s1) return;
+
+  // First sequence of the share: the last b with prefix[b] <= s0.
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pref[mid] <= s0)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  for (int b = lo; b < B && s_pref[b] < s1; ++b) {
+    const int ub = (s0 > s_pref[b] ? s0 : s_pref[b]) - s_pref[b];
+    const int ue = (s1 < s_pref[b + 1] ? s1 : s_pref[b + 1]) - s_pref[b];
+    if (ue <= ub) continue;  // empty sequence
+    const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+    const int nb = (ctx + bs - 1) / bs;
+    const int lb0 = (16 * ub) / bs;
+    const int n_lb = (16 * ue - 1) / bs - lb0 + 1;
+    __syncthreads();  // the previous sequence's table is no longer read
+    for (int e = tid; e < n_lb; e += kWaves * 64) {
+      const int lb = lb0 + e;
+      const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
+      s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
+    }
+    __syncthreads();
+    auto desc = [&](int u, int& pb, int& row0, int& nv) {
+      const int tok = 16 * (ub + u);
+      const int x = s_pb[tok / bs - lb0];
+      row0 = tok & (bs - 1);
+      int n = ctx - tok;
+      n = n < 0 ? 0 : (n > 16 ? 16 : n);
+      if (x < 0) n = 0;
+      nv = uniform(n);
+      pb = uniform(x < 0 ? 0 : x);
+    };
+    const size_t slot = (size_t)wg + b;
+    for (int g = wave; g < Hkv; g += kWaves) {
+      const size_t unit = slot * Hkv + g;
+      attend_head<D>(p.c, b, g, ue - ub, desc, p.part_o + unit * G * D, p.part_lse + unit * G);
     }
   }
 }
 
+// ---------------------------------------------------------------------------
+// Combine: out = sum_u w_u O_u / sum_u w_u, w_u = 2^(lse_u - max lse)
+// ---------------------------------------------------------------------------
+
+// Each unit's normaliser is taken relative to one common maximum ([TL18] 4.1).
+// One 256-thread workgroup per (sequence, query head): 16-byte loads, D/4 threads
+// per unit row, so a pass over the workgroup reads 256*4/D units at once and many
+// unit rows are in flight.
 struct CombineParams {
   float* out;               // [B, H_q, D]
   const float* part_o;
   const float* part_lse;
-  const int* ctx;
-  int Hq, Hkv, G, max_ctx, num_splits, split_tokens, sparse;
+  const int* ctx;           // split path
+  const int* prefix;        // balanced path
+  int Hq, Hkv, G, max_ctx, num_splits, split_tokens, sparse, balanced, B, nwg;
 };
 
-// out = sum_s w_s O_s / sum_s w_s with w_s = 2^(lse_s - max lse): each split's
-// normaliser taken relative to one common maximum ([TL18] 4.1). One wave per
-// (sequence, query head).
+constexpr int kCombineThreads = 256;
+
+// Units of (sequence b, KV head g, query head hl of the group) are u in
+// [u_begin, u_end); unit u's lse and output sit at lse0 + u * lstride and
+// o0 + u * ostride (balanced: u is a workgroup id and the slot is u + b).
+struct UnitRange {
+  int u_begin, u_end;
+  long long S;
+  bool check_live;          // only when some workgroups had an empty share
+  const float* lse0;
+  const float* o0;
+  size_t lstride, ostride;
+  int nwg;
+  __device__ bool live(int u) const {
+    if (!check_live) return true;
+    return (long long)u * S / nwg < (long long)(u + 1) * S / nwg;
+  }
+};
+
 template <int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const CombineParams p) {
-  constexpr int CP = D / 64;
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+__device__ __forceinline__ UnitRange unit_range(const CombineParams& p, int b, int g, int hl) {
+  UnitRange r;
+  const int G = p.G;
+  r.nwg = p.nwg;
+  r.S = 0;
+  if (p.balanced) {
+    const long long pre0 = p.prefix[b];
+    const long long pre1 = p.prefix[b + 1];
+    r.S = p.prefix[p.B];
+    if (pre1 <= pre0) {
+      r.u_begin = r.u_end = 0;
+    } else {
+      r.u_begin = (int)(((pre0 + 1) * p.nwg - 1) / r.S);  // workgroup holding sub-tile pre0
+      r.u_end = (int)((pre1 * p.nwg - 1) / r.S) + 1;      // ... and sub-tile pre1 - 1
+    }
+    r.lstride = (size_t)p.Hkv * G;
+    r.ostride = r.lstride * D;
+    r.lse0 = p.part_lse + ((size_t)b * p.Hkv + g) * G + hl;
+    r.o0 = p.part_o + (((size_t)b * p.Hkv + g) * G + hl) * D;
+  } else {
+    const int ctx = p.ctx[b] < 0 ? 0 : (p.ctx[b] > p.max_ctx ? p.max_ctx : p.ctx[b]);
+    r.u_begin = 0;
+    r.u_end = p.sparse ? p.num_splits : (ctx + p.split_tokens - 1) / p.split_tokens;
+    const size_t unit0 = ((size_t)b * p.Hkv + g) * p.num_splits;
+    r.lstride = G;
+    r.ostride = (size_t)G * D;
+    r.lse0 = p.part_lse + unit0 * G + hl;
+    r.o0 = p.part_o + (unit0 * G + hl) * D;
+  }
+  r.check_live = p.balanced && r.S < p.nwg;
+  return r;
+}
+
+// Few units per sequence: one workgroup per (sequence, KV head); each group of
+// D/4 threads (a "slot") owns query heads hl, hl + slots, ... of the group and
+// merges that head's units on its own, without barriers.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_heads_kernel(const CombineParams p) {
+  constexpr int TPU = D / 4;
+  constexpr int SLOTS = kCombineThreads / TPU;
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int slot = tid / TPU, c4 = tid % TPU;
+  for (int hl = slot; hl < p.G; hl += SLOTS) {
+    const UnitRange r = unit_range<D>(p, b, g, hl);
+    float M = -INFINITY;
+    for (int u = r.u_begin; u < r.u_end; ++u)
+      if (r.live(u)) M = fmaxf(M, r.lse0[(size_t)u * r.lstride]);
+    const float Mr = (M == -INFINITY) ? 0.f : M;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    int u = r.u_begin;
+    for (; u + 3 < r.u_end; u += 4) {
+      float l[4];
+      f32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bool ok = r.live(u + k);
+        l[k] = ok ? r.lse0[(size_t)(u + k) * r.lstride] : -INFINITY;
+        v[k] = ok ? *(const f32x4*)(r.o0 + (size_t)(u + k) * r.ostride + 4 * c4)
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float w = __builtin_amdgcn_exp2f(l[k] - Mr);
+        W += w;
+        acc += w * v[k];
+      }
+    }
+    for (; u < r.u_end; ++u) {
+      if (!r.live(u)) continue;
+      const float w = __builtin_amdgcn_exp2f(r.lse0[(size_t)u * r.lstride] - Mr);
+      W += w;
+      acc += w * *(const f32x4*)(r.o0 + (size_t)u * r.ostride + 4 * c4);
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    *(f32x4*)(p.out + ((size_t)b * p.Hq + (size_t)g * p.G + hl) * D + 4 * c4) = acc * inv;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const CombineParams p) {
+  constexpr int TPU = D / 4;                       // threads per unit row
+  constexpr int UPP = kCombineThreads / TPU;       // units per pass
+  __shared__ float s_red[kCombineThreads];
+  __shared__ f32x4 s_acc[UPP][TPU];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int G = p.G;
   const int g = h / G, hl = h - g * G;
-  int ctx = p.ctx[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
-  const int ns = p.sparse ? p.num_splits : (ctx + p.split_tokens - 1) / p.split_tokens;
-  const size_t unit0 = ((size_t)b * p.Hkv + g) * p.num_splits;
-  const float* lse = p.part_lse + unit0 * G + hl;
-  const float* po = p.part_o + unit0 * (size_t)G * D + (size_t)hl * D + lane * CP;
+  float* out = p.out + ((size_t)b * p.Hq + h) * D;
 
+  const UnitRange r = unit_range<D>(p, b, g, hl);
+  if (r.u_end <= r.u_begin) {
+    for (int c = tid; c < D; c += kCombineThreads) out[c] = 0.f;
+    return;
+  }
+  const int u_begin = r.u_begin, u_end = r.u_end;
+  const float* lse0 = r.lse0;
+  const float* o0 = r.o0;
+  const size_t lstride = r.lstride, ostride = r.ostride;
+  auto live = [&](int u) { return r.live(u); };
+
+  // Common maximum of the units' lse.
+  const int lane = tid & 63, wave = tid >> 6;
   float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, lse[(size_t)s * G]);
+  for (int u = u_begin + tid; u < u_end; u += kCombineThreads)
+    if (live(u)) M = fmaxf(M, lse0[(size_t)u * lstride]);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) s_red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const float Mr = (M == -INFINITY) ? 0.f : M;
 
-  float acc[CP];
-#pragma unroll
-  for (int c = 0; c < CP; ++c) acc[c] = 0.f;
+  // Weighted sum: thread (unit slot us, float4 column c4) walks units us, us+UPP,
+  // ..., eight loads in flight at a time.
+  constexpr int UNROLL = 8;
+  const int us = tid / TPU, c4 = tid % TPU;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __builtin_amdgcn_exp2f(lse[(size_t)s * G] - Mr);
-    W += w;
-    const float* src = po + (size_t)s * G * D;
+  int u = u_begin + us;
+  for (; u + (UNROLL - 1) * UPP < u_end; u += UNROLL * UPP) {
+    float l[UNROLL];
+    f32x4 v[UNROLL];
 #pragma unroll
-    for (int c = 0; c < CP; ++c) acc[c] += w * src[c];
+    for (int k = 0; k < UNROLL; ++k) {
+      const int uu = u + k * UPP;
+      const bool ok = live(uu);
+      l[k] = ok ? lse0[(size_t)uu * lstride] : -INFINITY;
+      v[k] = ok ? *(const f32x4*)(o0 + (size_t)uu * ostride + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+      const float w = __builtin_amdgcn_exp2f(l[k] - Mr);
+      W += w;
+      acc += w * v[k];
+    }
   }
-  float* o = p.out + ((size_t)b * p.Hq + h) * D + lane * CP;
+  for (; u < u_end; u += UPP) {
+    if (!live(u)) continue;
+    const float w = __builtin_amdgcn_exp2f(lse0[(size_t)u * lstride] - Mr);
+    W += w;
+    acc += w * *(const f32x4*)(o0 + (size_t)u * ostride + 4 * c4);
+  }
+  __syncthreads();  // s_red is reused below
+  s_acc[us][c4] = acc;
+  if (c4 == 0) s_red[us] = W;
+  __syncthreads();
+  if (tid < TPU) {
+    f32x4 a = s_acc[0][tid];
+    float wt = s_red[0];
 #pragma unroll
-  for (int c = 0; c < CP; ++c) o[c] = (W > 0.f) ? acc[c] / W : 0.f;
+    for (int k = 1; k < UPP; ++k) {
+      a += s_acc[k][tid];
+      wt += s_red[k];
+    }
+    const float inv = wt > 0.f ? 1.f / wt : 0.f;
+    *(f32x4*)(out + 4 * tid) = a * inv;
+  }
 }
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct Plan {
-  int split_tokens, num_splits;
-  size_t o_bytes, lse_bytes;
-};
+// Workgroups of the balanced kernel the current device runs at once.
+static int balanced_capacity(int D) {
+  static std::mutex mu;
+  static int cache[64][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 1024;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  int& slot = cache[dev][D == 128 ? 1 : 0];
+  if (slot == 0) {
+    int cus = 0, per_cu = 0;
+    const hipError_t e1 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const hipError_t e2 =
+        D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_balanced_kernel<128>,
+                                                                kWaves * 64, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_balanced_kernel<64>,
+                                                                kWaves * 64, 0);
+    if (e1 != hipSuccess || e2 != hipSuccess || cus <= 0 || per_cu <= 0) {
+      (void)hipGetLastError();
+      return 1024;
+    }
+    slot = cus * per_cu;
+  }
+  return slot;
+}
 
-static int waves_per_wg(int Hkv) { return Hkv < kMaxWaves ? Hkv : kMaxWaves; }
+struct Plan {
+  bool balanced;
+  int split_tokens, num_splits, nwg;
+  size_t o_bytes, lse_bytes, prefix_bytes;
+};
 
 static Plan make_plan(bool sparse, int B, int Hq, int Hkv, int D, int bs, int span) {
   Plan pl;
   const int G = Hq / Hkv;
+  pl.balanced = !sparse && B <= kMaxBalBatch;
   pl.split_tokens = split_tokens_for(B, Hkv, span);
-  // The split's block-table entries (per KV head when sparse) must fit in LDS.
   const int per_token_entries = sparse ? Hkv : 1;
   while (pl.split_tokens > 128 && (pl.split_tokens / bs) * per_token_entries > kMaxTable)
     pl.split_tokens >>= 1;
   pl.num_splits = (span + pl.split_tokens - 1) / pl.split_tokens;
   if (pl.num_splits < 1) pl.num_splits = 1;
-  const size_t units = (size_t)B * Hkv * pl.num_splits;
+  size_t units;
+  if (pl.balanced) {
+    // As many workgroups as run at once, more only if a share would exceed the
+    // per-workgroup table; never more than there are sub-tiles.
+    const long long max_sub = (long long)B * ((span + 15) / 16);
+    long long n = balanced_capacity(D);
+    const long long need = (max_sub + kMaxSubPerWG - 1) / kMaxSubPerWG;
+    if (n < need) n = need;
+    if (n > max_sub) n = max_sub;
+    if (n < 1) n = 1;
+    pl.nwg = (int)n;
+    units = ((size_t)pl.nwg + B) * Hkv;
+  } else {
+    pl.nwg = 0;
+    units = (size_t)B * Hkv * pl.num_splits;
+  }
   pl.o_bytes = align256(units * G * D * sizeof(float));
   pl.lse_bytes = align256(units * G * sizeof(float));
+  pl.prefix_bytes = pl.balanced ? align256(((size_t)B + 1) * sizeof(int)) : 0;
   return pl;
 }
 
@@ -421,57 +768,83 @@ static int attn_run(bool sparse, float* out, const void* query, const void* kc, 
   const long long span_ll = sparse ? (long long)K * bs : (long long)max_ctx;
   if (span_ll > (1LL << 30)) return fail(GPKV_ERR_SHAPE, "%s: token span too large", fn);
   if (sparse && (128 / bs) * Hkv > kMaxTable)
-    return fail(GPKV_ERR_UNSUPPORTED, "%s: num_kv_heads=%d too large for block_size %d", fn, Hkv, bs);
+    return fail(GPKV_ERR_UNSUPPORTED, "%s: num_kv_heads=%d too large for block_size %d", fn, Hkv,
+                bs);
   const Plan pl = make_plan(sparse, B, Hq, Hkv, D, bs, (int)span_ll);
-  const size_t need = pl.o_bytes + pl.lse_bytes;
+  const size_t need = pl.o_bytes + pl.lse_bytes + pl.prefix_bytes;
   if (!ws || ws_bytes < need)
     return fail(GPKV_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn,
                 ws ? ws_bytes : (size_t)0, need);
 
   const int G = Hq / Hkv;
-  SplitParams sp;
-  sp.part_o = (float*)ws;
-  sp.part_lse = (float*)((char*)ws + pl.o_bytes);
-  sp.q = (const unsigned short*)query;
-  sp.kc = (const unsigned char*)kc;
-  sp.vc = (const unsigned char*)vc;
-  sp.block_tables = bt;
-  sp.ctx = ctx;
-  sp.topk = topk;
-  sp.row_bytes = Hkv * D * 2;
-  sp.block_bytes = (long long)bs * sp.row_bytes;
-  sp.Hq = Hq;
-  sp.Hkv = Hkv;
-  sp.G = G;
-  sp.bs = bs;
-  sp.max_blocks = max_blocks;
-  sp.max_ctx = max_ctx;
-  sp.NB = NB;
-  sp.num_splits = pl.num_splits;
-  sp.split_tokens = pl.split_tokens;
-  sp.topk_blocks = sparse ? K : 0;
-  sp.qk_scale_log2 = scale * 1.4426950408889634f;
+  AttnCommon c;
+  c.q = (const unsigned short*)query;
+  c.kc = (const unsigned char*)kc;
+  c.vc = (const unsigned char*)vc;
+  c.row_bytes = Hkv * D * 2;
+  c.block_bytes = (long long)bs * c.row_bytes;
+  c.Hq = Hq;
+  c.Hkv = Hkv;
+  c.G = G;
+  c.bs = bs;
+  c.qk_scale_log2 = scale * 1.4426950408889634f;
+  float* part_o = (float*)ws;
+  float* part_lse = (float*)((char*)ws + pl.o_bytes);
+  int* prefix = (int*)((char*)ws + pl.o_bytes + pl.lse_bytes);
 
-  const dim3 grid(pl.num_splits, B), block(64 * waves_per_wg(Hkv));
-  if (D == 128) {
-    if (sparse)
-      attn_split_kernel<128, true><<<grid, block, 0, stream>>>(sp);
+  if (pl.balanced) {
+    BalParams bp;
+    bp.c = c;
+    bp.part_o = part_o;
+    bp.part_lse = part_lse;
+    bp.prefix = prefix;
+    bp.block_tables = bt;
+    bp.ctx = ctx;
+    bp.NB = NB;
+    bp.B = B;
+    bp.max_blocks = max_blocks;
+    bp.max_ctx = max_ctx;
+    bp.nwg = pl.nwg;
+    if (D == 128)
+      attn_balanced_kernel<128><<<dim3(pl.nwg), dim3(kWaves * 64), 0, stream>>>(bp);
     else
-      attn_split_kernel<128, false><<<grid, block, 0, stream>>>(sp);
+      attn_balanced_kernel<64><<<dim3(pl.nwg), dim3(kWaves * 64), 0, stream>>>(bp);
   } else {
-    if (sparse)
-      attn_split_kernel<64, true><<<grid, block, 0, stream>>>(sp);
-    else
-      attn_split_kernel<64, false><<<grid, block, 0, stream>>>(sp);
+    SplitParams sp;
+    sp.c = c;
+    sp.part_o = part_o;
+    sp.part_lse = part_lse;
+    sp.block_tables = bt;
+    sp.ctx = ctx;
+    sp.topk = topk;
+    sp.NB = NB;
+    sp.max_blocks = max_blocks;
+    sp.max_ctx = max_ctx;
+    sp.num_splits = pl.num_splits;
+    sp.split_tokens = pl.split_tokens;
+    sp.topk_blocks = sparse ? K : 0;
+    const dim3 grid(pl.num_splits, B), block(kWaves * 64);
+    if (D == 128) {
+      if (sparse)
+        attn_split_kernel<128, true><<<grid, block, 0, stream>>>(sp);
+      else
+        attn_split_kernel<128, false><<<grid, block, 0, stream>>>(sp);
+    } else {
+      if (sparse)
+        attn_split_kernel<64, true><<<grid, block, 0, stream>>>(sp);
+      else
+        attn_split_kernel<64, false><<<grid, block, 0, stream>>>(sp);
+    }
   }
   st = check_launch(fn);
   if (st) return st;
 
   CombineParams cp;
   cp.out = out;
-  cp.part_o = sp.part_o;
-  cp.part_lse = sp.part_lse;
+  cp.part_o = part_o;
+  cp.part_lse = part_lse;
   cp.ctx = ctx;
+  cp.prefix = prefix;
   cp.Hq = Hq;
   cp.Hkv = Hkv;
   cp.G = G;
@@ -479,11 +852,27 @@ static int attn_run(bool sparse, float* out, const void* query, const void* kc, 
   cp.num_splits = pl.num_splits;
   cp.split_tokens = pl.split_tokens;
   cp.sparse = sparse ? 1 : 0;
-  const dim3 cgrid(Hq, B), cblock(64);
-  if (D == 128)
-    attn_combine_kernel<128><<<cgrid, cblock, 0, stream>>>(cp);
-  else
-    attn_combine_kernel<64><<<cgrid, cblock, 0, stream>>>(cp);
+  cp.balanced = pl.balanced ? 1 : 0;
+  cp.B = B;
+  cp.nwg = pl.nwg;
+  // Many units per sequence (long sequences over many workgroups or splits): one
+  // workgroup per query head, its threads spread over the units. Few units: one
+  // workgroup per KV head, a slot of threads per query head.
+  const long long units_per_seq = pl.balanced ? (long long)pl.nwg / B + 1 : pl.num_splits;
+  const dim3 cblock(kCombineThreads);
+  if (units_per_seq >= 6) {
+    const dim3 cgrid(Hq, B);
+    if (D == 128)
+      attn_combine_kernel<128><<<cgrid, cblock, 0, stream>>>(cp);
+    else
+      attn_combine_kernel<64><<<cgrid, cblock, 0, stream>>>(cp);
+  } else {
+    const dim3 cgrid(Hkv, B);
+    if (D == 128)
+      attn_combine_heads_kernel<128><<<cgrid, cblock, 0, stream>>>(cp);
+    else
+      attn_combine_heads_kernel<64><<<cgrid, cblock, 0, stream>>>(cp);
+  }
   return check_launch(fn);
 }
 
@@ -500,7 +889,7 @@ extern "C" size_t gpkv_paged_attention_workspace_bytes(int32_t batch, int32_t nu
     return 0;
   const Plan pl = make_plan(false, batch, num_q_heads, num_kv_heads, head_dim, block_size,
                             max_context_len);
-  return pl.o_bytes + pl.lse_bytes;
+  return pl.o_bytes + pl.lse_bytes + pl.prefix_bytes;
 }
 
 extern "C" size_t gpkv_sparse_attention_workspace_bytes(int32_t batch, int32_t num_q_heads,
@@ -512,7 +901,7 @@ extern "C" size_t gpkv_sparse_attention_workspace_bytes(int32_t batch, int32_t n
     return 0;
   const Plan pl = make_plan(true, batch, num_q_heads, num_kv_heads, head_dim, block_size,
                             topk_blocks * block_size);
-  return pl.o_bytes + pl.lse_bytes;
+  return pl.o_bytes + pl.lse_bytes + pl.prefix_bytes;
 }
 
 extern "C" int gpkv_paged_attention_decode(float* out, const void* query, const void* key_cache,
