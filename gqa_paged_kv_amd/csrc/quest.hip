@@ -14,6 +14,8 @@
 // costs 2*D float64 FMAs. Scores stay in float64 so near-equal blocks keep their
 // exact order; ties go to the lower logical block.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "gpkv_internal.h"
 
@@ -114,93 +116,31 @@ __global__ __launch_bounds__(256) void quest_meta_kernel(const MetaParams p) {
   }
 }
 
+// Metadata loads of the score kernels: each row is read once per step, and
+// non-temporal loads measured faster than default-policy ones here too.
+__device__ __forceinline__ u32x4 meta_load(const u32x4* ptr) { return __builtin_nontemporal_load(ptr); }
+
 // ---------------------------------------------------------------------------
 // Scores: one float64 per (sequence, KV head, logical block)
 // ---------------------------------------------------------------------------
 
-constexpr int kScoreBlocksPerWG = 64;
+constexpr int kSelectThreads = 256;       // two-kernel path
+constexpr int kMaxSelectThreads = 1024;   // fused path: up to 128 blocks per pass
+constexpr int kScoreUnroll = 4;           // passes of loads in flight (two-kernel path)
+constexpr int kFusedUnroll = 2;           // ... (fused path, 1024 threads: fewer registers)
+constexpr int kScoreBlocksPerWG = kSelectThreads / 8 * kScoreUnroll;   // two-kernel path
+constexpr int kMaxLdsKeys = 6144;        // keys of one (b, g) that fit in LDS (48 KB)
 
 struct ScoreParams {
-  double* scores;              // [B, H_kv, max_blocks]
+  double* scores;              // [B, H_kv, max_blocks] (two-kernel path)
+  int* out;                    // [B, H_kv, K] (fused path)
   const unsigned short* q;     // [B, H_q, D]
   const unsigned short* kmin;  // [NB, H_kv, D]
   const unsigned short* kmax;
   const int* bt;
   const int* ctx;
   long long NB;
-  int Hq, Hkv, G, bs, max_blocks, max_ctx;
-};
-
-// Eight lanes score one block (D/8 channels each) and merge with xor shuffles;
-// a workgroup covers 64 consecutive logical blocks of one (b, g).
-template <int D>
-__global__ __launch_bounds__(256) void quest_score_kernel(const ScoreParams p) {
-  constexpr int CH = D / 8;
-  __shared__ double s_pos[D];
-  __shared__ double s_neg[D];
-  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  int ctx = p.ctx[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
-  const int nb = (ctx + p.bs - 1) / p.bs;
-  const int lb0 = chunk * kScoreBlocksPerWG;
-  if (lb0 >= nb) return;
-
-  for (int c = tid; c < D; c += 256) {
-    double pos = 0.0, neg = 0.0;
-    const unsigned short* qh = p.q + ((size_t)b * p.Hq + (size_t)g * p.G) * D + c;
-    for (int h = 0; h < p.G; ++h) {
-      const double v = (double)__uint_as_float((unsigned)qh[(size_t)h * D] << 16);
-      if (v > 0.0)
-        pos += v;
-      else
-        neg += v;
-    }
-    s_pos[c] = pos;
-    s_neg[c] = neg;
-  }
-  __syncthreads();
-
-  const int sub = tid & 7, slot = tid >> 3;
-  for (int it = 0; it < kScoreBlocksPerWG / 32; ++it) {
-    const int lb = lb0 + it * 32 + slot;
-    int pb = -1;
-    if (lb < nb) pb = p.bt[(size_t)b * p.max_blocks + lb];
-    const bool ok = lb < nb && pb >= 0 && pb < p.NB;
-    double acc = 0.0;
-    if (ok) {
-      const size_t o = ((size_t)pb * p.Hkv + g) * D + (size_t)sub * CH;
-      const u32x4* mn = (const u32x4*)(p.kmin + o);
-      const u32x4* mx = (const u32x4*)(p.kmax + o);
-#pragma unroll
-      for (int v = 0; v < CH / 8; ++v) {
-        const u32x4 a = mn[v], c4 = mx[v];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int ch = sub * CH + v * 8 + 2 * k;
-          acc = fma((double)bf16_lo(c4[k]), s_pos[ch], acc);
-          acc = fma((double)bf16_lo(a[k]), s_neg[ch], acc);
-          acc = fma((double)bf16_hi(c4[k]), s_pos[ch + 1], acc);
-          acc = fma((double)bf16_hi(a[k]), s_neg[ch + 1], acc);
-        }
-      }
-    }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
-    if (lb < nb && sub == 0)
-      p.scores[((size_t)b * p.Hkv + g) * p.max_blocks + lb] = ok ? acc : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Top-K: radix select on order-preserving 64-bit keys, ties to the lower index
-// ---------------------------------------------------------------------------
-
-struct TopkParams {
-  int* out;                // [B, H_kv, K]
-  const double* scores;    // [B, H_kv, max_blocks]
-  const int* ctx;
-  int Hkv, bs, max_blocks, max_ctx, K;
+  int Hq, Hkv, G, bs, max_blocks, max_ctx, K;
 };
 
 __device__ __forceinline__ unsigned long long score_key(double x) {
@@ -209,7 +149,203 @@ __device__ __forceinline__ unsigned long long score_key(double x) {
   return bits < 0 ? ~(unsigned long long)bits : ((unsigned long long)bits | 0x8000000000000000ull);
 }
 
-// Exclusive prefix sum of v over the 256 threads; *total receives the sum.
+// LDS layout of the per-channel query sums: a score lane (sub = 0..7) owns the
+// contiguous channels sub*D/8 .. +D/8, so channel c is stored at
+// (c % (D/8)) * 8 + c / (D/8): the eight lanes of a block read eight consecutive
+// doubles (no bank conflicts). Per KV head the arrays are padded to D + 8.
+template <int D>
+__device__ __forceinline__ int qb_index(int c) {
+  return (c % (D / 8)) * 8 + c / (D / 8);
+}
+constexpr int kQbPad = 8;
+
+// Query rows of heads [h0, h0 + nh) of sequence b into LDS as raw bf16, with one
+// round of 16-byte loads (nh * D * 2 bytes).
+template <int D>
+__device__ __forceinline__ void stage_query(const ScoreParams& p, int b, int h0, int nh,
+                                            unsigned short* s_q) {
+  const u32x4* src = (const u32x4*)(p.q + ((size_t)b * p.Hq + h0) * D);
+  u32x4* dst = (u32x4*)s_q;
+  for (int i = threadIdx.x; i < nh * D / 8; i += blockDim.x) dst[i] = src[i];
+}
+
+// pos[c] = sum of the positive q[h][c] over the G heads of a group, neg[c] = sum of
+// the negative ones, in head order (the exact identity of the block bound needs
+// only kmin <= kmax). s_qg holds the group's G query rows.
+template <int D>
+__device__ __forceinline__ void group_bounds(const unsigned short* s_qg, int G, int c,
+                                             double* pos_out, double* neg_out) {
+  double pos = 0.0, neg = 0.0;
+  for (int h = 0; h < G; ++h) {
+    const double v = (double)__uint_as_float((unsigned)s_qg[h * D + c] << 16);
+    if (v > 0.0)
+      pos += v;
+    else
+      neg += v;
+  }
+  *pos_out = pos;
+  *neg_out = neg;
+}
+
+// s_pos / s_neg for one (b, g); s_q is scratch LDS for G * D bf16. Ends with a
+// barrier.
+template <int D>
+__device__ __forceinline__ void query_bounds(const ScoreParams& p, int b, int g, unsigned short* s_q,
+                                             double* s_pos, double* s_neg) {
+  stage_query<D>(p, b, g * p.G, p.G, s_q);
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += blockDim.x)
+    group_bounds<D>(s_q, p.G, c, s_pos + qb_index<D>(c), s_neg + qb_index<D>(c));
+  __syncthreads();
+}
+
+// Scores of logical blocks lb0 + P*u + slot (P = blockDim/8 blocks per pass,
+// u < UNROLL) for one (b, g): eight lanes per block (sub = lane & 7) each
+// take D/8 channels, all loads are issued before any arithmetic, and xor shuffles
+// merge the eight partial sums. Calls emit(lb, key) from the sub == 0 lane of every
+// block lb < nb. Every lane of the workgroup must call this with the same lb0.
+template <int D, int UNROLL, class Emit>
+__device__ __forceinline__ void score_blocks(const ScoreParams& p, int b, int g, int nb, int lb0,
+                                             const double* s_pos, const double* s_neg,
+                                             const Emit& emit) {
+  constexpr int CH = D / 8;       // channels per lane
+  constexpr int NV = CH / 8;      // 16-byte vectors per lane per array
+  const int sub = threadIdx.x & 7, slot = threadIdx.x >> 3;
+  const int P = blockDim.x >> 3;
+  u32x4 mn[UNROLL][NV], mx[UNROLL][NV];
+  bool ok[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int lb = lb0 + P * u + slot;
+    const int pb = lb < nb ? p.bt[(size_t)b * p.max_blocks + lb] : -1;
+    ok[u] = pb >= 0 && pb < p.NB;
+    const size_t o = ((size_t)(ok[u] ? pb : 0) * p.Hkv + g) * D + (size_t)sub * CH;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      mn[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmin + o) + v) : u32x4{0, 0, 0, 0};
+      mx[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmax + o) + v) : u32x4{0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    double acc = 0.0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = (v * 8 + 2 * k) * 8 + sub;   // qb_index of channel sub*CH + v*8 + 2k
+        acc = fma((double)bf16_lo(mx[u][v][k]), s_pos[j], acc);
+        acc = fma((double)bf16_lo(mn[u][v][k]), s_neg[j], acc);
+        acc = fma((double)bf16_hi(mx[u][v][k]), s_pos[j + 8], acc);
+        acc = fma((double)bf16_hi(mn[u][v][k]), s_neg[j + 8], acc);
+      }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    const int lb = lb0 + P * u + slot;
+    if (lb < nb && sub == 0) emit(lb, score_key(ok[u] ? acc : -INFINITY));
+  }
+}
+
+// Two-kernel path, scoring: a workgroup covers kScoreBlocksPerWG consecutive logical
+// blocks of one (b, g) and writes float64 scores (as their order-preserving keys).
+template <int D>
+__global__ __launch_bounds__(kSelectThreads) void quest_score_kernel(const ScoreParams p) {
+  __shared__ double s_pos[D];
+  __shared__ double s_neg[D];
+  __shared__ unsigned short s_q[kMaxGroup * D];
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int ctx = p.ctx[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  const int nb = (ctx + p.bs - 1) / p.bs;
+  const int lb0 = chunk * kScoreBlocksPerWG;
+  if (lb0 >= nb || p.K >= nb) return;  // nothing to rank: every block is selected
+  query_bounds<D>(p, b, g, s_q, s_pos, s_neg);
+  unsigned long long* keys = (unsigned long long*)p.scores + ((size_t)b * p.Hkv + g) * p.max_blocks;
+  score_blocks<D, kScoreUnroll>(p, b, g, nb, lb0, s_pos, s_neg,
+                                [&](int lb, unsigned long long key) { keys[lb] = key; });
+}
+
+// Two-kernel path, scoring by whole metadata rows: a workgroup covers a chunk of
+// logical blocks of one sequence for every KV head. The eight-lane groups of a
+// block take its KV heads side by side, so a block's key-min row and key-max row
+// (all KV heads, H_kv * D * 2 bytes each) are read whole and contiguously.
+constexpr int kRowScoreUnroll = 4;
+constexpr int kMaxRowHeads = 32;
+
+template <int D>
+__global__ __launch_bounds__(kSelectThreads) void quest_score_rows_kernel(const ScoreParams p) {
+  extern __shared__ double s_qb[];   // [H_kv][2][D + kQbPad]: positive / negative query sums
+  constexpr int CH = D / 8;
+  constexpr int NV = CH / 8;
+  const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int Hkv = p.Hkv;
+  int ctx = p.ctx[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  const int nb = (ctx + p.bs - 1) / p.bs;
+  const int bpp = (kSelectThreads / 8) / Hkv;        // blocks per pass
+  const int lb0 = chunk * bpp * kRowScoreUnroll;
+  if (lb0 >= nb || p.K >= nb) return;  // nothing to rank: every block is selected
+  unsigned short* s_q = (unsigned short*)(s_qb + (size_t)Hkv * 2 * (D + kQbPad));   // [H_q][D] bf16
+  stage_query<D>(p, b, 0, p.Hq, s_q);
+  const int sub = tid & 7, pair = tid >> 3;
+  const int blk = pair / Hkv, g = pair % Hkv;
+  const bool active = blk < bpp;
+  u32x4 mn[kRowScoreUnroll][NV], mx[kRowScoreUnroll][NV];
+  bool ok[kRowScoreUnroll];
+#pragma unroll
+  for (int u = 0; u < kRowScoreUnroll; ++u) {
+    const int lb = lb0 + u * bpp + blk;
+    const int pb = (active && lb < nb) ? p.bt[(size_t)b * p.max_blocks + lb] : -1;
+    ok[u] = pb >= 0 && pb < p.NB;
+    const size_t o = ((size_t)(ok[u] ? pb : 0) * Hkv + g) * D + (size_t)sub * CH;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      mn[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmin + o) + v) : u32x4{0, 0, 0, 0};
+      mx[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmax + o) + v) : u32x4{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < Hkv * D; i += kSelectThreads) {
+    const int gg = i / D, c = i % D;
+    group_bounds<D>(s_q + (size_t)gg * p.G * D, p.G, c,
+                    &s_qb[(gg * 2) * (D + kQbPad) + qb_index<D>(c)],
+                    &s_qb[(gg * 2 + 1) * (D + kQbPad) + qb_index<D>(c)]);
+  }
+  __syncthreads();
+  const double* s_pos = s_qb + (g * 2) * (D + kQbPad);
+  const double* s_neg = s_qb + (g * 2 + 1) * (D + kQbPad);
+  unsigned long long* keys = (unsigned long long*)p.scores + ((size_t)b * Hkv + g) * p.max_blocks;
+#pragma unroll
+  for (int u = 0; u < kRowScoreUnroll; ++u) {
+    double acc = 0.0;
+    if (active) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int j = (v * 8 + 2 * k) * 8 + sub;   // qb_index of channel sub*CH + v*8 + 2k
+          acc = fma((double)bf16_lo(mx[u][v][k]), s_pos[j], acc);
+          acc = fma((double)bf16_lo(mn[u][v][k]), s_neg[j], acc);
+          acc = fma((double)bf16_hi(mx[u][v][k]), s_pos[j + 8], acc);
+          acc = fma((double)bf16_hi(mn[u][v][k]), s_neg[j + 8], acc);
+        }
+      }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    const int lb = lb0 + u * bpp + blk;
+    if (active && lb < nb && sub == 0) keys[lb] = score_key(ok[u] ? acc : -INFINITY);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-K: radix select on order-preserving 64-bit keys, ties to the lower index
+// ---------------------------------------------------------------------------
+
+// Exclusive prefix sum of v over the workgroup's threads; *total receives the sum.
 __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
@@ -221,8 +357,7 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   if (lane == 63) s_wave[wave] = inc;
   __syncthreads();
   int off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
     const int x = s_wave[w];
     off += w < wave ? x : 0;
     tot += x;
@@ -232,38 +367,65 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   return off + inc - v;
 }
 
-__global__ __launch_bounds__(256) void quest_topk_kernel(const TopkParams p) {
-  __shared__ unsigned hist[256];
-  __shared__ int s_wave[4];
-  __shared__ int s_digit, s_above, s_cnt;
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  int ctx = p.ctx[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
-  const int n = (ctx + p.bs - 1) / p.bs;
-  const int K = p.K;
-  int* out = p.out + ((size_t)b * p.Hkv + g) * K;
-  if (K >= n) {  // every block is selected
-    for (int i = tid; i < K; i += 256) out[i] = i < n ? i : -1;
-    return;
-  }
-  const double* sc = p.scores + ((size_t)b * p.Hkv + g) * p.max_blocks;
-  const int C = (n + 255) / 256;
-  const int i0 = min(n, tid * C), i1 = min(n, i0 + C);
+struct SelectShared {
+  unsigned hist[256];
+  int wave_sums[kMaxSelectThreads / 64];
+  unsigned long long red_and[kMaxSelectThreads / 64], red_or[kMaxSelectThreads / 64];
+  int digit, above, cnt;
+};
 
-  unsigned long long prefix = 0, mask = 0;
-  int need = K, shift = 56;
+// Writes the ascending ids of the K largest keys among key_at(0..n-1) (K < n) to
+// out[0..K); equal keys are taken lowest index first. Keys are read through
+// key_at; every thread of the workgroup must call this.
+template <class KeyAt>
+__device__ void radix_topk(int n, int K, const KeyAt& key_at, int* out, SelectShared& sh) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int C = (n + nt - 1) / nt;
+  const int i0 = min(n, tid * C), i1 = min(n, i0 + C);
   if (tid == 0) {
-    s_digit = 0;
-    s_above = 0;
-    s_cnt = 0;
+    sh.digit = 0;
+    sh.above = 0;
+    sh.cnt = 0;
   }
-  for (int pass = 0; pass < 8; ++pass) {
-    shift = 56 - 8 * pass;
-    hist[tid] = 0;
+  // Bits every key shares need no pass: start at the highest bit where keys differ.
+  unsigned long long k_and = ~0ull, k_or = 0ull;
+  for (int i = i0; i < i1; ++i) {
+    const unsigned long long key = key_at(i);
+    k_and &= key;
+    k_or |= key;
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    const unsigned long long a = ((unsigned long long)__shfl_xor((unsigned)(k_and >> 32), o) << 32) |
+                                 (unsigned)__shfl_xor((unsigned)k_and, o);
+    const unsigned long long b = ((unsigned long long)__shfl_xor((unsigned)(k_or >> 32), o) << 32) |
+                                 (unsigned)__shfl_xor((unsigned)k_or, o);
+    k_and &= a;
+    k_or |= b;
+  }
+  if ((tid & 63) == 0) {
+    sh.red_and[tid >> 6] = k_and;
+    sh.red_or[tid >> 6] = k_or;
+  }
+  __syncthreads();
+  k_and = ~0ull;
+  k_or = 0ull;
+  for (int w = 0; w < (nt >> 6); ++w) {
+    k_and &= sh.red_and[w];
+    k_or |= sh.red_or[w];
+  }
+  const unsigned long long diff = k_and ^ k_or;
+  const int top = diff ? 63 - __clzll((long long)diff) : -1;   // highest differing bit
+  unsigned long long mask = top >= 63 ? 0ull : (~0ull << (top + 1));
+  unsigned long long prefix = k_and & mask;
+  int need = K, shift = 0;
+  for (int pass = 0; top >= 0 && pass < 8; ++pass) {
+    shift = top - 7 - 8 * pass;
+    if (shift < 0) shift = 0;
+    for (int d = tid; d < 256; d += nt) sh.hist[d] = 0;
     __syncthreads();
     for (int i = i0; i < i1; ++i) {
-      const unsigned long long key = score_key(sc[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1u);
+      const unsigned long long key = key_at(i);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255], 1u);
     }
     __syncthreads();
     if (tid < 64) {
@@ -271,7 +433,7 @@ __global__ __launch_bounds__(256) void quest_topk_kernel(const TopkParams p) {
       unsigned c[4], t = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        c[k] = hist[255 - 4 * tid - k];
+        c[k] = sh.hist[255 - 4 * tid - k];
         t += c[k];
       }
       unsigned inc = t;
@@ -286,9 +448,9 @@ __global__ __launch_bounds__(256) void quest_topk_kernel(const TopkParams p) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           if (above + c[k] >= (unsigned)need) {
-            s_digit = 255 - 4 * tid - k;
-            s_above = (int)above;
-            s_cnt = (int)c[k];
+            sh.digit = 255 - 4 * tid - k;
+            sh.above = (int)above;
+            sh.cnt = (int)c[k];
             break;
           }
           above += c[k];
@@ -296,24 +458,24 @@ __global__ __launch_bounds__(256) void quest_topk_kernel(const TopkParams p) {
       }
     }
     __syncthreads();
-    const int digit = s_digit, above = s_above, cnt = s_cnt;
+    const int digit = sh.digit, above = sh.above, cnt = sh.cnt;
     need -= above;
     prefix |= (unsigned long long)digit << shift;
     mask |= 0xFFull << shift;
     __syncthreads();
-    if (cnt == need) break;  // the whole bucket is selected
+    if (cnt == need || shift == 0) break;  // bucket fully selected, or every bit resolved
   }
 
   // Selected: keys above the resolved prefix, plus the first `need` (by index)
   // of those equal to it.
   const unsigned long long ref = prefix >> shift;
   int n_eq = 0;
-  for (int i = i0; i < i1; ++i) n_eq += (score_key(sc[i]) >> shift) == ref;
+  for (int i = i0; i < i1; ++i) n_eq += (key_at(i) >> shift) == ref;
   int tot;
-  int rank = block_exclusive_scan(n_eq, s_wave, &tot);
+  int rank = block_exclusive_scan(n_eq, sh.wave_sums, &tot);
   int n_sel = 0;
   for (int i = i0; i < i1; ++i) {
-    const unsigned long long k = score_key(sc[i]) >> shift;
+    const unsigned long long k = key_at(i) >> shift;
     if (k > ref) {
       ++n_sel;
     } else if (k == ref) {
@@ -321,10 +483,10 @@ __global__ __launch_bounds__(256) void quest_topk_kernel(const TopkParams p) {
       ++rank;
     }
   }
-  int pos = block_exclusive_scan(n_sel, s_wave, &tot);
+  int pos = block_exclusive_scan(n_sel, sh.wave_sums, &tot);
   rank -= n_eq;
   for (int i = i0; i < i1; ++i) {
-    const unsigned long long k = score_key(sc[i]) >> shift;
+    const unsigned long long k = key_at(i) >> shift;
     bool sel = false;
     if (k > ref) {
       sel = true;
@@ -334,6 +496,63 @@ __global__ __launch_bounds__(256) void quest_topk_kernel(const TopkParams p) {
     }
     if (sel && pos < K) out[pos++] = i;  // pos < K always holds; the check keeps writes in the row
   }
+}
+
+__device__ __forceinline__ bool select_all(int n, int K, int* out) {
+  if (K < n) return false;
+  for (int i = threadIdx.x; i < K; i += blockDim.x) out[i] = i < n ? i : -1;
+  return true;
+}
+
+// Two-kernel path, selection: one workgroup per (b, g) over the stored keys,
+// staged in LDS when they fit.
+struct TopkParams {
+  int* out;                          // [B, H_kv, K]
+  const unsigned long long* keys;    // [B, H_kv, max_blocks]
+  const int* ctx;
+  int Hkv, bs, max_blocks, max_ctx, K, lds_keys;
+};
+
+__global__ __launch_bounds__(kSelectThreads) void quest_topk_kernel(const TopkParams p) {
+  extern __shared__ unsigned long long s_key[];
+  __shared__ SelectShared sh;
+  const int g = blockIdx.x, b = blockIdx.y;
+  int ctx = p.ctx[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  const int n = (ctx + p.bs - 1) / p.bs;
+  int* out = p.out + ((size_t)b * p.Hkv + g) * p.K;
+  if (select_all(n, p.K, out)) return;
+  const unsigned long long* keys = p.keys + ((size_t)b * p.Hkv + g) * p.max_blocks;
+  if (n <= p.lds_keys) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) s_key[i] = keys[i];
+    __syncthreads();
+    radix_topk(n, p.K, [&](int i) { return s_key[i]; }, out, sh);
+  } else {
+    radix_topk(n, p.K, [&](int i) { return keys[i]; }, out, sh);
+  }
+}
+
+// Fused path: one workgroup per (b, g) scores all its blocks into LDS keys and
+// selects from them -- one launch, and the keys never leave the CU.
+template <int D>
+__global__ __launch_bounds__(kMaxSelectThreads) void quest_select_fused_kernel(const ScoreParams p) {
+  extern __shared__ unsigned long long s_key[];
+  __shared__ double s_pos[D];
+  __shared__ double s_neg[D];
+  __shared__ unsigned short s_q[kMaxGroup * D];
+  __shared__ SelectShared sh;
+  const int g = blockIdx.x, b = blockIdx.y;
+  int ctx = p.ctx[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  const int nb = (ctx + p.bs - 1) / p.bs;
+  int* out = p.out + ((size_t)b * p.Hkv + g) * p.K;
+  if (select_all(nb, p.K, out)) return;
+  query_bounds<D>(p, b, g, s_q, s_pos, s_neg);
+  for (int lb0 = 0; lb0 < nb; lb0 += (int)(blockDim.x >> 3) * kFusedUnroll)
+    score_blocks<D, kFusedUnroll>(p, b, g, nb, lb0, s_pos, s_neg,
+                                  [&](int lb, unsigned long long key) { s_key[lb] = key; });
+  __syncthreads();
+  radix_topk(nb, p.K, [&](int i) { return s_key[i]; }, out, sh);
 }
 
 static int check_quest(const char* fn, int B, int Hkv, int D, int bs, long long NB,
@@ -427,38 +646,75 @@ extern "C" int gpkv_quest_select_topk(int32_t* topk_indices, const void* query,
                 workspace ? workspace_bytes : (size_t)0, need);
   hipStream_t s = (hipStream_t)stream;
   const int max_nb = (max_context_len + block_size - 1) / block_size;
-  if (max_nb > 0) {
-    ScoreParams sp;
-    sp.scores = (double*)workspace;
-    sp.q = (const unsigned short*)query;
-    sp.kmin = (const unsigned short*)key_min;
-    sp.kmax = (const unsigned short*)key_max;
-    sp.bt = block_tables;
-    sp.ctx = context_lens;
-    sp.NB = num_blocks;
-    sp.Hq = num_q_heads;
-    sp.Hkv = num_kv_heads;
-    sp.G = num_q_heads / num_kv_heads;
-    sp.bs = block_size;
-    sp.max_blocks = max_blocks_per_seq;
-    sp.max_ctx = max_context_len;
+  ScoreParams sp;
+  sp.scores = (double*)workspace;
+  sp.out = topk_indices;
+  sp.q = (const unsigned short*)query;
+  sp.kmin = (const unsigned short*)key_min;
+  sp.kmax = (const unsigned short*)key_max;
+  sp.bt = block_tables;
+  sp.ctx = context_lens;
+  sp.NB = num_blocks;
+  sp.Hq = num_q_heads;
+  sp.Hkv = num_kv_heads;
+  sp.G = num_q_heads / num_kv_heads;
+  sp.bs = block_size;
+  sp.max_blocks = max_blocks_per_seq;
+  sp.max_ctx = max_context_len;
+  sp.K = topk_blocks;
+  // Enough (b, g) pairs to spread over the GPU and keys that fit in LDS: one fused
+  // launch. Otherwise score with a grid over blocks first, then select.
+  // GPKV_QUEST_SELECT_PATH=fused|two_kernel overrides the choice (tuning aid).
+  const char* forced = getenv("GPKV_QUEST_SELECT_PATH");
+  // Measured on MI355X: one fused launch wins for many (b, g) pairs with long
+  // tables (it skips the round trip of the keys); short tables and few pairs are
+  // faster with the grid-wide scoring kernel.
+  bool fused = (long long)batch * num_kv_heads >= 128 && max_nb >= 512;
+  if (forced && strcmp(forced, "fused") == 0) fused = true;
+  if (forced && strcmp(forced, "two_kernel") == 0) fused = false;
+  if (fused && max_nb <= kMaxLdsKeys) {
+    const size_t lds = (size_t)(max_nb > 0 ? max_nb : 1) * sizeof(unsigned long long);
+    // Threads so that one round of kFusedUnroll passes covers the longest table.
+    int threads = kSelectThreads;
+    while (threads < kMaxSelectThreads && threads / 8 * kFusedUnroll < max_nb) threads <<= 1;
+    const dim3 grid(num_kv_heads, batch);
+    if (head_dim == 128)
+      quest_select_fused_kernel<128><<<grid, dim3(threads), lds, s>>>(sp);
+    else
+      quest_select_fused_kernel<64><<<grid, dim3(threads), lds, s>>>(sp);
+    return check_launch(fn);
+  }
+  const size_t row_lds = (size_t)num_kv_heads * 2 * (head_dim + kQbPad) * sizeof(double) +
+                         (size_t)num_q_heads * head_dim * sizeof(unsigned short);
+  if (max_nb > 0 && num_kv_heads <= kMaxRowHeads && row_lds <= 48 * 1024) {
+    const int per_wg = (kSelectThreads / 8) / num_kv_heads * kRowScoreUnroll;
+    const dim3 grid((max_nb + per_wg - 1) / per_wg, batch);
+    if (head_dim == 128)
+      quest_score_rows_kernel<128><<<grid, dim3(kSelectThreads), row_lds, s>>>(sp);
+    else
+      quest_score_rows_kernel<64><<<grid, dim3(kSelectThreads), row_lds, s>>>(sp);
+    st = check_launch(fn);
+    if (st) return st;
+  } else if (max_nb > 0) {
     const dim3 grid((max_nb + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG, num_kv_heads, batch);
     if (head_dim == 128)
-      quest_score_kernel<128><<<grid, dim3(256), 0, s>>>(sp);
+      quest_score_kernel<128><<<grid, dim3(kSelectThreads), 0, s>>>(sp);
     else
-      quest_score_kernel<64><<<grid, dim3(256), 0, s>>>(sp);
+      quest_score_kernel<64><<<grid, dim3(kSelectThreads), 0, s>>>(sp);
     st = check_launch(fn);
     if (st) return st;
   }
   TopkParams tp;
   tp.out = topk_indices;
-  tp.scores = (const double*)workspace;
+  tp.keys = (const unsigned long long*)workspace;
   tp.ctx = context_lens;
   tp.Hkv = num_kv_heads;
   tp.bs = block_size;
   tp.max_blocks = max_blocks_per_seq;
   tp.max_ctx = max_context_len;
   tp.K = topk_blocks;
-  quest_topk_kernel<<<dim3(num_kv_heads, batch), dim3(256), 0, s>>>(tp);
+  tp.lds_keys = max_nb <= kMaxLdsKeys ? max_nb : 0;
+  const size_t lds = (size_t)(tp.lds_keys > 0 ? tp.lds_keys : 1) * sizeof(unsigned long long);
+  quest_topk_kernel<<<dim3(num_kv_heads, batch), dim3(kSelectThreads), lds, s>>>(tp);
   return check_launch(fn);
 }

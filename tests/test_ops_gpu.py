@@ -358,3 +358,25 @@ def test_composed_quest_step_matches_oracle_chain():
     ref = oracle.sparse_paged_attention_decode(w.query, kc, vc, w.block_tables, w.context_lens,
                                                osel, w.scale)
     assert max_abs(out.cpu().numpy(), ref) <= ATOL
+
+
+def test_quest_topk_fused_path_ties_and_ragged():
+    """Enough (sequence, KV head) pairs for the one-launch select path: ragged lengths,
+    K above and below nb, and an exact tie planted in two sequences."""
+    rng = np.random.default_rng(350)
+    ctx = rng.integers(1, 700, size=40).tolist()
+    ctx[3], ctx[7] = 480, 640
+    w = workloads.random_case(350, batch=40, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                              block_size=16, context_lens=ctx)
+    kc = w.key_cache.copy()
+    for b in (3, 7):   # copy the best block of KV head 0 into a later block of the sequence
+        omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+        s = oracle.quest_block_scores(w.query, omin, omax, w.block_tables, w.context_lens, 16, b, 0)
+        a = int(np.argmax(s))
+        later = int(s.size - 1 if a != s.size - 1 else s.size - 2)
+        kc[int(w.block_tables[b, later])] = kc[int(w.block_tables[b, a])]
+    w.key_cache = kc
+    for K in (1, 5, 24):
+        assert 40 * 4 >= 128
+        _, got, exp = _topk_case(w, K)
+        assert np.array_equal(got, exp), K
