@@ -260,6 +260,30 @@ def main():
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
+    # The same step captured into one HIP graph (TileLang tutorial ch. 18, section
+    # 6.2: replay removes the host launch cost only); timed separately, flushed alike.
+    graph_us = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gts = []
+        for k in range(args.steps):
+            flush.fill_(k & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            gts.append(e0.elapsed_time(e1) * 1e3)
+        graph_us = float(np.mean(gts))
+        del g
+    except RuntimeError as exc:   # report, do not fail the eager measurement
+        print(f"[bench] graph capture unavailable: {exc}", file=sys.stderr)
+
     per_call = {name: np.array([evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)])
                 for i, name in enumerate(calls)}
     step_us = np.array([evs[k][0].elapsed_time(evs[k][len(calls)]) * 1e3 for k in range(args.steps)])
@@ -317,6 +341,7 @@ def main():
                                + calls_out["paged_attention_decode"]["us_mean"], 2),
         "quest_step_us": round(quest_us, 2) if quest_us is not None else None,
         "quest_full_metadata_rebuild_us": round(t_full, 2) if t_full is not None else None,
+        "graph_replay_us_per_step": round(graph_us, 2) if graph_us is not None else None,
         "calls": calls_out,
         "step_algorithmic_bytes": int(step_bytes),
         "wall_s_timed_region_incl_flush": round(wall, 4),

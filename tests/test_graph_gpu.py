@@ -1,0 +1,98 @@
+"""The whole decode step captured into a HIP graph: replay equals eager, bit for bit.
+
+[TL18] 6.2 (TileLang tutorial ch. 18, graph capture): graph mode only removes the
+host-side launch cost, so the check is that replays give exactly the eager results.
+Every call launches on torch's current stream with a grid fixed by host scalars and
+no memset, so it is capturable. Replays are interleaved with eager work and
+synchronisations, and every replay is compared with the eager result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_paged_kv_amd as gp
+import workloads
+from gpu_util import BF, Dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _step_buffers(w, d, K):
+    B, Hq, Hkv, D, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    mcl = w.max_context_len
+    buf = {
+        "out_d": torch.empty((B, Hq, D), dtype=torch.float32, device="cuda"),
+        "out_s": torch.empty((B, Hq, D), dtype=torch.float32, device="cuda"),
+        "ws_d": torch.empty(gp.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl),
+                            dtype=torch.uint8, device="cuda"),
+        "ws_sel": torch.empty(gp.quest_select_workspace_bytes(B, Hkv, w.max_blocks_per_seq),
+                              dtype=torch.uint8, device="cuda"),
+        "ws_sp": torch.empty(gp.sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K),
+                             dtype=torch.uint8, device="cuda"),
+        "sel": torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda"),
+        "kmin": torch.zeros((w.num_blocks, Hkv, D), dtype=BF, device="cuda"),
+        "kmax": torch.zeros((w.num_blocks, Hkv, D), dtype=BF, device="cuda"),
+    }
+    gp.quest_block_metadata(d.kc, d.bt, d.ctx, buf["kmin"], buf["kmax"], max_context_len=mcl)
+    return buf
+
+
+def _step(w, d, buf, K):
+    mcl, bs, scale = w.max_context_len, w.block_size, float(w.scale)
+    gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
+    gp.paged_attention_decode(d.q, d.kc, d.vc, d.bt, d.ctx, max_context_len=mcl, scale=scale,
+                              out=buf["out_d"], workspace=buf["ws_d"])
+    gp.quest_block_metadata(d.kc, d.bt, d.ctx, buf["kmin"], buf["kmax"], max_context_len=mcl,
+                            last_block_only=True)
+    gp.quest_select_topk(d.q, buf["kmin"], buf["kmax"], d.bt, d.ctx, block_size=bs,
+                         topk_blocks=K, max_context_len=mcl, out=buf["sel"],
+                         workspace=buf["ws_sel"])
+    gp.sparse_paged_attention_decode(d.q, d.kc, d.vc, d.bt, d.ctx, buf["sel"],
+                                     max_context_len=mcl, scale=scale, out=buf["out_s"],
+                                     workspace=buf["ws_sp"])
+
+
+def _snapshot(buf, d):
+    return {k: v.clone() for k, v in (("out_d", buf["out_d"]), ("out_s", buf["out_s"]),
+                                      ("sel", buf["sel"]), ("kmin", buf["kmin"]),
+                                      ("kmax", buf["kmax"]), ("kc", d.kc), ("vc", d.vc))}
+
+
+@pytest.mark.parametrize("case", ["random", "config3"])
+def test_graph_replay_equals_eager(case):
+    if case == "random":
+        w = workloads.random_case(401, batch=6, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                                  block_size=16, context_lens=[900, 33, 2500, 16, 1200, 700],
+                                  num_tokens=6, neg_slots=1)
+        K = 12
+    else:
+        w = workloads.make(3)
+        K = w.topk_list[0]
+    d = Dev(w)
+    buf = _step_buffers(w, d, K)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm-up on the capture stream
+        _step(w, d, buf, K)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    _step(w, d, buf, K)                 # eager reference (the write is idempotent)
+    torch.cuda.synchronize()
+    ref = _snapshot(buf, d)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _step(w, d, buf, K)
+    scratch = torch.empty(1 << 20, device="cuda")
+    for rep in range(4):
+        # eager work between replays: clobber the outputs, then replay
+        buf["out_d"].fill_(float("nan"))
+        buf["out_s"].fill_(float("nan"))
+        buf["sel"].fill_(-7)
+        scratch.normal_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = _snapshot(buf, d)
+        for k in ref:
+            assert torch.equal(got[k], ref[k]), f"replay {rep}: {k} differs from eager"

@@ -240,8 +240,11 @@ def _topk_case(w, K):
     return d, sel.cpu().numpy(), exp
 
 
+@pytest.mark.parametrize("path", ["auto", "fused", "two_kernel"])
 @pytest.mark.parametrize("config,K", [(1, 3), (1, 5), (3, 64), (4, 256), (5, 32)])
-def test_quest_topk_config(config, K):
+def test_quest_topk_config(config, K, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("GPKV_QUEST_SELECT_PATH", path)
     w = workload(config)
     _, got, exp = _topk_case(w, K)
     mism = int((got != exp).any(axis=2).sum())
@@ -364,9 +367,9 @@ def test_quest_topk_fused_path_ties_and_ragged():
     """Enough (sequence, KV head) pairs for the one-launch select path: ragged lengths,
     K above and below nb, and an exact tie planted in two sequences."""
     rng = np.random.default_rng(350)
-    ctx = rng.integers(1, 700, size=40).tolist()
-    ctx[3], ctx[7] = 480, 640
-    w = workloads.random_case(350, batch=40, num_q_heads=28, num_kv_heads=4, head_dim=128,
+    ctx = rng.integers(1, 9000, size=32).tolist()
+    ctx[3], ctx[7], ctx[9] = 480, 640, 8500      # one table of more than 512 blocks
+    w = workloads.random_case(350, batch=32, num_q_heads=28, num_kv_heads=4, head_dim=128,
                               block_size=16, context_lens=ctx)
     kc = w.key_cache.copy()
     for b in (3, 7):   # copy the best block of KV head 0 into a later block of the sequence
@@ -376,7 +379,6 @@ def test_quest_topk_fused_path_ties_and_ragged():
         later = int(s.size - 1 if a != s.size - 1 else s.size - 2)
         kc[int(w.block_tables[b, later])] = kc[int(w.block_tables[b, a])]
     w.key_cache = kc
-    for K in (1, 5, 24):
-        assert 40 * 4 >= 128
+    for K in (1, 5, 24, 300):
         _, got, exp = _topk_case(w, K)
         assert np.array_equal(got, exp), K
