@@ -1,10 +1,12 @@
 """Decode-step benchmark of the paged GQA attention library on one MI355X.
 
 One step = the whole hot path once over one batch of synthetic input:
-  reshape_and_cache (one new token per sequence)
+  reshape_and_cache_quest (one new token per sequence, and the incremental Quest
+  min / max of its block, in one launch)
   -> paged_attention_decode (dense, split-KV + combine)
-  -> quest_block_metadata (last block of each sequence)
   -> quest_select_topk -> sparse_paged_attention_decode.
+With --write-path separate the first call is reshape_and_cache and a
+quest_block_metadata refresh of each sequence's last block follows the dense call.
 Inputs are resident in HBM before timing. Before every timed step a 1 GiB buffer
 is written so that no KV bytes survive in the 256 MB Infinity Cache; the
 per-call durations come from HIP events on the launch stream and exclude that
@@ -45,6 +47,9 @@ def parse_args():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte calibration)")
+    ap.add_argument("--write-path", choices=["fused", "separate"], default="fused",
+                    help="fused: reshape_and_cache_quest; separate: reshape_and_cache + "
+                         "quest_block_metadata(last_block_only)")
     ap.add_argument("--details", action="store_true", help="print per-call timings to stderr")
     return ap.parse_args()
 
@@ -189,14 +194,23 @@ def main():
     flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    calls = ["reshape_and_cache", "paged_attention_decode"]
-    if K:
-        calls += ["quest_block_metadata", "quest_select_topk", "sparse_paged_attention_decode"]
+    fused = bool(K) and args.write_path == "fused"
+    if fused:
+        calls = ["reshape_and_cache_quest", "paged_attention_decode", "quest_select_topk",
+                 "sparse_paged_attention_decode"]
+    elif K:
+        calls = ["reshape_and_cache", "paged_attention_decode", "quest_block_metadata",
+                 "quest_select_topk", "sparse_paged_attention_decode"]
+    else:
+        calls = ["reshape_and_cache", "paged_attention_decode"]
 
     def run_call(name):
         if name == "reshape_and_cache":
             if w.num_tokens:
                 gp.reshape_and_cache(nk, nv, kc, vc, slots)
+        elif name == "reshape_and_cache_quest":
+            if w.num_tokens:
+                gp.reshape_and_cache_quest(nk, nv, kc, vc, kmin, kmax, slots)
         elif name == "paged_attention_decode":
             gp.paged_attention_decode(q, kc, vc, bt, ctx, max_context_len=mcl, scale=scale,
                                       out=out_d, workspace=ws_d)
@@ -217,9 +231,13 @@ def main():
         if events is not None:
             events[len(calls)].record(stream)
 
-    # Prefill-time work: full metadata build (timed once, outside the step).
+    # Prefill-time work: full metadata build (timed once, outside the step), over a
+    # cache that already holds this step's tokens, so that the step's incremental
+    # update (idempotent) leaves exactly the metadata of the written cache.
     t_full = None
     if K:
+        if w.num_tokens:
+            gp.reshape_and_cache(nk, nv, kc, vc, slots)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         flush.fill_(1)
         e0.record(stream)
@@ -292,13 +310,14 @@ def main():
     sel_host = sel.cpu().numpy() if K else None
     by = {
         "reshape_and_cache": R.write_bytes(w.slot_mapping, w.num_blocks, bs, Hkv, D),
+        "reshape_and_cache_quest": R.fused_write_bytes(w.slot_mapping, w.num_blocks, bs, Hkv, D),
         "paged_attention_decode": R.dense_attention_bytes(w.context_lens, Hkv, D),
     }
     if K:
         by["quest_block_metadata"] = R.metadata_step_bytes(w.context_lens, bs, Hkv, D)
         by["quest_select_topk"] = R.select_bytes(w.context_lens, bs, Hkv, D)
         by["sparse_paged_attention_decode"] = R.sparse_attention_bytes(sel_host, w.context_lens, bs, D)
-    step_bytes = sum(by.values())
+    step_bytes = sum(by[n] for n in calls)
     mean_step = float(step_us.mean())
     value = step_bytes / (mean_step * 1e-6) / 1e9
 
@@ -315,7 +334,11 @@ def main():
     dense_t = per_call["paged_attention_decode"].mean()
     achieved = by["paged_attention_decode"] / (dense_t * 1e-6) / 1e9
     traffic = committed_traffic(args.config)
-    quest_us = sum(calls_out[n]["us_mean"] for n in calls[2:]) if K else None
+    # Both step figures include the write: dense = write + dense attention; Quest =
+    # write (+ metadata refresh) + select + sparse attention.
+    write_us = calls_out[calls[0]]["us_mean"]
+    quest_us = (sum(calls_out[n]["us_mean"] for n in calls if n != "paged_attention_decode")
+                if K else None)
 
     line = {
         "metric": "paged decode attention KV-read HBM GB/s over one decode step (write + dense + Quest)",
@@ -333,12 +356,12 @@ def main():
         "config": {"workload": w.name, "global_batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": bs, "sum_context": int(w.context_lens.sum()),
                    "max_context_len": mcl, "topk_blocks": K, "parallelism": "single-gpu",
+                   "write_path": args.write_path if K else "plain",
                    "sparse_split_tokens": gp.split_tokens(B, Hkv, K * bs) if K else None},
         "pct_of_peak": round(100 * value / R.MI355X_HBM_GBPS, 1),
         "us_per_step": round(mean_step, 2),
         "us_per_step_median": round(float(np.median(step_us)), 2),
-        "dense_step_us": round(calls_out["reshape_and_cache"]["us_mean"]
-                               + calls_out["paged_attention_decode"]["us_mean"], 2),
+        "dense_step_us": round(write_us + calls_out["paged_attention_decode"]["us_mean"], 2),
         "quest_step_us": round(quest_us, 2) if quest_us is not None else None,
         "quest_full_metadata_rebuild_us": round(t_full, 2) if t_full is not None else None,
         "graph_replay_us_per_step": round(graph_us, 2) if graph_us is not None else None,

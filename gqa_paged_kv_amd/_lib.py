@@ -20,6 +20,8 @@ vp = ctypes.c_void_p
 SIGNATURES = {
     "gpkv_reshape_and_cache": (c_int32, [vp, vp, vp, vp, vp, c_int32, c_int32, c_int32, c_int32,
                                          c_int64, vp]),
+    "gpkv_reshape_and_cache_quest": (c_int32, [vp, vp, vp, vp, vp, vp, vp, c_int32, c_int32,
+                                               c_int32, c_int32, c_int64, vp]),
     "gpkv_paged_attention_workspace_bytes": (c_size, [c_int32] * 6),
     "gpkv_paged_attention_decode": (c_int32, [vp, vp, vp, vp, vp, vp, c_int32, c_int32, c_int32,
                                               c_int32, c_int32, c_int64, c_int32, c_int32,

@@ -30,6 +30,45 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
   }
 }
 
+
+// Fused write path: the same row copy, plus an incremental update of the Quest
+// key min / max of the block each token lands in (the token is the newest row of
+// its block: row 0 starts the block's metadata afresh, any later row folds into
+// the block's current metadata with min / max). Results are input values, so the
+// update is exact.
+__global__ __launch_bounds__(64) void reshape_and_cache_quest_kernel(
+    const u32x4* __restrict__ key, const u32x4* __restrict__ value, u32x4* __restrict__ key_cache,
+    u32x4* __restrict__ value_cache, u32x4* __restrict__ key_min, u32x4* __restrict__ key_max,
+    const int64_t* __restrict__ slot_mapping, int row_vec, int block_size, long long num_slots) {
+  const int i = blockIdx.x;
+  const long long s = slot_mapping[i];
+  if (s < 0 || s >= num_slots) return;
+  const long long blk = s / block_size;
+  const long long off = s - blk * block_size;
+  const size_t dst = (size_t)(blk * block_size + off) * (size_t)row_vec;
+  const size_t src = (size_t)i * (size_t)row_vec;
+  const size_t meta = (size_t)blk * (size_t)row_vec;
+  for (int c = threadIdx.x; c < row_vec; c += 64) {
+    const u32x4 k = key[src + c];
+    key_cache[dst + c] = k;
+    value_cache[dst + c] = value[src + c];
+    u32x4 mn = k, mx = k;
+    if (off > 0) {
+      const u32x4 om = key_min[meta + c], ox = key_max[meta + c];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float klo = bf16_lo(k[w]), khi = bf16_hi(k[w]);
+        mn[w] = (__float_as_uint(fminf(bf16_lo(om[w]), klo)) >> 16) |
+                (__float_as_uint(fminf(bf16_hi(om[w]), khi)) & 0xffff0000u);
+        mx[w] = (__float_as_uint(fmaxf(bf16_lo(ox[w]), klo)) >> 16) |
+                (__float_as_uint(fmaxf(bf16_hi(ox[w]), khi)) & 0xffff0000u);
+      }
+    }
+    key_min[meta + c] = mn;
+    key_max[meta + c] = mx;
+  }
+}
+
 }  // namespace gpkv
 
 extern "C" int gpkv_reshape_and_cache(const void* key, const void* value, void* key_cache,
@@ -53,4 +92,31 @@ extern "C" int gpkv_reshape_and_cache(const void* key, const void* value, void* 
       (const u32x4*)key, (const u32x4*)value, (u32x4*)key_cache, (u32x4*)value_cache,
       slot_mapping, row_vec, block_size, (long long)num_blocks * block_size);
   return check_launch("reshape_and_cache");
+}
+
+extern "C" int gpkv_reshape_and_cache_quest(const void* key, const void* value, void* key_cache,
+                                            void* value_cache, void* key_min, void* key_max,
+                                            const int64_t* slot_mapping, int32_t num_tokens,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int64_t num_blocks, void* stream) {
+  using namespace gpkv;
+  clear_error();
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
+    return fail(GPKV_ERR_SHAPE,
+                "reshape_and_cache_quest: num_tokens=%d num_kv_heads=%d num_blocks=%lld",
+                num_tokens, num_kv_heads, (long long)num_blocks);
+  if (!supported_head_dim(head_dim))
+    return fail(GPKV_ERR_UNSUPPORTED, "reshape_and_cache_quest: head_dim=%d (64 or 128)", head_dim);
+  if (!supported_block_size(block_size))
+    return fail(GPKV_ERR_UNSUPPORTED, "reshape_and_cache_quest: block_size=%d (16/32/64/128)",
+                block_size);
+  if (num_tokens == 0) return GPKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !key_min || !key_max || !slot_mapping)
+    return fail(GPKV_ERR_NULL, "reshape_and_cache_quest: null pointer argument");
+  const int row_vec = num_kv_heads * head_dim * 2 / 16;
+  reshape_and_cache_quest_kernel<<<dim3(num_tokens), dim3(64), 0, (hipStream_t)stream>>>(
+      (const u32x4*)key, (const u32x4*)value, (u32x4*)key_cache, (u32x4*)value_cache,
+      (u32x4*)key_min, (u32x4*)key_max, slot_mapping, row_vec, block_size,
+      (long long)num_blocks * block_size);
+  return check_launch("reshape_and_cache_quest");
 }

@@ -12,7 +12,8 @@ import torch
 from ._lib import lib
 
 __all__ = [
-    "GpkvError", "reshape_and_cache", "paged_attention_decode", "quest_block_metadata",
+    "GpkvError", "reshape_and_cache", "reshape_and_cache_quest", "paged_attention_decode",
+    "quest_block_metadata",
     "quest_select_topk", "sparse_paged_attention_decode", "paged_attention_workspace_bytes",
     "quest_select_workspace_bytes", "sparse_attention_workspace_bytes", "split_tokens",
 ]
@@ -102,6 +103,27 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, strea
     _check(lib().gpkv_reshape_and_cache(
         _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T, Hkv, D,
         bs, NB, _stream(stream)))
+
+
+def reshape_and_cache_quest(key, value, key_cache, value_cache, key_min, key_max, slot_mapping,
+                            *, stream=None) -> None:
+    """reshape_and_cache plus the incremental Quest key min / max of each written block."""
+    _dev("key_cache", key_cache, torch.bfloat16, 4)
+    _dev("value_cache", value_cache, torch.bfloat16, 4)
+    _dev("key", key, torch.bfloat16, 3)
+    _dev("value", value, torch.bfloat16, 3)
+    _dev("key_min", key_min, torch.bfloat16, 3)
+    _dev("key_max", key_max, torch.bfloat16, 3)
+    _dev("slot_mapping", slot_mapping, torch.int64, 1)
+    NB, bs, Hkv, D = _cache_dims(key_cache)
+    T = key.shape[0]
+    if value_cache.shape != key_cache.shape or key.shape != (T, Hkv, D) or value.shape != key.shape \
+            or slot_mapping.shape[0] != T or key_min.shape != (NB, Hkv, D) \
+            or key_max.shape != (NB, Hkv, D):
+        raise ValueError("reshape_and_cache_quest: inconsistent shapes")
+    _check(lib().gpkv_reshape_and_cache_quest(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(key_min), _ptr(key_max),
+        _ptr(slot_mapping), T, Hkv, D, bs, NB, _stream(stream)))
 
 
 def _attn_checks(query, key_cache, value_cache, block_tables, context_lens):

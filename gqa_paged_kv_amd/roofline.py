@@ -39,6 +39,18 @@ def write_bytes(slot_mapping, num_blocks: int, block_size: int, num_kv_heads: in
     return valid * kv_bytes_per_token_layer(num_kv_heads, head_dim) * 2
 
 
+def fused_write_bytes(slot_mapping, num_blocks: int, block_size: int, num_kv_heads: int,
+                      head_dim: int) -> int:
+    """The K/V write, plus per written token its block's min / max row: read when the
+    token is not at row 0 of its block, always written."""
+    s = np.asarray(slot_mapping, dtype=np.int64)
+    s = s[(s >= 0) & (s < num_blocks * block_size)]
+    row = num_kv_heads * head_dim * BF16
+    folded = int((s % block_size != 0).sum())
+    return write_bytes(s, num_blocks, block_size, num_kv_heads, head_dim) + folded * 2 * row \
+        + int(s.size) * 2 * row
+
+
 def metadata_step_bytes(context_lens, block_size: int, num_kv_heads: int, head_dim: int) -> int:
     """Read the valid K rows of each sequence's last block; write its min and max."""
     ctx = np.asarray(context_lens, dtype=np.int64)

@@ -5,6 +5,7 @@
  * Quest long-context variant. Five operations:
  *
  *   gpkv_reshape_and_cache           write new tokens' K/V rows into the cache
+ *   gpkv_reshape_and_cache_quest     ... and update those blocks' Quest key min / max
  *   gpkv_paged_attention_decode      dense GQA paged attention (split-KV + combine)
  *   gpkv_quest_block_metadata        per-block, per-channel key min / max
  *   gpkv_quest_select_topk           Quest block scores + Top-K per KV head
@@ -16,7 +17,12 @@
  *          correctness", "Sparse precision", "memory optimisation".
  *   [TL18] TileLang tutorial, chapter 18 (end-to-end inference serving):
  *          2.4 KV-cache structure, 2.6 paged KV, 4.1 split-KV decode attention,
- *          6.1 kernels on the framework's current stream, 6.2 graph capture.
+ *          6.1 kernels on the framework's current stream, 6.2 graph capture,
+ *          8 item (2) the per-step KV write.
+ *   [DSA]  The article on adapting a sparse-attention model to a new accelerator:
+ *          section on the four key levels of the sparse-attention kernel, items 2
+ *          (per-block metadata, updated block by block at decode) and 3 (KV-cache
+ *          update merged into the decode kernel's launch).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -83,6 +89,25 @@ int gpkv_reshape_and_cache(const void* key, const void* value, void* key_cache,
                            void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int64_t num_blocks, void* stream);
+
+/* Fused write path: ReshapeAndCache plus the Quest metadata of the written blocks,
+ * in one launch ([ASC] "ReshapeAndCache" and "Quest Sparse Attention"; the per-step
+ * KV write is a real cost, [TL18] 8 item (2); the cache update shares a launch and
+ * block metadata is updated incrementally at decode, [DSA] items 2-3). Writes key[i] / value[i] exactly as gpkv_reshape_and_cache and, for
+ * each written token with block = slot / bs and row = slot % bs, sets for every KV
+ * head g and channel c:
+ *   row == 0:  key_min[block, g, c] = key_max[block, g, c] = key[i, g, c]
+ *   row  > 0:  key_min[block, g, c] = min(key_min[block, g, c], key[i, g, c]), same for max.
+ * This equals recomputing the block's metadata over rows 0..row (as
+ * gpkv_quest_block_metadata with last_block_only does) when the token is the newest
+ * valid row of its block and the block's metadata covered rows 0..row-1 before the
+ * call -- the decode-append case. At most one token per block per call
+ * (precondition). key_min, key_max: [num_blocks, num_kv_heads, head_dim] bf16. */
+int gpkv_reshape_and_cache_quest(const void* key, const void* value, void* key_cache,
+                                 void* value_cache, void* key_min, void* key_max,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, void* stream);
 
 /* Bytes of workspace gpkv_paged_attention_decode needs for these sizes (0 if the
  * sizes are invalid). The workspace holds split-KV partial outputs and their

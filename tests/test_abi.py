@@ -28,7 +28,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(L):
     from gqa_paged_kv_amd._lib import SIGNATURES
     names = declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert sorted(SIGNATURES) == names

@@ -37,13 +37,17 @@ def _step_buffers(w, d, K):
     return buf
 
 
-def _step(w, d, buf, K):
+def _step(w, d, buf, K, fused):
     mcl, bs, scale = w.max_context_len, w.block_size, float(w.scale)
-    gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
+    if fused:   # write + incremental metadata in one launch (both idempotent)
+        gp.reshape_and_cache_quest(d.nk, d.nv, d.kc, d.vc, buf["kmin"], buf["kmax"], d.slots)
+    else:
+        gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
     gp.paged_attention_decode(d.q, d.kc, d.vc, d.bt, d.ctx, max_context_len=mcl, scale=scale,
                               out=buf["out_d"], workspace=buf["ws_d"])
-    gp.quest_block_metadata(d.kc, d.bt, d.ctx, buf["kmin"], buf["kmax"], max_context_len=mcl,
-                            last_block_only=True)
+    if not fused:
+        gp.quest_block_metadata(d.kc, d.bt, d.ctx, buf["kmin"], buf["kmax"],
+                                max_context_len=mcl, last_block_only=True)
     gp.quest_select_topk(d.q, buf["kmin"], buf["kmax"], d.bt, d.ctx, block_size=bs,
                          topk_blocks=K, max_context_len=mcl, out=buf["sel"],
                          workspace=buf["ws_sel"])
@@ -58,8 +62,9 @@ def _snapshot(buf, d):
                                       ("kmax", buf["kmax"]), ("kc", d.kc), ("vc", d.vc))}
 
 
-@pytest.mark.parametrize("case", ["random", "config3"])
-def test_graph_replay_equals_eager(case):
+@pytest.mark.parametrize("case,fused", [("random", False), ("config3", False), ("random", True),
+                                        ("config3", True)])
+def test_graph_replay_equals_eager(case, fused):
     if case == "random":
         w = workloads.random_case(401, batch=6, num_q_heads=28, num_kv_heads=4, head_dim=128,
                                   block_size=16, context_lens=[900, 33, 2500, 16, 1200, 700],
@@ -73,16 +78,16 @@ def test_graph_replay_equals_eager(case):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):       # warm-up on the capture stream
-        _step(w, d, buf, K)
+        _step(w, d, buf, K, fused)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    _step(w, d, buf, K)                 # eager reference (the write is idempotent)
+    _step(w, d, buf, K, fused)                 # eager reference (the write is idempotent)
     torch.cuda.synchronize()
     ref = _snapshot(buf, d)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _step(w, d, buf, K)
+        _step(w, d, buf, K, fused)
     scratch = torch.empty(1 << 20, device="cuda")
     for rep in range(4):
         # eager work between replays: clobber the outputs, then replay

@@ -228,6 +228,102 @@ def test_quest_metadata_step_after_write():
     assert _meta_equal(bits(kmin), emin) and _meta_equal(bits(kmax), emax)
 
 
+def _before_write_lens(w):
+    """Context lengths before this step's write: ctx - 1 for a sequence whose
+    newest slot (position ctx - 1) is written by a valid slot of slot_mapping."""
+    ctx, bt, bs = w.context_lens.astype(np.int64), w.block_tables, w.block_size
+    valid = set(int(s) for s in w.slot_mapping if 0 <= s < w.num_blocks * bs)
+    before = ctx.copy()
+    for b in np.nonzero(ctx > 0)[0]:
+        pos = ctx[b] - 1
+        if int(bt[b, pos // bs]) * bs + int(pos % bs) in valid:
+            before[b] -= 1
+    return before.astype(np.int32)
+
+
+def _check_fused_write(w):
+    """reshape_and_cache_quest against the oracle chain: write, then refresh each
+    sequence's last block, starting from metadata that covers the pre-write
+    context (the decode-append contract)."""
+    before = _before_write_lens(w)
+    assert (before < w.context_lens).any(), "the case writes no token"
+    base = np.full((w.num_blocks, w.num_kv_heads, w.head_dim), SENTINEL, np.uint16)
+    pmin, pmax = oracle.quest_block_metadata(w.key_cache, w.block_tables, before, w.block_size,
+                                             last_block_only=True, key_min=base, key_max=base)
+    d = Dev(w)
+    kmin, kmax = to_dev(pmin, BF), to_dev(pmax, BF)
+    gp.reshape_and_cache_quest(d.nk, d.nv, d.kc, d.vc, kmin, kmax, d.slots)
+    torch.cuda.synchronize()
+    ek, ev = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                      w.slot_mapping, w.block_size)
+    assert np.array_equal(bits(d.kc), ek), "key cache differs from the oracle"
+    assert np.array_equal(bits(d.vc), ev), "value cache differs from the oracle"
+    emin, emax = oracle.quest_block_metadata(ek, w.block_tables, w.context_lens, w.block_size,
+                                             last_block_only=True, key_min=pmin, key_max=pmax)
+    assert _meta_equal(bits(kmin), emin), "key_min differs from the oracle chain"
+    assert _meta_equal(bits(kmax), emax), "key_max differs from the oracle chain"
+
+
+@pytest.mark.parametrize("config", [1, 3, 5])
+def test_fused_write_config(config):
+    _check_fused_write(workload(config))
+
+
+@pytest.mark.parametrize("seed,Hkv,D,bs", [(501, 1, 64, 16), (502, 4, 128, 16), (503, 8, 128, 128),
+                                           (504, 2, 64, 64), (505, 4, 128, 32)])
+def test_fused_write_random(seed, Hkv, D, bs):
+    """Context lengths put the new token at row 0, at the last row, and in between."""
+    ctx = [1, 2, 16, 17, 33, 64, 65, 100, 128, 129, 257, 300]
+    w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hkv * 2, num_kv_heads=Hkv,
+                              head_dim=D, block_size=bs, context_lens=ctx, num_tokens=len(ctx),
+                              neg_slots=2)
+    _check_fused_write(w)
+
+
+def test_fused_write_empty_and_all_negative():
+    w = workloads.make(1)
+    d = Dev(w)
+    kmin = to_dev(np.full((w.num_blocks, 1, 64), SENTINEL, np.uint16), BF)
+    kmax = kmin.clone()
+    before = [bits(t) for t in (d.kc, d.vc, kmin, kmax)]
+    gp.reshape_and_cache_quest(d.nk, d.nv, d.kc, d.vc, kmin, kmax, torch.full_like(d.slots, -1))
+    empty = torch.empty((0, 1, 64), dtype=BF, device="cuda")
+    gp.reshape_and_cache_quest(empty, empty, d.kc, d.vc, kmin, kmax,
+                               torch.empty((0,), dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    for a, t in zip(before, (d.kc, d.vc, kmin, kmax)):
+        assert np.array_equal(bits(t), a)
+
+
+def test_fused_write_then_quest_step_matches_oracle_chain():
+    """Full build at prefill, fused write at decode, then select + sparse."""
+    w = workloads.random_case(341, batch=5, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                              block_size=16, context_lens=[2000, 700, 17, 1234, 3001],
+                              num_tokens=5, neg_slots=1)
+    K = 24
+    before = _before_write_lens(w)
+    d = Dev(w)
+    base = np.zeros((w.num_blocks, 4, 128), np.uint16)
+    kmin, kmax = to_dev(base, BF), to_dev(base, BF)
+    d_ctx_before = to_dev(before, torch.int32)
+    gp.quest_block_metadata(d.kc, d.bt, d_ctx_before, kmin, kmax,
+                            max_context_len=w.max_context_len)       # prefill-time build
+    gp.reshape_and_cache_quest(d.nk, d.nv, d.kc, d.vc, kmin, kmax, d.slots)
+    sel = gp.quest_select_topk(d.q, kmin, kmax, d.bt, d.ctx, block_size=16, topk_blocks=K,
+                               max_context_len=w.max_context_len)
+    out = _sparse(d, w, sel)
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                      w.slot_mapping, 16)
+    omin, omax = oracle.quest_block_metadata(kc, w.block_tables, w.context_lens, 16,
+                                             key_min=base, key_max=base)
+    osel = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens, 16, K)
+    assert np.array_equal(sel.cpu().numpy(), osel)
+    ref = oracle.sparse_paged_attention_decode(w.query, kc, vc, w.block_tables, w.context_lens,
+                                               osel, w.scale)
+    assert max_abs(out.cpu().numpy(), ref) <= ATOL
+
+
 def _topk_case(w, K):
     d = Dev(w)
     kmin, kmax = _meta(d, w)

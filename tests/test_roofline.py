@@ -32,3 +32,5 @@ def test_sparse_and_metadata_accounting_by_hand():
     assert R.metadata_step_bytes([37, 32], 16, 1, 64) == (5 + 16) * 128 + 2 * 2 * 128
     assert R.select_bytes([37, 32], 16, 1, 64) == (3 + 2) * 2 * 64 * 2
     assert R.write_bytes([5, -1, 10**9], 16, 16, 1, 64) == 1 * 2 * 64 * 2 * 2
+    # slot 5 folds into its block (row 5), slot 32 starts a block (row 0)
+    assert R.fused_write_bytes([5, 32, -1], 16, 16, 1, 64) == 2 * 4 * 128 + 1 * 2 * 128 + 2 * 2 * 128
