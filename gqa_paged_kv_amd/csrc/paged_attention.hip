@@ -41,11 +41,11 @@
 // Workgroups hold 4 waves; the waves of a workgroup take different KV heads of
 // the same tokens, so whole cache rows (every KV head of a token) stream from
 // HBM together.
-//  - Dense (balanced): the grid is exactly as many workgroups as the GPU holds at
-//    once. Each workgroup computes the prefix sums of the sequences' 16-token
-//    sub-tile counts and takes an equal share of the flattened (sequence,
-//    sub-tile) space, so ragged batches cost no tail: every workgroup moves the
-//    same number of KV bytes. A workgroup writes one partial per sequence it
+//  - Dense (balanced): the grid is one workgroup per compute unit. Each
+//    workgroup computes the prefix sums of the sequences' 16-token sub-tile
+//    counts and takes an equal share of the flattened (sequence, sub-tile)
+//    space, so ragged batches cost no tail: every workgroup moves the same
+//    number of KV bytes. A workgroup writes one partial per sequence it
 //    touches into slot (workgroup + sequence), which is unique because shares are
 //    ordered; the combine recomputes which workgroups covered a sequence.
 //  - Sparse, and dense batches too large for the balanced table: a workgroup per
@@ -141,11 +141,18 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
       }
     }
   };
-  // The next tile with at least one valid row, or n_tiles.
+  // The next tile with at least one valid row, or n_tiles with an empty
+  // descriptor (nv = 0, so loads issued for it read nothing).
   auto next_tile = [&](int k, int* pb, int* row0, int* nv) {
     for (; k < n_tiles; ++k) {
       describe(k, pb, row0, nv);
       if ((nv[0] | nv[1]) != 0) return k;
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      pb[sub] = 0;
+      row0[sub] = 0;
+      nv[sub] = 0;
     }
     return n_tiles;
   };
@@ -171,12 +178,20 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
     }
   };
 
-  int pb[2], row0[2], nv[2];
+  // Loads are issued unconditionally (an empty descriptor past the last tile
+  // reads nothing): with a load issued on only some paths, the compiler's
+  // wait-count merge would make the P.V step wait for the prefetched K as well.
+  // The next tile's descriptor is found one tile ahead, so its table reads are
+  // off the path between the q.k MFMAs and the K prefetch.
+  int pb[2], row0[2], nv[2], pbn[2], row0n[2], nvn[2];
   int k = next_tile(0, pb, row0, nv);
-  if (k < n_tiles) {
-    issue_k(pb, row0, nv);
-    issue_v(pb, row0, nv);
-  }
+  int kn = next_tile(k + 1, pbn, row0n, nvn);
+  // K before V on every path into the loop (the scheduler may not swap them),
+  // so waiting for K at the top of an iteration leaves V in flight.
+  issue_k(pb, row0, nv);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_v(pb, row0, nv);
+  __builtin_amdgcn_sched_barrier(0);
   while (k < n_tiles) {
     // S^T for both sub-tiles.
     f32x4 sacc[2];
@@ -186,9 +201,7 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) sacc[sub] = mfma16x16x32(kf[sub][s], qf[s], sacc[sub]);
     }
-    int pbn[2], row0n[2], nvn[2];
-    const int kn = next_tile(k + 1, pbn, row0n, nvn);
-    if (kn < n_tiles) issue_k(pbn, row0n, nvn);
+    issue_k(pbn, row0n, nvn);
 
     // Online softmax over this tile for head r (base 2).
     float sv[8];
@@ -245,7 +258,7 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
       oacc[j] = mfma16x16x32(va, phi, oacc[j]);
       oacc[j] = mfma16x16x32(va, plo, oacc[j]);
     }
-    if (kn < n_tiles) issue_v(pbn, row0n, nvn);
+    issue_v(pbn, row0n, nvn);
     k = kn;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -253,6 +266,7 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
       row0[sub] = row0n[sub];
       nv[sub] = nvn[sub];
     }
+    kn = next_tile(k + 1, pbn, row0n, nvn);
   }
 
   // The unit's result: normalised output and base-2 log-sum-exp.
@@ -391,7 +405,7 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* s_wave, int* total)
 }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_balanced_kernel(const BalParams p) {
+__global__ __launch_bounds__(kWaves * 64) void attn_balanced_kernel(const BalParams p) {
   __shared__ int s_pref[kMaxBalBatch + 1];
   __shared__ int s_pb[kMaxSubPerWG + 8];
   __shared__ int s_wave[kWaves];
@@ -664,30 +678,31 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workgroups of the balanced kernel the current device runs at once.
-static int balanced_capacity(int D) {
+// Workgroups of the balanced kernel: one per compute unit. Measured on MI355X
+// over an 8K-average ragged batch: one 4-wave workgroup per CU streams the KV
+// cache at ~6.1 TB/s, while two or three per CU (all resident) reach only 5.7
+// and 5.4 TB/s, and counts that are not a multiple of the CU count (192, 320,
+// 384) leave some CUs with two shares. One wave per SIMD, each with a 32-token
+// tile in flight, already covers HBM latency; more concurrent streams only add
+// DRAM conflicts.
+static int balanced_capacity() {
   static std::mutex mu;
-  static int cache[64][2];
+  static int cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
-    return 1024;
+    return 256;
   }
   std::lock_guard<std::mutex> lock(mu);
-  int& slot = cache[dev][D == 128 ? 1 : 0];
+  int& slot = cache[dev];
   if (slot == 0) {
-    int cus = 0, per_cu = 0;
-    const hipError_t e1 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const hipError_t e2 =
-        D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_balanced_kernel<128>,
-                                                                kWaves * 64, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_balanced_kernel<64>,
-                                                                kWaves * 64, 0);
-    if (e1 != hipSuccess || e2 != hipSuccess || cus <= 0 || per_cu <= 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
       (void)hipGetLastError();
-      return 1024;
+      return 256;
     }
-    slot = cus * per_cu;
+    slot = cus;
   }
   return slot;
 }
@@ -713,7 +728,7 @@ static Plan make_plan(bool sparse, int B, int Hq, int Hkv, int D, int bs, int sp
     // As many workgroups as run at once, more only if a share would exceed the
     // per-workgroup table; never more than there are sub-tiles.
     const long long max_sub = (long long)B * ((span + 15) / 16);
-    long long n = balanced_capacity(D);
+    long long n = balanced_capacity();
     const long long need = (max_sub + kMaxSubPerWG - 1) / kMaxSubPerWG;
     if (n < need) n = need;
     if (n > max_sub) n = max_sub;
