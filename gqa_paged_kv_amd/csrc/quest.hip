@@ -127,9 +127,11 @@ __device__ __forceinline__ u32x4 meta_load(const u32x4* ptr) { return __builtin_
 constexpr int kSelectThreads = 256;       // two-kernel path
 constexpr int kMaxSelectThreads = 1024;   // fused path: up to 128 blocks per pass
 constexpr int kScoreUnroll = 4;           // passes of loads in flight (two-kernel path)
-constexpr int kFusedUnroll = 2;           // ... (fused path, 1024 threads: fewer registers)
+constexpr int kFusedUnroll = 4;           // ... (fused path: block-table row staged in LDS)
+constexpr int kFusedThreads = 512;        // fused path: 2 waves per SIMD (no spills at 4 passes)
 constexpr int kScoreBlocksPerWG = kSelectThreads / 8 * kScoreUnroll;   // two-kernel path
 constexpr int kMaxLdsKeys = 6144;        // keys of one (b, g) that fit in LDS (48 KB)
+constexpr int kMaxFusedBlocks = 4096;    // fused path: keys + block-table row (48 KB)
 
 struct ScoreParams {
   double* scores;              // [B, H_kv, max_blocks] (two-kernel path)
@@ -149,13 +151,15 @@ __device__ __forceinline__ unsigned long long score_key(double x) {
   return bits < 0 ? ~(unsigned long long)bits : ((unsigned long long)bits | 0x8000000000000000ull);
 }
 
-// LDS layout of the per-channel query sums: a score lane (sub = 0..7) owns the
-// contiguous channels sub*D/8 .. +D/8, so channel c is stored at
-// (c % (D/8)) * 8 + c / (D/8): the eight lanes of a block read eight consecutive
-// doubles (no bank conflicts). Per KV head the arrays are padded to D + 8.
+// Channels of a score lane: the eight lanes (sub = 0..7) of a block read its
+// metadata row in 128-byte pieces, lane sub taking channels 64v + 8 sub .. +8 for
+// v < D/64, so each load instruction covers whole 128-byte lines. The per-channel
+// query sums sit in LDS at ((c / 64) * 8 + c % 8) * 8 + (c / 8) % 8: for a given
+// (v, channel pair) the eight lanes of a block read eight consecutive doubles (no
+// bank conflicts). Per KV head the arrays are padded to D + 8.
 template <int D>
 __device__ __forceinline__ int qb_index(int c) {
-  return (c % (D / 8)) * 8 + c / (D / 8);
+  return ((c >> 6) * 8 + (c & 7)) * 8 + ((c >> 3) & 7);
 }
 constexpr int kQbPad = 8;
 
@@ -202,14 +206,15 @@ __device__ __forceinline__ void query_bounds(const ScoreParams& p, int b, int g,
 // Scores of logical blocks lb0 + P*u + slot (P = blockDim/8 blocks per pass,
 // u < UNROLL) for one (b, g): eight lanes per block (sub = lane & 7) each
 // take D/8 channels, all loads are issued before any arithmetic, and xor shuffles
-// merge the eight partial sums. Calls emit(lb, key) from the sub == 0 lane of every
-// block lb < nb. Every lane of the workgroup must call this with the same lb0.
-template <int D, int UNROLL, class Emit>
-__device__ __forceinline__ void score_blocks(const ScoreParams& p, int b, int g, int nb, int lb0,
-                                             const double* s_pos, const double* s_neg,
-                                             const Emit& emit) {
-  constexpr int CH = D / 8;       // channels per lane
-  constexpr int NV = CH / 8;      // 16-byte vectors per lane per array
+// merge the eight partial sums. pb_at(lb) gives the physical block of lb < nb (any
+// value outside [0, NB) scores as -inf). Calls emit(lb, key) from the sub == 0 lane
+// of every block lb < nb. Every lane of the workgroup must call this with the same
+// lb0.
+template <int D, int UNROLL, class PbAt, class Emit>
+__device__ __forceinline__ void score_blocks(const ScoreParams& p, int g, int nb, int lb0,
+                                             const PbAt& pb_at, const double* s_pos,
+                                             const double* s_neg, const Emit& emit) {
+  constexpr int NV = D / 64;      // 16-byte vectors per lane per array
   const int sub = threadIdx.x & 7, slot = threadIdx.x >> 3;
   const int P = blockDim.x >> 3;
   u32x4 mn[UNROLL][NV], mx[UNROLL][NV];
@@ -217,13 +222,13 @@ __device__ __forceinline__ void score_blocks(const ScoreParams& p, int b, int g,
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
     const int lb = lb0 + P * u + slot;
-    const int pb = lb < nb ? p.bt[(size_t)b * p.max_blocks + lb] : -1;
+    const int pb = lb < nb ? pb_at(lb) : -1;
     ok[u] = pb >= 0 && pb < p.NB;
-    const size_t o = ((size_t)(ok[u] ? pb : 0) * p.Hkv + g) * D + (size_t)sub * CH;
+    const size_t o = ((size_t)(ok[u] ? pb : 0) * p.Hkv + g) * D + (size_t)sub * 8;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      mn[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmin + o) + v) : u32x4{0, 0, 0, 0};
-      mx[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmax + o) + v) : u32x4{0, 0, 0, 0};
+      mn[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmin + o + 64 * v)) : u32x4{0, 0, 0, 0};
+      mx[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmax + o + 64 * v)) : u32x4{0, 0, 0, 0};
     }
   }
 #pragma unroll
@@ -233,7 +238,7 @@ __device__ __forceinline__ void score_blocks(const ScoreParams& p, int b, int g,
     for (int v = 0; v < NV; ++v) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int j = (v * 8 + 2 * k) * 8 + sub;   // qb_index of channel sub*CH + v*8 + 2k
+        const int j = (v * 8 + 2 * k) * 8 + sub;   // qb_index of channel 64v + 8 sub + 2k
         acc = fma((double)bf16_lo(mx[u][v][k]), s_pos[j], acc);
         acc = fma((double)bf16_lo(mn[u][v][k]), s_neg[j], acc);
         acc = fma((double)bf16_hi(mx[u][v][k]), s_pos[j + 8], acc);
@@ -263,7 +268,9 @@ __global__ __launch_bounds__(kSelectThreads) void quest_score_kernel(const Score
   if (lb0 >= nb || p.K >= nb) return;  // nothing to rank: every block is selected
   query_bounds<D>(p, b, g, s_q, s_pos, s_neg);
   unsigned long long* keys = (unsigned long long*)p.scores + ((size_t)b * p.Hkv + g) * p.max_blocks;
-  score_blocks<D, kScoreUnroll>(p, b, g, nb, lb0, s_pos, s_neg,
+  score_blocks<D, kScoreUnroll>(p, g, nb, lb0,
+                               [&](int lb) { return p.bt[(size_t)b * p.max_blocks + lb]; },
+                               s_pos, s_neg,
                                 [&](int lb, unsigned long long key) { keys[lb] = key; });
 }
 
@@ -277,8 +284,7 @@ constexpr int kMaxRowHeads = 32;
 template <int D>
 __global__ __launch_bounds__(kSelectThreads) void quest_score_rows_kernel(const ScoreParams p) {
   extern __shared__ double s_qb[];   // [H_kv][2][D + kQbPad]: positive / negative query sums
-  constexpr int CH = D / 8;
-  constexpr int NV = CH / 8;
+  constexpr int NV = D / 64;
   const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int Hkv = p.Hkv;
   int ctx = p.ctx[b];
@@ -299,11 +305,11 @@ __global__ __launch_bounds__(kSelectThreads) void quest_score_rows_kernel(const 
     const int lb = lb0 + u * bpp + blk;
     const int pb = (active && lb < nb) ? p.bt[(size_t)b * p.max_blocks + lb] : -1;
     ok[u] = pb >= 0 && pb < p.NB;
-    const size_t o = ((size_t)(ok[u] ? pb : 0) * Hkv + g) * D + (size_t)sub * CH;
+    const size_t o = ((size_t)(ok[u] ? pb : 0) * Hkv + g) * D + (size_t)sub * 8;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      mn[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmin + o) + v) : u32x4{0, 0, 0, 0};
-      mx[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmax + o) + v) : u32x4{0, 0, 0, 0};
+      mn[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmin + o + 64 * v)) : u32x4{0, 0, 0, 0};
+      mx[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmax + o + 64 * v)) : u32x4{0, 0, 0, 0};
     }
   }
   __syncthreads();
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(kSelectThreads) void quest_score_rows_kernel(const 
       for (int v = 0; v < NV; ++v) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int j = (v * 8 + 2 * k) * 8 + sub;   // qb_index of channel sub*CH + v*8 + 2k
+          const int j = (v * 8 + 2 * k) * 8 + sub;   // qb_index of channel 64v + 8 sub + 2k
           acc = fma((double)bf16_lo(mx[u][v][k]), s_pos[j], acc);
           acc = fma((double)bf16_lo(mn[u][v][k]), s_neg[j], acc);
           acc = fma((double)bf16_hi(mx[u][v][k]), s_pos[j + 8], acc);
@@ -535,7 +541,8 @@ __global__ __launch_bounds__(kSelectThreads) void quest_topk_kernel(const TopkPa
 // Fused path: one workgroup per (b, g) scores all its blocks into LDS keys and
 // selects from them -- one launch, and the keys never leave the CU.
 template <int D>
-__global__ __launch_bounds__(kMaxSelectThreads) void quest_select_fused_kernel(const ScoreParams p) {
+__global__ __launch_bounds__(kFusedThreads) void quest_select_fused_kernel(const ScoreParams p) {
+  // Dynamic LDS: the keys of the sequence's blocks, then its block-table row.
   extern __shared__ unsigned long long s_key[];
   __shared__ double s_pos[D];
   __shared__ double s_neg[D];
@@ -547,9 +554,18 @@ __global__ __launch_bounds__(kMaxSelectThreads) void quest_select_fused_kernel(c
   const int nb = (ctx + p.bs - 1) / p.bs;
   int* out = p.out + ((size_t)b * p.Hkv + g) * p.K;
   if (select_all(nb, p.K, out)) return;
-  query_bounds<D>(p, b, g, s_q, s_pos, s_neg);
+  int* s_pb = (int*)(s_key + nb);
+  // One round of loads for the query group and the whole block-table row, so the
+  // metadata loads below depend on LDS only.
+  stage_query<D>(p, b, g * p.G, p.G, s_q);
+  for (int lb = threadIdx.x; lb < nb; lb += blockDim.x)
+    s_pb[lb] = p.bt[(size_t)b * p.max_blocks + lb];
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += blockDim.x)
+    group_bounds<D>(s_q, p.G, c, s_pos + qb_index<D>(c), s_neg + qb_index<D>(c));
+  __syncthreads();
   for (int lb0 = 0; lb0 < nb; lb0 += (int)(blockDim.x >> 3) * kFusedUnroll)
-    score_blocks<D, kFusedUnroll>(p, b, g, nb, lb0, s_pos, s_neg,
+    score_blocks<D, kFusedUnroll>(p, g, nb, lb0, [&](int lb) { return s_pb[lb]; }, s_pos, s_neg,
                                   [&](int lb, unsigned long long key) { s_key[lb] = key; });
   __syncthreads();
   radix_topk(nb, p.K, [&](int i) { return s_key[i]; }, out, sh);
@@ -672,11 +688,11 @@ extern "C" int gpkv_quest_select_topk(int32_t* topk_indices, const void* query,
   bool fused = (long long)batch * num_kv_heads >= 128 && max_nb >= 512;
   if (forced && strcmp(forced, "fused") == 0) fused = true;
   if (forced && strcmp(forced, "two_kernel") == 0) fused = false;
-  if (fused && max_nb <= kMaxLdsKeys) {
-    const size_t lds = (size_t)(max_nb > 0 ? max_nb : 1) * sizeof(unsigned long long);
+  if (fused && max_nb <= kMaxFusedBlocks) {
+    const size_t lds = (size_t)(max_nb > 0 ? max_nb : 1) * (sizeof(unsigned long long) + sizeof(int));
     // Threads so that one round of kFusedUnroll passes covers the longest table.
     int threads = kSelectThreads;
-    while (threads < kMaxSelectThreads && threads / 8 * kFusedUnroll < max_nb) threads <<= 1;
+    while (threads < kFusedThreads && threads / 8 * kFusedUnroll < max_nb) threads <<= 1;
     const dim3 grid(num_kv_heads, batch);
     if (head_dim == 128)
       quest_select_fused_kernel<128><<<grid, dim3(threads), lds, s>>>(sp);
