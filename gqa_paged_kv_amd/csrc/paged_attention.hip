@@ -53,6 +53,8 @@
 //    entries (per KV head when sparse) staged in LDS.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -63,7 +65,8 @@ namespace gpkv {
 constexpr int kWaves = 4;               // waves per workgroup
 constexpr int kMaxTable = 2048;         // split path: block-table entries staged in LDS
 constexpr int kMaxBalBatch = 4096;      // balanced path: largest batch (prefix in LDS)
-constexpr int kMaxSubPerWG = 2048;      // balanced path: most sub-tiles per workgroup
+constexpr int kMaxSubPerWG = 2048;      // balanced path: most sub-tiles per workgroup (dense)
+constexpr int kBalTab = 4096;           // balanced path: table entries staged in LDS
 
 struct AttnCommon {
   const unsigned short* q;   // [B, H_q, D] bf16
@@ -377,8 +380,9 @@ struct BalParams {
   int* prefix;               // [B + 1] sub-tile prefix sums, written by workgroup 0
   const int* block_tables;
   const int* ctx;
+  const int* topk;           // [B, H_kv, K] logical block ids (sparse only)
   long long NB;
-  int B, max_blocks, max_ctx, nwg;
+  int B, max_blocks, max_ctx, nwg, topk_blocks;
 };
 
 // Exclusive prefix sum over the workgroup's 256 threads; *total gets the sum.
@@ -404,21 +408,36 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* s_wave, int* total)
   return off + inc - v;
 }
 
-template <int D>
+// Work of a sequence, in 16-token sub-tiles: dense, its context; sparse,
+// min(K, blocks) blocks. Valid ids of one KV head's list are distinct blocks of the
+// sequence, so no head has more valid entries than that, wherever they sit in its
+// list; lists from Top-K have exactly that many.
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(kWaves * 64) void attn_balanced_kernel(const BalParams p) {
   __shared__ int s_pref[kMaxBalBatch + 1];
-  __shared__ int s_pb[kMaxSubPerWG + 8];
+  __shared__ int s_pb[kBalTab];                  // physical block per table entry (-1: none)
+  __shared__ int s_tok0[SPARSE ? kBalTab : 1];   // sparse: logical position of its row 0
   __shared__ int s_wave[kWaves];
-  const int wg = blockIdx.x, tid = threadIdx.x;
+  const int wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int B = p.B, bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
+  const int spb = bs >> 4;   // sub-tiles per block
 
   // Sub-tile counts of every sequence, and their prefix sums (all workgroups
   // compute the same values; workgroup 0 also hands them to the combine).
   int carry = 0;
   for (int base = 0; base < B; base += kWaves * 64) {
     const int bb = base + tid;
-    const int n = bb < B ? (clamp_ctx(p.ctx[bb], p.max_ctx) + 15) >> 4 : 0;
+    int n = 0;
+    if (bb < B) {
+      const int ctx = clamp_ctx(p.ctx[bb], p.max_ctx);
+      if (SPARSE) {
+        const int nb = (ctx + bs - 1) / bs;
+        n = (nb < p.topk_blocks ? nb : p.topk_blocks) * spb;
+      } else {
+        n = (ctx + 15) >> 4;
+      }
+    }
     int tot;
     const int ex = wg_exclusive_scan(n, s_wave, &tot);
     if (bb < B) s_pref[bb + 1] = carry + ex + n;
@@ -448,27 +467,58 @@ __global__ __launch_bounds__(kWaves * 64) void attn_balanced_kernel(const BalPar
     if (ue <= ub) continue;  // empty sequence
     const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
     const int nb = (ctx + bs - 1) / bs;
-    const int lb0 = (16 * ub) / bs;
-    const int n_lb = (16 * ue - 1) / bs - lb0 + 1;
+    // Table entries (blocks) the share touches: dense, logical blocks e0 ..;
+    // sparse, positions e0 .. of each KV head's list with the invalid ids removed.
+    const int e0 = ub / spb;
+    const int n_ent = (ue - 1) / spb - e0 + 1;
     __syncthreads();  // the previous sequence's table is no longer read
-    for (int e = tid; e < n_lb; e += kWaves * 64) {
-      const int lb = lb0 + e;
-      const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
-      s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
+    if (!SPARSE) {
+      for (int e = tid; e < n_ent; e += kWaves * 64) {
+        const int lb = e0 + e;
+        const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
+        s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
+      }
+    } else {
+      for (int i = tid; i < Hkv * n_ent; i += kWaves * 64) s_pb[i] = -1;
+      __syncthreads();
+      // Compaction of each head's list, 64 entries per step: a valid entry's
+      // position is the number of valid entries before it.
+      for (int g = wave; g < Hkv; g += kWaves) {
+        const int* lst = p.topk + ((size_t)b * Hkv + g) * p.topk_blocks;
+        int run = 0;
+        for (int c0 = 0; c0 < p.topk_blocks && run < e0 + n_ent; c0 += 64) {
+          const int e = c0 + lane;
+          const int id = e < p.topk_blocks ? lst[e] : -1;
+          const bool valid = id >= 0 && id < nb;
+          const unsigned long long m = __ballot(valid);
+          const int pos = run + __popcll(m & ((1ull << lane) - 1ull));
+          if (valid && pos >= e0 && pos < e0 + n_ent) {
+            const int pb = p.block_tables[(size_t)b * p.max_blocks + id];
+            const int i = g * n_ent + (pos - e0);
+            s_pb[i] = (pb >= 0 && pb < p.NB) ? pb : -1;
+            s_tok0[i] = id * bs;
+          }
+          run += __popcll(m);
+        }
+      }
     }
     __syncthreads();
-    auto desc = [&](int u, int& pb, int& row0, int& nv) {
-      const int tok = 16 * (ub + u);
-      const int x = s_pb[tok / bs - lb0];
-      row0 = tok & (bs - 1);
-      int n = ctx - tok;
-      n = n < 0 ? 0 : (n > 16 ? 16 : n);
-      if (x < 0) n = 0;
-      nv = uniform(n);
-      pb = uniform(x < 0 ? 0 : x);
-    };
     const size_t slot = (size_t)wg + b;
     for (int g = wave; g < Hkv; g += kWaves) {
+      const int* tab = s_pb + (SPARSE ? g * n_ent : 0);
+      const int* tok = s_tok0 + (SPARSE ? g * n_ent : 0);
+      auto desc = [&](int u, int& pb, int& row0, int& nv) {
+        const int v = ub + u;
+        const int blk = v / spb;
+        row0 = (v - blk * spb) * 16;
+        const int x = tab[blk - e0];
+        const int t0 = SPARSE ? tok[blk - e0] + row0 : 16 * v;
+        int n = ctx - t0;
+        n = n < 0 ? 0 : (n > 16 ? 16 : n);
+        if (x < 0) n = 0;
+        nv = uniform(n);
+        pb = uniform(x < 0 ? 0 : x);
+      };
       const size_t unit = slot * Hkv + g;
       attend_head<D>(p.c, b, g, ue - ub, desc, p.part_o + unit * G * D, p.part_lse + unit * G);
     }
@@ -713,10 +763,16 @@ struct Plan {
   size_t o_bytes, lse_bytes, prefix_bytes;
 };
 
+// GPKV_ATTN_SCHEDULE=balanced|split forces the schedule (tuning and test switch,
+// read per call); by default the balanced schedule serves every batch its
+// prefix and tables fit.
 static Plan make_plan(bool sparse, int B, int Hq, int Hkv, int D, int bs, int span) {
   Plan pl;
   const int G = Hq / Hkv;
-  pl.balanced = !sparse && B <= kMaxBalBatch;
+  const int spb = bs / 16;
+  pl.balanced = B <= kMaxBalBatch && (!sparse || kBalTab / Hkv >= 3);
+  const char* forced = getenv("GPKV_ATTN_SCHEDULE");
+  if (forced && strcmp(forced, "split") == 0) pl.balanced = false;
   pl.split_tokens = split_tokens_for(B, Hkv, span);
   const int per_token_entries = sparse ? Hkv : 1;
   while (pl.split_tokens > 128 && (pl.split_tokens / bs) * per_token_entries > kMaxTable)
@@ -725,11 +781,13 @@ static Plan make_plan(bool sparse, int B, int Hq, int Hkv, int D, int bs, int sp
   if (pl.num_splits < 1) pl.num_splits = 1;
   size_t units;
   if (pl.balanced) {
-    // As many workgroups as run at once, more only if a share would exceed the
-    // per-workgroup table; never more than there are sub-tiles.
-    const long long max_sub = (long long)B * ((span + 15) / 16);
+    // One workgroup per CU, more only if a share would exceed the per-workgroup
+    // table (sparse: H_kv entries per block of the share); never more than there
+    // are sub-tiles.
+    const long long max_sub = sparse ? (long long)B * (span / bs) * spb : (long long)B * ((span + 15) / 16);
+    const long long share_max = sparse ? (long long)(kBalTab / Hkv - 2) * spb : kMaxSubPerWG;
     long long n = balanced_capacity();
-    const long long need = (max_sub + kMaxSubPerWG - 1) / kMaxSubPerWG;
+    const long long need = (max_sub + share_max - 1) / share_max;
     if (n < need) n = need;
     if (n > max_sub) n = max_sub;
     if (n < 1) n = 1;
@@ -820,10 +878,20 @@ static int attn_run(bool sparse, float* out, const void* query, const void* kc, 
     bp.max_blocks = max_blocks;
     bp.max_ctx = max_ctx;
     bp.nwg = pl.nwg;
-    if (D == 128)
-      attn_balanced_kernel<128><<<dim3(pl.nwg), dim3(kWaves * 64), 0, stream>>>(bp);
-    else
-      attn_balanced_kernel<64><<<dim3(pl.nwg), dim3(kWaves * 64), 0, stream>>>(bp);
+    bp.topk = topk;
+    bp.topk_blocks = sparse ? K : 0;
+    const dim3 grid(pl.nwg), block(kWaves * 64);
+    if (D == 128) {
+      if (sparse)
+        attn_balanced_kernel<128, true><<<grid, block, 0, stream>>>(bp);
+      else
+        attn_balanced_kernel<128, false><<<grid, block, 0, stream>>>(bp);
+    } else {
+      if (sparse)
+        attn_balanced_kernel<64, true><<<grid, block, 0, stream>>>(bp);
+      else
+        attn_balanced_kernel<64, false><<<grid, block, 0, stream>>>(bp);
+    }
   } else {
     SplitParams sp;
     sp.c = c;

@@ -102,8 +102,13 @@ DENSE_CASES = [
 ]
 
 
+SCHEDULES = ["balanced", "split"]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx", DENSE_CASES)
-def test_dense_random(seed, Hq, Hkv, D, bs, ctx):
+def test_dense_random(seed, Hq, Hkv, D, bs, ctx, schedule, monkeypatch):
+    monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
     w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                               block_size=bs, context_lens=ctx)
     d = Dev(w)
@@ -121,6 +126,7 @@ def test_dense_random(seed, Hq, Hkv, D, bs, ctx):
 @pytest.mark.parametrize("split", [128, 256, 512, 1024, 2048])
 def test_dense_split_sizes_agree(split, monkeypatch):
     """Any split partition gives the same attention (the combine identity)."""
+    monkeypatch.setenv("GPKV_ATTN_SCHEDULE", "split")
     monkeypatch.setenv("GPKV_SPLIT_TOKENS", str(split))
     assert gp.split_tokens(3, 4, 4000) == split
     w = workloads.random_case(210, batch=3, num_q_heads=28, num_kv_heads=4, head_dim=128,
@@ -383,9 +389,11 @@ def _sparse(d, w, sel):
                                             scale=float(w.scale))
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("config,K", [(1, 3), (1, 5), (3, 64), (4, 256), (5, 32)])
-def test_sparse_config_fixed_selection(config, K):
+def test_sparse_config_fixed_selection(config, K, schedule, monkeypatch):
     """Sparse kernel judged with the selection fixed to the oracle's Top-K."""
+    monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
     w = workload(config)
     d = Dev(w)
     omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, w.block_size)
@@ -400,7 +408,9 @@ def test_sparse_config_fixed_selection(config, K):
     assert err <= ATOL
 
 
-def test_sparse_all_blocks_equals_dense_and_handles_holes():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_sparse_all_blocks_equals_dense_and_handles_holes(schedule, monkeypatch):
+    monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
     w = workloads.random_case(330, batch=3, num_q_heads=28, num_kv_heads=4, head_dim=128,
                               block_size=16, context_lens=[300, 17, 1000])
     d = Dev(w)
@@ -419,6 +429,7 @@ def test_sparse_all_blocks_equals_dense_and_handles_holes():
     sel2[0, 0] = [5, -1, 2, 18, -1, 0]
     sel2[0, 1] = [-1, -1, -1, -1, -1, 1]
     sel2[1, 2] = [1, 0, -1, -1, -1, -1]
+    sel2[1, 3] = [-1, -1, -1, -1, 1, 0]   # valid ids only past position min(K, blocks) = 2
     sel2[2, 3] = [62, 61, 3, -1, 9, 10]
     out = _sparse(d, w, to_dev(sel2, torch.int32)).cpu().numpy()
     ref2 = oracle.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache,
