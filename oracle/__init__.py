@@ -32,6 +32,12 @@ Readings where the pages are silent (each also listed in the design doc):
      ascending, padded with -1; K >= nb selects every block.
   R6 masked / unselected tokens contribute exactly nothing (even if their K/V
      bits are NaN).
+  R7 FP8 KV cache (the KV-quantisation lever of [TL18] 2.5 and 3.1): codes are
+     OCP FP8 E4M3 (bias 7, no infinities, largest finite 448); K and V each carry
+     one float32 scale per KV head. Stored code = the E4M3 value nearest to
+     float32(x) * float32(1 / scale) (both float32 operations), ties to the even
+     code, magnitudes past 448 saturating to 448, NaN to 0x7F; the value read back
+     is code * scale.
 
 Parity pins for every function live in tests/test_oracle.py; none of them
 re-types a formula from here.
@@ -46,7 +52,8 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16_exact", "reshape_and_cache", "gather_sequence",
     "paged_attention_decode", "quest_block_metadata", "quest_block_scores",
     "quest_select_topk", "sparse_token_positions", "sparse_paged_attention_decode",
-    "split_kv_partials", "split_kv_combine",
+    "split_kv_partials", "split_kv_combine", "e4m3_to_f64", "e4m3_from_f32",
+    "fp8_inverse_scale", "quantize_fp8", "reshape_and_cache_fp8", "paged_attention_decode_fp8",
 ]
 
 
@@ -327,4 +334,91 @@ def sparse_paged_attention_decode(query, key_cache, value_cache, block_tables, c
             v = bf16_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs))[:, g]
             heads = slice(g * G, (g + 1) * G)
             out[b, heads] = _softmax_attention(q[b, heads], k, v, sc)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# C7 -- FP8 (OCP E4M3) KV cache: quantise on write, dequantise on read  (R7)
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Closed-form decode: sign s, exponent e (4 bits, bias 7), mantissa m (3 bits);
+    e = 0 is subnormal (m * 2^-9); e = 15 with m = 7 is NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >= 128, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+# The finite non-negative values in code order (codes 0x00 .. 0x7E), increasing.
+_E4M3_POS = e4m3_to_f64(np.arange(127, dtype=np.uint8))
+
+
+def e4m3_from_f32(y: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 value to each float32 y (by value), ties to the even code;
+    |y| > 448 saturates to 448; NaN gives 0x7F. The sign bit follows y's (so -0
+    and negative values that round to zero give 0x80)."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y.astype(np.float64))
+    a_clip = np.minimum(a, E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a_clip, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = np.abs(a_clip - _E4M3_POS[lo])
+    d_hi = np.abs(_E4M3_POS[hi] - a_clip)
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = pick.astype(np.uint8) | np.where(np.signbit(y), np.uint8(0x80), np.uint8(0))
+    return np.where(np.isnan(y), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def fp8_inverse_scale(scale) -> np.ndarray:
+    """float32(1 / scale), one float32 division per KV head."""
+    return np.float32(1.0) / np.asarray(scale, dtype=np.float32)
+
+
+def quantize_fp8(x_bits: np.ndarray, scale) -> np.ndarray:
+    """bf16 rows [..., H_kv, D] -> E4M3 codes, per KV head g: e4m3(x * (1/scale_g))."""
+    x = (np.asarray(x_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    inv = fp8_inverse_scale(scale)                      # [H_kv]
+    y = (x * inv[:, None]).astype(np.float32)           # one float32 rounding
+    return e4m3_from_f32(y)
+
+
+def reshape_and_cache_fp8(key_cache, value_cache, key, value, slot_mapping, block_size,
+                          k_scale, v_scale):
+    """ReshapeAndCache into E4M3 caches: the same slot rule as ``reshape_and_cache``,
+    each row quantised with its KV head's scale. Returns new (key_cache, value_cache)."""
+    kq = quantize_fp8(key, k_scale)
+    vq = quantize_fp8(value, v_scale)
+    return reshape_and_cache(key_cache, value_cache, kq, vq, slot_mapping, block_size)
+
+
+def paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                               context_lens, scale, seqs=None):
+    """Dense decode attention over E4M3 caches: the definition of
+    ``paged_attention_decode`` applied to K = code * k_scale[g], V = code * v_scale[g]."""
+    B, Hq, D = query.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    if Hq % Hkv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = Hq // Hkv
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    _check_table(block_tables, ctx, bs, NB)
+    ks = np.asarray(k_scale, dtype=np.float32).astype(np.float64)
+    vs = np.asarray(v_scale, dtype=np.float32).astype(np.float64)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    q = bf16_to_f64(query)
+    sc = float(np.float32(scale))
+    for b in (range(B) if seqs is None else seqs):
+        pos = np.arange(int(ctx[b]))
+        k = e4m3_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs)) * ks[:, None]
+        v = e4m3_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs)) * vs[:, None]
+        for g in range(Hkv):
+            heads = slice(g * G, (g + 1) * G)
+            out[b, heads] = _softmax_attention(q[b, heads], k[:, g], v[:, g], sc)
     return out

@@ -487,4 +487,134 @@ def pin_sparse_brute_force(orc):
             assert np.abs(s[b, h] - ref).max() <= TOL, (b, h)
 
 
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) KV cache
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3(values_f32):
+    """torch's CPU float8_e4m3fn conversion (round to nearest even), as codes."""
+    import torch
+    t = torch.from_numpy(np.asarray(values_f32, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_fp8_decode_matches_torch(orc):
+    import torch
+    c = np.arange(256, dtype=np.uint8)
+    got = orc.e4m3_to_f64(c)
+    exp = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(exp))
+    ok = ~np.isnan(exp)
+    assert np.array_equal(got[ok], exp[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(exp[ok]))
+
+
+def pin_fp8_encode_matches_torch_in_range(orc):
+    """Every finite bf16 value of magnitude <= 448 encodes as torch encodes it."""
+    bits = np.arange(65536, dtype=np.uint32) << np.uint32(16)
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v) & (np.abs(v) <= 448.0)]
+    assert np.array_equal(orc.e4m3_from_f32(v), _torch_e4m3(v))
+
+
+def pin_fp8_encode_saturates_nan_and_sign(orc):
+    big = np.array([448.5, 463.9, 464.0, 470.0, 1e4, 3e38, np.inf], np.float32)
+    assert (orc.e4m3_from_f32(big) == 0x7E).all()
+    assert (orc.e4m3_from_f32(-big) == 0xFE).all()
+    assert orc.e4m3_from_f32(np.array([np.nan], np.float32))[0] == 0x7F
+    assert orc.e4m3_from_f32(np.array([-0.0], np.float32))[0] == 0x80
+    assert orc.e4m3_from_f32(np.array([-1e-30], np.float32))[0] == 0x80
+
+
+def _e4m3_value_py(code):
+    s, e, m = code >> 7, (code >> 3) & 15, code & 7
+    v = Fraction(m, 512) if e == 0 else Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+    return -v if s else v
+
+
+def pin_fp8_encode_nearest_bruteforce(orc):
+    """The code of y is a nearest finite value (exact rational distances); on an
+    exact tie, the even code."""
+    rng = np.random.default_rng(71)
+    mags = np.exp2(rng.uniform(-13.0, 9.0, size=400)).astype(np.float32)
+    ys = np.concatenate([mags, -mags, np.array([2.0 ** -10, 1.0625, 1.1875, 3 * 2.0 ** -11,
+                                                 0.0, 432.0, 240.0], np.float32)])
+    finite = [c for c in range(256) if not ((c >> 3) & 15 == 15 and c & 7 == 7)]
+    vals = {c: _e4m3_value_py(c) for c in finite}
+    codes = orc.e4m3_from_f32(ys)
+    for y, c in zip(ys.tolist(), codes.tolist()):
+        fy = Fraction(y)
+        best = min(abs(v - fy) for v in vals.values())
+        assert abs(vals[c] - fy) == best, (y, hex(c))
+        ties = [k for k, v in vals.items() if abs(v - fy) == best and (v != 0 or k in (0, 0x80))]
+        ties = sorted({k & 0x7F for k in ties})
+        if len(ties) > 1:
+            assert (c & 0x7F) % 2 == 0, (y, hex(c))
+
+
+def pin_fp8_quantize_hand_worked(orc):
+    """x = 1.0 with scale 3: float32(1/3) * 1.0 = 0.33333334; the E4M3 neighbours
+    are 0.3125 (0x2A) and 0.34375 (0x2B); the nearer is 0x2B. With scale 0.5 the
+    product is 2.0 exactly: code 0x40."""
+    one = np.array([[[0x3F80]]], np.uint16)                 # bf16 1.0, [1, 1, 1]
+    assert orc.quantize_fp8(one, [3.0])[0, 0, 0] == 0x2B
+    assert orc.quantize_fp8(one, [0.5])[0, 0, 0] == 0x40
+    neg = np.array([[[0xC0A0]]], np.uint16)                 # bf16 -5.0
+    assert orc.quantize_fp8(neg, [0.5])[0, 0, 0] == 0xD2    # -10 = -(1.25 * 2^3)
+
+
+def _representable_case(seed, scales):
+    """A small paged case whose K/V values are E4M3 values times a power-of-two scale
+    per KV head (exact in bf16 and exact under quantisation)."""
+    w = workloads.random_case(seed, batch=3, num_q_heads=6, num_kv_heads=2, head_dim=64,
+                              block_size=16, context_lens=[1, 40, 70])
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(255) if c not in (0x7F,)], np.uint8)
+
+    def pick(shape):
+        codes = rng.choice(finite, size=shape)
+        vals = np.asarray(_e4m3_f64_ref(codes)) * np.asarray(scales)[:, None]
+        return (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w.key_cache = pick(w.key_cache.shape)
+    w.value_cache = pick(w.value_cache.shape)
+    return w
+
+
+def _e4m3_f64_ref(codes):
+    return np.vectorize(lambda c: float(_e4m3_value_py(int(c))))(codes)
+
+
+def pin_fp8_write_roundtrip_exact(orc):
+    scales = [0.5, 4.0]
+    w = _representable_case(72, scales)
+    NB, bs, Hkv, D = w.key_cache.shape
+    slots = np.array([3, 40, -1, 17], np.int64)
+    rows = w.key_cache[slots[slots >= 0] // bs, slots[slots >= 0] % bs]   # representable rows
+    key = np.concatenate([rows, rows[:1]])
+    kc0 = np.zeros((NB, bs, Hkv, D), np.uint8)
+    kc, vc = orc.reshape_and_cache_fp8(kc0, kc0, key, key, slots, bs, scales, scales)
+    back = orc.e4m3_to_f64(kc) * np.asarray(scales)[None, None, :, None]
+    for i, s_ in enumerate(slots.tolist()):
+        if s_ < 0:
+            continue
+        assert np.array_equal(back[s_ // bs, s_ % bs], _dec(key[i]))
+    written = np.zeros((NB, bs), bool)
+    written[slots[slots >= 0] // bs, slots[slots >= 0] % bs] = True
+    assert (kc[~written] == 0).all() and np.array_equal(kc, vc)
+
+
+def pin_fp8_attention_equals_bf16_on_representable(orc):
+    """With values exactly representable, FP8 attention is bf16 attention."""
+    scales_k, scales_v = [0.5, 4.0], [2.0, 0.25]
+    w = _representable_case(73, scales_k)
+    wv = _representable_case(74, scales_v)
+    vcache = wv.value_cache
+    kq = orc.quantize_fp8(w.key_cache, scales_k)
+    vq = orc.quantize_fp8(vcache, scales_v)
+    got = orc.paged_attention_decode_fp8(w.query, kq, vq, scales_k, scales_v, w.block_tables,
+                                         w.context_lens, w.scale)
+    exp = orc.paged_attention_decode(w.query, w.key_cache, vcache, w.block_tables,
+                                     w.context_lens, w.scale)
+    assert np.abs(got - exp).max() <= TOL
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -39,6 +39,16 @@ MUTANTS = [
      "pos.extend(range(lb * block_size, (lb + 1) * block_size))"),
     ("sparse: selection of KV head 0 for all", "pos = sparse_token_positions(topk_indices[b, g], ctx[b], bs)",
      "pos = sparse_token_positions(topk_indices[b, 0], ctx[b], bs)"),
+    ("fp8: ties away from zero", "np.where(lo % 2 == 0, lo, hi)", "hi"),
+    ("fp8: exponent bias 8", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    ("fp8: subnormal step 2^-8", "m * 2.0 ** -9", "m * 2.0 ** -8"),
+    ("fp8: sign dropped on encode",
+     "code = pick.astype(np.uint8) | np.where(np.signbit(y), np.uint8(0x80), np.uint8(0))",
+     "code = pick.astype(np.uint8)"),
+    ("fp8: scale multiplied on write", "y = (x * inv[:, None])",
+     "y = (x * np.asarray(scale, dtype=np.float32)[:, None])"),
+    ("fp8: k scale dropped on read", "* ks[:, None]", "* 1.0"),
+    ("fp8: v scale dropped on read", "* vs[:, None]", "* 1.0"),
 ]
 
 
