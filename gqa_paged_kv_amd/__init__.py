@@ -8,11 +8,13 @@ kernels; there is no CPU or PyTorch fallback.
 from .ops import (GpkvError, paged_attention_decode, paged_attention_workspace_bytes,
                   quest_block_metadata, quest_select_topk, quest_select_workspace_bytes,
                   reshape_and_cache, reshape_and_cache_quest, sparse_attention_workspace_bytes,
-                  sparse_paged_attention_decode, split_tokens)
+                  sparse_paged_attention_decode, split_tokens, reshape_and_cache_fp8,
+                  paged_attention_decode_fp8, sparse_paged_attention_decode_fp8)
 
 __all__ = [
     "GpkvError", "reshape_and_cache", "reshape_and_cache_quest", "paged_attention_decode",
     "quest_block_metadata",
     "quest_select_topk", "sparse_paged_attention_decode", "paged_attention_workspace_bytes",
     "quest_select_workspace_bytes", "sparse_attention_workspace_bytes", "split_tokens",
+    "reshape_and_cache_fp8", "paged_attention_decode_fp8", "sparse_paged_attention_decode_fp8",
 ]

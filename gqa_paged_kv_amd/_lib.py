@@ -37,6 +37,15 @@ SIGNATURES = {
                                                      c_int32, c_int32, c_int32, c_int32,
                                                      c_int64, c_int32, c_int32, c_int32,
                                                      c_float, vp, c_size, vp]),
+    "gpkv_reshape_and_cache_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, vp, c_int32, c_int32,
+                                             c_int32, c_int32, c_int64, vp]),
+    "gpkv_paged_attention_decode_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, c_int32,
+                                                  c_int32, c_int32, c_int32, c_int32, c_int64,
+                                                  c_int32, c_int32, c_float, vp, c_size, vp]),
+    "gpkv_sparse_paged_attention_decode_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                         c_int32, c_int32, c_int32, c_int32,
+                                                         c_int32, c_int64, c_int32, c_int32,
+                                                         c_int32, c_float, vp, c_size, vp]),
     "gpkv_status_string": (ctypes.c_char_p, [c_int32]),
     "gpkv_last_error_message": (ctypes.c_char_p, []),
     "gpkv_split_tokens": (c_int32, [c_int32, c_int32, c_int32]),

@@ -26,6 +26,7 @@ def command(out: str = LIB) -> list[str]:
     return [
         HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-fhip-fp32-correctly-rounded-divide-sqrt",
         "-Wno-unused-command-line-argument",
         "-I", INCLUDE, "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],

@@ -55,6 +55,9 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned o
 __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLoadNT);
 }
+__device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kLoadNT);
+}
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
@@ -65,6 +68,37 @@ __device__ __forceinline__ unsigned pack_lo16(unsigned a, unsigned b) {
 }
 __device__ __forceinline__ unsigned pack_hi16(unsigned a, unsigned b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 (OCP E4M3: bias 7, no infinities, largest finite 448, NaN = S.1111.111)
+// ---------------------------------------------------------------------------
+
+// Nearest E4M3 code of a float32, ties to the even code, |y| > 448 saturating to
+// 448, NaN -> 0x7F; the sign bit is y's. Integer arithmetic on the float32 bits.
+__device__ __forceinline__ unsigned e4m3_from_f32(float y) {
+  const unsigned u = __float_as_uint(y);
+  const unsigned sign = (u >> 24) & 0x80u;
+  const unsigned a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;             // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;     // |y| >= 448 (and inf)
+  if (a < 0x3c800000u) {                         // |y| < 2^-6: steps of 2^-9
+    const float t = __uint_as_float(a) * 512.0f;  // exact, t < 8
+    return sign | (unsigned)__builtin_rintf(t);  // ties to even; 8 is the first normal
+  }
+  // Normal: keep 3 of the 23 mantissa bits, rounding to nearest even.
+  const unsigned r = a + 0x7ffffu + ((a >> 20) & 1u);
+  const unsigned code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+  return sign | code;                            // a < 448 keeps code <= 0x7e
+}
+
+// Four E4M3 codes (one per byte of w, lowest byte first) -> four bf16 values
+// packed two per word. Every E4M3 value is exact in bf16.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(unsigned w) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);   // bytes 0, 1
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);    // bytes 2, 3
+  return u32x2{pack_hi16(__float_as_uint(lo[0]), __float_as_uint(lo[1])),
+               pack_hi16(__float_as_uint(hi[0]), __float_as_uint(hi[1]))};
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {

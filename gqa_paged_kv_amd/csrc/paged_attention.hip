@@ -70,10 +70,12 @@ constexpr int kBalTab = 4096;           // balanced path: table entries staged i
 
 struct AttnCommon {
   const unsigned short* q;   // [B, H_q, D] bf16
-  const unsigned char* kc;   // [NB, bs, H_kv, D] bf16
+  const unsigned char* kc;   // [NB, bs, H_kv, D] bf16 or E4M3 codes
   const unsigned char* vc;
-  long long block_bytes;     // bs * H_kv * D * 2
-  int row_bytes;             // H_kv * D * 2
+  const float* k_scale;      // [H_kv] (E4M3 caches only)
+  const float* v_scale;
+  long long block_bytes;     // bs * H_kv * D * element bytes
+  int row_bytes;             // H_kv * D * element bytes
   int Hq, Hkv, G, bs;
   float qk_scale_log2;       // softmax scale * log2(e)
 };
@@ -99,23 +101,70 @@ struct VecT<64> {
 // unit; `desc(u, pb, row0, nv)` names sub-tile u's physical block, first row and
 // valid rows (nv = 0: nothing selected). Writes the unit's normalised output
 // o_dst[h][D] and base-2 log-sum-exp lse_dst[h] for h < G.
-template <int D, class Desc>
+// Channel of contraction slot j (< 8) of k-step s in lane group qd. bf16 caches:
+// 32s + 8qd + j, so one 16-byte load per k-step. E4M3 caches: k-steps pair up
+// (s = 2t + h) on 64t + 16qd + 8h + j, so one 16-byte load of codes serves two
+// k-steps. The query operand follows the same order.
+template <bool FP8>
+__device__ __forceinline__ int kstep_channel(int s, int qd) {
+  return FP8 ? 64 * (s >> 1) + 16 * qd + 8 * (s & 1) : 32 * s + 8 * qd;
+}
+
+// E4M3 code words -> bf16 operands: 16 codes (u32x4) give two k-step operands;
+// one token's CPL codes give its V^T slice.
+__device__ __forceinline__ void k_codes_to_bf16(u32x4 w, u32x4& s0, u32x4& s1) {
+  const u32x2 a = e4m3x4_to_bf16(w[0]), b = e4m3x4_to_bf16(w[1]);
+  const u32x2 c = e4m3x4_to_bf16(w[2]), d = e4m3x4_to_bf16(w[3]);
+  s0 = u32x4{a[0], a[1], b[0], b[1]};
+  s1 = u32x4{c[0], c[1], d[0], d[1]};
+}
+template <int D>
+struct VCodes;
+template <>
+struct VCodes<128> {   // 8 codes per token
+  typedef u32x2 type;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return buf_load8(r, off);
+  }
+  static __device__ __forceinline__ u32x4 to_bf16(type w) {
+    const u32x2 a = e4m3x4_to_bf16(w[0]), b = e4m3x4_to_bf16(w[1]);
+    return u32x4{a[0], a[1], b[0], b[1]};
+  }
+};
+template <>
+struct VCodes<64> {    // 4 codes per token
+  typedef unsigned type;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return buf_load4(r, off);
+  }
+  static __device__ __forceinline__ u32x2 to_bf16(type w) { return e4m3x4_to_bf16(w); }
+};
+
+template <int D, bool FP8, class Desc>
 __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, int n_sub,
                                             const Desc& desc, float* o_dst, float* lse_dst) {
   constexpr int KSTEPS = D / 32;  // k-steps of the q.k contraction
+  constexpr int KLOADS = FP8 ? D / 64 : KSTEPS;   // 16-byte K loads per sub-tile
   constexpr int CPL = D / 16;     // channels per lane in the V^T operand / O^T tiles
-  constexpr int VBYTES = CPL * 2;
+  constexpr int EB = FP8 ? 1 : 2; // bytes per cached element
   typedef typename VecT<D>::type vvec;
+  typedef typename VCodes<D>::type vcodes;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, qd = lane >> 4;
   const int G = c.G;
+  // E4M3 caches: K's scale joins the softmax scale, V's scales the output.
+  float qk_scale = c.qk_scale_log2, v_scale = 1.f;
+  if constexpr (FP8) {
+    qk_scale *= c.k_scale[g];
+    v_scale = c.v_scale[g];
+  }
 
-  // Q^T operand: lane holds head r's channels 32s + 8qd .. +8 (zero rows past G).
+  // Q^T operand: lane holds head r's channels of each k-step (zero rows past G).
   u32x4 qf[KSTEPS];
   if (r < G) {
     const unsigned short* qrow = c.q + ((size_t)b * c.Hq + (size_t)g * G + r) * D;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qrow + 32 * s + 8 * qd);
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qrow + kstep_channel<FP8>(s, qd));
   } else {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
@@ -127,8 +176,8 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
   float m_run = -INFINITY;  // running max of head r (base 2), same in its 4 lanes
   float l_run = 0.f;        // this lane's share of the normaliser
 
-  const unsigned off_k = (unsigned)(r * c.row_bytes + g * D * 2 + qd * 16);
-  const unsigned off_v = (unsigned)(4 * qd * c.row_bytes + g * D * 2 + r * VBYTES);
+  const unsigned off_k = (unsigned)(r * c.row_bytes + g * D * EB + qd * 16);
+  const unsigned off_v = (unsigned)(4 * qd * c.row_bytes + g * D * EB + r * CPL * EB);
   const int n_tiles = (n_sub + 1) >> 1;
 
   auto describe = [&](int k, int* pb, int* row0, int* nv) {
@@ -160,15 +209,24 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
     return n_tiles;
   };
 
+  // In flight: bf16 operands (kf, vf), or E4M3 codes (kq, vq) converted to bf16
+  // operands right before their MFMAs.
   u32x4 kf[2][KSTEPS];
   vvec vf[2][4];
+  u32x4 kq[2][KLOADS];
+  vcodes vq[2][4];
   auto issue_k = [&](const int* pb, const int* row0, const int* nv) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const size_t base = (size_t)pb[sub] * (size_t)c.block_bytes + (size_t)row0[sub] * c.row_bytes;
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(c.kc + base, (unsigned)(nv[sub] * c.row_bytes));
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) kf[sub][s] = buf_load16(rk, off_k + 64 * s);
+      for (int s = 0; s < KLOADS; ++s) {
+        if constexpr (FP8)
+          kq[sub][s] = buf_load16(rk, off_k + 64 * s);
+        else
+          kf[sub][s] = buf_load16(rk, off_k + 64 * s);
+      }
     }
   };
   auto issue_v = [&](const int* pb, const int* row0, const int* nv) {
@@ -177,7 +235,12 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
       const size_t base = (size_t)pb[sub] * (size_t)c.block_bytes + (size_t)row0[sub] * c.row_bytes;
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(c.vc + base, (unsigned)(nv[sub] * c.row_bytes));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vf[sub][i] = VecT<D>::load(rv, off_v + i * c.row_bytes);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (FP8)
+          vq[sub][i] = VCodes<D>::load(rv, off_v + i * c.row_bytes);
+        else
+          vf[sub][i] = VecT<D>::load(rv, off_v + i * c.row_bytes);
+      }
     }
   };
 
@@ -196,6 +259,12 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
   issue_v(pb, row0, nv);
   __builtin_amdgcn_sched_barrier(0);
   while (k < n_tiles) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int t = 0; t < KLOADS; ++t) k_codes_to_bf16(kq[sub][t], kf[sub][2 * t], kf[sub][2 * t + 1]);
+    }
     // S^T for both sub-tiles.
     f32x4 sacc[2];
 #pragma unroll
@@ -212,7 +281,7 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = sacc[sub][i] * c.qk_scale_log2;
+        const float x = sacc[sub][i] * qk_scale;
         sv[sub * 4 + i] = (4 * qd + i < nv[sub]) ? x : -INFINITY;
       }
     float mx = sv[0];
@@ -248,6 +317,12 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
       plo[d] = pack_hi16(__float_as_uint(ra), __float_as_uint(rc));
     }
 
+    if constexpr (FP8) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vf[sub][i] = VCodes<D>::to_bf16(vq[sub][i]);
+    }
     // O^T += V^T P^T, one 16-channel tile j at a time.
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -276,7 +351,7 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (r < G) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
     float* dst = o_dst + (size_t)r * D + CPL * 4 * qd;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -311,7 +386,7 @@ struct SplitParams {
   int max_blocks, max_ctx, num_splits, split_tokens, topk_blocks;
 };
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool FP8>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_split_kernel(const SplitParams p) {
   // Entry e covers virtual tokens [t0 + e*bs, t0 + (e+1)*bs): s_pb = physical
   // block (-1: nothing selected), s_tok0 = logical position of the block's row 0.
@@ -365,7 +440,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       pb = uniform(x < 0 ? 0 : x);
     };
     const size_t unit = ((size_t)b * Hkv + g) * p.num_splits + split;
-    attend_head<D>(p.c, b, g, T / 16, desc, p.part_o + unit * G * D, p.part_lse + unit * G);
+    attend_head<D, FP8>(p.c, b, g, T / 16, desc, p.part_o + unit * G * D, p.part_lse + unit * G);
   }
 }
 
@@ -412,7 +487,7 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* s_wave, int* total)
 // min(K, blocks) blocks. Valid ids of one KV head's list are distinct blocks of the
 // sequence, so no head has more valid entries than that, wherever they sit in its
 // list; lists from Top-K have exactly that many.
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool FP8>
 __global__ __launch_bounds__(kWaves * 64) void attn_balanced_kernel(const BalParams p) {
   __shared__ int s_pref[kMaxBalBatch + 1];
   __shared__ int s_pb[kBalTab];                  // physical block per table entry (-1: none)
@@ -520,7 +595,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_balanced_kernel(const BalPar
         pb = uniform(x < 0 ? 0 : x);
       };
       const size_t unit = slot * Hkv + g;
-      attend_head<D>(p.c, b, g, ue - ub, desc, p.part_o + unit * G * D, p.part_lse + unit * G);
+      attend_head<D, FP8>(p.c, b, g, ue - ub, desc, p.part_o + unit * G * D, p.part_lse + unit * G);
     }
   }
 }
@@ -827,16 +902,29 @@ static int check_common(const char* fn, int B, int Hq, int Hkv, int D, int bs, l
   return GPKV_OK;
 }
 
-static int attn_run(bool sparse, float* out, const void* query, const void* kc, const void* vc,
-                    const int* bt, const int* ctx, const int* topk, int B, int Hq, int Hkv, int D,
-                    int bs, long long NB, int max_blocks, int max_ctx, int K, float scale,
-                    void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = sparse ? "sparse_paged_attention_decode" : "paged_attention_decode";
+template <int D, bool SPARSE, bool FP8>
+static void launch_attention(bool balanced, const BalParams& bp, const SplitParams& sp, int nwg,
+                             int num_splits, int B, hipStream_t stream) {
+  const dim3 block(kWaves * 64);
+  if (balanced)
+    attn_balanced_kernel<D, SPARSE, FP8><<<dim3(nwg), block, 0, stream>>>(bp);
+  else
+    attn_split_kernel<D, SPARSE, FP8><<<dim3(num_splits, B), block, 0, stream>>>(sp);
+}
+
+static int attn_run(bool sparse, bool fp8, float* out, const void* query, const void* kc,
+                    const void* vc, const float* k_scale, const float* v_scale, const int* bt,
+                    const int* ctx, const int* topk, int B, int Hq, int Hkv, int D, int bs,
+                    long long NB, int max_blocks, int max_ctx, int K, float scale, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  const char* fn = sparse ? (fp8 ? "sparse_paged_attention_decode_fp8" : "sparse_paged_attention_decode")
+                          : (fp8 ? "paged_attention_decode_fp8" : "paged_attention_decode");
   int st = check_common(fn, B, Hq, Hkv, D, bs, NB, max_blocks, max_ctx);
   if (st) return st;
   if (sparse && K < 1) return fail(GPKV_ERR_SHAPE, "%s: topk_blocks=%d < 1", fn, K);
   if (B == 0) return GPKV_OK;
-  if (!out || !query || !kc || !vc || !bt || !ctx || (sparse && !topk))
+  if (!out || !query || !kc || !vc || !bt || !ctx || (sparse && !topk) ||
+      (fp8 && (!k_scale || !v_scale)))
     return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
   const long long span_ll = sparse ? (long long)K * bs : (long long)max_ctx;
   if (span_ll > (1LL << 30)) return fail(GPKV_ERR_SHAPE, "%s: token span too large", fn);
@@ -854,7 +942,9 @@ static int attn_run(bool sparse, float* out, const void* query, const void* kc, 
   c.q = (const unsigned short*)query;
   c.kc = (const unsigned char*)kc;
   c.vc = (const unsigned char*)vc;
-  c.row_bytes = Hkv * D * 2;
+  c.k_scale = k_scale;
+  c.v_scale = v_scale;
+  c.row_bytes = Hkv * D * (fp8 ? 1 : 2);
   c.block_bytes = (long long)bs * c.row_bytes;
   c.Hq = Hq;
   c.Hkv = Hkv;
@@ -865,59 +955,43 @@ static int attn_run(bool sparse, float* out, const void* query, const void* kc, 
   float* part_lse = (float*)((char*)ws + pl.o_bytes);
   int* prefix = (int*)((char*)ws + pl.o_bytes + pl.lse_bytes);
 
-  if (pl.balanced) {
-    BalParams bp;
-    bp.c = c;
-    bp.part_o = part_o;
-    bp.part_lse = part_lse;
-    bp.prefix = prefix;
-    bp.block_tables = bt;
-    bp.ctx = ctx;
-    bp.NB = NB;
-    bp.B = B;
-    bp.max_blocks = max_blocks;
-    bp.max_ctx = max_ctx;
-    bp.nwg = pl.nwg;
-    bp.topk = topk;
-    bp.topk_blocks = sparse ? K : 0;
-    const dim3 grid(pl.nwg), block(kWaves * 64);
-    if (D == 128) {
-      if (sparse)
-        attn_balanced_kernel<128, true><<<grid, block, 0, stream>>>(bp);
-      else
-        attn_balanced_kernel<128, false><<<grid, block, 0, stream>>>(bp);
-    } else {
-      if (sparse)
-        attn_balanced_kernel<64, true><<<grid, block, 0, stream>>>(bp);
-      else
-        attn_balanced_kernel<64, false><<<grid, block, 0, stream>>>(bp);
-    }
-  } else {
-    SplitParams sp;
-    sp.c = c;
-    sp.part_o = part_o;
-    sp.part_lse = part_lse;
-    sp.block_tables = bt;
-    sp.ctx = ctx;
-    sp.topk = topk;
-    sp.NB = NB;
-    sp.max_blocks = max_blocks;
-    sp.max_ctx = max_ctx;
-    sp.num_splits = pl.num_splits;
-    sp.split_tokens = pl.split_tokens;
-    sp.topk_blocks = sparse ? K : 0;
-    const dim3 grid(pl.num_splits, B), block(kWaves * 64);
-    if (D == 128) {
-      if (sparse)
-        attn_split_kernel<128, true><<<grid, block, 0, stream>>>(sp);
-      else
-        attn_split_kernel<128, false><<<grid, block, 0, stream>>>(sp);
-    } else {
-      if (sparse)
-        attn_split_kernel<64, true><<<grid, block, 0, stream>>>(sp);
-      else
-        attn_split_kernel<64, false><<<grid, block, 0, stream>>>(sp);
-    }
+  BalParams bp;
+  bp.c = c;
+  bp.part_o = part_o;
+  bp.part_lse = part_lse;
+  bp.prefix = prefix;
+  bp.block_tables = bt;
+  bp.ctx = ctx;
+  bp.topk = topk;
+  bp.NB = NB;
+  bp.B = B;
+  bp.max_blocks = max_blocks;
+  bp.max_ctx = max_ctx;
+  bp.nwg = pl.nwg;
+  bp.topk_blocks = sparse ? K : 0;
+  SplitParams sp;
+  sp.c = c;
+  sp.part_o = part_o;
+  sp.part_lse = part_lse;
+  sp.block_tables = bt;
+  sp.ctx = ctx;
+  sp.topk = topk;
+  sp.NB = NB;
+  sp.max_blocks = max_blocks;
+  sp.max_ctx = max_ctx;
+  sp.num_splits = pl.num_splits;
+  sp.split_tokens = pl.split_tokens;
+  sp.topk_blocks = sparse ? K : 0;
+  const int sel = (D == 128 ? 4 : 0) + (sparse ? 2 : 0) + (fp8 ? 1 : 0);
+  switch (sel) {
+    case 0: launch_attention<64, false, false>(pl.balanced, bp, sp, pl.nwg, pl.num_splits, B, stream); break;
+    case 1: launch_attention<64, false, true>(pl.balanced, bp, sp, pl.nwg, pl.num_splits, B, stream); break;
+    case 2: launch_attention<64, true, false>(pl.balanced, bp, sp, pl.nwg, pl.num_splits, B, stream); break;
+    case 3: launch_attention<64, true, true>(pl.balanced, bp, sp, pl.nwg, pl.num_splits, B, stream); break;
+    case 4: launch_attention<128, false, false>(pl.balanced, bp, sp, pl.nwg, pl.num_splits, B, stream); break;
+    case 5: launch_attention<128, false, true>(pl.balanced, bp, sp, pl.nwg, pl.num_splits, B, stream); break;
+    case 6: launch_attention<128, true, false>(pl.balanced, bp, sp, pl.nwg, pl.num_splits, B, stream); break;
+    default: launch_attention<128, true, true>(pl.balanced, bp, sp, pl.nwg, pl.num_splits, B, stream); break;
   }
   st = check_launch(fn);
   if (st) return st;
@@ -996,10 +1070,10 @@ extern "C" int gpkv_paged_attention_decode(float* out, const void* query, const 
                                            int32_t max_context_len, float scale, void* workspace,
                                            size_t workspace_bytes, void* stream) {
   clear_error();
-  return attn_run(false, out, query, key_cache, value_cache, block_tables, context_lens, nullptr,
-                  batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                  max_blocks_per_seq, max_context_len, 0, scale, workspace, workspace_bytes,
-                  (hipStream_t)stream);
+  return attn_run(false, false, out, query, key_cache, value_cache, nullptr, nullptr,
+                  block_tables, context_lens, nullptr, batch, num_q_heads, num_kv_heads, head_dim,
+                  block_size, num_blocks, max_blocks_per_seq, max_context_len, 0, scale,
+                  workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 extern "C" int gpkv_sparse_paged_attention_decode(
@@ -1009,8 +1083,35 @@ extern "C" int gpkv_sparse_paged_attention_decode(
     int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t topk_blocks, float scale, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
-  return attn_run(true, out, query, key_cache, value_cache, block_tables, context_lens,
-                  topk_indices, batch, num_q_heads, num_kv_heads, head_dim, block_size,
-                  num_blocks, max_blocks_per_seq, max_context_len, topk_blocks, scale, workspace,
-                  workspace_bytes, (hipStream_t)stream);
+  return attn_run(true, false, out, query, key_cache, value_cache, nullptr, nullptr,
+                  block_tables, context_lens, topk_indices, batch, num_q_heads, num_kv_heads,
+                  head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                  topk_blocks, scale, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" int gpkv_paged_attention_decode_fp8(
+    float* out, const void* query, const void* key_cache, const void* value_cache,
+    const float* k_scale, const float* v_scale, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return attn_run(false, true, out, query, key_cache, value_cache, k_scale, v_scale,
+                  block_tables, context_lens, nullptr, batch, num_q_heads, num_kv_heads, head_dim,
+                  block_size, num_blocks, max_blocks_per_seq, max_context_len, 0, scale,
+                  workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" int gpkv_sparse_paged_attention_decode_fp8(
+    float* out, const void* query, const void* key_cache, const void* value_cache,
+    const float* k_scale, const float* v_scale, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* topk_indices, int32_t batch, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t topk_blocks, float scale,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return attn_run(true, true, out, query, key_cache, value_cache, k_scale, v_scale,
+                  block_tables, context_lens, topk_indices, batch, num_q_heads, num_kv_heads,
+                  head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                  topk_blocks, scale, workspace, workspace_bytes, (hipStream_t)stream);
 }

@@ -69,6 +69,43 @@ __global__ __launch_bounds__(64) void reshape_and_cache_quest_kernel(
   }
 }
 
+
+// FP8 write path: the same slot rule; each row is quantised to OCP E4M3 with its
+// KV head's scale: code = e4m3(x * (1 / scale)), both float32 operations (the
+// reciprocal is a correctly rounded division). 16 bf16 in, 16 bytes out per lane.
+__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv) {
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4& src = j < 2 ? a : b;
+    const unsigned w0 = src[(2 * j) & 3], w1 = src[(2 * j + 1) & 3];
+    const float y0 = bf16_lo(w0) * inv, y1 = bf16_hi(w0) * inv;
+    const float y2 = bf16_lo(w1) * inv, y3 = bf16_hi(w1) * inv;
+    out[j] = e4m3_from_f32(y0) | (e4m3_from_f32(y1) << 8) | (e4m3_from_f32(y2) << 16) |
+             (e4m3_from_f32(y3) << 24);
+  }
+  return out;
+}
+
+__global__ __launch_bounds__(64) void reshape_and_cache_fp8_kernel(
+    const u32x4* __restrict__ key, const u32x4* __restrict__ value, u32x4* __restrict__ key_cache,
+    u32x4* __restrict__ value_cache, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, const int64_t* __restrict__ slot_mapping, int row_vec8,
+    int head_dim, int block_size, long long num_slots) {
+  const int i = blockIdx.x;
+  const long long s = slot_mapping[i];
+  if (s < 0 || s >= num_slots) return;
+  const int row_vec = row_vec8 / 2;   // 16-byte vectors of one E4M3 row
+  const size_t dst = (size_t)s * (size_t)row_vec;
+  const size_t src = (size_t)i * (size_t)row_vec8;
+  for (int c = threadIdx.x; c < row_vec; c += 64) {
+    const int g = (16 * c) / head_dim;
+    const float kinv = 1.0f / k_scale[g], vinv = 1.0f / v_scale[g];
+    key_cache[dst + c] = quantize16(key[src + 2 * c], key[src + 2 * c + 1], kinv);
+    value_cache[dst + c] = quantize16(value[src + 2 * c], value[src + 2 * c + 1], vinv);
+  }
+}
+
 }  // namespace gpkv
 
 extern "C" int gpkv_reshape_and_cache(const void* key, const void* value, void* key_cache,
@@ -119,4 +156,31 @@ extern "C" int gpkv_reshape_and_cache_quest(const void* key, const void* value, 
       (u32x4*)key_min, (u32x4*)key_max, slot_mapping, row_vec, block_size,
       (long long)num_blocks * block_size);
   return check_launch("reshape_and_cache_quest");
+}
+
+extern "C" int gpkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                          void* value_cache, const float* k_scale,
+                                          const float* v_scale, const int64_t* slot_mapping,
+                                          int32_t num_tokens, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size,
+                                          int64_t num_blocks, void* stream) {
+  using namespace gpkv;
+  clear_error();
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
+    return fail(GPKV_ERR_SHAPE,
+                "reshape_and_cache_fp8: num_tokens=%d num_kv_heads=%d num_blocks=%lld",
+                num_tokens, num_kv_heads, (long long)num_blocks);
+  if (!supported_head_dim(head_dim))
+    return fail(GPKV_ERR_UNSUPPORTED, "reshape_and_cache_fp8: head_dim=%d (64 or 128)", head_dim);
+  if (!supported_block_size(block_size))
+    return fail(GPKV_ERR_UNSUPPORTED, "reshape_and_cache_fp8: block_size=%d (16/32/64/128)",
+                block_size);
+  if (num_tokens == 0) return GPKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !k_scale || !v_scale || !slot_mapping)
+    return fail(GPKV_ERR_NULL, "reshape_and_cache_fp8: null pointer argument");
+  const int row_vec8 = num_kv_heads * head_dim / 8;   // 16-byte vectors of one bf16 row
+  reshape_and_cache_fp8_kernel<<<dim3(num_tokens), dim3(64), 0, (hipStream_t)stream>>>(
+      (const u32x4*)key, (const u32x4*)value, (u32x4*)key_cache, (u32x4*)value_cache, k_scale,
+      v_scale, slot_mapping, row_vec8, head_dim, block_size, (long long)num_blocks * block_size);
+  return check_launch("reshape_and_cache_fp8");
 }

@@ -16,6 +16,7 @@ __all__ = [
     "quest_block_metadata",
     "quest_select_topk", "sparse_paged_attention_decode", "paged_attention_workspace_bytes",
     "quest_select_workspace_bytes", "sparse_attention_workspace_bytes", "split_tokens",
+    "reshape_and_cache_fp8", "paged_attention_decode_fp8", "sparse_paged_attention_decode_fp8",
 ]
 
 
@@ -223,4 +224,90 @@ def sparse_paged_attention_decode(query, key_cache, value_cache, block_tables, c
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
         _ptr(context_lens), _ptr(topk_indices), B, Hq, Hkv, D, bs, NB, MB, int(max_context_len),
         K, float(scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) caches: uint8 codes, float32 scale per KV head for K and for V
+# ---------------------------------------------------------------------------
+
+def _scales(k_scale, v_scale, Hkv):
+    _dev("k_scale", k_scale, torch.float32, 1)
+    _dev("v_scale", v_scale, torch.float32, 1)
+    if k_scale.shape[0] != Hkv or v_scale.shape[0] != Hkv:
+        raise ValueError("k_scale / v_scale must have num_kv_heads entries")
+
+
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, k_scale, v_scale, slot_mapping, *,
+                          stream=None) -> None:
+    """Quantise key[i] / value[i] to E4M3 with the per-head scales into slot slot_mapping[i]."""
+    _dev("key_cache", key_cache, torch.uint8, 4)
+    _dev("value_cache", value_cache, torch.uint8, 4)
+    _dev("key", key, torch.bfloat16, 3)
+    _dev("value", value, torch.bfloat16, 3)
+    _dev("slot_mapping", slot_mapping, torch.int64, 1)
+    NB, bs, Hkv, D = _cache_dims(key_cache)
+    _scales(k_scale, v_scale, Hkv)
+    T = key.shape[0]
+    if value_cache.shape != key_cache.shape or key.shape != (T, Hkv, D) or value.shape != key.shape \
+            or slot_mapping.shape[0] != T:
+        raise ValueError("reshape_and_cache_fp8: inconsistent shapes")
+    _check(lib().gpkv_reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(slot_mapping), T, Hkv, D, bs, NB, _stream(stream)))
+
+
+def _attn_checks_fp8(query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens):
+    _dev("query", query, torch.bfloat16, 3)
+    _dev("key_cache", key_cache, torch.uint8, 4)
+    _dev("value_cache", value_cache, torch.uint8, 4)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    NB, bs, Hkv, D = _cache_dims(key_cache)
+    _scales(k_scale, v_scale, Hkv)
+    B, Hq, Dq = query.shape
+    if value_cache.shape != key_cache.shape or Dq != D or block_tables.shape[0] != B \
+            or context_lens.shape[0] != B:
+        raise ValueError("inconsistent shapes between query, caches, block_tables, context_lens")
+    return B, Hq, Hkv, D, bs, NB, int(block_tables.shape[1])
+
+
+def paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                               context_lens, *, max_context_len: int, scale: float, out=None,
+                               workspace=None, stream=None) -> torch.Tensor:
+    """Dense GQA paged decode attention over E4M3 caches; returns [B, H_q, D] float32."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks_fp8(query, key_cache, value_cache, k_scale, v_scale,
+                                                 block_tables, context_lens)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    need = paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_paged_attention_decode_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs, NB, MB, int(max_context_len),
+        float(scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def sparse_paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_scale,
+                                      block_tables, context_lens, topk_indices, *,
+                                      max_context_len: int, scale: float, out=None,
+                                      workspace=None, stream=None) -> torch.Tensor:
+    """Attention over the selected logical blocks of E4M3 caches; returns [B, H_q, D] float32."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks_fp8(query, key_cache, value_cache, k_scale, v_scale,
+                                                 block_tables, context_lens)
+    _dev("topk_indices", topk_indices, torch.int32, 3)
+    if topk_indices.shape[0] != B or topk_indices.shape[1] != Hkv:
+        raise ValueError("sparse_paged_attention_decode_fp8: topk_indices must be [B, H_kv, K]")
+    K = int(topk_indices.shape[2])
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    need = sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_sparse_paged_attention_decode_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), _ptr(topk_indices), B, Hq, Hkv, D, bs, NB, MB,
+        int(max_context_len), K, float(scale), _ptr(ws), ws.numel(), _stream(stream)))
     return out

@@ -10,6 +10,7 @@
  *   gpkv_quest_block_metadata        per-block, per-channel key min / max
  *   gpkv_quest_select_topk           Quest block scores + Top-K per KV head
  *   gpkv_sparse_paged_attention_decode  exact attention over the selected blocks
+ *   ..._fp8 variants of the write and both attention calls over E4M3 caches
  *
  * Sources, by page title and section:
  *   [ASC]  "Ascend Kernel-to-Serving Pipeline": sections "ReshapeAndCache",
@@ -17,6 +18,7 @@
  *          correctness", "Sparse precision", "memory optimisation".
  *   [TL18] TileLang tutorial, chapter 18 (end-to-end inference serving):
  *          2.4 KV-cache structure, 2.6 paged KV, 4.1 split-KV decode attention,
+ *          2.5 item 3 and 3.1 item 4 (KV quantisation as the long-context lever),
  *          6.1 kernels on the framework's current stream, 6.2 graph capture,
  *          8 item (2) the per-step KV write.
  *   [DSA]  The article on adapting a sparse-attention model to a new accelerator:
@@ -200,6 +202,56 @@ int gpkv_sparse_paged_attention_decode(float* out, const void* query, const void
                                        int32_t max_context_len, int32_t topk_blocks,
                                        float scale, void* workspace, size_t workspace_bytes,
                                        void* stream);
+
+/* ---------------------------------------------------------------------------
+ * FP8 KV cache. The pages name KV quantisation as the lever for long-context
+ * decode, where the KV stream is the cost ([TL18] 2.5 item 3, 3.1 item 4); they
+ * fix no format. Here: K and V caches hold OCP FP8 E4M3 codes (1 byte per
+ * element: sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities;
+ * largest finite 448; NaN = S.1111.111), with one float32 scale per KV head for
+ * K (k_scale[H_kv]) and one for V (v_scale[H_kv]), in device memory, positive and
+ * finite (precondition). The value of a code is code * scale.
+ * Layouts are those of the bf16 calls with 1-byte elements:
+ * key_cache, value_cache: [num_blocks, block_size, num_kv_heads, head_dim] uint8.
+ * Workspaces: gpkv_paged_attention_workspace_bytes and
+ * gpkv_sparse_attention_workspace_bytes give the sizes for these calls too.
+ * --------------------------------------------------------------------------- */
+
+/* ReshapeAndCache into E4M3 caches: the slot rule of gpkv_reshape_and_cache; each
+ * element x of KV head g is stored as the E4M3 value nearest to
+ * float32(x) * float32(1 / scale[g]) (a correctly rounded float32 division, then
+ * one float32 product), ties to the even code, magnitudes past 448 saturating to
+ * 448, NaN to 0x7F. key, value: [num_tokens, num_kv_heads, head_dim] bf16. */
+int gpkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const float* k_scale, const float* v_scale,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, void* stream);
+
+/* gpkv_paged_attention_decode over E4M3 caches: K_t = code * k_scale[g],
+ * V_t = code * v_scale[g]; query bf16, output float32 as in the bf16 call. */
+int gpkv_paged_attention_decode_fp8(float* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const float* k_scale,
+                                    const float* v_scale, const int32_t* block_tables,
+                                    const int32_t* context_lens, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    float scale, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* gpkv_sparse_paged_attention_decode over E4M3 caches (values as above). */
+int gpkv_sparse_paged_attention_decode_fp8(float* out, const void* query, const void* key_cache,
+                                           const void* value_cache, const float* k_scale,
+                                           const float* v_scale, const int32_t* block_tables,
+                                           const int32_t* context_lens,
+                                           const int32_t* topk_indices, int32_t batch,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int64_t num_blocks, int32_t max_blocks_per_seq,
+                                           int32_t max_context_len, int32_t topk_blocks,
+                                           float scale, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* gpkv_status_string(int status);

@@ -28,7 +28,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(L):
     from gqa_paged_kv_amd._lib import SIGNATURES
     names = declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
     assert sorted(SIGNATURES) == names
@@ -85,6 +85,23 @@ def test_other_entry_points_checks(L):
                                                 0.1, 8, 1 << 30, None) == -1
     assert L.gpkv_sparse_paged_attention_decode(8, 8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 0,
                                                 0.1, 8, 1 << 30, None) == -2
+    # fused write: null metadata, bad block size; zero tokens is a no-op
+    assert L.gpkv_reshape_and_cache_quest(8, 8, 8, 8, None, 8, 8, 2, 1, 64, 16, 16, None) == -1
+    assert L.gpkv_reshape_and_cache_quest(8, 8, 8, 8, 8, 8, 8, 2, 1, 64, 24, 16, None) == -3
+    assert L.gpkv_reshape_and_cache_quest(None, None, None, None, None, None, None, 0, 1, 64, 16,
+                                          16, None) == 0
+    # FP8 write: null scale, bad head_dim, zero tokens
+    assert L.gpkv_reshape_and_cache_fp8(8, 8, 8, 8, None, 8, 8, 2, 1, 64, 16, 16, None) == -1
+    assert L.gpkv_reshape_and_cache_fp8(8, 8, 8, 8, 8, 8, 8, 2, 1, 96, 16, 16, None) == -3
+    assert L.gpkv_reshape_and_cache_fp8(None, None, None, None, None, None, None, 0, 1, 64, 16, 16,
+                                        None) == 0
+    # FP8 attention: null scales, small workspace; sparse FP8: null list
+    assert L.gpkv_paged_attention_decode_fp8(8, 8, 8, 8, None, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80,
+                                             0.1, 8, 1 << 30, None) == -1
+    assert L.gpkv_paged_attention_decode_fp8(8, 8, 8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80,
+                                             0.1, 8, 16, None) == -4
+    assert L.gpkv_sparse_paged_attention_decode_fp8(8, 8, 8, 8, 8, 8, 8, 8, None, 2, 4, 1, 64, 16,
+                                                    16, 5, 80, 3, 0.1, 8, 1 << 30, None) == -1
 
 
 def test_workspace_queries(L):

@@ -1,0 +1,232 @@
+"""GPU parity of the FP8 (OCP E4M3) cache path against the CPU oracle.
+
+Bars: cache codes bit-exact; attention within max-abs 2e-3 of the float64 oracle
+evaluated on the oracle's own codes (the error of quantising itself is not part of
+the bar; it is printed). On the full-size workloads the GPU quantises the whole
+pool with its own write call, and the oracle quantises the blocks of the sampled
+sequences independently: those blocks must agree bit for bit before attention is
+compared.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_paged_kv_amd as gp
+import oracle
+import workloads
+from gpu_util import BF, Dev, max_abs, sample_seqs, to_dev, workload
+
+pytestmark = pytest.mark.gpu
+ATOL = 2e-3
+U8 = torch.uint8
+
+
+def _scales(cache_bits, divisor=256.0, stride=7):
+    """Per KV head: max |x| over a fixed subsample of the cache, / divisor (so the
+    largest values land near 256 of E4M3's 448)."""
+    Hkv, D = cache_bits.shape[-2:]
+    sub = cache_bits.reshape(-1, Hkv, D)[::stride]
+    x = (sub.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    amax = np.abs(np.nan_to_num(x, nan=0.0, posinf=0.0, neginf=0.0)).max(axis=(0, 2))
+    return np.maximum(amax / divisor, 1e-3).astype(np.float32)
+
+
+def _codes(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Write path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ks,vs", [((0.1, 7.0), (1.0, 0.0625)), ((1.0, 3.0), (250.0, 1e-3))])
+def test_fp8_write_every_bf16_value(ks, vs):
+    """All 65536 bf16 patterns (NaN, inf, subnormals, both zeros) through the write."""
+    Hkv, D, bs, NB = 2, 128, 16, 40
+    T = 65536 // (Hkv * D)
+    allbits = np.arange(65536, dtype=np.uint16)
+    key = allbits.reshape(T, Hkv, D)
+    value = allbits[::-1].copy().reshape(T, Hkv, D)
+    rng = np.random.default_rng(5)
+    slots = rng.permutation(NB * bs)[:T].astype(np.int64)
+    slots[[3, 77]] = -1
+    zeros = np.zeros((NB, bs, Hkv, D), np.uint8)
+    kc, vc = torch.zeros((NB, bs, Hkv, D), dtype=U8, device="cuda"), torch.zeros(
+        (NB, bs, Hkv, D), dtype=U8, device="cuda")
+    d_ks = torch.tensor(ks, dtype=torch.float32, device="cuda")
+    d_vs = torch.tensor(vs, dtype=torch.float32, device="cuda")
+    gp.reshape_and_cache_fp8(to_dev(key, BF), to_dev(value, BF), kc, vc, d_ks, d_vs,
+                             to_dev(slots, torch.int64))
+    torch.cuda.synchronize()
+    ek, ev = oracle.reshape_and_cache_fp8(zeros, zeros, key, value, slots, bs, ks, vs)
+    assert np.array_equal(_codes(kc), ek), "key codes differ from the oracle"
+    assert np.array_equal(_codes(vc), ev), "value codes differ from the oracle"
+
+
+@pytest.mark.parametrize("config", [1, 3])
+def test_fp8_write_config(config):
+    w = workload(config)
+    ks, vs = _scales(w.key_cache), _scales(w.value_cache)
+    shape = w.key_cache.shape
+    kc = torch.zeros(shape, dtype=U8, device="cuda")
+    vc = torch.zeros(shape, dtype=U8, device="cuda")
+    gp.reshape_and_cache_fp8(to_dev(w.new_key, BF), to_dev(w.new_value, BF), kc, vc,
+                             to_dev(ks, torch.float32), to_dev(vs, torch.float32),
+                             to_dev(w.slot_mapping, torch.int64))
+    torch.cuda.synchronize()
+    s = w.slot_mapping[w.slot_mapping >= 0]
+    bs = w.block_size
+    z = np.zeros(shape, np.uint8)
+    ek, ev = oracle.reshape_and_cache_fp8(z, z, w.new_key, w.new_value, w.slot_mapping, bs, ks, vs)
+    got_k, got_v = _codes(kc), _codes(vc)
+    assert np.array_equal(got_k[s // bs, s % bs], ek[s // bs, s % bs])
+    assert np.array_equal(got_v[s // bs, s % bs], ev[s // bs, s % bs])
+    untouched = np.ones(shape[:2], bool)
+    untouched[s // bs, s % bs] = False
+    assert not got_k[untouched].any() and not got_v[untouched].any()
+
+
+def test_fp8_write_empty_and_negative():
+    w = workloads.make(1)
+    kc = torch.full(w.key_cache.shape, 0x5A, dtype=U8, device="cuda")
+    vc = kc.clone()
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    gp.reshape_and_cache_fp8(to_dev(w.new_key, BF), to_dev(w.new_value, BF), kc, vc, one, one,
+                             torch.full((w.num_tokens,), -1, dtype=torch.int64, device="cuda"))
+    empty = torch.empty((0, 1, 64), dtype=BF, device="cuda")
+    gp.reshape_and_cache_fp8(empty, empty, kc, vc, one, one,
+                             torch.empty((0,), dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    assert (_codes(kc) == 0x5A).all() and (_codes(vc) == 0x5A).all()
+
+
+# ---------------------------------------------------------------------------
+# Attention over E4M3 caches
+# ---------------------------------------------------------------------------
+
+class Fp8Case:
+    """A workload's E4M3 caches: the GPU's (whole pool, written by the GPU) and the
+    oracle's (blocks of ``seqs`` only, quantised on the CPU)."""
+
+    def __init__(self, w, seqs):
+        self.w, self.seqs = w, seqs
+        self.ks, self.vs = _scales(w.key_cache), _scales(w.value_cache)
+        d = Dev(w)
+        self.d = d
+        NB, bs, Hkv, D = w.key_cache.shape
+        self.kc = torch.empty((NB, bs, Hkv, D), dtype=U8, device="cuda")
+        self.vc = torch.empty_like(self.kc)
+        self.d_ks = to_dev(self.ks, torch.float32)
+        self.d_vs = to_dev(self.vs, torch.float32)
+        all_slots = torch.arange(NB * bs, dtype=torch.int64, device="cuda")
+        gp.reshape_and_cache_fp8(d.kc.view(NB * bs, Hkv, D), d.vc.view(NB * bs, Hkv, D), self.kc,
+                                 self.vc, self.d_ks, self.d_vs, all_slots)
+        torch.cuda.synchronize()
+        # the oracle's codes for the blocks the sampled sequences read
+        self.okc = np.zeros((NB, bs, Hkv, D), np.uint8)
+        self.ovc = np.zeros((NB, bs, Hkv, D), np.uint8)
+        blocks = sorted({int(x) for b in seqs
+                         for x in w.block_tables[b, :-(-int(w.context_lens[b]) // bs)]})
+        blocks = np.array(blocks, dtype=np.int64)
+        if blocks.size:
+            self.okc[blocks] = oracle.quantize_fp8(w.key_cache[blocks], self.ks)
+            self.ovc[blocks] = oracle.quantize_fp8(w.value_cache[blocks], self.vs)
+            got_k = self.kc[torch.from_numpy(blocks).cuda()].cpu().numpy()
+            got_v = self.vc[torch.from_numpy(blocks).cuda()].cpu().numpy()
+            assert np.array_equal(got_k, self.okc[blocks]), "GPU key codes differ from the oracle"
+            assert np.array_equal(got_v, self.ovc[blocks]), "GPU value codes differ from the oracle"
+
+    def dense(self):
+        w, d = self.w, self.d
+        return gp.paged_attention_decode_fp8(d.q, self.kc, self.vc, self.d_ks, self.d_vs, d.bt,
+                                             d.ctx, max_context_len=w.max_context_len,
+                                             scale=float(w.scale)).cpu().numpy()
+
+    def sparse(self, sel):
+        w, d = self.w, self.d
+        return gp.sparse_paged_attention_decode_fp8(
+            d.q, self.kc, self.vc, self.d_ks, self.d_vs, d.bt, d.ctx, to_dev(sel, torch.int32),
+            max_context_len=w.max_context_len, scale=float(w.scale)).cpu().numpy()
+
+    def ref_dense(self):
+        w = self.w
+        return oracle.paged_attention_decode_fp8(w.query, self.okc, self.ovc, self.ks, self.vs,
+                                                 w.block_tables, w.context_lens, w.scale,
+                                                 seqs=self.seqs)
+
+
+@pytest.mark.parametrize("config", [1, 3, 4, 5])
+def test_fp8_dense_config(config):
+    w = workload(config)
+    seqs = list(range(w.batch)) if w.batch <= 4 else sample_seqs(w)
+    c = Fp8Case(w, seqs)
+    out = c.dense()
+    ref = c.ref_dense()
+    err = max_abs(out[seqs], ref[seqs])
+    bf = oracle.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                       w.context_lens, w.scale, seqs=seqs)
+    print(f"config {config}: FP8 max-abs vs oracle {err:.3e}; "
+          f"quantisation effect vs bf16 attention {max_abs(ref[seqs], bf[seqs]):.3e}")
+    assert err <= ATOL
+
+
+FP8_CASES = [
+    (601, 4, 1, 64, 16, [0, 1, 15, 16, 17, 33]),
+    (602, 28, 4, 128, 16, [31, 32, 33, 500, 1023, 1025]),
+    (603, 16, 16, 128, 32, [7, 64, 65, 300]),
+    (604, 16, 1, 128, 64, [129, 2047, 4100]),
+    (605, 64, 8, 128, 128, [1, 127, 128, 129, 3000]),
+    (606, 14, 2, 64, 128, [250, 1, 700]),
+]
+
+
+@pytest.mark.parametrize("schedule", ["balanced", "split"])
+@pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx", FP8_CASES)
+def test_fp8_dense_random(seed, Hq, Hkv, D, bs, ctx, schedule, monkeypatch):
+    monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
+    w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                              block_size=bs, context_lens=ctx)
+    c = Fp8Case(w, list(range(w.batch)))
+    out = c.dense()
+    err = max_abs(out, c.ref_dense())
+    print(f"seed {seed}: FP8 max-abs {err:.3e}")
+    assert err <= ATOL
+    for b, L in enumerate(ctx):
+        if L == 0:
+            assert (out[b] == 0).all()
+
+
+@pytest.mark.parametrize("schedule", ["balanced", "split"])
+@pytest.mark.parametrize("config,K", [(1, 3), (3, 64), (5, 32)])
+def test_fp8_sparse_config(config, K, schedule, monkeypatch):
+    monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
+    w = workload(config)
+    seqs = list(range(w.batch)) if w.batch <= 4 else sample_seqs(w)
+    c = Fp8Case(w, seqs)
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens,
+                                             w.block_size)
+    sel = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens,
+                                   w.block_size, K)
+    out = c.sparse(sel)
+    # the oracle's FP8 sparse result: dense FP8 attention restricted to the selected
+    # blocks, via a block table listing only them
+    ref = np.zeros_like(out, dtype=np.float64)
+    G = w.num_q_heads // w.num_kv_heads
+    for b in seqs:
+        for g in range(w.num_kv_heads):
+            lbs = sorted(x for x in sel[b, g].tolist() if x >= 0)
+            if not lbs:
+                continue
+            bt1 = np.array([[int(w.block_tables[b, lb]) for lb in lbs]], np.int32)
+            ctx_b = int(w.context_lens[b])
+            last = lbs[-1]
+            n = (len(lbs) - 1) * w.block_size + min(w.block_size, ctx_b - last * w.block_size)
+            q1 = w.query[b:b + 1]
+            r = oracle.paged_attention_decode_fp8(q1, c.okc, c.ovc, c.ks, c.vs, bt1,
+                                                  np.array([n], np.int64), w.scale)
+            ref[b, g * G:(g + 1) * G] = r[0, g * G:(g + 1) * G]
+    err = max_abs(out[seqs], ref[seqs])
+    print(f"config {config} K={K}: FP8 sparse max-abs {err:.3e}")
+    assert err <= ATOL
