@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 DEFAULT_CONFIG = 3
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = "attn_balanced_dense_long8k_traffic.md"
-DOMINANT_KERNEL = "attn_balanced_kernel<128>"
+DOMINANT_KERNEL = "attn_balanced_kernel<128, false, false>"
 
 
 def parse_args():
@@ -50,6 +50,7 @@ def parse_args():
     ap.add_argument("--write-path", choices=["fused", "separate"], default="fused",
                     help="fused: reshape_and_cache_quest; separate: reshape_and_cache + "
                          "quest_block_metadata(last_block_only)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) cache timing")
     ap.add_argument("--details", action="store_true", help="print per-call timings to stderr")
     return ap.parse_args()
 
@@ -181,14 +182,14 @@ def main():
 
     out_d = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     out_s = torch.empty_like(out_d)
-    ws_d = torch.empty(gp.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl), dtype=torch.uint8,
+    ws_d = torch.zeros(gp.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl), dtype=torch.uint8,
                        device="cuda")
     kmin = torch.zeros((w.num_blocks, Hkv, D), dtype=bf, device="cuda")
     kmax = torch.zeros_like(kmin)
     if K:
         ws_sel = torch.empty(gp.quest_select_workspace_bytes(B, Hkv, w.max_blocks_per_seq),
                              dtype=torch.uint8, device="cuda")
-        ws_sp = torch.empty(gp.sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K),
+        ws_sp = torch.zeros(gp.sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K),
                             dtype=torch.uint8, device="cuda")
         sel = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda")
     flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
@@ -302,6 +303,49 @@ def main():
     except RuntimeError as exc:   # report, do not fail the eager measurement
         print(f"[bench] graph capture unavailable: {exc}", file=sys.stderr)
 
+    # FP8 (E4M3) KV cache on the same workload: the pool quantised once by the FP8
+    # write (every slot), then its write and dense calls timed like the bf16 ones.
+    fp8 = None
+    if not args.no_fp8:
+        kc8 = torch.empty(kc.shape, dtype=torch.uint8, device="cuda")
+        vc8 = torch.empty_like(kc8)
+        def amax_scale(t):
+            return (t.float().abs().amax(dim=(0, 1, 3)) / 256.0).clamp_min(1e-3).contiguous()
+        ks8, vs8 = amax_scale(kc), amax_scale(vc)
+        NBs = kc.shape[0] * kc.shape[1]
+        gp.reshape_and_cache_fp8(kc.view(NBs, Hkv, D), vc.view(NBs, Hkv, D), kc8, vc8, ks8, vs8,
+                                 torch.arange(NBs, dtype=torch.int64, device="cuda"))
+        out8 = torch.empty_like(out_d)
+        fcalls = {
+            "reshape_and_cache_fp8": lambda: gp.reshape_and_cache_fp8(nk, nv, kc8, vc8, ks8, vs8,
+                                                                      slots),
+            "paged_attention_decode_fp8": lambda: gp.paged_attention_decode_fp8(
+                q, kc8, vc8, ks8, vs8, bt, ctx, max_context_len=mcl, scale=scale, out=out8,
+                workspace=ws_d),
+        }
+        fbytes = {"reshape_and_cache_fp8": R.write_bytes(w.slot_mapping, w.num_blocks, bs, Hkv, D)
+                  * 3 // 4,
+                  "paged_attention_decode_fp8": R.dense_attention_bytes_fp8(w.context_lens, Hkv, D)}
+        fp8 = {}
+        for name, f in fcalls.items():
+            for _ in range(3):
+                f()
+            ts = []
+            for k in range(args.steps):
+                flush.fill_(k & 0xFF)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                f()
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            t = float(np.mean(ts))
+            fp8[name] = {"us_mean": round(t, 2), "algorithmic_bytes": int(fbytes[name]),
+                         "gbps": round(fbytes[name] / (t * 1e-6) / 1e9, 1),
+                         "pct_of_peak": round(100 * fbytes[name] / (t * 1e-6) / 1e9
+                                              / R.MI355X_HBM_GBPS, 1)}
+        del kc8, vc8
+
     per_call = {name: np.array([evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)])
                 for i, name in enumerate(calls)}
     step_us = np.array([evs[k][0].elapsed_time(evs[k][len(calls)]) * 1e3 for k in range(args.steps)])
@@ -365,13 +409,14 @@ def main():
         "quest_step_us": round(quest_us, 2) if quest_us is not None else None,
         "quest_full_metadata_rebuild_us": round(t_full, 2) if t_full is not None else None,
         "graph_replay_us_per_step": round(graph_us, 2) if graph_us is not None else None,
+        "fp8_kv": fp8,
         "calls": calls_out,
         "step_algorithmic_bytes": int(step_bytes),
         "wall_s_timed_region_incl_flush": round(wall, 4),
         "flush_mib_between_steps": args.flush_mib,
         "roofline": {
             "bound": "hbm",
-            "kernel": f"paged_attention_decode call: {DOMINANT_KERNEL} + attn_combine_kernel<128>",
+            "kernel": f"paged_attention_decode call: {DOMINANT_KERNEL} + its combine kernel",
             "achieved": round(achieved, 1), "peak": R.MI355X_HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved / R.MI355X_HBM_GBPS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": int(by["paged_attention_decode"]),

@@ -31,6 +31,12 @@ def dense_attention_bytes(context_lens, num_kv_heads: int, head_dim: int) -> int
         num_kv_heads, head_dim)
 
 
+def dense_attention_bytes_fp8(context_lens, num_kv_heads: int, head_dim: int) -> int:
+    """K + V codes of every valid token (1 byte per element)."""
+    return int(np.asarray(context_lens, dtype=np.int64).sum()) * kv_bytes_per_token_layer(
+        num_kv_heads, head_dim, elem_bytes=1)
+
+
 def write_bytes(slot_mapping, num_blocks: int, block_size: int, num_kv_heads: int,
                 head_dim: int) -> int:
     """Read the new K/V rows and write them into the cache."""

@@ -23,11 +23,11 @@ def _step_buffers(w, d, K):
     buf = {
         "out_d": torch.empty((B, Hq, D), dtype=torch.float32, device="cuda"),
         "out_s": torch.empty((B, Hq, D), dtype=torch.float32, device="cuda"),
-        "ws_d": torch.empty(gp.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl),
+        "ws_d": torch.zeros(gp.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl),
                             dtype=torch.uint8, device="cuda"),
         "ws_sel": torch.empty(gp.quest_select_workspace_bytes(B, Hkv, w.max_blocks_per_seq),
                               dtype=torch.uint8, device="cuda"),
-        "ws_sp": torch.empty(gp.sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K),
+        "ws_sp": torch.zeros(gp.sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K),
                              dtype=torch.uint8, device="cuda"),
         "sel": torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda"),
         "kmin": torch.zeros((w.num_blocks, Hkv, D), dtype=BF, device="cuda"),

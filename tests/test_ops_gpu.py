@@ -143,6 +143,35 @@ def test_dense_split_sizes_agree(split, monkeypatch):
     assert max_abs(sp, ref) <= ATOL
 
 
+def test_balanced_workspace_reused_across_batches():
+    """One workspace through calls of different batches, dense then sparse: the
+    arrival counters return to zero after every call, so each call merges."""
+    cases = [workloads.random_case(215 + i, batch=len(ctx), num_q_heads=28, num_kv_heads=4,
+                                   head_dim=128, block_size=16, context_lens=ctx)
+             for i, ctx in enumerate([[900, 0, 2500, 16], [3000, 1], [17, 400, 0, 5000, 33, 1]])]
+    need = max(gp.paged_attention_workspace_bytes(w.batch, 28, 4, 128, 16, w.max_context_len)
+               for w in cases)
+    need = max(need, max(gp.sparse_attention_workspace_bytes(w.batch, 28, 4, 128, 16, 400)
+                         for w in cases))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for w in cases:
+            d = Dev(w)
+            out = torch.full((w.batch, 28, 128), float("nan"), device="cuda")
+            _dense(d, w, out=out, workspace=ws)
+            ref = oracle.paged_attention_decode(w.query, w.key_cache, w.value_cache,
+                                                w.block_tables, w.context_lens, w.scale)
+            assert max_abs(out.cpu().numpy(), ref) <= ATOL, (rep, w.batch)
+            sel = np.full((w.batch, 4, 400), -1, np.int32)
+            for b, nb in enumerate(w.nblocks().tolist()):
+                sel[b, :, :nb] = np.arange(nb)
+            sp = torch.full((w.batch, 28, 128), float("nan"), device="cuda")
+            gp.sparse_paged_attention_decode(d.q, d.kc, d.vc, d.bt, d.ctx, to_dev(sel, torch.int32),
+                                             max_context_len=w.max_context_len,
+                                             scale=float(w.scale), out=sp, workspace=ws)
+            assert max_abs(sp.cpu().numpy(), ref) <= ATOL, (rep, w.batch)
+
+
 def test_dense_invariants_permuted_poison_deterministic():
     w = workloads.random_case(220, batch=4, num_q_heads=28, num_kv_heads=4, head_dim=128,
                               block_size=16, context_lens=[700, 37, 1600, 16], slack=9)
