@@ -32,6 +32,10 @@ Readings where the pages are silent (each also listed in the design doc):
      ascending, padded with -1; K >= nb selects every block.
   R6 masked / unselected tokens contribute exactly nothing (even if their K/V
      bits are NaN).
+  R8 multi-token queries ([TL18] 2.7 varlen batches, 3.3 item 4): the query rows of
+     sequence b are its newest q_len_b positions, already in the cache; row j
+     (0-based) sees positions t <= ctx_b - q_len_b + j (a causal mask aligned to
+     the right); a row that sees no position gets a zero output.
   R7 FP8 KV cache (the KV-quantisation lever of [TL18] 2.5 and 3.1): codes are
      OCP FP8 E4M3 (bias 7, no infinities, largest finite 448); K and V each carry
      one float32 scale per KV head. Stored code = the E4M3 value nearest to
@@ -54,6 +58,7 @@ __all__ = [
     "quest_select_topk", "sparse_token_positions", "sparse_paged_attention_decode",
     "split_kv_partials", "split_kv_combine", "e4m3_to_f64", "e4m3_from_f32",
     "fp8_inverse_scale", "quantize_fp8", "reshape_and_cache_fp8", "paged_attention_decode_fp8",
+    "paged_attention_varlen",
 ]
 
 
@@ -421,4 +426,49 @@ def paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_scale, 
         for g in range(Hkv):
             heads = slice(g * G, (g + 1) * G)
             out[b, heads] = _softmax_attention(q[b, heads], k[:, g], v[:, g], sc)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# C8 -- multi-token queries over the paged cache  (R8; [TL18] 2.7, 3.3)
+# ---------------------------------------------------------------------------
+
+def paged_attention_varlen(query, key_cache, value_cache, block_tables, context_lens,
+                           cu_seqlens_q, scale, seqs=None):
+    """out[r, h, :] for every query row r: row j of sequence b (r = cu[b] + j) is
+    softmax_t(scale * q[r,h].K_t) . V_t over positions t <= ctx_b - q_len_b + j, by
+    definition (all scores, the masked ones set to -inf, then the softmax).
+    query: [sum q_len, H_q, D] bf16 bits; returns float64 of that shape."""
+    UQ, Hq, D = query.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    if Hq % Hkv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = Hq // Hkv
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    _check_table(block_tables, ctx, bs, NB)
+    out = np.zeros((UQ, Hq, D), dtype=np.float64)
+    q = bf16_to_f64(query)
+    sc = float(np.float32(scale))
+    for b in (range(ctx.size) if seqs is None else seqs):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        L = int(ctx[b])
+        if r1 <= r0 or L == 0:
+            continue
+        pos = np.arange(L)
+        k = bf16_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs))
+        v = bf16_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs))
+        lim = L - (r1 - r0) + np.arange(r1 - r0)          # last visible position per row
+        visible = pos[None, :] <= lim[:, None]            # [q_len, L]
+        for g in range(Hkv):
+            for hl in range(G):
+                h = g * G + hl
+                s_ = sc * (q[r0:r1, h] @ k[:, g].T)        # [q_len, L]
+                s_ = np.where(visible, s_, -np.inf)
+                m = s_.max(axis=1, keepdims=True)
+                m = np.where(np.isfinite(m), m, 0.0)
+                e = np.where(visible, np.exp(s_ - m), 0.0)
+                den = e.sum(axis=1, keepdims=True)
+                p = np.divide(e, den, out=np.zeros_like(e), where=den > 0)
+                out[r0:r1, h] = p @ v[:, g]
     return out

@@ -617,4 +617,104 @@ def pin_fp8_attention_equals_bf16_on_representable(orc):
     assert np.abs(got - exp).max() <= TOL
 
 
+# ---------------------------------------------------------------------------
+# Multi-token queries (varlen, right-aligned causal mask)
+# ---------------------------------------------------------------------------
+
+def pin_varlen_single_token_is_decode(orc):
+    """One query token per sequence: the causal limit is the whole context."""
+    for w in _tiny_cases():
+        w2 = workloads.varlen_case(81, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                                   head_dim=w.head_dim, block_size=w.block_size,
+                                   context_lens=w.context_lens, q_lens=[1] * w.batch)
+        got = orc.paged_attention_varlen(w2.query_varlen, w2.key_cache, w2.value_cache,
+                                         w2.block_tables, w2.context_lens, w2.cu_seqlens_q,
+                                         w2.scale)
+        exp = orc.paged_attention_decode(w2.query_varlen, w2.key_cache, w2.value_cache,
+                                         w2.block_tables, w2.context_lens, w2.scale)
+        assert np.abs(got - exp).max() <= TOL
+
+
+def pin_varlen_torch_sdpa_bottom_right_mask(orc):
+    """torch's float64 scaled_dot_product_attention with an explicit boolean mask
+    that lets row j see the first ctx - q_len + j + 1 positions, GQA enabled."""
+    import torch
+    w = workloads.varlen_case(82, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                              context_lens=[37, 80, 16, 5], q_lens=[4, 16, 1, 5])
+    got = orc.paged_attention_varlen(w.query_varlen, w.key_cache, w.value_cache, w.block_tables,
+                                     w.context_lens, w.cu_seqlens_q, w.scale)
+    cu = w.cu_seqlens_q
+    for b, L in enumerate(w.context_lens.tolist()):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        n = r1 - r0
+        rows = [int(x) for x in w.block_tables[b, :-(-L // 16)]]
+        k = np.concatenate([_dec(w.key_cache[p_]) for p_ in rows])[:L]     # [L, Hkv, D]
+        v = np.concatenate([_dec(w.value_cache[p_]) for p_ in rows])[:L]
+        q = _dec(w.query_varlen[r0:r1])                                      # [n, Hq, D]
+        mask = np.zeros((n, L), bool)
+        for j in range(n):
+            mask[j, :max(0, L - n + j + 1)] = True
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q).permute(1, 0, 2)[None], torch.from_numpy(k).permute(1, 0, 2)[None],
+            torch.from_numpy(v).permute(1, 0, 2)[None], attn_mask=torch.from_numpy(mask),
+            scale=float(np.float32(w.scale)), enable_gqa=True)[0].permute(1, 0, 2).numpy()
+        ok = mask.any(axis=1)
+        assert np.abs(got[r0:r1][ok] - ref[ok]).max() <= TOL
+        assert (got[r0:r1][~ok] == 0).all()
+
+
+def pin_varlen_brute_force_and_short_context(orc):
+    """Pure-Python loops with math.fsum; one sequence has more query rows than
+    positions, so its first rows see nothing (zero rows)."""
+    w = workloads.varlen_case(83, num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                              context_lens=[3, 20], q_lens=[5, 6])
+    got = orc.paged_attention_varlen(w.query_varlen, w.key_cache, w.value_cache, w.block_tables,
+                                     w.context_lens, w.cu_seqlens_q, w.scale)
+    sc = float(np.float32(w.scale))
+    cu = w.cu_seqlens_q
+    for b, L in enumerate(w.context_lens.tolist()):
+        n = int(cu[b + 1] - cu[b])
+        for j in range(n):
+            r = int(cu[b]) + j
+            vis = [t for t in range(L) if t <= L - n + j]
+            for h in range(4):
+                g = h // 2
+                qv = _dec(w.query_varlen[r, h]).tolist()
+                if not vis:
+                    assert (got[r, h] == 0).all()
+                    continue
+                sc_ = []
+                for t in vis:
+                    pb = int(w.block_tables[b, t // 16])
+                    kv = _dec(w.key_cache[pb, t % 16, g]).tolist()
+                    sc_.append(sc * math.fsum(a * c for a, c in zip(qv, kv)))
+                m = max(sc_)
+                e = [math.exp(x - m) for x in sc_]
+                den = math.fsum(e)
+                for d in range(64):
+                    num = math.fsum(e[i] * float(_dec(w.value_cache[int(w.block_tables[b, t // 16]),
+                                                                    t % 16, g, d]))
+                                    for i, t in enumerate(vis))
+                    assert abs(num / den - got[r, h, d]) <= TOL
+
+
+def pin_varlen_mask_edge(orc):
+    """Row j of a 6-token chunk over 40 positions sees positions 0 .. 34 + j: changing
+    K/V at 35 + j leaves it unchanged, changing 34 + j moves it."""
+    w = workloads.varlen_case(84, num_q_heads=2, num_kv_heads=1, head_dim=64, block_size=16,
+                              context_lens=[40], q_lens=[6])
+    base = orc.paged_attention_varlen(w.query_varlen, w.key_cache, w.value_cache, w.block_tables,
+                                      w.context_lens, w.cu_seqlens_q, w.scale)
+    for j in (0, 2, 4):
+        for t, moves in ((35 + j, False), (34 + j, True)):
+            kc, vc = w.key_cache.copy(), w.value_cache.copy()
+            pb = int(w.block_tables[0, t // 16])
+            kc[pb, t % 16] ^= np.uint16(0x0040)
+            vc[pb, t % 16] ^= np.uint16(0x0040)
+            out = orc.paged_attention_varlen(w.query_varlen, kc, vc, w.block_tables,
+                                             w.context_lens, w.cu_seqlens_q, w.scale)
+            changed = np.abs(out[j] - base[j]).max() > 0
+            assert changed == moves, (j, t)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -49,6 +49,10 @@ MUTANTS = [
      "y = (x * np.asarray(scale, dtype=np.float32)[:, None])"),
     ("fp8: k scale dropped on read", "* ks[:, None]", "* 1.0"),
     ("fp8: v scale dropped on read", "* vs[:, None]", "* 1.0"),
+    ("varlen: mask aligned left", "lim = L - (r1 - r0) + np.arange(r1 - r0)", "lim = np.arange(r1 - r0)"),
+    ("varlen: mask off by one", "visible = pos[None, :] <= lim[:, None]", "visible = pos[None, :] < lim[:, None]"),
+    ("varlen: no causal mask", "visible = pos[None, :] <= lim[:, None]", "visible = pos[None, :] >= 0"),
+    ("varlen: query rows shifted", "s_ = sc * (q[r0:r1, h] @ k[:, g].T)", "s_ = sc * (q[r0 + 1:r1 + 1, h] @ k[:, g].T)"),
 ]
 
 

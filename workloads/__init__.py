@@ -74,6 +74,10 @@ class Workload:
     slot_mapping: np.ndarray          # [T] int64, <0 = skip
     topk_list: list = field(default_factory=list)   # Quest topk_blocks values to run
     scale: np.float32 = np.float32(0.0)
+    # Multi-token queries (varlen): sequence b's query rows are
+    # query_varlen[cu_seqlens_q[b]:cu_seqlens_q[b + 1]].
+    cu_seqlens_q: np.ndarray | None = None  # [B + 1] int32
+    query_varlen: np.ndarray | None = None  # [sum q_len, H_q, D] uint16
 
     @property
     def max_context_len(self) -> int:
@@ -248,6 +252,27 @@ def random_case(seed: int, *, batch: int, num_q_heads: int, num_kv_heads: int, h
         max_blocks_per_seq=max_blocks_per_seq, context_lens=ctx, block_tables=bt,
         key_cache=kc, value_cache=vc, query=q, new_key=nk, new_value=nv, slot_mapping=slots,
         topk_list=[], scale=np.float32(1.0 / math.sqrt(head_dim)))
+
+
+def varlen_case(seed: int, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                block_size: int, context_lens, q_lens, slack: int = 3) -> Workload:
+    """Multi-token queries over a paged cache: sequence b brings q_lens[b] query
+    tokens, the newest q_lens[b] of its context_lens[b] positions (their K/V already
+    in the cache). Caches and tables as ``random_case(seed, ...)``; the query rows
+    are drawn from a second seeded stream."""
+    ctx = np.asarray(context_lens, dtype=np.int32)
+    w = random_case(seed, batch=int(ctx.size), num_q_heads=num_q_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                    context_lens=ctx, slack=slack)
+    ql = np.asarray(q_lens, dtype=np.int32)
+    assert ql.size == ctx.size and (ql >= 0).all()
+    cu = np.zeros(ctx.size + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(ql)
+    rng = np.random.default_rng(seed + 7919)
+    w.query_varlen = _normal_bf16(rng, (int(cu[-1]), num_q_heads, head_dim))
+    w.cu_seqlens_q = cu
+    w.name = f"varlen_seed{seed}"
+    return w
 
 
 def shape_summary(w: Workload) -> dict:
