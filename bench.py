@@ -51,6 +51,7 @@ def parse_args():
                     help="fused: reshape_and_cache_quest; separate: reshape_and_cache + "
                          "quest_block_metadata(last_block_only)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) cache timing")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the multi-token query timing")
     ap.add_argument("--details", action="store_true", help="print per-call timings to stderr")
     return ap.parse_args()
 
@@ -346,6 +347,52 @@ def main():
                                               / R.MI355X_HBM_GBPS, 1)}
         del kc8, vc8
 
+    # Multi-token queries on the same caches: a mixed batch in which six sequences
+    # bring prefill chunks (the newest positions of their contexts) and the rest
+    # decode one token.
+    varlen = None
+    if not args.no_varlen and B >= 6:
+        ql = np.ones(B, dtype=np.int64)
+        ql[:6] = [128, 256, 64, 512, 32, 128]
+        ql = np.minimum(ql, w.context_lens.astype(np.int64))
+        cu = np.zeros(B + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(ql)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(12)
+        qv = torch.randn((int(cu[-1]), Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+        cu_d = torch.from_numpy(cu).cuda()
+        ws_v = torch.empty(gp.paged_attention_varlen_workspace_bytes(B, int(ql.max()), Hq, Hkv, D,
+                                                                     bs, mcl),
+                           dtype=torch.uint8, device="cuda")
+        out_v = torch.empty((int(cu[-1]), Hq, D), dtype=torch.float32, device="cuda")
+        fv = lambda: gp.paged_attention_varlen(qv, kc, vc, bt, ctx, cu_d, max_q_len=int(ql.max()),
+                                               max_context_len=mcl, scale=scale, out=out_v,
+                                               workspace=ws_v)
+        for _ in range(3):
+            fv()
+        ts = []
+        for k in range(args.steps):
+            flush.fill_(k & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fv()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        t = float(np.mean(ts))
+        kv_bytes = R.dense_attention_bytes(w.context_lens, Hkv, D)
+        ctx64 = w.context_lens.astype(np.int64)
+        visible = int(sum(int((ctx64[b] - ql[b] + 1 + np.arange(ql[b])).sum()) for b in range(B)))
+        flops = 4 * D * Hq * visible
+        varlen = {"workload": "8K-average caches; q_len 128/256/64/512/32/128 for six sequences, "
+                              "1 for the rest", "query_rows": int(cu[-1]), "us_mean": round(t, 2),
+                  "kv_bytes_read_once": int(kv_bytes),
+                  "gbps_kv_once": round(kv_bytes / (t * 1e-6) / 1e9, 1),
+                  "tflops": round(flops / (t * 1e-6) / 1e12, 2),
+                  "pct_of_8tbps": round(100 * kv_bytes / (t * 1e-6) / 1e9 / R.MI355X_HBM_GBPS, 1),
+                  "pct_of_bf16_mfma_2500tflops": round(100 * flops / (t * 1e-6) / 1e12 / 2500.0, 2)}
+        del qv, ws_v, out_v
+
     per_call = {name: np.array([evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)])
                 for i, name in enumerate(calls)}
     step_us = np.array([evs[k][0].elapsed_time(evs[k][len(calls)]) * 1e3 for k in range(args.steps)])
@@ -410,6 +457,7 @@ def main():
         "quest_full_metadata_rebuild_us": round(t_full, 2) if t_full is not None else None,
         "graph_replay_us_per_step": round(graph_us, 2) if graph_us is not None else None,
         "fp8_kv": fp8,
+        "varlen_mixed": varlen,
         "calls": calls_out,
         "step_algorithmic_bytes": int(step_bytes),
         "wall_s_timed_region_incl_flush": round(wall, 4),

@@ -140,9 +140,16 @@ struct VCodes<64> {    // 4 codes per token
   static __device__ __forceinline__ u32x2 to_bf16(type w) { return e4m3x4_to_bf16(w); }
 };
 
-template <int D, bool FP8, class Desc>
-__device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, int n_sub,
-                                            const Desc& desc, float* o_dst, float* lse_dst) {
+// Attention of up to 16 query rows against KV head g over sub-tiles [0, n_sub) of
+// one unit. Lane row r (= lane % 16) reads its query from qrow (nullptr: a padding
+// row of zeros); rows r < n_rows are written to o_dst[r][D] (normalised) and
+// lse_dst[r] (base-2 log-sum-exp). Decode: the rows are the G query heads of the
+// group. CAUSAL (multi-token queries): sub-tile u covers positions pos0 + 16u ..,
+// and row r sees only positions < row_limit (its own bound).
+template <int D, bool FP8, bool CAUSAL, class Desc>
+__device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_sub, const Desc& desc,
+                                            const unsigned short* qrow, int n_rows, int pos0,
+                                            int row_limit, float* o_dst, float* lse_dst) {
   constexpr int KSTEPS = D / 32;  // k-steps of the q.k contraction
   constexpr int KLOADS = FP8 ? D / 64 : KSTEPS;   // 16-byte K loads per sub-tile
   constexpr int CPL = D / 16;     // channels per lane in the V^T operand / O^T tiles
@@ -151,7 +158,6 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
   typedef typename VCodes<D>::type vcodes;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, qd = lane >> 4;
-  const int G = c.G;
   // E4M3 caches: K's scale joins the softmax scale, V's scales the output.
   float qk_scale = c.qk_scale_log2, v_scale = 1.f;
   if constexpr (FP8) {
@@ -159,10 +165,9 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
     v_scale = c.v_scale[g];
   }
 
-  // Q^T operand: lane holds head r's channels of each k-step (zero rows past G).
+  // Q^T operand: lane holds row r's channels of each k-step (zero for padding rows).
   u32x4 qf[KSTEPS];
-  if (r < G) {
-    const unsigned short* qrow = c.q + ((size_t)b * c.Hq + (size_t)g * G + r) * D;
+  if (qrow != nullptr) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qrow + kstep_channel<FP8>(s, qd));
   } else {
@@ -282,7 +287,9 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x = sacc[sub][i] * qk_scale;
-        sv[sub * 4 + i] = (4 * qd + i < nv[sub]) ? x : -INFINITY;
+        bool ok = 4 * qd + i < nv[sub];
+        if constexpr (CAUSAL) ok = ok && pos0 + 16 * (2 * k + sub) + 4 * qd + i < row_limit;
+        sv[sub * 4 + i] = ok ? x : -INFINITY;
       }
     float mx = sv[0];
 #pragma unroll
@@ -350,7 +357,7 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int b, int g, i
   // The unit's result: normalised output and base-2 log-sum-exp.
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (r < G) {
+  if (r < n_rows) {
     const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
     float* dst = o_dst + (size_t)r * D + CPL * 4 * qd;
 #pragma unroll
@@ -440,7 +447,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       pb = uniform(x < 0 ? 0 : x);
     };
     const size_t unit = ((size_t)b * Hkv + g) * p.num_splits + split;
-    attend_head<D, FP8>(p.c, b, g, T / 16, desc, p.part_o + unit * G * D, p.part_lse + unit * G);
+    const int rr = tid & 15;
+    const unsigned short* qrow = rr < G ? p.c.q + ((size_t)b * p.c.Hq + (size_t)g * G + rr) * D : nullptr;
+    attend_head<D, FP8, false>(p.c, g, T / 16, desc, qrow, G, 0, 0, p.part_o + unit * G * D,
+                               p.part_lse + unit * G);
   }
 }
 
@@ -595,7 +605,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_balanced_kernel(const BalPar
         pb = uniform(x < 0 ? 0 : x);
       };
       const size_t unit = slot * Hkv + g;
-      attend_head<D, FP8>(p.c, b, g, ue - ub, desc, p.part_o + unit * G * D, p.part_lse + unit * G);
+      const int rr = tid & 15;
+      const unsigned short* qrow =
+          rr < G ? p.c.q + ((size_t)b * p.c.Hq + (size_t)g * G + rr) * D : nullptr;
+      attend_head<D, FP8, false>(p.c, g, ue - ub, desc, qrow, G, 0, 0, p.part_o + unit * G * D,
+                                 p.part_lse + unit * G);
     }
   }
 }
@@ -794,6 +808,136 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
     }
     const float inv = wt > 0.f ? 1.f / wt : 0.f;
     *(f32x4*)(out + 4 * tid) = a * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-token queries (varlen): rows = (query token, head) pairs, causal mask
+// aligned to the right ([TL18] 2.7, 3.3)
+// ---------------------------------------------------------------------------
+//
+// Query row m of sequence b's chunk (m < q_len * G) is token j = m / G, head
+// g * G + m % G; a 16-row tile of these rows is one MFMA row block, so a chunk
+// of q_len tokens costs ceil(q_len * G / 16) passes over the KV it sees (one pass
+// for decode-sized chunks: q_len * G <= 16). Row j sees positions
+// t <= ctx - q_len + j. Grid (row tile, split, sequence): the row tiles of one
+// KV split are neighbours in launch order, so they read that split together.
+
+struct VarlenParams {
+  AttnCommon c;
+  float* part_o;             // [B, H_kv, n_rt, S, 16, D] fp32
+  float* part_lse;           // [B, H_kv, n_rt, S, 16] fp32 (base 2)
+  float* out;                // [total_q, H_q, D] fp32 (combine)
+  const int* block_tables;
+  const int* ctx;
+  const int* cu;             // [B + 1] query row offsets
+  long long NB;
+  int max_blocks, max_ctx, num_splits, split_tokens, n_rt, total_q;
+};
+
+// A sequence's query rows, with bad offsets (outside [0, total_q] or decreasing)
+// read as an empty chunk so that no row outside the query buffer is touched.
+__device__ __forceinline__ void varlen_rows(const VarlenParams& p, int b, int& q0, int& qn) {
+  q0 = p.cu[b];
+  const int q1 = p.cu[b + 1];
+  if (q0 < 0 || q1 < q0 || q1 > p.total_q) {
+    q0 = 0;
+    qn = 0;
+  } else {
+    qn = q1 - q0;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_varlen_kernel(const VarlenParams p) {
+  __shared__ int s_pb[kMaxTable];
+  const int rt = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
+  const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+  int q0, qn;
+  varlen_rows(p, b, q0, qn);
+  const int rows = qn * G;
+  const int m0 = 16 * rt;
+  if (m0 >= rows) return;
+  const int n_rows = rows - m0 < 16 ? rows - m0 : 16;
+  // Positions the tile's last row sees (the others see fewer).
+  int tile_lim = ctx - qn + (m0 + n_rows - 1) / G + 1;
+  tile_lim = tile_lim < 0 ? 0 : (tile_lim > ctx ? ctx : tile_lim);
+  const int T = p.split_tokens;
+  const int t0 = split * T;
+  if (t0 >= tile_lim) return;   // the combine counts only splits below tile_lim
+  const int e0 = t0 / bs;
+  const int n_ent = T / bs;
+  const int nb = (ctx + bs - 1) / bs;
+  for (int e = tid; e < n_ent; e += kWaves * 64) {
+    const int lb = e0 + e;
+    const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
+    s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
+  }
+  __syncthreads();
+  const int span = tile_lim - t0 < T ? tile_lim - t0 : T;
+  const int r = tid & 15;
+  const int m = m0 + r;
+  const int j = m / G;
+  for (int g = wave; g < Hkv; g += kWaves) {
+    auto desc = [&](int u, int& pb, int& row0, int& nv) {
+      const int tok = t0 + 16 * u;
+      const int x = s_pb[tok / bs - e0];
+      row0 = tok & (bs - 1);
+      int n = t0 + span - tok;
+      n = n < 0 ? 0 : (n > 16 ? 16 : n);
+      if (x < 0) n = 0;
+      nv = uniform(n);
+      pb = uniform(x < 0 ? 0 : x);
+    };
+    const unsigned short* qrow =
+        r < n_rows ? p.c.q + ((size_t)(q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
+                   : nullptr;
+    const int row_limit = ctx - qn + j + 1;
+    const size_t unit = (((size_t)b * Hkv + g) * p.n_rt + rt) * p.num_splits + split;
+    attend_head<D, false, true>(p.c, g, (span + 15) / 16, desc, qrow, n_rows, t0, row_limit,
+                                p.part_o + unit * 16 * D, p.part_lse + unit * 16);
+  }
+}
+
+// Merge of one (row tile, KV head, sequence) over its splits, written to the
+// flattened output rows.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void attn_varlen_combine_kernel(const VarlenParams p) {
+  constexpr int TPR = D / 4;   // threads per row, 4 channels each
+  const int rt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = p.c.G, Hq = p.c.Hq;
+  const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+  int q0, qn;
+  varlen_rows(p, b, q0, qn);
+  const int rows = qn * G;
+  const int m0 = 16 * rt;
+  if (m0 >= rows) return;
+  const int n_rows = rows - m0 < 16 ? rows - m0 : 16;
+  int tile_lim = ctx - qn + (m0 + n_rows - 1) / G + 1;
+  tile_lim = tile_lim < 0 ? 0 : (tile_lim > ctx ? ctx : tile_lim);
+  const int n_units = (tile_lim + p.split_tokens - 1) / p.split_tokens;
+  const size_t unit0 = (((size_t)b * p.c.Hkv + g) * p.n_rt + rt) * p.num_splits;
+  for (int i = threadIdx.x; i < n_rows * TPR; i += kCombineThreads) {
+    const int r = i / TPR, c4 = i - (i / TPR) * TPR;
+    const float* lse0 = p.part_lse + unit0 * 16 + r;
+    const float* o0 = p.part_o + (unit0 * 16 + r) * D + 4 * c4;
+    float M = -INFINITY;
+    for (int u = 0; u < n_units; ++u) M = fmaxf(M, lse0[(size_t)u * 16]);
+    const float Mr = (M == -INFINITY) ? 0.f : M;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    for (int u = 0; u < n_units; ++u) {
+      const float w = __builtin_amdgcn_exp2f(lse0[(size_t)u * 16] - Mr);
+      W += w;
+      acc += w * *(const f32x4*)(o0 + (size_t)u * 16 * D);
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    const int m = m0 + r, j = m / G;
+    *(f32x4*)(p.out + ((size_t)(q0 + j) * Hq + (size_t)g * G + (m - j * G)) * D + 4 * c4) =
+        acc * inv;
   }
 }
 
@@ -1033,9 +1177,124 @@ static int attn_run(bool sparse, bool fp8, float* out, const void* query, const 
   return check_launch(fn);
 }
 
+// Multi-token queries: row tiles per sequence, split size and workspace.
+constexpr long long kVarlenMaxUnits = 1LL << 18;   // partial-row blocks (about 2 GB at D = 128)
+
+struct VarlenPlan {
+  int n_rt, split_tokens, num_splits;
+  size_t o_bytes, lse_bytes;
+};
+
+static VarlenPlan make_varlen_plan(int B, int max_q_len, int Hq, int Hkv, int D, int bs,
+                                   int max_ctx) {
+  VarlenPlan pl;
+  const long long G = Hq / Hkv;
+  const long long n_rt = (max_q_len * G + 15) / 16;
+  pl.n_rt = (int)(n_rt > 0 ? n_rt : 1);
+  const long long rows_b = (long long)B * pl.n_rt;
+  int T = split_tokens_for(rows_b > (1 << 30) ? (1 << 30) : (int)rows_b, Hkv, max_ctx);
+  auto units = [&](int t) {
+    const long long ns = ((long long)max_ctx + t - 1) / t;
+    return (long long)B * Hkv * pl.n_rt * (ns > 0 ? ns : 1);
+  };
+  while (units(T) > kVarlenMaxUnits && T < 16384) T <<= 1;
+  while (T / bs > kMaxTable) T >>= 1;
+  pl.split_tokens = T;
+  pl.num_splits = (int)(((long long)max_ctx + T - 1) / T);
+  if (pl.num_splits < 1) pl.num_splits = 1;
+  const size_t u = (size_t)B * Hkv * pl.n_rt * pl.num_splits;
+  pl.o_bytes = align256(u * 16 * D * sizeof(float));
+  pl.lse_bytes = align256(u * 16 * sizeof(float));
+  return pl;
+}
+
 }  // namespace gpkv
 
 using namespace gpkv;
+
+extern "C" size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int32_t max_q_len,
+                                                              int32_t num_q_heads,
+                                                              int32_t num_kv_heads,
+                                                              int32_t head_dim,
+                                                              int32_t block_size,
+                                                              int32_t max_context_len) {
+  if (batch < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads || !supported_head_dim(head_dim) ||
+      !supported_block_size(block_size) || max_context_len < 0)
+    return 0;
+  const VarlenPlan pl = make_varlen_plan(batch, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                         block_size, max_context_len);
+  return pl.o_bytes + pl.lse_bytes;
+}
+
+extern "C" int gpkv_paged_attention_varlen(
+    float* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens_q,
+    int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* fn = "paged_attention_varlen";
+  int st = check_common(fn, batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        max_blocks_per_seq, max_context_len);
+  if (st) return st;
+  if (total_q < 0 || max_q_len < 0)
+    return fail(GPKV_ERR_SHAPE, "%s: total_q=%d max_q_len=%d", fn, total_q, max_q_len);
+  if (batch == 0 || total_q == 0) return GPKV_OK;
+  if (max_q_len == 0) return fail(GPKV_ERR_SHAPE, "%s: max_q_len=0 with total_q=%d", fn, total_q);
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !cu_seqlens_q)
+    return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
+  const VarlenPlan pl = make_varlen_plan(batch, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                         block_size, max_context_len);
+  if (pl.num_splits > 65535)
+    return fail(GPKV_ERR_SHAPE, "%s: max_context_len=%d needs too many splits", fn,
+                max_context_len);
+  const size_t need = pl.o_bytes + pl.lse_bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(GPKV_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  hipStream_t s = (hipStream_t)stream;
+  VarlenParams vp;
+  vp.c.q = (const unsigned short*)query;
+  vp.c.kc = (const unsigned char*)key_cache;
+  vp.c.vc = (const unsigned char*)value_cache;
+  vp.c.k_scale = nullptr;
+  vp.c.v_scale = nullptr;
+  vp.c.row_bytes = num_kv_heads * head_dim * 2;
+  vp.c.block_bytes = (long long)block_size * vp.c.row_bytes;
+  vp.c.Hq = num_q_heads;
+  vp.c.Hkv = num_kv_heads;
+  vp.c.G = num_q_heads / num_kv_heads;
+  vp.c.bs = block_size;
+  vp.c.qk_scale_log2 = scale * 1.4426950408889634f;
+  vp.part_o = (float*)workspace;
+  vp.part_lse = (float*)((char*)workspace + pl.o_bytes);
+  vp.out = out;
+  vp.block_tables = block_tables;
+  vp.ctx = context_lens;
+  vp.cu = cu_seqlens_q;
+  vp.NB = num_blocks;
+  vp.max_blocks = max_blocks_per_seq;
+  vp.max_ctx = max_context_len;
+  vp.num_splits = pl.num_splits;
+  vp.split_tokens = pl.split_tokens;
+  vp.n_rt = pl.n_rt;
+  vp.total_q = total_q;
+  const dim3 grid(pl.n_rt, pl.num_splits, batch), block(kWaves * 64);
+  if (head_dim == 128)
+    attn_varlen_kernel<128><<<grid, block, 0, s>>>(vp);
+  else
+    attn_varlen_kernel<64><<<grid, block, 0, s>>>(vp);
+  st = check_launch(fn);
+  if (st) return st;
+  const dim3 cgrid(pl.n_rt, num_kv_heads, batch), cblock(kCombineThreads);
+  if (head_dim == 128)
+    attn_varlen_combine_kernel<128><<<cgrid, cblock, 0, s>>>(vp);
+  else
+    attn_varlen_combine_kernel<64><<<cgrid, cblock, 0, s>>>(vp);
+  return check_launch(fn);
+}
 
 extern "C" size_t gpkv_paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                                        int32_t num_kv_heads, int32_t head_dim,

@@ -17,6 +17,7 @@ __all__ = [
     "quest_select_topk", "sparse_paged_attention_decode", "paged_attention_workspace_bytes",
     "quest_select_workspace_bytes", "sparse_attention_workspace_bytes", "split_tokens",
     "reshape_and_cache_fp8", "paged_attention_decode_fp8", "sparse_paged_attention_decode_fp8",
+    "paged_attention_varlen", "paged_attention_varlen_workspace_bytes",
 ]
 
 
@@ -310,4 +311,45 @@ def sparse_paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(context_lens), _ptr(topk_indices), B, Hq, Hkv, D, bs, NB, MB,
         int(max_context_len), K, float(scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Multi-token queries (varlen, causal mask aligned to the right)
+# ---------------------------------------------------------------------------
+
+def paged_attention_varlen_workspace_bytes(batch, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                           block_size, max_context_len) -> int:
+    return int(lib().gpkv_paged_attention_varlen_workspace_bytes(
+        batch, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len))
+
+
+def paged_attention_varlen(query, key_cache, value_cache, block_tables, context_lens, cu_seqlens_q,
+                           *, max_q_len: int, max_context_len: int, scale: float, out=None,
+                           workspace=None, stream=None) -> torch.Tensor:
+    """Attention of every query row of a flattened multi-token batch; returns
+    [total_q, H_q, D] float32. Row j of sequence b sees positions
+    <= context_lens[b] - q_len_b + j."""
+    _dev("query", query, torch.bfloat16, 3)
+    _dev("key_cache", key_cache, torch.bfloat16, 4)
+    _dev("value_cache", value_cache, torch.bfloat16, 4)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    _dev("cu_seqlens_q", cu_seqlens_q, torch.int32, 1)
+    NB, bs, Hkv, D = _cache_dims(key_cache)
+    UQ, Hq, Dq = query.shape
+    B = int(context_lens.shape[0])
+    if value_cache.shape != key_cache.shape or Dq != D or block_tables.shape[0] != B \
+            or cu_seqlens_q.shape[0] != B + 1:
+        raise ValueError("paged_attention_varlen: inconsistent shapes")
+    if out is None:
+        out = torch.empty((UQ, Hq, D), dtype=torch.float32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    need = paged_attention_varlen_workspace_bytes(B, max_q_len, Hq, Hkv, D, bs, max_context_len)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_paged_attention_varlen(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(cu_seqlens_q), B, UQ, int(max_q_len), Hq, Hkv, D, bs, NB,
+        int(block_tables.shape[1]), int(max_context_len), float(scale), _ptr(ws), ws.numel(),
+        _stream(stream)))
     return out

@@ -11,13 +11,15 @@
  *   gpkv_quest_select_topk           Quest block scores + Top-K per KV head
  *   gpkv_sparse_paged_attention_decode  exact attention over the selected blocks
  *   ..._fp8 variants of the write and both attention calls over E4M3 caches
+ *   gpkv_paged_attention_varlen      multi-token queries (causal, right-aligned)
  *
  * Sources, by page title and section:
  *   [ASC]  "Ascend Kernel-to-Serving Pipeline": sections "ReshapeAndCache",
  *          "GQA Paged Attention", "Quest Sparse Attention", "single-operator
  *          correctness", "Sparse precision", "memory optimisation".
  *   [TL18] TileLang tutorial, chapter 18 (end-to-end inference serving):
- *          2.4 KV-cache structure, 2.6 paged KV, 4.1 split-KV decode attention,
+ *          2.4 KV-cache structure, 2.6 paged KV, 2.7 varlen batches, 3.3 varlen
+ *          kernel requirements, 4.1 split-KV decode attention,
  *          2.5 item 3 and 3.1 item 4 (KV quantisation as the long-context lever),
  *          6.1 kernels on the framework's current stream, 6.2 graph capture,
  *          8 item (2) the per-step KV write.
@@ -252,6 +254,39 @@ int gpkv_sparse_paged_attention_decode_fp8(float* out, const void* query, const 
                                            int32_t max_context_len, int32_t topk_blocks,
                                            float scale, void* workspace,
                                            size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Multi-token queries (varlen batches: [TL18] 2.7 continuous batching with
+ * ragged lengths; 3.3 flattened queries with cu_seqlens and the causal mask
+ * aligned to the right, item 4). Sequence b brings q_len_b =
+ * cu_seqlens_q[b + 1] - cu_seqlens_q[b] query tokens: the newest q_len_b of its
+ * context_lens[b] positions, whose K/V are already in the cache (written by
+ * gpkv_reshape_and_cache). Query token j (0-based) of sequence b attends to the
+ * positions t <= context_lens[b] - q_len_b + j:
+ *   out[r, h, :] = sum_t p_t V_t, p = softmax_t(scale * q[r, h, :] . K_t),
+ * r = cu_seqlens_q[b] + j, K_t / V_t of KV head h / G. A row that sees no
+ * position (q_len_b > context_lens[b], j small) gets a zero row.
+ * query: [total_q, num_q_heads, head_dim] bf16; out: same shape, float32.
+ * cu_seqlens_q: [batch + 1] int32 in device memory, non-decreasing from 0 to
+ *   total_q (a sequence whose offsets fall outside [0, total_q] or decrease is
+ *   treated as empty). max_q_len: a host bound of every q_len_b (rows past it are
+ *   not computed). Decode is the case q_len_b = 1.
+ * workspace: at least gpkv_paged_attention_varlen_workspace_bytes(...) bytes;
+ *   contents on entry ignored.
+ * --------------------------------------------------------------------------- */
+size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int32_t max_q_len,
+                                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t head_dim, int32_t block_size,
+                                                   int32_t max_context_len);
+
+int gpkv_paged_attention_varlen(float* out, const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* cu_seqlens_q,
+                                int32_t batch, int32_t total_q, int32_t max_q_len,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* gpkv_status_string(int status);

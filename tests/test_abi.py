@@ -28,7 +28,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(L):
     from gqa_paged_kv_amd._lib import SIGNATURES
     names = declared_symbols()
-    assert len(names) == 15
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert sorted(SIGNATURES) == names
@@ -102,6 +102,16 @@ def test_other_entry_points_checks(L):
                                              0.1, 8, 16, None) == -4
     assert L.gpkv_sparse_paged_attention_decode_fp8(8, 8, 8, 8, 8, 8, 8, 8, None, 2, 4, 1, 64, 16,
                                                     16, 5, 80, 3, 0.1, 8, 1 << 30, None) == -1
+    # varlen: null cu_seqlens, zero rows is a no-op, max_q_len 0 with rows, small workspace
+    assert L.gpkv_paged_attention_varlen(8, 8, 8, 8, 8, 8, None, 2, 5, 4, 4, 1, 64, 16, 16, 5, 80,
+                                         0.1, 8, 1 << 30, None) == -1
+    assert L.gpkv_paged_attention_varlen(None, None, None, None, None, None, None, 2, 0, 4, 4, 1,
+                                         64, 16, 16, 5, 80, 0.1, None, 0, None) == 0
+    assert L.gpkv_paged_attention_varlen(8, 8, 8, 8, 8, 8, 8, 2, 5, 0, 4, 1, 64, 16, 16, 5, 80,
+                                         0.1, 8, 1 << 30, None) == -2
+    assert L.gpkv_paged_attention_varlen(8, 8, 8, 8, 8, 8, 8, 2, 5, 4, 4, 1, 64, 16, 16, 5, 80,
+                                         0.1, 8, 16, None) == -4
+    assert L.gpkv_paged_attention_varlen_workspace_bytes(2, 4, 4, 1, 64, 16, 80) > 0
 
 
 def test_workspace_queries(L):

@@ -1,0 +1,115 @@
+"""GPU parity of multi-token queries (varlen, causal mask aligned to the right)
+against the CPU oracle. Bar: max-abs 2e-3 (bf16 inputs, fp32 accumulation)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_paged_kv_amd as gp
+import oracle
+import workloads
+from gpu_util import BF, Dev, max_abs, to_dev
+
+pytestmark = pytest.mark.gpu
+ATOL = 2e-3
+
+
+def _run(w, **kw):
+    d = Dev(w)
+    qv = to_dev(w.query_varlen, BF)
+    cu = to_dev(w.cu_seqlens_q, torch.int32)
+    ql = np.diff(w.cu_seqlens_q)
+    out = gp.paged_attention_varlen(qv, d.kc, d.vc, d.bt, d.ctx, cu, max_q_len=int(ql.max()),
+                                    max_context_len=w.max_context_len, scale=float(w.scale), **kw)
+    return d, out.cpu().numpy()
+
+
+def _ref(w, seqs=None):
+    return oracle.paged_attention_varlen(w.query_varlen, w.key_cache, w.value_cache,
+                                         w.block_tables, w.context_lens, w.cu_seqlens_q, w.scale,
+                                         seqs=seqs)
+
+
+VARLEN_CASES = [
+    # seed, Hq, Hkv, D, bs, ctx, q_lens
+    (701, 28, 4, 128, 16, [900, 33, 2500, 16, 1200, 700], [1, 7, 64, 16, 3, 1]),
+    (702, 4, 1, 64, 16, [0, 1, 15, 17, 40, 5], [3, 1, 15, 2, 40, 9]),      # q_len >= ctx rows
+    (703, 16, 16, 128, 32, [300, 65, 1000], [2, 65, 200]),                   # G = 1
+    (704, 16, 1, 128, 64, [129, 2047, 4100], [16, 1, 130]),                  # G = 16
+    (705, 64, 8, 128, 128, [1, 127, 3000, 129], [1, 5, 100, 129]),
+    (706, 14, 2, 64, 128, [250, 1, 700], [250, 1, 33]),
+    (707, 12, 3, 64, 32, [513, 514, 96], [1, 2, 96]),
+]
+
+
+@pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx,ql", VARLEN_CASES)
+def test_varlen_random(seed, Hq, Hkv, D, bs, ctx, ql):
+    w = workloads.varlen_case(seed, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                              context_lens=ctx, q_lens=ql)
+    _, out = _run(w)
+    ref = _ref(w)
+    err = max_abs(out, ref)
+    print(f"seed {seed}: varlen max-abs {err:.3e}")
+    assert err <= ATOL
+    assert (out[np.all(ref == 0, axis=(1, 2))] == 0).all(), "rows that see nothing are zero"
+
+
+@pytest.mark.parametrize("split", [128, 256, 512, 2048])
+def test_varlen_split_sizes(split, monkeypatch):
+    """Chunks whose rows end in different splits of the KV range."""
+    monkeypatch.setenv("GPKV_SPLIT_TOKENS", str(split))
+    w = workloads.varlen_case(710, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
+                              context_lens=[4000, 2500, 129, 700], q_lens=[300, 1, 129, 20])
+    _, out = _run(w)
+    assert max_abs(out, _ref(w)) <= ATOL
+
+
+def test_varlen_single_tokens_equal_decode():
+    """q_len = 1 everywhere: the same rows as the decode call."""
+    ctx = [900, 33, 2500, 16, 0, 700]
+    w = workloads.varlen_case(711, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
+                              context_lens=ctx, q_lens=[1] * 6)
+    d, out = _run(w)
+    dec = gp.paged_attention_decode(to_dev(w.query_varlen, BF), d.kc, d.vc, d.bt, d.ctx,
+                                    max_context_len=w.max_context_len,
+                                    scale=float(w.scale)).cpu().numpy()
+    ref = _ref(w)
+    assert max_abs(out, ref) <= ATOL and max_abs(dec, ref) <= ATOL
+    assert max_abs(out, dec) <= 1e-5
+
+
+def test_varlen_mixed_batch_8k():
+    """An 8K-average batch in which a few sequences bring prefill chunks and the rest
+    decode one token each; sampled sequences against the oracle."""
+    rng = np.random.default_rng(712)
+    ctx = np.clip(np.round(rng.normal(8192, 2048, 64)), 2048, 16384).astype(np.int32)
+    ql = np.ones(64, np.int32)
+    ql[:6] = [128, 256, 64, 512, 32, 128]
+    w = workloads.varlen_case(712, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
+                              context_lens=ctx, q_lens=ql)
+    _, out = _run(w)
+    seqs = [0, 1, 3, 5, 17, 63]
+    ref = _ref(w, seqs=seqs)
+    rows = np.concatenate([np.arange(w.cu_seqlens_q[b], w.cu_seqlens_q[b + 1]) for b in seqs])
+    err = max_abs(out[rows], ref[rows])
+    print(f"mixed 8K batch: varlen max-abs {err:.3e}")
+    assert err <= ATOL
+
+
+def test_varlen_bad_offsets_read_as_empty():
+    """A decreasing cu_seqlens entry makes that sequence empty; the others are
+    unaffected and nothing outside the buffers is touched."""
+    w = workloads.varlen_case(713, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                              context_lens=[40, 50, 60], q_lens=[4, 3, 5])
+    d = Dev(w)
+    bad = np.array([0, 4, 2, 13], np.int32)   # sequence 1 decreasing; sequence 2 past total_q
+    qv = to_dev(w.query_varlen, BF)
+    out = torch.full((12, 8, 64), 7.0, device="cuda")
+    gp.paged_attention_varlen(qv, d.kc, d.vc, d.bt, d.ctx, to_dev(bad, torch.int32), max_q_len=10,
+                              max_context_len=w.max_context_len, scale=float(w.scale), out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = _ref(w)
+    assert max_abs(got[:4], ref[:4]) <= ATOL          # sequence 0 intact
+    assert (got[4:] == 7.0).all(), "rows of the empty sequences are not written"
