@@ -49,14 +49,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 constexpr int kLoadNT = 2;
 
 // Buffer loads: an offset at or past `bytes` of the descriptor returns zeros.
+// AUX = kLoadNT streams data read once; AUX = 0 keeps it in the caches for
+// readers that share it.
+template <int AUX = kLoadNT>
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadNT);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
 }
+template <int AUX = kLoadNT>
 __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLoadNT);
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX);
 }
+template <int AUX = kLoadNT>
 __device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kLoadNT);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, AUX);
 }
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }

@@ -85,15 +85,17 @@ struct VecT;
 template <>
 struct VecT<128> {
   typedef u32x4 type;
+  template <int AUX>
   static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    return buf_load16(r, off);
+    return buf_load16<AUX>(r, off);
   }
 };
 template <>
 struct VecT<64> {
   typedef u32x2 type;
+  template <int AUX>
   static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    return buf_load8(r, off);
+    return buf_load8<AUX>(r, off);
   }
 };
 
@@ -123,8 +125,9 @@ struct VCodes;
 template <>
 struct VCodes<128> {   // 8 codes per token
   typedef u32x2 type;
+  template <int AUX>
   static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    return buf_load8(r, off);
+    return buf_load8<AUX>(r, off);
   }
   static __device__ __forceinline__ u32x4 to_bf16(type w) {
     const u32x2 a = e4m3x4_to_bf16(w[0]), b = e4m3x4_to_bf16(w[1]);
@@ -134,26 +137,41 @@ struct VCodes<128> {   // 8 codes per token
 template <>
 struct VCodes<64> {    // 4 codes per token
   typedef unsigned type;
+  template <int AUX>
   static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    return buf_load4(r, off);
+    return buf_load4<AUX>(r, off);
   }
   static __device__ __forceinline__ u32x2 to_bf16(type w) { return e4m3x4_to_bf16(w); }
 };
 
-// Attention of up to 16 query rows against KV head g over sub-tiles [0, n_sub) of
-// one unit. Lane row r (= lane % 16) reads its query from qrow (nullptr: a padding
-// row of zeros); rows r < n_rows are written to o_dst[r][D] (normalised) and
-// lse_dst[r] (base-2 log-sum-exp). Decode: the rows are the G query heads of the
-// group. CAUSAL (multi-token queries): sub-tile u covers positions pos0 + 16u ..,
-// and row r sees only positions < row_limit (its own bound).
-template <int D, bool FP8, bool CAUSAL, class Desc>
+// RT tiles of up to 16 query rows that share every loaded K / V tile. For tile t,
+// lane row r (= lane % 16): q[t] is the row's query (nullptr: a padding row of
+// zeros), limit[t] its causal bound (CAUSAL only); rows r < n_rows[t] are written
+// to o[t][r][D] (normalised) and lse[t][r] (base-2 log-sum-exp).
+template <int RT>
+struct RowTiles {
+  const unsigned short* q[RT];
+  int n_rows[RT];
+  int limit[RT];
+  float* o[RT];
+  float* lse[RT];
+};
+
+// Attention of RT row tiles against KV head g over sub-tiles [0, n_sub) of one
+// unit. Decode: one tile, the G query heads of the group. CAUSAL (multi-token
+// queries): sub-tile u covers positions pos0 + 16u .., and a row sees only the
+// positions below its bound; several row tiles per wave multiply the MFMA work
+// done per K / V byte loaded.
+template <int D, bool FP8, bool CAUSAL, int RT, class Desc>
 __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_sub, const Desc& desc,
-                                            const unsigned short* qrow, int n_rows, int pos0,
-                                            int row_limit, float* o_dst, float* lse_dst) {
+                                            int pos0, const RowTiles<RT>& rows) {
   constexpr int KSTEPS = D / 32;  // k-steps of the q.k contraction
   constexpr int KLOADS = FP8 ? D / 64 : KSTEPS;   // 16-byte K loads per sub-tile
   constexpr int CPL = D / 16;     // channels per lane in the V^T operand / O^T tiles
   constexpr int EB = FP8 ? 1 : 2; // bytes per cached element
+  // Decode reads every K / V byte once: non-temporal loads. Multi-token queries
+  // re-read a split's K / V from every row tile of the chunk: cached loads.
+  constexpr int AUX = CAUSAL ? 0 : kLoadNT;
   typedef typename VecT<D>::type vvec;
   typedef typename VCodes<D>::type vcodes;
   const int lane = threadIdx.x & 63;
@@ -165,21 +183,30 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
     v_scale = c.v_scale[g];
   }
 
-  // Q^T operand: lane holds row r's channels of each k-step (zero for padding rows).
-  u32x4 qf[KSTEPS];
-  if (qrow != nullptr) {
+  // Q^T operands: lane holds row r's channels of each k-step (zero for padding rows).
+  u32x4 qf[RT][KSTEPS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qrow + kstep_channel<FP8>(s, qd));
-  } else {
+  for (int t = 0; t < RT; ++t) {
+    if (rows.q[t] != nullptr) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < KSTEPS; ++s)
+        qf[t][s] = *(const u32x4*)(rows.q[t] + kstep_channel<FP8>(s, qd));
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[t][s] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
-  f32x4 oacc[CPL];
+  f32x4 oacc[RT][CPL];
+  float m_run[RT], l_run[RT];  // running max of row r (base 2, same in its 4 lanes) and
+                               // this lane's share of the normaliser
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of head r (base 2), same in its 4 lanes
-  float l_run = 0.f;        // this lane's share of the normaliser
+  for (int t = 0; t < RT; ++t) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) oacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+  }
 
   const unsigned off_k = (unsigned)(r * c.row_bytes + g * D * EB + qd * 16);
   const unsigned off_v = (unsigned)(4 * qd * c.row_bytes + g * D * EB + r * CPL * EB);
@@ -228,9 +255,9 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
 #pragma unroll
       for (int s = 0; s < KLOADS; ++s) {
         if constexpr (FP8)
-          kq[sub][s] = buf_load16(rk, off_k + 64 * s);
+          kq[sub][s] = buf_load16<AUX>(rk, off_k + 64 * s);
         else
-          kf[sub][s] = buf_load16(rk, off_k + 64 * s);
+          kf[sub][s] = buf_load16<AUX>(rk, off_k + 64 * s);
       }
     }
   };
@@ -242,9 +269,9 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (FP8)
-          vq[sub][i] = VCodes<D>::load(rv, off_v + i * c.row_bytes);
+          vq[sub][i] = VCodes<D>::template load<AUX>(rv, off_v + i * c.row_bytes);
         else
-          vf[sub][i] = VecT<D>::load(rv, off_v + i * c.row_bytes);
+          vf[sub][i] = VecT<D>::template load<AUX>(rv, off_v + i * c.row_bytes);
       }
     }
   };
@@ -271,57 +298,63 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
         for (int t = 0; t < KLOADS; ++t) k_codes_to_bf16(kq[sub][t], kf[sub][2 * t], kf[sub][2 * t + 1]);
     }
     // S^T for both sub-tiles.
-    f32x4 sacc[2];
+    f32x4 sacc[RT][2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) sacc[sub] = mfma16x16x32(kf[sub][s], qf[s], sacc[sub]);
-    }
+      for (int sub = 0; sub < 2; ++sub) {
+        sacc[t][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+          sacc[t][sub] = mfma16x16x32(kf[sub][s], qf[t][s], sacc[t][sub]);
+      }
     issue_k(pbn, row0n, nvn);
 
-    // Online softmax over this tile for head r (base 2).
-    float sv[8];
+    // Online softmax over this tile for row r of each row tile (base 2), and the
+    // P^T operands as bf16 hi + lo parts.
+    u32x4 phi[RT], plo[RT];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int t = 0; t < RT; ++t) {
+      float sv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = sacc[sub][i] * qk_scale;
-        bool ok = 4 * qd + i < nv[sub];
-        if constexpr (CAUSAL) ok = ok && pos0 + 16 * (2 * k + sub) + 4 * qd + i < row_limit;
-        sv[sub * 4 + i] = ok ? x : -INFINITY;
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = sacc[t][sub][i] * qk_scale;
+          bool ok = 4 * qd + i < nv[sub];
+          if constexpr (CAUSAL)
+            ok = ok && pos0 + 16 * (2 * k + sub) + 4 * qd + i < rows.limit[t];
+          sv[sub * 4 + i] = ok ? x : -INFINITY;
+        }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[t], mx);
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_ref);
+      float pv[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+        psum += pv[i];
       }
-    float mx = sv[0];
+      l_run[t] = l_run[t] * alpha + psum;
+      m_run[t] = m_new;
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    float pv[8];
-    float psum = 0.f;
+        for (int j = 0; j < CPL; ++j) oacc[t][j] *= alpha;
+      }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
-      psum += pv[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) oacc[j] *= alpha;
-    }
-
-    // P^T operand as bf16 hi + lo parts.
-    u32x4 phi, plo;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const unsigned a = __float_as_uint(pv[2 * d]), cc = __float_as_uint(pv[2 * d + 1]);
-      phi[d] = pack_hi16(a, cc);
-      const float ra = pv[2 * d] - __uint_as_float(a & 0xffff0000u);
-      const float rc = pv[2 * d + 1] - __uint_as_float(cc & 0xffff0000u);
-      plo[d] = pack_hi16(__float_as_uint(ra), __float_as_uint(rc));
+      for (int d = 0; d < 4; ++d) {
+        const unsigned a = __float_as_uint(pv[2 * d]), cc = __float_as_uint(pv[2 * d + 1]);
+        phi[t][d] = pack_hi16(a, cc);
+        const float ra = pv[2 * d] - __uint_as_float(a & 0xffff0000u);
+        const float rc = pv[2 * d + 1] - __uint_as_float(cc & 0xffff0000u);
+        plo[t][d] = pack_hi16(__float_as_uint(ra), __float_as_uint(rc));
+      }
     }
 
     if constexpr (FP8) {
@@ -340,8 +373,11 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
         const unsigned w0 = vf[sub][i0][j >> 1], w1 = vf[sub][i0 + 1][j >> 1];
         va[d] = (j & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
       }
-      oacc[j] = mfma16x16x32(va, phi, oacc[j]);
-      oacc[j] = mfma16x16x32(va, plo, oacc[j]);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        oacc[t][j] = mfma16x16x32(va, phi[t], oacc[t][j]);
+        oacc[t][j] = mfma16x16x32(va, plo[t], oacc[t][j]);
+      }
     }
     issue_v(pbn, row0n, nvn);
     k = kn;
@@ -354,23 +390,26 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
     kn = next_tile(k + 1, pbn, row0n, nvn);
   }
 
-  // The unit's result: normalised output and base-2 log-sum-exp.
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (r < n_rows) {
-    const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
-    float* dst = o_dst + (size_t)r * D + CPL * 4 * qd;
+  // The unit's result per row tile: normalised output and base-2 log-sum-exp.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int t = 0; t < RT; ++t) {
+    float l_tot = l_run[t] + __shfl_xor(l_run[t], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (r < rows.n_rows[t]) {
+      const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
+      float* dst = rows.o[t] + (size_t)r * D + CPL * 4 * qd;
 #pragma unroll
-      for (int j0 = 0; j0 < CPL; j0 += 4) {
-        f32x4 v;
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v[jj] = oacc[j0 + jj][i] * inv;
-        *(f32x4*)(dst + CPL * i + j0) = v;
+        for (int j0 = 0; j0 < CPL; j0 += 4) {
+          f32x4 v;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) v[jj] = oacc[t][j0 + jj][i] * inv;
+          *(f32x4*)(dst + CPL * i + j0) = v;
+        }
       }
+      if (qd == 0) rows.lse[t][r] = l_tot > 0.f ? m_run[t] + log2f(l_tot) : -INFINITY;
     }
-    if (qd == 0) lse_dst[r] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
   }
 }
 
@@ -448,9 +487,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     };
     const size_t unit = ((size_t)b * Hkv + g) * p.num_splits + split;
     const int rr = tid & 15;
-    const unsigned short* qrow = rr < G ? p.c.q + ((size_t)b * p.c.Hq + (size_t)g * G + rr) * D : nullptr;
-    attend_head<D, FP8, false>(p.c, g, T / 16, desc, qrow, G, 0, 0, p.part_o + unit * G * D,
-                               p.part_lse + unit * G);
+    RowTiles<1> rows;
+    rows.q[0] = rr < G ? p.c.q + ((size_t)b * p.c.Hq + (size_t)g * G + rr) * D : nullptr;
+    rows.n_rows[0] = G;
+    rows.limit[0] = 0;
+    rows.o[0] = p.part_o + unit * G * D;
+    rows.lse[0] = p.part_lse + unit * G;
+    attend_head<D, FP8, false, 1>(p.c, g, T / 16, desc, 0, rows);
   }
 }
 
@@ -606,10 +649,13 @@ __global__ __launch_bounds__(kWaves * 64) void attn_balanced_kernel(const BalPar
       };
       const size_t unit = slot * Hkv + g;
       const int rr = tid & 15;
-      const unsigned short* qrow =
-          rr < G ? p.c.q + ((size_t)b * p.c.Hq + (size_t)g * G + rr) * D : nullptr;
-      attend_head<D, FP8, false>(p.c, g, ue - ub, desc, qrow, G, 0, 0, p.part_o + unit * G * D,
-                                 p.part_lse + unit * G);
+      RowTiles<1> rows;
+      rows.q[0] = rr < G ? p.c.q + ((size_t)b * p.c.Hq + (size_t)g * G + rr) * D : nullptr;
+      rows.n_rows[0] = G;
+      rows.limit[0] = 0;
+      rows.o[0] = p.part_o + unit * G * D;
+      rows.lse[0] = p.part_lse + unit * G;
+      attend_head<D, FP8, false, 1>(p.c, g, ue - ub, desc, 0, rows);
     }
   }
 }
@@ -848,10 +894,10 @@ __device__ __forceinline__ void varlen_rows(const VarlenParams& p, int b, int& q
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_varlen_kernel(const VarlenParams p) {
+template <int D, int RT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 1))) void attn_varlen_kernel(const VarlenParams p) {
   __shared__ int s_pb[kMaxTable];
-  const int rt = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  const int tg = blockIdx.x, split = blockIdx.y, b = blockIdx.z;   // tg: group of RT row tiles
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
@@ -859,15 +905,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   int q0, qn;
   varlen_rows(p, b, q0, qn);
   const int rows = qn * G;
-  const int m0 = 16 * rt;
-  if (m0 >= rows) return;
-  const int n_rows = rows - m0 < 16 ? rows - m0 : 16;
-  // Positions the tile's last row sees (the others see fewer).
-  int tile_lim = ctx - qn + (m0 + n_rows - 1) / G + 1;
+  const int m_first = 16 * RT * tg;
+  if (m_first >= rows) return;
+  // Positions the group's last row sees (the others see fewer).
+  const int m_last = (m_first + 16 * RT < rows ? m_first + 16 * RT : rows) - 1;
+  int tile_lim = ctx - qn + m_last / G + 1;
   tile_lim = tile_lim < 0 ? 0 : (tile_lim > ctx ? ctx : tile_lim);
   const int T = p.split_tokens;
   const int t0 = split * T;
-  if (t0 >= tile_lim) return;   // the combine counts only splits below tile_lim
+  if (t0 >= tile_lim) return;   // the combine counts only the splits a tile sees
   const int e0 = t0 / bs;
   const int n_ent = T / bs;
   const int nb = (ctx + bs - 1) / bs;
@@ -879,8 +925,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   __syncthreads();
   const int span = tile_lim - t0 < T ? tile_lim - t0 : T;
   const int r = tid & 15;
-  const int m = m0 + r;
-  const int j = m / G;
   for (int g = wave; g < Hkv; g += kWaves) {
     auto desc = [&](int u, int& pb, int& row0, int& nv) {
       const int tok = t0 + 16 * u;
@@ -892,13 +936,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       nv = uniform(n);
       pb = uniform(x < 0 ? 0 : x);
     };
-    const unsigned short* qrow =
-        r < n_rows ? p.c.q + ((size_t)(q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
-                   : nullptr;
-    const int row_limit = ctx - qn + j + 1;
-    const size_t unit = (((size_t)b * Hkv + g) * p.n_rt + rt) * p.num_splits + split;
-    attend_head<D, false, true>(p.c, g, (span + 15) / 16, desc, qrow, n_rows, t0, row_limit,
-                                p.part_o + unit * 16 * D, p.part_lse + unit * 16);
+    RowTiles<RT> tiles;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int rt = RT * tg + t;
+      const int m0 = 16 * rt;
+      const int n_rows = rows - m0 < 0 ? 0 : (rows - m0 < 16 ? rows - m0 : 16);
+      const int m = m0 + r, j = m / G;
+      tiles.q[t] = r < n_rows
+                       ? p.c.q + ((size_t)(q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
+                       : nullptr;
+      tiles.n_rows[t] = n_rows;
+      tiles.limit[t] = ctx - qn + j + 1;
+      const size_t unit = (((size_t)b * Hkv + g) * p.n_rt + (n_rows > 0 ? rt : 0)) * p.num_splits + split;
+      tiles.o[t] = p.part_o + unit * 16 * D;
+      tiles.lse[t] = p.part_lse + unit * 16;
+    }
+    attend_head<D, false, true, RT>(p.c, g, (span + 15) / 16, desc, t0, tiles);
   }
 }
 
@@ -1179,6 +1233,7 @@ static int attn_run(bool sparse, bool fp8, float* out, const void* query, const 
 
 // Multi-token queries: row tiles per sequence, split size and workspace.
 constexpr long long kVarlenMaxUnits = 1LL << 18;   // partial-row blocks (about 2 GB at D = 128)
+constexpr int kVarlenRT = 2;   // row tiles per wave when a chunk spans more than one tile
 
 struct VarlenPlan {
   int n_rt, split_tokens, num_splits;
@@ -1281,11 +1336,22 @@ extern "C" int gpkv_paged_attention_varlen(
   vp.split_tokens = pl.split_tokens;
   vp.n_rt = pl.n_rt;
   vp.total_q = total_q;
-  const dim3 grid(pl.n_rt, pl.num_splits, batch), block(kWaves * 64);
-  if (head_dim == 128)
-    attn_varlen_kernel<128><<<grid, block, 0, s>>>(vp);
-  else
-    attn_varlen_kernel<64><<<grid, block, 0, s>>>(vp);
+  // One row tile per wave for decode-sized chunks; otherwise kVarlenRT tiles share
+  // every K / V tile a wave loads.
+  const int rt_per_wave = pl.n_rt > 1 ? kVarlenRT : 1;
+  const dim3 grid((pl.n_rt + rt_per_wave - 1) / rt_per_wave, pl.num_splits, batch);
+  const dim3 block(kWaves * 64);
+  if (rt_per_wave == 1) {
+    if (head_dim == 128)
+      attn_varlen_kernel<128, 1><<<grid, block, 0, s>>>(vp);
+    else
+      attn_varlen_kernel<64, 1><<<grid, block, 0, s>>>(vp);
+  } else {
+    if (head_dim == 128)
+      attn_varlen_kernel<128, kVarlenRT><<<grid, block, 0, s>>>(vp);
+    else
+      attn_varlen_kernel<64, kVarlenRT><<<grid, block, 0, s>>>(vp);
+  }
   st = check_launch(fn);
   if (st) return st;
   const dim3 cgrid(pl.n_rt, num_kv_heads, batch), cblock(kCombineThreads);
