@@ -361,8 +361,8 @@ def main():
         gen.manual_seed(12)
         qv = torch.randn((int(cu[-1]), Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
         cu_d = torch.from_numpy(cu).cuda()
-        ws_v = torch.empty(gp.paged_attention_varlen_workspace_bytes(B, int(ql.max()), Hq, Hkv, D,
-                                                                     bs, mcl),
+        ws_v = torch.empty(gp.paged_attention_varlen_workspace_bytes(B, int(cu[-1]), int(ql.max()),
+                                                                     Hq, Hkv, D, bs, mcl),
                            dtype=torch.uint8, device="cuda")
         out_v = torch.empty((int(cu[-1]), Hq, D), dtype=torch.float32, device="cuda")
         fv = lambda: gp.paged_attention_varlen(qv, kc, vc, bt, ctx, cu_d, max_q_len=int(ql.max()),

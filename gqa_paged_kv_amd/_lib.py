@@ -46,7 +46,7 @@ SIGNATURES = {
                                                          c_int32, c_int32, c_int32, c_int32,
                                                          c_int32, c_int64, c_int32, c_int32,
                                                          c_int32, c_float, vp, c_size, vp]),
-    "gpkv_paged_attention_varlen_workspace_bytes": (c_size, [c_int32] * 7),
+    "gpkv_paged_attention_varlen_workspace_bytes": (c_size, [c_int32] * 8),
     "gpkv_paged_attention_varlen": (c_int32, [vp, vp, vp, vp, vp, vp, vp, c_int32, c_int32,
                                               c_int32, c_int32, c_int32, c_int32, c_int32,
                                               c_int64, c_int32, c_int32, c_float, vp, c_size,

@@ -871,15 +871,22 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
 
 struct VarlenParams {
   AttnCommon c;
-  float* part_o;             // [B, H_kv, n_rt, S, 16, D] fp32
-  float* part_lse;           // [B, H_kv, n_rt, S, 16] fp32 (base 2)
+  float* part_o;             // [tiles, H_kv, S, 16, D] fp32 (tile = tile_base(b) + rt)
+  float* part_lse;           // [tiles, H_kv, S, 16] fp32 (base 2)
   float* out;                // [total_q, H_q, D] fp32 (combine)
   const int* block_tables;
   const int* ctx;
   const int* cu;             // [B + 1] query row offsets
   long long NB;
-  int max_blocks, max_ctx, num_splits, split_tokens, n_rt, total_q;
+  int max_blocks, max_ctx, num_splits, split_tokens, n_rt, total_q, B;
 };
+
+// Partial rows of sequence b's row tiles sit at tiles tile_base(b) + rt: the
+// (token, head) rows of the whole batch in 16-row steps, plus one per sequence
+// for its partial last tile -- disjoint, and fewer than ceil(total_q * G / 16) + B.
+__device__ __forceinline__ size_t tile_base(int q0, int G, int b) {
+  return ((size_t)q0 * G) / 16 + (size_t)b;
+}
 
 // A sequence's query rows, with bad offsets (outside [0, total_q] or decreasing)
 // read as an empty chunk so that no row outside the query buffer is touched.
@@ -894,104 +901,181 @@ __device__ __forceinline__ void varlen_rows(const VarlenParams& p, int b, int& q
   }
 }
 
+// Prefix over the sequences of per-sequence counts n(b) into s_pref[0..B] (every
+// thread of the workgroup calls it; B <= kMaxBalBatch). Returns the total.
+template <class Count>
+__device__ __forceinline__ int sequence_prefix(int B, int* s_pref, int* s_wave, const Count& count) {
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < B; base += kWaves * 64) {
+    const int bb = base + tid;
+    const int n = bb < B ? count(bb) : 0;
+    int tot;
+    const int ex = wg_exclusive_scan(n, s_wave, &tot);
+    if (bb < B) s_pref[bb + 1] = carry + ex + n;
+    carry += tot;
+  }
+  if (tid == 0) s_pref[0] = 0;
+  __syncthreads();
+  return s_pref[B];
+}
+
+// The last b with s_pref[b] <= u (u < s_pref[B]).
+__device__ __forceinline__ int sequence_of(const int* s_pref, int B, int u) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pref[mid] <= u)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Work units of multi-token queries: (sequence, group of RT row tiles, KV split),
+// split-major within a sequence so that the units running together read the
+// same split. A fixed grid takes them grid-stride: no workgroup is launched for a
+// sequence's missing row tiles.
 template <int D, int RT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 1))) void attn_varlen_kernel(const VarlenParams p) {
   __shared__ int s_pb[kMaxTable];
-  const int tg = blockIdx.x, split = blockIdx.y, b = blockIdx.z;   // tg: group of RT row tiles
+  __shared__ int s_pref[kMaxBalBatch + 1];
+  __shared__ int s_wave[kWaves];
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
-  const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
-  int q0, qn;
-  varlen_rows(p, b, q0, qn);
-  const int rows = qn * G;
-  const int m_first = 16 * RT * tg;
-  if (m_first >= rows) return;
-  // Positions the group's last row sees (the others see fewer).
-  const int m_last = (m_first + 16 * RT < rows ? m_first + 16 * RT : rows) - 1;
-  int tile_lim = ctx - qn + m_last / G + 1;
-  tile_lim = tile_lim < 0 ? 0 : (tile_lim > ctx ? ctx : tile_lim);
   const int T = p.split_tokens;
-  const int t0 = split * T;
-  if (t0 >= tile_lim) return;   // the combine counts only the splits a tile sees
-  const int e0 = t0 / bs;
-  const int n_ent = T / bs;
-  const int nb = (ctx + bs - 1) / bs;
-  for (int e = tid; e < n_ent; e += kWaves * 64) {
-    const int lb = e0 + e;
-    const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
-    s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
-  }
-  __syncthreads();
-  const int span = tile_lim - t0 < T ? tile_lim - t0 : T;
+  auto n_groups = [&](int qn) { return ((qn * G + 15) / 16 + RT - 1) / RT; };
+  const int U = sequence_prefix(p.B, s_pref, s_wave, [&](int b) {
+    const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+    int q0, qn;
+    varlen_rows(p, b, q0, qn);
+    return (qn > 0 && ctx > 0) ? n_groups(qn) * ((ctx + T - 1) / T) : 0;
+  });
   const int r = tid & 15;
-  for (int g = wave; g < Hkv; g += kWaves) {
-    auto desc = [&](int u, int& pb, int& row0, int& nv) {
-      const int tok = t0 + 16 * u;
-      const int x = s_pb[tok / bs - e0];
-      row0 = tok & (bs - 1);
-      int n = t0 + span - tok;
-      n = n < 0 ? 0 : (n > 16 ? 16 : n);
-      if (x < 0) n = 0;
-      nv = uniform(n);
-      pb = uniform(x < 0 ? 0 : x);
-    };
-    RowTiles<RT> tiles;
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int rt = RT * tg + t;
-      const int m0 = 16 * rt;
-      const int n_rows = rows - m0 < 0 ? 0 : (rows - m0 < 16 ? rows - m0 : 16);
-      const int m = m0 + r, j = m / G;
-      tiles.q[t] = r < n_rows
-                       ? p.c.q + ((size_t)(q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
-                       : nullptr;
-      tiles.n_rows[t] = n_rows;
-      tiles.limit[t] = ctx - qn + j + 1;
-      const size_t unit = (((size_t)b * Hkv + g) * p.n_rt + (n_rows > 0 ? rt : 0)) * p.num_splits + split;
-      tiles.o[t] = p.part_o + unit * 16 * D;
-      tiles.lse[t] = p.part_lse + unit * 16;
+  for (int u = blockIdx.x; u < U; u += gridDim.x) {
+    const int b = sequence_of(s_pref, p.B, u);
+    const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+    int q0, qn;
+    varlen_rows(p, b, q0, qn);
+    const int rows = qn * G;
+    const int ntg = n_groups(qn);
+    const int local = u - s_pref[b];
+    const int tg = local % ntg, split = local / ntg;
+    const int m_first = 16 * RT * tg;
+    // Positions the group's last row sees (the others see fewer).
+    const int m_last = (m_first + 16 * RT < rows ? m_first + 16 * RT : rows) - 1;
+    int tile_lim = ctx - qn + m_last / G + 1;
+    tile_lim = tile_lim < 0 ? 0 : (tile_lim > ctx ? ctx : tile_lim);
+    const int t0 = split * T;
+    if (t0 >= tile_lim) continue;   // uniform: the combine counts only the splits a tile sees
+    const int e0 = t0 / bs;
+    const int n_ent = T / bs;
+    const int nb = (ctx + bs - 1) / bs;
+    __syncthreads();                // the previous unit's table is no longer read
+    for (int e = tid; e < n_ent; e += kWaves * 64) {
+      const int lb = e0 + e;
+      const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
+      s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
     }
-    attend_head<D, false, true, RT>(p.c, g, (span + 15) / 16, desc, t0, tiles);
+    __syncthreads();
+    const int span = tile_lim - t0 < T ? tile_lim - t0 : T;
+    for (int g = wave; g < Hkv; g += kWaves) {
+      auto desc = [&](int uu, int& pb, int& row0, int& nv) {
+        const int tok = t0 + 16 * uu;
+        const int x = s_pb[tok / bs - e0];
+        row0 = tok & (bs - 1);
+        int n = t0 + span - tok;
+        n = n < 0 ? 0 : (n > 16 ? 16 : n);
+        if (x < 0) n = 0;
+        nv = uniform(n);
+        pb = uniform(x < 0 ? 0 : x);
+      };
+      RowTiles<RT> tiles;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int rt = RT * tg + t;
+        const int m0 = 16 * rt;
+        const int n_rows = rows - m0 < 0 ? 0 : (rows - m0 < 16 ? rows - m0 : 16);
+        const int m = m0 + r, j = m / G;
+        tiles.q[t] = r < n_rows
+                         ? p.c.q + ((size_t)(q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
+                         : nullptr;
+        tiles.n_rows[t] = n_rows;
+        tiles.limit[t] = ctx - qn + j + 1;
+        const size_t unit =
+            ((tile_base(q0, G, b) + (n_rows > 0 ? rt : 0)) * Hkv + g) * p.num_splits + split;
+        tiles.o[t] = p.part_o + unit * 16 * D;
+        tiles.lse[t] = p.part_lse + unit * 16;
+      }
+      attend_head<D, false, true, RT>(p.c, g, (span + 15) / 16, desc, t0, tiles);
+    }
   }
 }
 
-// Merge of one (row tile, KV head, sequence) over its splits, written to the
-// flattened output rows.
+// Merge of each (sequence, row tile, KV head) over its splits, written to the
+// flattened output rows; the triples taken grid-stride.
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void attn_varlen_combine_kernel(const VarlenParams p) {
+  __shared__ int s_pref[kMaxBalBatch + 1];
+  __shared__ int s_wave[kWaves];
   constexpr int TPR = D / 4;   // threads per row, 4 channels each
-  const int rt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = p.c.G, Hq = p.c.Hq;
-  const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
-  int q0, qn;
-  varlen_rows(p, b, q0, qn);
-  const int rows = qn * G;
-  const int m0 = 16 * rt;
-  if (m0 >= rows) return;
-  const int n_rows = rows - m0 < 16 ? rows - m0 : 16;
-  int tile_lim = ctx - qn + (m0 + n_rows - 1) / G + 1;
-  tile_lim = tile_lim < 0 ? 0 : (tile_lim > ctx ? ctx : tile_lim);
-  const int n_units = (tile_lim + p.split_tokens - 1) / p.split_tokens;
-  const size_t unit0 = (((size_t)b * p.c.Hkv + g) * p.n_rt + rt) * p.num_splits;
-  for (int i = threadIdx.x; i < n_rows * TPR; i += kCombineThreads) {
-    const int r = i / TPR, c4 = i - (i / TPR) * TPR;
-    const float* lse0 = p.part_lse + unit0 * 16 + r;
-    const float* o0 = p.part_o + (unit0 * 16 + r) * D + 4 * c4;
-    float M = -INFINITY;
-    for (int u = 0; u < n_units; ++u) M = fmaxf(M, lse0[(size_t)u * 16]);
-    const float Mr = (M == -INFINITY) ? 0.f : M;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float W = 0.f;
-    for (int u = 0; u < n_units; ++u) {
-      const float w = __builtin_amdgcn_exp2f(lse0[(size_t)u * 16] - Mr);
-      W += w;
-      acc += w * *(const f32x4*)(o0 + (size_t)u * 16 * D);
+  const int G = p.c.G, Hq = p.c.Hq, Hkv = p.c.Hkv;
+  const int U = sequence_prefix(p.B, s_pref, s_wave, [&](int b) {
+    int q0, qn;
+    varlen_rows(p, b, q0, qn);
+    return (qn * G + 15) / 16 * Hkv;
+  });
+  for (int u = blockIdx.x; u < U; u += gridDim.x) {
+    const int b = sequence_of(s_pref, p.B, u);
+    const int local = u - s_pref[b];
+    const int rt = local / Hkv, g = local - (local / Hkv) * Hkv;
+    const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+    int q0, qn;
+    varlen_rows(p, b, q0, qn);
+    const int rows = qn * G;
+    const int m0 = 16 * rt;
+    const int n_rows = rows - m0 < 16 ? rows - m0 : 16;
+    int tile_lim = ctx - qn + (m0 + n_rows - 1) / G + 1;
+    tile_lim = tile_lim < 0 ? 0 : (tile_lim > ctx ? ctx : tile_lim);
+    const int n_units = (tile_lim + p.split_tokens - 1) / p.split_tokens;
+    const size_t unit0 = ((tile_base(q0, G, b) + rt) * Hkv + g) * p.num_splits;
+    for (int i = threadIdx.x; i < n_rows * TPR; i += kCombineThreads) {
+      const int rr = i / TPR, c4 = i - (i / TPR) * TPR;
+      const float* lse0 = p.part_lse + unit0 * 16 + rr;
+      const float* o0 = p.part_o + (unit0 * 16 + rr) * D + 4 * c4;
+      float M = -INFINITY;
+      for (int k = 0; k < n_units; ++k) M = fmaxf(M, lse0[(size_t)k * 16]);
+      const float Mr = (M == -INFINITY) ? 0.f : M;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      float W = 0.f;
+      int k = 0;
+      for (; k + 3 < n_units; k += 4) {   // four splits' rows in flight
+        float l[4];
+        f32x4 v[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          l[x] = lse0[(size_t)(k + x) * 16];
+          v[x] = *(const f32x4*)(o0 + (size_t)(k + x) * 16 * D);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float w = __builtin_amdgcn_exp2f(l[x] - Mr);
+          W += w;
+          acc += w * v[x];
+        }
+      }
+      for (; k < n_units; ++k) {
+        const float w = __builtin_amdgcn_exp2f(lse0[(size_t)k * 16] - Mr);
+        W += w;
+        acc += w * *(const f32x4*)(o0 + (size_t)k * 16 * D);
+      }
+      const float inv = W > 0.f ? 1.f / W : 0.f;
+      const int m = m0 + rr, j = m / G;
+      *(f32x4*)(p.out + ((size_t)(q0 + j) * Hq + (size_t)g * G + (m - j * G)) * D + 4 * c4) =
+          acc * inv;
     }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    const int m = m0 + r, j = m / G;
-    *(f32x4*)(p.out + ((size_t)(q0 + j) * Hq + (size_t)g * G + (m - j * G)) * D + 4 * c4) =
-        acc * inv;
   }
 }
 
@@ -1240,24 +1324,28 @@ struct VarlenPlan {
   size_t o_bytes, lse_bytes;
 };
 
-static VarlenPlan make_varlen_plan(int B, int max_q_len, int Hq, int Hkv, int D, int bs,
-                                   int max_ctx) {
+// Row tiles of the longest chunk (the grid), split size, and the workspace for at
+// most ceil(total_q * G / 16) + B row tiles. Decode-sized chunks split the KV like
+// decode; longer chunks keep splits short (512 positions) so that no workgroup
+// walks a long KV range alone.
+static VarlenPlan make_varlen_plan(int B, int total_q, int max_q_len, int Hq, int Hkv, int D,
+                                   int bs, int max_ctx) {
   VarlenPlan pl;
   const long long G = Hq / Hkv;
   const long long n_rt = (max_q_len * G + 15) / 16;
   pl.n_rt = (int)(n_rt > 0 ? n_rt : 1);
-  const long long rows_b = (long long)B * pl.n_rt;
-  int T = split_tokens_for(rows_b > (1 << 30) ? (1 << 30) : (int)rows_b, Hkv, max_ctx);
+  const long long tiles = ((long long)total_q * G + 15) / 16 + B;
+  int T = pl.n_rt > 1 ? 512 : split_tokens_for(B, Hkv, max_ctx);
   auto units = [&](int t) {
     const long long ns = ((long long)max_ctx + t - 1) / t;
-    return (long long)B * Hkv * pl.n_rt * (ns > 0 ? ns : 1);
+    return tiles * Hkv * (ns > 0 ? ns : 1);
   };
   while (units(T) > kVarlenMaxUnits && T < 16384) T <<= 1;
   while (T / bs > kMaxTable) T >>= 1;
   pl.split_tokens = T;
   pl.num_splits = (int)(((long long)max_ctx + T - 1) / T);
   if (pl.num_splits < 1) pl.num_splits = 1;
-  const size_t u = (size_t)B * Hkv * pl.n_rt * pl.num_splits;
+  const size_t u = (size_t)tiles * Hkv * pl.num_splits;
   pl.o_bytes = align256(u * 16 * D * sizeof(float));
   pl.lse_bytes = align256(u * 16 * sizeof(float));
   return pl;
@@ -1267,18 +1355,19 @@ static VarlenPlan make_varlen_plan(int B, int max_q_len, int Hq, int Hkv, int D,
 
 using namespace gpkv;
 
-extern "C" size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int32_t max_q_len,
+extern "C" size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int32_t total_q,
+                                                              int32_t max_q_len,
                                                               int32_t num_q_heads,
                                                               int32_t num_kv_heads,
                                                               int32_t head_dim,
                                                               int32_t block_size,
                                                               int32_t max_context_len) {
-  if (batch < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads || !supported_head_dim(head_dim) ||
       !supported_block_size(block_size) || max_context_len < 0)
     return 0;
-  const VarlenPlan pl = make_varlen_plan(batch, max_q_len, num_q_heads, num_kv_heads, head_dim,
-                                         block_size, max_context_len);
+  const VarlenPlan pl = make_varlen_plan(batch, total_q, max_q_len, num_q_heads, num_kv_heads,
+                                         head_dim, block_size, max_context_len);
   return pl.o_bytes + pl.lse_bytes;
 }
 
@@ -1297,11 +1386,13 @@ extern "C" int gpkv_paged_attention_varlen(
     return fail(GPKV_ERR_SHAPE, "%s: total_q=%d max_q_len=%d", fn, total_q, max_q_len);
   if (batch == 0 || total_q == 0) return GPKV_OK;
   if (max_q_len == 0) return fail(GPKV_ERR_SHAPE, "%s: max_q_len=0 with total_q=%d", fn, total_q);
+  if (batch > kMaxBalBatch)
+    return fail(GPKV_ERR_UNSUPPORTED, "%s: batch=%d > %d", fn, batch, kMaxBalBatch);
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
       !cu_seqlens_q)
     return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
-  const VarlenPlan pl = make_varlen_plan(batch, max_q_len, num_q_heads, num_kv_heads, head_dim,
-                                         block_size, max_context_len);
+  const VarlenPlan pl = make_varlen_plan(batch, total_q, max_q_len, num_q_heads, num_kv_heads,
+                                         head_dim, block_size, max_context_len);
   if (pl.num_splits > 65535)
     return fail(GPKV_ERR_SHAPE, "%s: max_context_len=%d needs too many splits", fn,
                 max_context_len);
@@ -1336,11 +1427,15 @@ extern "C" int gpkv_paged_attention_varlen(
   vp.split_tokens = pl.split_tokens;
   vp.n_rt = pl.n_rt;
   vp.total_q = total_q;
+  vp.B = batch;
   // One row tile per wave for decode-sized chunks; otherwise kVarlenRT tiles share
-  // every K / V tile a wave loads.
+  // every K / V tile a wave loads. Both kernels take their work units grid-stride
+  // from a fixed grid of at most four workgroups per CU.
   const int rt_per_wave = pl.n_rt > 1 ? kVarlenRT : 1;
-  const dim3 grid((pl.n_rt + rt_per_wave - 1) / rt_per_wave, pl.num_splits, batch);
-  const dim3 block(kWaves * 64);
+  const long long tiles = ((long long)total_q * vp.c.G + 15) / 16 + batch;
+  const long long units_max = (tiles / rt_per_wave + batch) * pl.num_splits;
+  const long long cap = 4LL * balanced_capacity();
+  const dim3 grid((unsigned)(units_max < cap ? units_max : cap)), block(kWaves * 64);
   if (rt_per_wave == 1) {
     if (head_dim == 128)
       attn_varlen_kernel<128, 1><<<grid, block, 0, s>>>(vp);
@@ -1354,7 +1449,8 @@ extern "C" int gpkv_paged_attention_varlen(
   }
   st = check_launch(fn);
   if (st) return st;
-  const dim3 cgrid(pl.n_rt, num_kv_heads, batch), cblock(kCombineThreads);
+  const long long ctiles = tiles * num_kv_heads;
+  const dim3 cgrid((unsigned)(ctiles < cap ? ctiles : cap)), cblock(kCombineThreads);
   if (head_dim == 128)
     attn_varlen_combine_kernel<128><<<cgrid, cblock, 0, s>>>(vp);
   else

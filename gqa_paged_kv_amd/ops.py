@@ -318,10 +318,11 @@ def sparse_paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_
 # Multi-token queries (varlen, causal mask aligned to the right)
 # ---------------------------------------------------------------------------
 
-def paged_attention_varlen_workspace_bytes(batch, max_q_len, num_q_heads, num_kv_heads, head_dim,
-                                           block_size, max_context_len) -> int:
+def paged_attention_varlen_workspace_bytes(batch, total_q, max_q_len, num_q_heads, num_kv_heads,
+                                           head_dim, block_size, max_context_len) -> int:
     return int(lib().gpkv_paged_attention_varlen_workspace_bytes(
-        batch, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len))
+        batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+        max_context_len))
 
 
 def paged_attention_varlen(query, key_cache, value_cache, block_tables, context_lens, cu_seqlens_q,
@@ -345,7 +346,8 @@ def paged_attention_varlen(query, key_cache, value_cache, block_tables, context_
     if out is None:
         out = torch.empty((UQ, Hq, D), dtype=torch.float32, device=query.device)
     _dev("out", out, torch.float32, 3)
-    need = paged_attention_varlen_workspace_bytes(B, max_q_len, Hq, Hkv, D, bs, max_context_len)
+    need = paged_attention_varlen_workspace_bytes(B, UQ, max_q_len, Hq, Hkv, D, bs,
+                                                  max_context_len)
     ws = _workspace(need, query.device, workspace)
     _check(lib().gpkv_paged_attention_varlen(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),

@@ -274,10 +274,10 @@ int gpkv_sparse_paged_attention_decode_fp8(float* out, const void* query, const 
  * workspace: at least gpkv_paged_attention_varlen_workspace_bytes(...) bytes;
  *   contents on entry ignored.
  * --------------------------------------------------------------------------- */
-size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int32_t max_q_len,
-                                                   int32_t num_q_heads, int32_t num_kv_heads,
-                                                   int32_t head_dim, int32_t block_size,
-                                                   int32_t max_context_len);
+size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int32_t total_q,
+                                                   int32_t max_q_len, int32_t num_q_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim,
+                                                   int32_t block_size, int32_t max_context_len);
 
 int gpkv_paged_attention_varlen(float* out, const void* query, const void* key_cache,
                                 const void* value_cache, const int32_t* block_tables,

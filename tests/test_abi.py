@@ -111,7 +111,7 @@ def test_other_entry_points_checks(L):
                                          0.1, 8, 1 << 30, None) == -2
     assert L.gpkv_paged_attention_varlen(8, 8, 8, 8, 8, 8, 8, 2, 5, 4, 4, 1, 64, 16, 16, 5, 80,
                                          0.1, 8, 16, None) == -4
-    assert L.gpkv_paged_attention_varlen_workspace_bytes(2, 4, 4, 1, 64, 16, 80) > 0
+    assert L.gpkv_paged_attention_varlen_workspace_bytes(2, 5, 4, 4, 1, 64, 16, 80) > 0
 
 
 def test_workspace_queries(L):
