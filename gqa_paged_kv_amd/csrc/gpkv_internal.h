@@ -26,6 +26,8 @@ constexpr int kMaxGroup = 16;
 // Tokens per split-KV work unit (a multiple of 128); identical for the workspace
 // query and the launch.
 int split_tokens_for(int batch, int num_kv_heads, int span_tokens);
+// The GPKV_SPLIT_TOKENS override (0 when unset or invalid).
+int env_split_tokens();
 
 // ---------------------------------------------------------------------------
 // Device side

@@ -936,9 +936,10 @@ __device__ __forceinline__ int sequence_of(const int* s_pref, int B, int u) {
 // Work units of multi-token queries: (sequence, group of RT row tiles, KV split),
 // split-major within a sequence so that the units running together read the
 // same split. A fixed grid takes them grid-stride: no workgroup is launched for a
-// sequence's missing row tiles.
+// sequence's missing row tiles. Two waves per SIMD (at most 256 registers) let one
+// wave's MFMA work hide the other's loads; RT = 2 fits without spilling at D = 128.
 template <int D, int RT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 1))) void attn_varlen_kernel(const VarlenParams p) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 2))) void attn_varlen_kernel(const VarlenParams p) {
   __shared__ int s_pb[kMaxTable];
   __shared__ int s_pref[kMaxBalBatch + 1];
   __shared__ int s_wave[kWaves];
@@ -1335,7 +1336,11 @@ static VarlenPlan make_varlen_plan(int B, int total_q, int max_q_len, int Hq, in
   const long long n_rt = (max_q_len * G + 15) / 16;
   pl.n_rt = (int)(n_rt > 0 ? n_rt : 1);
   const long long tiles = ((long long)total_q * G + 15) / 16 + B;
-  int T = pl.n_rt > 1 ? 512 : split_tokens_for(B, Hkv, max_ctx);
+  // Multi-token chunks: long splits keep each group of row tiles on its tile loop and
+  // cut the partial rows the combine reads (2048 measured best for mixed batches of
+  // 8K-token contexts); one-token rows use the decode heuristic.
+  const int forced = env_split_tokens();
+  int T = forced ? forced : (pl.n_rt > 1 ? 2048 : split_tokens_for(B, Hkv, max_ctx));
   auto units = [&](int t) {
     const long long ns = ((long long)max_ctx + t - 1) / t;
     return tiles * Hkv * (ns > 0 ? ns : 1);

@@ -40,7 +40,7 @@ int check_launch(const char* what) {
 // (max_context_len, or topk_blocks * block_size for the sparse path).
 // GPKV_SPLIT_TOKENS (a multiple of 128 in [128, 2048]) overrides the choice; it is
 // read on every call so the workspace query and the launch always agree.
-static int env_split_tokens() {
+int env_split_tokens() {
   const char* s = getenv("GPKV_SPLIT_TOKENS");
   if (!s) return 0;
   const int x = atoi(s);
