@@ -67,6 +67,7 @@ constexpr int kMaxTable = 2048;         // split path: block-table entries stage
 constexpr int kMaxBalBatch = 4096;      // balanced path: largest batch (prefix in LDS)
 constexpr int kMaxSubPerWG = 2048;      // balanced path: most sub-tiles per workgroup (dense)
 constexpr int kBalTab = 4096;           // balanced path: table entries staged in LDS
+constexpr int kDirTab = 2048;           // direct sparse path: longest Top-K list
 
 struct AttnCommon {
   const unsigned short* q;   // [B, H_q, D] bf16
@@ -661,6 +662,114 @@ __global__ __launch_bounds__(kWaves * 64) void attn_balanced_kernel(const BalPar
 }
 
 // ---------------------------------------------------------------------------
+// Direct sparse path: one workgroup per (sequence, KV head)
+// ---------------------------------------------------------------------------
+
+// Quest selects the same number of blocks, min(K, blocks), for every KV head of a
+// sequence, so when the batch's (sequence, KV head) pairs fill the GPU one
+// workgroup per pair is balanced without a global schedule. Its waves split the
+// pair's selected sub-tiles, and their partial rows meet in LDS: the output is
+// written here, with no partial rows in memory and no combine launch.
+struct DirectParams {
+  AttnCommon c;
+  float* out;                // [B, H_q, D] fp32
+  const int* block_tables;
+  const int* ctx;
+  const int* topk;           // [B, H_kv, K] logical block ids
+  long long NB;
+  int B, max_blocks, max_ctx, topk_blocks;
+};
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kWaves * 64) void attn_sparse_direct_kernel(const DirectParams p) {
+  __shared__ int s_pb[kDirTab];    // compacted list: physical block (-1: none)
+  __shared__ int s_tok0[kDirTab];  // logical position of the block's row 0
+  __shared__ float s_o[kWaves * kMaxGroup * D];
+  __shared__ float s_lse[kWaves * kMaxGroup];
+  __shared__ int s_wave[kWaves];
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int Hkv = p.c.Hkv, G = p.c.G, bs = p.c.bs, K = p.topk_blocks;
+  const int b = blockIdx.x / Hkv, g = blockIdx.x - b * Hkv;
+  const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+  const int nb = (ctx + bs - 1) / bs;
+  const int spb = bs >> 4;
+
+  // Compaction of the head's list: each thread takes a contiguous run of entries,
+  // and a valid entry's position is the number of valid entries before it.
+  const int* lst = p.topk + ((size_t)b * Hkv + g) * K;
+  const int per = (K + kWaves * 64 - 1) / (kWaves * 64);
+  const int e_begin = tid * per;
+  int n_mine = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e_begin + i;
+    const int id = e < K ? lst[e] : -1;
+    n_mine += (id >= 0 && id < nb) ? 1 : 0;
+  }
+  int n_valid;
+  int pos = wg_exclusive_scan(n_mine, s_wave, &n_valid);
+  for (int i = 0; i < per && n_mine > 0; ++i) {
+    const int e = e_begin + i;
+    const int id = e < K ? lst[e] : -1;
+    if (id >= 0 && id < nb) {
+      const int pb = p.block_tables[(size_t)b * p.max_blocks + id];
+      s_pb[pos] = (pb >= 0 && pb < p.NB) ? pb : -1;
+      s_tok0[pos] = id * bs;
+      ++pos;
+    }
+  }
+  __syncthreads();
+
+  // Wave w takes a contiguous quarter of the 32-token tiles.
+  const int n_sub = n_valid * spb;
+  const int n_tiles = (n_sub + 1) >> 1;
+  const int ta = wave * n_tiles / kWaves, tb = (wave + 1) * n_tiles / kWaves;
+  const int ub = 2 * ta;
+  const int ue = 2 * tb < n_sub ? 2 * tb : n_sub;
+  auto desc = [&](int u, int& pb, int& row0, int& nv) {
+    const int v = ub + u;
+    const int blk = v / spb;
+    row0 = (v - blk * spb) * 16;
+    const int x = s_pb[blk];
+    int n = ctx - (s_tok0[blk] + row0);
+    n = n < 0 ? 0 : (n > 16 ? 16 : n);
+    if (x < 0) n = 0;
+    nv = uniform(n);
+    pb = uniform(x < 0 ? 0 : x);
+  };
+  const int rr = tid & 15;
+  RowTiles<1> rows;
+  rows.q[0] = rr < G ? p.c.q + ((size_t)b * p.c.Hq + (size_t)g * G + rr) * D : nullptr;
+  rows.n_rows[0] = G;
+  rows.limit[0] = 0;
+  rows.o[0] = s_o + wave * kMaxGroup * D;
+  rows.lse[0] = s_lse + wave * kMaxGroup;
+  attend_head<D, FP8, false, 1>(p.c, g, ue > ub ? ue - ub : 0, desc, 0, rows);
+  __syncthreads();
+
+  // out = sum_w 2^(lse_w - M) O_w / sum_w 2^(lse_w - M); no valid token: zeros.
+  float* dst = p.out + ((size_t)b * p.c.Hq + (size_t)g * G) * D;
+  for (int i = tid; i < G * (D / 4); i += kWaves * 64) {
+    const int h = i / (D / 4), d = 4 * (i - h * (D / 4));
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, s_lse[w * kMaxGroup + h]);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = __builtin_amdgcn_exp2f(s_lse[w * kMaxGroup + h] - m);
+        acc += wt * *(const f32x4*)(s_o + (w * kMaxGroup + h) * D + d);
+        den += wt;
+      }
+      acc *= 1.f / den;
+    }
+    *(f32x4*)(dst + (size_t)h * D + d) = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Combine: out = sum_u w_u O_u / sum_u w_u, w_u = 2^(lse_u - max lse)
 // ---------------------------------------------------------------------------
 
@@ -1116,21 +1225,31 @@ static int balanced_capacity() {
 }
 
 struct Plan {
-  bool balanced;
+  bool balanced, direct;
   int split_tokens, num_splits, nwg;
   size_t o_bytes, lse_bytes, prefix_bytes;
 };
 
-// GPKV_ATTN_SCHEDULE=balanced|split forces the schedule (tuning and test switch,
-// read per call); by default the balanced schedule serves every batch its
-// prefix and tables fit.
+// GPKV_ATTN_SCHEDULE=balanced|split|direct forces the schedule (tuning and test
+// switch, read per call; direct applies to sparse calls only); by default the
+// balanced schedule serves every batch its prefix and tables fit. The workspace
+// size does not depend on the choice.
 static Plan make_plan(bool sparse, int B, int Hq, int Hkv, int D, int bs, int span) {
   Plan pl;
   const int G = Hq / Hkv;
   const int spb = bs / 16;
   pl.balanced = B <= kMaxBalBatch && (!sparse || kBalTab / Hkv >= 3);
+  // Sparse: the direct path when the (sequence, KV head) pairs fill the GPU and are
+  // all resident at once (two workgroups per CU). With more pairs each later round
+  // of workgroups pays the list -> table -> first tile latency again: 2048 pairs of
+  // ragged sequences ran 18% slower than the balanced schedule and its combine.
+  const bool direct_fits = sparse && span / bs <= kDirTab && (long long)B * Hkv <= (1LL << 22);
+  const long long pairs = (long long)B * Hkv;
+  pl.direct = direct_fits && pairs >= balanced_capacity() && pairs <= 2LL * balanced_capacity();
   const char* forced = getenv("GPKV_ATTN_SCHEDULE");
-  if (forced && strcmp(forced, "split") == 0) pl.balanced = false;
+  if (forced && strcmp(forced, "split") == 0) pl.balanced = pl.direct = false;
+  if (forced && strcmp(forced, "balanced") == 0) pl.direct = false;
+  if (forced && strcmp(forced, "direct") == 0) pl.direct = direct_fits;
   pl.split_tokens = split_tokens_for(B, Hkv, span);
   const int per_token_entries = sparse ? Hkv : 1;
   while (pl.split_tokens > 128 && (pl.split_tokens / bs) * per_token_entries > kMaxTable)
@@ -1237,6 +1356,33 @@ static int attn_run(bool sparse, bool fp8, float* out, const void* query, const 
   float* part_o = (float*)ws;
   float* part_lse = (float*)((char*)ws + pl.o_bytes);
   int* prefix = (int*)((char*)ws + pl.o_bytes + pl.lse_bytes);
+
+  if (pl.direct) {
+    DirectParams dp;
+    dp.c = c;
+    dp.out = out;
+    dp.block_tables = bt;
+    dp.ctx = ctx;
+    dp.topk = topk;
+    dp.NB = NB;
+    dp.B = B;
+    dp.max_blocks = max_blocks;
+    dp.max_ctx = max_ctx;
+    dp.topk_blocks = K;
+    const dim3 grid((unsigned)((long long)B * Hkv)), block(kWaves * 64);
+    if (D == 128) {
+      if (fp8)
+        attn_sparse_direct_kernel<128, true><<<grid, block, 0, stream>>>(dp);
+      else
+        attn_sparse_direct_kernel<128, false><<<grid, block, 0, stream>>>(dp);
+    } else {
+      if (fp8)
+        attn_sparse_direct_kernel<64, true><<<grid, block, 0, stream>>>(dp);
+      else
+        attn_sparse_direct_kernel<64, false><<<grid, block, 0, stream>>>(dp);
+    }
+    return check_launch(fn);
+  }
 
   BalParams bp;
   bp.c = c;

@@ -193,7 +193,11 @@ size_t gpkv_sparse_attention_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * masked). Entries equal to -1 (or outside [0, nb_b)) are ignored; listing a
  * block twice is a precondition violation. Output as in
  * gpkv_paged_attention_decode (zero row when no token is selected).
- * topk_indices: [batch, num_kv_heads, topk_blocks] int32 logical block ids. */
+ * topk_indices: [batch, num_kv_heads, topk_blocks] int32 logical block ids.
+ * When the batch's (sequence, KV head) pairs fill the GPU, each pair is one
+ * workgroup that writes its rows directly (one launch, workspace untouched);
+ * otherwise the split phase writes partial rows to the workspace and a second
+ * launch combines them. The workspace size is the same either way. */
 int gpkv_sparse_paged_attention_decode(float* out, const void* query, const void* key_cache,
                                        const void* value_cache, const int32_t* block_tables,
                                        const int32_t* context_lens,

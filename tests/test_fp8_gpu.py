@@ -198,7 +198,7 @@ def test_fp8_dense_random(seed, Hq, Hkv, D, bs, ctx, schedule, monkeypatch):
             assert (out[b] == 0).all()
 
 
-@pytest.mark.parametrize("schedule", ["balanced", "split"])
+@pytest.mark.parametrize("schedule", ["balanced", "split", "direct"])
 @pytest.mark.parametrize("config,K", [(1, 3), (3, 64), (5, 32)])
 def test_fp8_sparse_config(config, K, schedule, monkeypatch):
     monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)

@@ -103,6 +103,9 @@ DENSE_CASES = [
 
 
 SCHEDULES = ["balanced", "split"]
+# Sparse calls also have the direct path (one workgroup per sequence and KV head),
+# the default when those pairs fill the GPU; forcing it covers small batches too.
+SPARSE_SCHEDULES = SCHEDULES + ["direct"]
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
@@ -418,7 +421,7 @@ def _sparse(d, w, sel):
                                             scale=float(w.scale))
 
 
-@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("schedule", SPARSE_SCHEDULES)
 @pytest.mark.parametrize("config,K", [(1, 3), (1, 5), (3, 64), (4, 256), (5, 32)])
 def test_sparse_config_fixed_selection(config, K, schedule, monkeypatch):
     """Sparse kernel judged with the selection fixed to the oracle's Top-K."""
@@ -437,7 +440,7 @@ def test_sparse_config_fixed_selection(config, K, schedule, monkeypatch):
     assert err <= ATOL
 
 
-@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("schedule", SPARSE_SCHEDULES)
 def test_sparse_all_blocks_equals_dense_and_handles_holes(schedule, monkeypatch):
     monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
     w = workloads.random_case(330, batch=3, num_q_heads=28, num_kv_heads=4, head_dim=128,
