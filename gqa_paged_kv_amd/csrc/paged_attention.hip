@@ -414,6 +414,202 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
   }
 }
 
+// Causal rows of one KV head shared by the whole workgroup: each wave carries two
+// row tiles, and every 32-token K / V tile is loaded once per workgroup into LDS
+// (double-buffered, loads for the next tile in flight while this one is used)
+// instead of once per wave. Same arithmetic as attend_head; every wave of the
+// workgroup must call it with the same n_sub, desc and pos0 (it has barriers).
+constexpr int kShareRowBytes(int D) { return 2 * D + 16; }   // padded LDS row
+constexpr int kShareLdsBytes(int D) { return 2 * 2 * 32 * kShareRowBytes(D); }
+
+template <int D, class Desc>
+__device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_sub,
+                                              const Desc& desc, int pos0, const RowTiles<2>& rows,
+                                              unsigned char* s_kv) {
+  constexpr int RT = 2;
+  constexpr int KSTEPS = D / 32;
+  constexpr int CPL = D / 16;
+  constexpr int ROWB = kShareRowBytes(D);
+  constexpr int TILEB = 32 * ROWB;           // one 32-token K or V tile in LDS
+  constexpr int PIECES = 2 * D / 16;         // 16-byte pieces per token row
+  constexpr int PER_T = 32 * PIECES / (kWaves * 64);   // pieces per thread per tile
+  static_assert(PER_T >= 1 && 32 * PIECES == PER_T * kWaves * 64, "tile split");
+  typedef typename VecT<D>::type vvec;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int r = lane & 15, qd = lane >> 4;
+  const bool active = rows.n_rows[0] > 0;   // the wave's second tile is empty if its first is
+
+  u32x4 qf[RT][KSTEPS];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      qf[t][s] = rows.q[t] != nullptr ? *(const u32x4*)(rows.q[t] + 32 * s + 8 * qd)
+                                      : u32x4{0u, 0u, 0u, 0u};
+  }
+  f32x4 oacc[RT][CPL];
+  float m_run[RT], l_run[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) oacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+  }
+
+  // Staging: piece i of a tile is token (tid + 256 i) / PIECES; a wave's pieces of
+  // one i lie in one 16-token sub-tile, so the descriptor is wave-uniform.
+  const int n_tiles = (n_sub + 1) >> 1;
+  u32x4 gk[PER_T], gv[PER_T];
+  auto gload = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int pc = tid + i * kWaves * 64;
+      const int tok = pc / PIECES, piece = pc - tok * PIECES;
+      const int u = 2 * k + (tok >> 4);
+      int pb = 0, row0 = 0, nv = 0;
+      if (u < n_sub) desc(u, pb, row0, nv);
+      const size_t base = (size_t)pb * (size_t)c.block_bytes + (size_t)row0 * c.row_bytes;
+      const unsigned off = (unsigned)((tok & 15) * c.row_bytes + g * D * 2 + piece * 16);
+      gk[i] = buf_load16<0>(make_rsrc(c.kc + base, (unsigned)(nv * c.row_bytes)), off);
+      gv[i] = buf_load16<0>(make_rsrc(c.vc + base, (unsigned)(nv * c.row_bytes)), off);
+    }
+  };
+  auto lstore = [&](int buf) {
+    unsigned char* kb = s_kv + buf * 2 * TILEB;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int pc = tid + i * kWaves * 64;
+      const int tok = pc / PIECES, piece = pc - tok * PIECES;
+      *(u32x4*)(kb + tok * ROWB + piece * 16) = gk[i];
+      *(u32x4*)(kb + TILEB + tok * ROWB + piece * 16) = gv[i];
+    }
+  };
+
+  if (n_tiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int k = 0; k < n_tiles; ++k) {
+    const bool more = k + 1 < n_tiles;
+    if (more) gload(k + 1);
+    if (active) {
+      const unsigned char* kb = s_kv + (k & 1) * 2 * TILEB;
+      const unsigned char* vb = kb + TILEB;
+      int nv[2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        int pb, row0;
+        nv[sub] = 0;
+        if (2 * k + sub < n_sub) desc(2 * k + sub, pb, row0, nv[sub]);
+      }
+      f32x4 sacc[RT][2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        u32x4 kf[KSTEPS];
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+          kf[s] = *(const u32x4*)(kb + (16 * sub + r) * ROWB + (32 * s + 8 * qd) * 2);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          sacc[t][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s) sacc[t][sub] = mfma16x16x32(kf[s], qf[t][s], sacc[t][sub]);
+        }
+      }
+      u32x4 phi[RT], plo[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        float sv[8];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = sacc[t][sub][i] * c.qk_scale_log2;
+            const bool ok = 4 * qd + i < nv[sub] &&
+                            pos0 + 16 * (2 * k + sub) + 4 * qd + i < rows.limit[t];
+            sv[sub * 4 + i] = ok ? x : -INFINITY;
+          }
+        float mx = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[t], mx);
+        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_ref);
+        float pv[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+          psum += pv[i];
+        }
+        l_run[t] = l_run[t] * alpha + psum;
+        m_run[t] = m_new;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) oacc[t][j] *= alpha;
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const unsigned a = __float_as_uint(pv[2 * d]), cc = __float_as_uint(pv[2 * d + 1]);
+          phi[t][d] = pack_hi16(a, cc);
+          const float ra = pv[2 * d] - __uint_as_float(a & 0xffff0000u);
+          const float rc = pv[2 * d + 1] - __uint_as_float(cc & 0xffff0000u);
+          plo[t][d] = pack_hi16(__float_as_uint(ra), __float_as_uint(rc));
+        }
+      }
+      // V rows 4 qd + i of each sub-tile, channels CPL r .. (as the global-load layout).
+      vvec vf[2][4];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vf[sub][i] = *(const vvec*)(vb + (16 * sub + 4 * qd + i) * ROWB + r * CPL * 2);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        u32x4 va;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int sub = d >> 1, i0 = (d & 1) * 2;
+          const unsigned w0 = vf[sub][i0][j >> 1], w1 = vf[sub][i0 + 1][j >> 1];
+          va[d] = (j & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
+        }
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          oacc[t][j] = mfma16x16x32(va, phi[t], oacc[t][j]);
+          oacc[t][j] = mfma16x16x32(va, plo[t], oacc[t][j]);
+        }
+      }
+    }
+    if (more) lstore((k + 1) & 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    float l_tot = l_run[t] + __shfl_xor(l_run[t], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (r < rows.n_rows[t]) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* dst = rows.o[t] + (size_t)r * D + CPL * 4 * qd;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j0 = 0; j0 < CPL; j0 += 4) {
+          f32x4 v;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) v[jj] = oacc[t][j0 + jj][i] * inv;
+          *(f32x4*)(dst + CPL * i + j0) = v;
+        }
+      }
+      if (qd == 0) rows.lse[t][r] = l_tot > 0.f ? m_run[t] + log2f(l_tot) : -INFINITY;
+    }
+  }
+}
+
 __device__ __forceinline__ int clamp_ctx(int v, int max_ctx) {
   return v < 0 ? 0 : (v > max_ctx ? max_ctx : v);
 }
@@ -1044,24 +1240,37 @@ __device__ __forceinline__ int sequence_of(const int* s_pref, int B, int u) {
 
 // Work units of multi-token queries: (sequence, group of RT row tiles, KV split),
 // split-major within a sequence so that the units running together read the
-// same split. A fixed grid takes them grid-stride: no workgroup is launched for a
-// sequence's missing row tiles. Two waves per SIMD (at most 256 registers) let one
-// wave's MFMA work hide the other's loads; RT = 2 fits without spilling at D = 128.
+// same split; a unit's waves take the KV heads. Sequences with kShareMinTiles row
+// tiles or more (chunks, RT > 1) instead take units of (sequence, KV head, group
+// of kShareTiles row tiles, split): the four waves share that head's K / V through
+// LDS (attend_shared). A fixed grid takes the units grid-stride: no workgroup is
+// launched for a sequence's missing row tiles. Two waves per SIMD (at most 256
+// registers) let one wave's MFMA work hide the other's loads; RT = 2 fits without
+// spilling at D = 128.
+constexpr int kShareTiles = 2 * kWaves;   // row tiles of one shared unit
+constexpr int kShareMinTiles = 4;
+
 template <int D, int RT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 2))) void attn_varlen_kernel(const VarlenParams p) {
   __shared__ int s_pb[kMaxTable];
   __shared__ int s_pref[kMaxBalBatch + 1];
   __shared__ int s_wave[kWaves];
+  __shared__ __align__(16) unsigned char s_kv[RT > 1 ? kShareLdsBytes(D) : 16];
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
   const int T = p.split_tokens;
-  auto n_groups = [&](int qn) { return ((qn * G + 15) / 16 + RT - 1) / RT; };
+  auto n_tiles_of = [&](int qn) { return (qn * G + 15) / 16; };
+  auto n_groups = [&](int qn) { return (n_tiles_of(qn) + RT - 1) / RT; };
+  auto shared_seq = [&](int qn) { return RT > 1 && n_tiles_of(qn) >= kShareMinTiles; };
   const int U = sequence_prefix(p.B, s_pref, s_wave, [&](int b) {
     const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
     int q0, qn;
     varlen_rows(p, b, q0, qn);
-    return (qn > 0 && ctx > 0) ? n_groups(qn) * ((ctx + T - 1) / T) : 0;
+    if (qn <= 0 || ctx <= 0) return 0;
+    const int ns = (ctx + T - 1) / T;
+    return shared_seq(qn) ? (n_tiles_of(qn) + kShareTiles - 1) / kShareTiles * Hkv * ns
+                          : n_groups(qn) * ns;
   });
   const int r = tid & 15;
   for (int u = blockIdx.x; u < U; u += gridDim.x) {
@@ -1070,12 +1279,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
     int q0, qn;
     varlen_rows(p, b, q0, qn);
     const int rows = qn * G;
-    const int ntg = n_groups(qn);
     const int local = u - s_pref[b];
-    const int tg = local % ntg, split = local / ntg;
-    const int m_first = 16 * RT * tg;
-    // Positions the group's last row sees (the others see fewer).
-    const int m_last = (m_first + 16 * RT < rows ? m_first + 16 * RT : rows) - 1;
+    const bool shared = shared_seq(qn);
+    int split, g_sh = 0, m_first, m_span;
+    if (shared) {
+      const int n_grp = (n_tiles_of(qn) + kShareTiles - 1) / kShareTiles;
+      const int grp = local % n_grp, rest = local / n_grp;
+      g_sh = rest % Hkv;
+      split = rest / Hkv;
+      m_first = 16 * kShareTiles * grp;
+      m_span = 16 * kShareTiles;
+    } else {
+      const int ntg = n_groups(qn);
+      split = local / ntg;
+      m_first = 16 * RT * (local % ntg);
+      m_span = 16 * RT;
+    }
+    // Positions the unit's last row sees (the others see fewer).
+    const int m_last = (m_first + m_span < rows ? m_first + m_span : rows) - 1;
     int tile_lim = ctx - qn + m_last / G + 1;
     tile_lim = tile_lim < 0 ? 0 : (tile_lim > ctx ? ctx : tile_lim);
     const int t0 = split * T;
@@ -1091,34 +1312,44 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
     }
     __syncthreads();
     const int span = tile_lim - t0 < T ? tile_lim - t0 : T;
+    auto desc = [&](int uu, int& pb, int& row0, int& nv) {
+      const int tok = t0 + 16 * uu;
+      const int x = s_pb[tok / bs - e0];
+      row0 = tok & (bs - 1);
+      int n = t0 + span - tok;
+      n = n < 0 ? 0 : (n > 16 ? 16 : n);
+      if (x < 0) n = 0;
+      nv = uniform(n);
+      pb = uniform(x < 0 ? 0 : x);
+    };
+    // Row tile rt of the sequence against KV head g, as slot t of a RowTiles.
+    auto fill = [&](auto& tiles, int t, int rt, int g) {
+      const int m0 = 16 * rt;
+      const int n_rows = rows - m0 < 0 ? 0 : (rows - m0 < 16 ? rows - m0 : 16);
+      const int m = m0 + r, j = m / G;
+      tiles.q[t] = r < n_rows
+                       ? p.c.q + ((size_t)(q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
+                       : nullptr;
+      tiles.n_rows[t] = n_rows;
+      tiles.limit[t] = ctx - qn + j + 1;
+      const size_t unit =
+          ((tile_base(q0, G, b) + (n_rows > 0 ? rt : 0)) * Hkv + g) * p.num_splits + split;
+      tiles.o[t] = p.part_o + unit * 16 * D;
+      tiles.lse[t] = p.part_lse + unit * 16;
+    };
+    if constexpr (RT > 1) {
+      if (shared) {
+        RowTiles<2> tiles;
+        fill(tiles, 0, m_first / 16 + 2 * wave, g_sh);
+        fill(tiles, 1, m_first / 16 + 2 * wave + 1, g_sh);
+        attend_shared<D>(p.c, g_sh, (span + 15) / 16, desc, t0, tiles, s_kv);
+        continue;
+      }
+    }
     for (int g = wave; g < Hkv; g += kWaves) {
-      auto desc = [&](int uu, int& pb, int& row0, int& nv) {
-        const int tok = t0 + 16 * uu;
-        const int x = s_pb[tok / bs - e0];
-        row0 = tok & (bs - 1);
-        int n = t0 + span - tok;
-        n = n < 0 ? 0 : (n > 16 ? 16 : n);
-        if (x < 0) n = 0;
-        nv = uniform(n);
-        pb = uniform(x < 0 ? 0 : x);
-      };
       RowTiles<RT> tiles;
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const int rt = RT * tg + t;
-        const int m0 = 16 * rt;
-        const int n_rows = rows - m0 < 0 ? 0 : (rows - m0 < 16 ? rows - m0 : 16);
-        const int m = m0 + r, j = m / G;
-        tiles.q[t] = r < n_rows
-                         ? p.c.q + ((size_t)(q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
-                         : nullptr;
-        tiles.n_rows[t] = n_rows;
-        tiles.limit[t] = ctx - qn + j + 1;
-        const size_t unit =
-            ((tile_base(q0, G, b) + (n_rows > 0 ? rt : 0)) * Hkv + g) * p.num_splits + split;
-        tiles.o[t] = p.part_o + unit * 16 * D;
-        tiles.lse[t] = p.part_lse + unit * 16;
-      }
+      for (int t = 0; t < RT; ++t) fill(tiles, t, m_first / 16 + t, g);
       attend_head<D, false, true, RT>(p.c, g, (span + 15) / 16, desc, t0, tiles);
     }
   }
