@@ -101,3 +101,45 @@ def test_graph_replay_equals_eager(case, fused):
         got = _snapshot(buf, d)
         for k in ref:
             assert torch.equal(got[k], ref[k]), f"replay {rep}: {k} differs from eager"
+
+
+def test_graph_replay_varlen_equals_eager():
+    """The multi-token call (chunks on the LDS-shared path, single tokens on the
+    per-head path, and its combine) captured and replayed: equal to eager."""
+    w = workloads.varlen_case(402, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
+                              context_lens=[900, 33, 2500, 16, 1200, 700],
+                              q_lens=[1, 7, 64, 16, 3, 1])
+    d = Dev(w)
+    qv = to_dev(w.query_varlen, BF)
+    cu = to_dev(w.cu_seqlens_q, torch.int32)
+    mq = int(np.diff(w.cu_seqlens_q).max())
+    out = torch.empty((qv.shape[0], w.num_q_heads, w.head_dim), dtype=torch.float32,
+                      device="cuda")
+    ws = torch.empty(gp.paged_attention_varlen_workspace_bytes(
+        w.batch, qv.shape[0], mq, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+        w.max_context_len), dtype=torch.uint8, device="cuda")
+
+    def call():
+        gp.paged_attention_varlen(qv, d.kc, d.vc, d.bt, d.ctx, cu, max_q_len=mq,
+                                  max_context_len=w.max_context_len, scale=float(w.scale),
+                                  out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)                  # stale partial rows must not leak into a replay
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from eager"
