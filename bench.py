@@ -4,9 +4,13 @@ One step = the whole hot path once over one batch of synthetic input:
   reshape_and_cache_quest (one new token per sequence, and the incremental Quest
   min / max of its block, in one launch)
   -> paged_attention_decode (dense, split-KV + combine)
-  -> quest_select_topk -> sparse_paged_attention_decode.
-With --write-path separate the first call is reshape_and_cache and a
-quest_block_metadata refresh of each sequence's last block follows the dense call.
+  -> quest_decode (Quest block selection and sparse attention over the selection;
+  one launch when the batch's (sequence, KV head) pairs fill the GPU).
+With --quest-path separate the last call is quest_select_topk followed by
+sparse_paged_attention_decode (the two calls are also timed on their own either
+way). With --write-path separate the first call is reshape_and_cache, a
+quest_block_metadata refresh of each sequence's last block follows the dense call,
+and the Quest part runs as the two separate calls.
 Inputs are resident in HBM before timing. Before every timed step a 1 GiB buffer
 is written so that no KV bytes survive in the 256 MB Infinity Cache; the
 per-call durations come from HIP events on the launch stream and exclude that
@@ -50,6 +54,8 @@ def parse_args():
     ap.add_argument("--write-path", choices=["fused", "separate"], default="fused",
                     help="fused: reshape_and_cache_quest; separate: reshape_and_cache + "
                          "quest_block_metadata(last_block_only)")
+    ap.add_argument("--quest-path", choices=["one_call", "separate"], default="one_call",
+                    help="Quest part of the step: quest_decode, or select + sparse calls")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) cache timing")
     ap.add_argument("--no-varlen", action="store_true", help="skip the multi-token query timing")
     ap.add_argument("--details", action="store_true", help="print per-call timings to stderr")
@@ -193,11 +199,16 @@ def main():
         ws_sp = torch.zeros(gp.sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K),
                             dtype=torch.uint8, device="cuda")
         sel = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda")
+        ws_qd = torch.zeros(gp.quest_decode_workspace_bytes(B, Hq, Hkv, D, bs, w.max_blocks_per_seq,
+                                                            K), dtype=torch.uint8, device="cuda")
     flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     fused = bool(K) and args.write_path == "fused"
-    if fused:
+    one_call = fused and args.quest_path == "one_call"
+    if one_call:
+        calls = ["reshape_and_cache_quest", "paged_attention_decode", "quest_decode"]
+    elif fused:
         calls = ["reshape_and_cache_quest", "paged_attention_decode", "quest_select_topk",
                  "sparse_paged_attention_decode"]
     elif K:
@@ -224,6 +235,9 @@ def main():
         elif name == "sparse_paged_attention_decode":
             gp.sparse_paged_attention_decode(q, kc, vc, bt, ctx, sel, max_context_len=mcl,
                                              scale=scale, out=out_s, workspace=ws_sp)
+        elif name == "quest_decode":
+            gp.quest_decode(q, kc, vc, kmin, kmax, bt, ctx, topk_blocks=K, max_context_len=mcl,
+                            scale=scale, out=out_s, topk_out=sel, workspace=ws_qd)
 
     def step(events=None):
         for i, name in enumerate(calls):
@@ -303,6 +317,26 @@ def main():
         del g
     except RuntimeError as exc:   # report, do not fail the eager measurement
         print(f"[bench] graph capture unavailable: {exc}", file=sys.stderr)
+
+    # The Quest part as its two separate calls, each timed alone (same flush), beside
+    # the one-call form the step uses.
+    quest_separate = None
+    if one_call:
+        quest_separate = {}
+        for name in ("quest_select_topk", "sparse_paged_attention_decode"):
+            for _ in range(3):
+                run_call(name)
+            ts = []
+            for k in range(args.steps):
+                flush.fill_(k & 0xFF)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run_call(name)
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            quest_separate[name] = round(float(np.mean(ts)), 2)
+        quest_separate["sum"] = round(sum(quest_separate.values()), 2)
 
     # FP8 (E4M3) KV cache on the same workload: the pool quantised once by the FP8
     # write (every slot), then its write and dense calls timed like the bf16 ones.
@@ -408,6 +442,7 @@ def main():
         by["quest_block_metadata"] = R.metadata_step_bytes(w.context_lens, bs, Hkv, D)
         by["quest_select_topk"] = R.select_bytes(w.context_lens, bs, Hkv, D)
         by["sparse_paged_attention_decode"] = R.sparse_attention_bytes(sel_host, w.context_lens, bs, D)
+        by["quest_decode"] = by["quest_select_topk"] + by["sparse_paged_attention_decode"]
     step_bytes = sum(by[n] for n in calls)
     mean_step = float(step_us.mean())
     value = step_bytes / (mean_step * 1e-6) / 1e9
@@ -448,6 +483,7 @@ def main():
                    "head_dim": D, "block_size": bs, "sum_context": int(w.context_lens.sum()),
                    "max_context_len": mcl, "topk_blocks": K, "parallelism": "single-gpu",
                    "write_path": args.write_path if K else "plain",
+                   "quest_path": ("one_call" if one_call else "separate") if K else None,
                    "sparse_split_tokens": gp.split_tokens(B, Hkv, K * bs) if K else None},
         "pct_of_peak": round(100 * value / R.MI355X_HBM_GBPS, 1),
         "us_per_step": round(mean_step, 2),
@@ -458,6 +494,7 @@ def main():
         "graph_replay_us_per_step": round(graph_us, 2) if graph_us is not None else None,
         "fp8_kv": fp8,
         "varlen_mixed": varlen,
+        "quest_separate_calls_us": quest_separate,
         "calls": calls_out,
         "step_algorithmic_bytes": int(step_bytes),
         "wall_s_timed_region_incl_flush": round(wall, 4),

@@ -228,6 +228,43 @@ def sparse_paged_attention_decode(query, key_cache, value_cache, block_tables, c
     return out
 
 
+def quest_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 max_blocks_per_seq, topk_blocks) -> int:
+    return int(lib().gpkv_quest_decode_workspace_bytes(batch, num_q_heads, num_kv_heads,
+                                                       head_dim, block_size, max_blocks_per_seq,
+                                                       topk_blocks))
+
+
+def quest_decode(query, key_cache, value_cache, key_min, key_max, block_tables, context_lens, *,
+                 topk_blocks: int, max_context_len: int, scale: float, out=None, topk_out=None,
+                 workspace=None, stream=None):
+    """Quest selection and sparse attention in one call; returns (out [B, H_q, D] float32,
+    topk_indices [B, H_kv, topk_blocks] int32), the results of quest_select_topk followed
+    by sparse_paged_attention_decode."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks(query, key_cache, value_cache, block_tables,
+                                             context_lens)
+    _dev("key_min", key_min, torch.bfloat16, 3)
+    _dev("key_max", key_max, torch.bfloat16, 3)
+    if key_min.shape != key_max.shape or tuple(key_min.shape) != (NB, Hkv, D):
+        raise ValueError("quest_decode: key_min / key_max must be [num_blocks, H_kv, D]")
+    K = int(topk_blocks)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+    if topk_out is None:
+        topk_out = torch.empty((B, Hkv, K), dtype=torch.int32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    _dev("topk_out", topk_out, torch.int32, 3)
+    if tuple(topk_out.shape) != (B, Hkv, K):
+        raise ValueError("quest_decode: topk_out must be [B, H_kv, topk_blocks]")
+    need = quest_decode_workspace_bytes(B, Hq, Hkv, D, bs, MB, K)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_quest_decode(
+        _ptr(out), _ptr(topk_out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+        _ptr(key_min), _ptr(key_max), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs,
+        NB, MB, int(max_context_len), K, float(scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, topk_out
+
+
 # ---------------------------------------------------------------------------
 # FP8 (E4M3) caches: uint8 codes, float32 scale per KV head for K and for V
 # ---------------------------------------------------------------------------

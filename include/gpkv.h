@@ -209,6 +209,30 @@ int gpkv_sparse_paged_attention_decode(float* out, const void* query, const void
                                        float scale, void* workspace, size_t workspace_bytes,
                                        void* stream);
 
+/* Quest decode step in one call ([ASC] "Quest Sparse Attention" and its notes on
+ * the sparse path's costs: scoring, Top-K, indexing and the scheduling of several
+ * kernels): the result of gpkv_quest_select_topk followed by
+ * gpkv_sparse_paged_attention_decode on the same arguments. topk_indices
+ * [batch, num_kv_heads, topk_blocks] int32 receives the selection (ascending, -1
+ * padding), out [batch, num_q_heads, head_dim] fp32 the attention over it. key_min /
+ * key_max as for gpkv_quest_select_topk, caches and scale as for the attention
+ * calls. When the (sequence, KV head) pairs fill between half of the GPU's CUs
+ * and all of them, one workgroup per pair selects in LDS and attends at once (one
+ * launch); otherwise the two calls run in turn. The workspace (size from
+ * gpkv_quest_decode_workspace_bytes) serves either. Errors: those of the two calls. */
+size_t gpkv_quest_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int32_t max_blocks_per_seq,
+                                         int32_t topk_blocks);
+int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* query,
+                      const void* key_cache, const void* value_cache, const void* key_min,
+                      const void* key_max, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                      int32_t topk_blocks, float scale, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* ---------------------------------------------------------------------------
  * FP8 KV cache. The pages name KV quantisation as the lever for long-context
  * decode, where the KV stream is the cost ([TL18] 2.5 item 3, 3.1 item 4); they

@@ -1,0 +1,108 @@
+"""The one-call Quest decode (selection, then sparse attention) against the oracle,
+on both of its paths, and against the two separate calls.
+
+Bars: selected ids bit-exact; attention max-abs 2e-3 against the float64 oracle,
+and 1e-5 between the one-launch path and the two calls (the same arithmetic, with
+a different split of each head's tokens over waves).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_paged_kv_amd as gp
+import oracle
+import workloads
+from gpu_util import BF, Dev, max_abs, sample_seqs, workload
+
+pytestmark = pytest.mark.gpu
+ATOL = 2e-3
+
+
+@functools.lru_cache(maxsize=None)
+def _oracle_selection(config, K):
+    w = workload(config)
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens,
+                                             w.block_size)
+    return oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens,
+                                    w.block_size, K)
+
+
+def _meta(d, w):
+    kmin = torch.zeros((w.num_blocks, w.num_kv_heads, w.head_dim), dtype=BF, device="cuda")
+    kmax = torch.zeros_like(kmin)
+    gp.quest_block_metadata(d.kc, d.bt, d.ctx, kmin, kmax, max_context_len=w.max_context_len)
+    return kmin, kmax
+
+
+def _decode(d, w, kmin, kmax, K):
+    out, sel = gp.quest_decode(d.q, d.kc, d.vc, kmin, kmax, d.bt, d.ctx, topk_blocks=K,
+                               max_context_len=w.max_context_len, scale=float(w.scale))
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), sel.cpu().numpy()
+
+
+@pytest.mark.parametrize("path", ["auto", "fused", "separate"])
+@pytest.mark.parametrize("config,K", [(1, 3), (1, 5), (3, 64), (4, 256), (5, 32)])
+def test_quest_decode_config(config, K, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", path)
+    w = workload(config)
+    d = Dev(w)
+    kmin, kmax = _meta(d, w)
+    out, sel = _decode(d, w, kmin, kmax, K)
+    exp = _oracle_selection(config, K)
+    assert np.array_equal(sel, exp), "selection differs from the oracle"
+    seqs = list(range(w.batch)) if w.batch <= 4 else sample_seqs(w)
+    ref = oracle.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache,
+                                               w.block_tables, w.context_lens, exp, w.scale,
+                                               seqs=seqs)
+    err = max_abs(out[seqs], ref[seqs])
+    print(f"config {config} K={K} path={path}: max-abs {err:.3e}")
+    assert err <= ATOL
+
+
+QD_CASES = [
+    # seed, Hq, Hkv, D, bs, ctx, K
+    (801, 28, 4, 128, 16, [900, 33, 2500, 16, 0, 700], 12),    # empty context, K > nb
+    (802, 16, 1, 128, 64, [129, 2047, 4100], 1),                 # G = 16, K = 1
+    (803, 14, 2, 64, 128, [250, 1, 700, 3000], 5),               # D = 64, bs = 128
+    (804, 12, 3, 64, 32, [513, 514, 96], 40),
+]
+
+
+@pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx,K", QD_CASES)
+def test_quest_decode_random_fused_equals_separate(seed, Hq, Hkv, D, bs, ctx, K, monkeypatch):
+    w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv,
+                              head_dim=D, block_size=bs, context_lens=ctx)
+    d = Dev(w)
+    kmin, kmax = _meta(d, w)
+    monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "fused")
+    out_f, sel_f = _decode(d, w, kmin, kmax, K)
+    monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "separate")
+    out_s, sel_s = _decode(d, w, kmin, kmax, K)
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, bs)
+    exp = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens, bs, K)
+    assert np.array_equal(sel_f, exp) and np.array_equal(sel_s, exp)
+    ref = oracle.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache,
+                                               w.block_tables, w.context_lens, exp, w.scale)
+    assert max_abs(out_f, ref) <= ATOL and max_abs(out_s, ref) <= ATOL
+    assert max_abs(out_f, out_s) <= 1e-5
+    for b, L in enumerate(ctx):
+        if L == 0:
+            assert (out_f[b] == 0).all() and (sel_f[b] == -1).all()
+
+
+def test_quest_decode_config3_fused_equals_separate(monkeypatch):
+    """The 8K-average batch (256 pairs: the one-launch path by default) against the
+    two separate calls, every sequence."""
+    w = workload(3)
+    d = Dev(w)
+    kmin, kmax = _meta(d, w)
+    K = w.topk_list[0]
+    out_f, sel_f = _decode(d, w, kmin, kmax, K)
+    monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "separate")
+    out_s, sel_s = _decode(d, w, kmin, kmax, K)
+    assert np.array_equal(sel_f, sel_s)
+    assert max_abs(out_f, out_s) <= 1e-5
