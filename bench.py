@@ -62,11 +62,42 @@ def parse_args():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def strip_c_comments(text: str) -> str:
+    """C / C++ source without comments, whitespace runs collapsed to one space (string
+    and character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the attention kernels' code (comments and layout ignored): the
+    committed counters stay valid across comment-only edits and no longer."""
     h = hashlib.sha256()
     for f in ("paged_attention.hip", "gpkv_internal.h"):
-        with open(os.path.join(ROOT, "gqa_paged_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        if read is None:
+            with open(os.path.join(ROOT, "gqa_paged_kv_amd", "csrc", f), encoding="utf-8") as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        h.update(strip_c_comments(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -970,9 +970,9 @@ __global__ __launch_bounds__(kWaves * 64) void attn_sparse_direct_kernel(const D
 // Quest decode in one launch: block selection, then attention over the selection
 // ---------------------------------------------------------------------------
 
-// ["Ascend Kernel-to-Serving Pipeline", "Quest Sparse Attention" and its
-// performance notes]: beyond the KV bytes it skips, the sparse path pays for
-// scoring, Top-K, indexing and the scheduling of several kernels. When the batch's
+// ["Ascend Kernel-to-Serving Pipeline", section "test results and interpretation",
+// item 4]: beyond the KV bytes it skips, the sparse path pays for scoring, Top-K,
+// indexing and the scheduling of several kernels. When the batch's
 // (sequence, KV head) pairs take at most one workgroup per CU, one workgroup per
 // pair does all of it: it stages the pair's block-table row once, scores every
 // block into LDS keys, radix-selects the Top-K ids into LDS (and writes them

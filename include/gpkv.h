@@ -209,9 +209,9 @@ int gpkv_sparse_paged_attention_decode(float* out, const void* query, const void
                                        float scale, void* workspace, size_t workspace_bytes,
                                        void* stream);
 
-/* Quest decode step in one call ([ASC] "Quest Sparse Attention" and its notes on
- * the sparse path's costs: scoring, Top-K, indexing and the scheduling of several
- * kernels): the result of gpkv_quest_select_topk followed by
+/* Quest decode step in one call ([ASC] "Quest Sparse Attention"; "test results and
+ * interpretation" item 4 names the sparse path's costs: scoring, Top-K, indexing
+ * and the scheduling of several kernels): the result of gpkv_quest_select_topk followed by
  * gpkv_sparse_paged_attention_decode on the same arguments. topk_indices
  * [batch, num_kv_heads, topk_blocks] int32 receives the selection (ascending, -1
  * padding), out [batch, num_q_heads, head_dim] fp32 the attention over it. key_min /
