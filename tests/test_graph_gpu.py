@@ -29,6 +29,9 @@ def _step_buffers(w, d, K):
                               dtype=torch.uint8, device="cuda"),
         "ws_sp": torch.zeros(gp.sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K),
                              dtype=torch.uint8, device="cuda"),
+        "ws_qd": torch.zeros(gp.quest_decode_workspace_bytes(B, Hq, Hkv, D, bs,
+                                                             w.max_blocks_per_seq, K),
+                             dtype=torch.uint8, device="cuda"),
         "sel": torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda"),
         "kmin": torch.zeros((w.num_blocks, Hkv, D), dtype=BF, device="cuda"),
         "kmax": torch.zeros((w.num_blocks, Hkv, D), dtype=BF, device="cuda"),
@@ -37,7 +40,7 @@ def _step_buffers(w, d, K):
     return buf
 
 
-def _step(w, d, buf, K, fused):
+def _step(w, d, buf, K, fused, one_call=False):
     mcl, bs, scale = w.max_context_len, w.block_size, float(w.scale)
     if fused:   # write + incremental metadata in one launch (both idempotent)
         gp.reshape_and_cache_quest(d.nk, d.nv, d.kc, d.vc, buf["kmin"], buf["kmax"], d.slots)
@@ -48,6 +51,11 @@ def _step(w, d, buf, K, fused):
     if not fused:
         gp.quest_block_metadata(d.kc, d.bt, d.ctx, buf["kmin"], buf["kmax"],
                                 max_context_len=mcl, last_block_only=True)
+    if one_call:
+        gp.quest_decode(d.q, d.kc, d.vc, buf["kmin"], buf["kmax"], d.bt, d.ctx, topk_blocks=K,
+                        max_context_len=mcl, scale=scale, out=buf["out_s"], topk_out=buf["sel"],
+                        workspace=buf["ws_qd"])
+        return
     gp.quest_select_topk(d.q, buf["kmin"], buf["kmax"], d.bt, d.ctx, block_size=bs,
                          topk_blocks=K, max_context_len=mcl, out=buf["sel"],
                          workspace=buf["ws_sel"])
@@ -62,9 +70,12 @@ def _snapshot(buf, d):
                                       ("kmax", buf["kmax"]), ("kc", d.kc), ("vc", d.vc))}
 
 
-@pytest.mark.parametrize("case,fused", [("random", False), ("config3", False), ("random", True),
-                                        ("config3", True)])
-def test_graph_replay_equals_eager(case, fused):
+@pytest.mark.parametrize("case,fused,one_call", [("random", False, False), ("config3", False, False),
+                                                 ("random", True, False), ("config3", True, False),
+                                                 ("random", True, True), ("config3", True, True)])
+def test_graph_replay_equals_eager(case, fused, one_call, monkeypatch):
+    if one_call:   # the one-launch Quest decode on both shapes
+        monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "fused")
     if case == "random":
         w = workloads.random_case(401, batch=6, num_q_heads=28, num_kv_heads=4, head_dim=128,
                                   block_size=16, context_lens=[900, 33, 2500, 16, 1200, 700],
@@ -78,16 +89,16 @@ def test_graph_replay_equals_eager(case, fused):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):       # warm-up on the capture stream
-        _step(w, d, buf, K, fused)
+        _step(w, d, buf, K, fused, one_call)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    _step(w, d, buf, K, fused)                 # eager reference (the write is idempotent)
+    _step(w, d, buf, K, fused, one_call)       # eager reference (the write is idempotent)
     torch.cuda.synchronize()
     ref = _snapshot(buf, d)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _step(w, d, buf, K, fused)
+        _step(w, d, buf, K, fused, one_call)
     scratch = torch.empty(1 << 20, device="cuda")
     for rep in range(4):
         # eager work between replays: clobber the outputs, then replay
