@@ -58,7 +58,7 @@ __all__ = [
     "quest_select_topk", "sparse_token_positions", "sparse_paged_attention_decode",
     "split_kv_partials", "split_kv_combine", "e4m3_to_f64", "e4m3_from_f32",
     "fp8_inverse_scale", "quantize_fp8", "reshape_and_cache_fp8", "paged_attention_decode_fp8",
-    "paged_attention_varlen",
+    "paged_attention_varlen", "paged_attention_varlen_fp8",
 ]
 
 
@@ -433,20 +433,16 @@ def paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_scale, 
 # C8 -- multi-token queries over the paged cache  (R8; [TL18] 2.7, 3.3)
 # ---------------------------------------------------------------------------
 
-def paged_attention_varlen(query, key_cache, value_cache, block_tables, context_lens,
-                           cu_seqlens_q, scale, seqs=None):
-    """out[r, h, :] for every query row r: row j of sequence b (r = cu[b] + j) is
-    softmax_t(scale * q[r,h].K_t) . V_t over positions t <= ctx_b - q_len_b + j, by
-    definition (all scores, the masked ones set to -inf, then the softmax).
-    query: [sum q_len, H_q, D] bf16 bits; returns float64 of that shape."""
+def _varlen_attention(query, cu_seqlens_q, context_lens, kv_of, num_kv_heads, scale, seqs):
+    """The definition behind the varlen functions: kv_of(b, positions) gives that
+    sequence's K and V values [L, H_kv, D] in float64."""
     UQ, Hq, D = query.shape
-    NB, bs, Hkv, _ = key_cache.shape
+    Hkv = num_kv_heads
     if Hq % Hkv:
         raise ValueError("H_q must be a multiple of H_kv")
     G = Hq // Hkv
     ctx = np.asarray(context_lens, dtype=np.int64)
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
-    _check_table(block_tables, ctx, bs, NB)
     out = np.zeros((UQ, Hq, D), dtype=np.float64)
     q = bf16_to_f64(query)
     sc = float(np.float32(scale))
@@ -456,8 +452,7 @@ def paged_attention_varlen(query, key_cache, value_cache, block_tables, context_
         if r1 <= r0 or L == 0:
             continue
         pos = np.arange(L)
-        k = bf16_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs))
-        v = bf16_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs))
+        k, v = kv_of(b, pos)
         lim = L - (r1 - r0) + np.arange(r1 - r0)          # last visible position per row
         visible = pos[None, :] <= lim[:, None]            # [q_len, L]
         for g in range(Hkv):
@@ -472,3 +467,33 @@ def paged_attention_varlen(query, key_cache, value_cache, block_tables, context_
                 p = np.divide(e, den, out=np.zeros_like(e), where=den > 0)
                 out[r0:r1, h] = p @ v[:, g]
     return out
+
+
+def paged_attention_varlen(query, key_cache, value_cache, block_tables, context_lens,
+                           cu_seqlens_q, scale, seqs=None):
+    """out[r, h, :] for every query row r: row j of sequence b (r = cu[b] + j) is
+    softmax_t(scale * q[r,h].K_t) . V_t over positions t <= ctx_b - q_len_b + j, by
+    definition (all scores, the masked ones set to -inf, then the softmax).
+    query: [sum q_len, H_q, D] bf16 bits; returns float64 of that shape."""
+    NB, bs, Hkv, _ = key_cache.shape
+    _check_table(block_tables, np.asarray(context_lens, dtype=np.int64), bs, NB)
+
+    def kv_of(b, pos):
+        return (bf16_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs)),
+                bf16_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs)))
+    return _varlen_attention(query, cu_seqlens_q, context_lens, kv_of, Hkv, scale, seqs)
+
+
+def paged_attention_varlen_fp8(query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                               context_lens, cu_seqlens_q, scale, seqs=None):
+    """paged_attention_varlen over E4M3 caches (R7 with R8): K = code * k_scale[g],
+    V = code * v_scale[g]."""
+    NB, bs, Hkv, _ = key_cache.shape
+    _check_table(block_tables, np.asarray(context_lens, dtype=np.int64), bs, NB)
+    ks = np.asarray(k_scale, dtype=np.float32).astype(np.float64)
+    vs = np.asarray(v_scale, dtype=np.float32).astype(np.float64)
+
+    def kv_of(b, pos):
+        return (e4m3_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs)) * ks[:, None],
+                e4m3_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs)) * vs[:, None])
+    return _varlen_attention(query, cu_seqlens_q, context_lens, kv_of, Hkv, scale, seqs)

@@ -717,4 +717,40 @@ def pin_varlen_mask_edge(orc):
             assert changed == moves, (j, t)
 
 
+# ---------------------------------------------------------------------------
+# Multi-token queries over E4M3 caches
+# ---------------------------------------------------------------------------
+
+def pin_varlen_fp8_single_token_is_fp8_decode(orc):
+    """One query token per sequence over quantised caches: the FP8 decode result."""
+    w = workloads.varlen_case(85, num_q_heads=6, num_kv_heads=2, head_dim=64, block_size=16,
+                              context_lens=[1, 40, 70], q_lens=[1, 1, 1])
+    ks, vs = [0.031, 0.2], [0.5, 0.0123]
+    kq = orc.quantize_fp8(w.key_cache, ks)
+    vq = orc.quantize_fp8(w.value_cache, vs)
+    got = orc.paged_attention_varlen_fp8(w.query_varlen, kq, vq, ks, vs, w.block_tables,
+                                         w.context_lens, w.cu_seqlens_q, w.scale)
+    exp = orc.paged_attention_decode_fp8(w.query_varlen, kq, vq, ks, vs, w.block_tables,
+                                         w.context_lens, w.scale)
+    assert np.abs(got - exp).max() <= TOL
+
+
+def pin_varlen_fp8_equals_bf16_on_representable(orc):
+    """With values exactly representable, FP8 varlen attention is bf16 varlen attention
+    (chunks longer than the context included)."""
+    scales_k, scales_v = [0.5, 4.0], [2.0, 0.25]
+    w = _representable_case(86, scales_k)
+    wv = _representable_case(87, scales_v)
+    wq = workloads.varlen_case(88, num_q_heads=6, num_kv_heads=2, head_dim=64, block_size=16,
+                               context_lens=w.context_lens.tolist(), q_lens=[3, 17, 40])
+    kq = orc.quantize_fp8(w.key_cache, scales_k)
+    vq = orc.quantize_fp8(wv.value_cache, scales_v)
+    got = orc.paged_attention_varlen_fp8(wq.query_varlen, kq, vq, scales_k, scales_v,
+                                         w.block_tables, w.context_lens, wq.cu_seqlens_q, w.scale)
+    exp = orc.paged_attention_varlen(wq.query_varlen, w.key_cache, wv.value_cache, w.block_tables,
+                                     w.context_lens, wq.cu_seqlens_q, w.scale)
+    assert np.abs(got - exp).max() <= TOL
+    assert (got[0] == 0).all() and (got[1] == 0).all()   # 3 rows over 1 position: two see nothing
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

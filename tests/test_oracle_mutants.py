@@ -52,6 +52,10 @@ MUTANTS = [
     ("varlen: mask aligned left", "lim = L - (r1 - r0) + np.arange(r1 - r0)", "lim = np.arange(r1 - r0)"),
     ("varlen: mask off by one", "visible = pos[None, :] <= lim[:, None]", "visible = pos[None, :] < lim[:, None]"),
     ("varlen: no causal mask", "visible = pos[None, :] <= lim[:, None]", "visible = pos[None, :] >= 0"),
+    ("fp8 varlen: K scale on V", "                e4m3_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs)) * vs[:, None])",
+     "                e4m3_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs)) * ks[:, None])"),
+    ("fp8 varlen: codes read as bf16", "        return (e4m3_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs)) * ks[:, None],",
+     "        return (bf16_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs)) * ks[:, None],"),
     ("varlen: query rows shifted", "s_ = sc * (q[r0:r1, h] @ k[:, g].T)", "s_ = sc * (q[r0 + 1:r1 + 1, h] @ k[:, g].T)"),
 ]
 
