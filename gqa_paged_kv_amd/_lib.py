@@ -55,6 +55,10 @@ SIGNATURES = {
                                               c_int32, c_int32, c_int32, c_int32, c_int32,
                                               c_int64, c_int32, c_int32, c_float, vp, c_size,
                                               vp]),
+    "gpkv_paged_attention_varlen_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int32,
+                                                  c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                  c_int32, c_int64, c_int32, c_int32, c_float,
+                                                  vp, c_size, vp]),
     "gpkv_status_string": (ctypes.c_char_p, [c_int32]),
     "gpkv_last_error_message": (ctypes.c_char_p, []),
     "gpkv_split_tokens": (c_int32, [c_int32, c_int32, c_int32]),

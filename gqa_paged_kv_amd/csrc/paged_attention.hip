@@ -1373,19 +1373,20 @@ __device__ __forceinline__ int sequence_of(const int* s_pref, int B, int u) {
 constexpr int kShareTiles = 2 * kWaves;   // row tiles of one shared unit
 constexpr int kShareMinTiles = 4;
 
-template <int D, int RT>
+template <int D, int RT, bool FP8>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 2))) void attn_varlen_kernel(const VarlenParams p) {
+  constexpr bool kShared = RT > 1 && !FP8;   // E4M3 caches: per-head units only
   __shared__ int s_pb[kMaxTable];
   __shared__ int s_pref[kMaxBalBatch + 1];
   __shared__ int s_wave[kWaves];
-  __shared__ __align__(16) unsigned char s_kv[RT > 1 ? kShareLdsBytes(D) : 16];
+  __shared__ __align__(16) unsigned char s_kv[kShared ? kShareLdsBytes(D) : 16];
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
   const int T = p.split_tokens;
   auto n_tiles_of = [&](int qn) { return (qn * G + 15) / 16; };
   auto n_groups = [&](int qn) { return (n_tiles_of(qn) + RT - 1) / RT; };
-  auto shared_seq = [&](int qn) { return RT > 1 && n_tiles_of(qn) >= kShareMinTiles; };
+  auto shared_seq = [&](int qn) { return kShared && n_tiles_of(qn) >= kShareMinTiles; };
   const int U = sequence_prefix(p.B, s_pref, s_wave, [&](int b) {
     const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
     int q0, qn;
@@ -1460,7 +1461,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
       tiles.o[t] = p.part_o + unit * 16 * D;
       tiles.lse[t] = p.part_lse + unit * 16;
     };
-    if constexpr (RT > 1) {
+    if constexpr (kShared) {
       if (shared) {
         RowTiles<2> tiles;
         fill(tiles, 0, m_first / 16 + 2 * wave, g_sh);
@@ -1473,7 +1474,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
       RowTiles<RT> tiles;
 #pragma unroll
       for (int t = 0; t < RT; ++t) fill(tiles, t, m_first / 16 + t, g);
-      attend_head<D, false, true, RT>(p.c, g, (span + 15) / 16, desc, t0, tiles);
+      attend_head<D, FP8, true, RT>(p.c, g, (span + 15) / 16, desc, t0, tiles);
     }
   }
 }
@@ -1876,14 +1877,31 @@ extern "C" size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int
   return pl.o_bytes + pl.lse_bytes;
 }
 
-extern "C" int gpkv_paged_attention_varlen(
-    float* out, const void* query, const void* key_cache, const void* value_cache,
-    const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens_q,
-    int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
-    int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
-  const char* fn = "paged_attention_varlen";
+template <bool FP8>
+static void launch_varlen(bool multi, int head_dim, dim3 grid, dim3 block, hipStream_t s,
+                          const VarlenParams& vp) {
+  if (!multi) {
+    if (head_dim == 128)
+      attn_varlen_kernel<128, 1, FP8><<<grid, block, 0, s>>>(vp);
+    else
+      attn_varlen_kernel<64, 1, FP8><<<grid, block, 0, s>>>(vp);
+  } else {
+    if (head_dim == 128)
+      attn_varlen_kernel<128, kVarlenRT, FP8><<<grid, block, 0, s>>>(vp);
+    else
+      attn_varlen_kernel<64, kVarlenRT, FP8><<<grid, block, 0, s>>>(vp);
+  }
+}
+
+static int varlen_run(bool fp8, float* out, const void* query, const void* key_cache,
+                      const void* value_cache, const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* cu_seqlens_q, int32_t batch, int32_t total_q,
+                      int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = fp8 ? "paged_attention_varlen_fp8" : "paged_attention_varlen";
   int st = check_common(fn, batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                         max_blocks_per_seq, max_context_len);
   if (st) return st;
@@ -1894,7 +1912,7 @@ extern "C" int gpkv_paged_attention_varlen(
   if (batch > kMaxBalBatch)
     return fail(GPKV_ERR_UNSUPPORTED, "%s: batch=%d > %d", fn, batch, kMaxBalBatch);
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
-      !cu_seqlens_q)
+      !cu_seqlens_q || (fp8 && (!k_scale || !v_scale)))
     return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
   const VarlenPlan pl = make_varlen_plan(batch, total_q, max_q_len, num_q_heads, num_kv_heads,
                                          head_dim, block_size, max_context_len);
@@ -1910,9 +1928,9 @@ extern "C" int gpkv_paged_attention_varlen(
   vp.c.q = (const unsigned short*)query;
   vp.c.kc = (const unsigned char*)key_cache;
   vp.c.vc = (const unsigned char*)value_cache;
-  vp.c.k_scale = nullptr;
-  vp.c.v_scale = nullptr;
-  vp.c.row_bytes = num_kv_heads * head_dim * 2;
+  vp.c.k_scale = k_scale;
+  vp.c.v_scale = v_scale;
+  vp.c.row_bytes = num_kv_heads * head_dim * (fp8 ? 1 : 2);
   vp.c.block_bytes = (long long)block_size * vp.c.row_bytes;
   vp.c.Hq = num_q_heads;
   vp.c.Hkv = num_kv_heads;
@@ -1941,17 +1959,10 @@ extern "C" int gpkv_paged_attention_varlen(
   const long long units_max = (tiles / rt_per_wave + batch) * pl.num_splits;
   const long long cap = 4LL * balanced_capacity();
   const dim3 grid((unsigned)(units_max < cap ? units_max : cap)), block(kWaves * 64);
-  if (rt_per_wave == 1) {
-    if (head_dim == 128)
-      attn_varlen_kernel<128, 1><<<grid, block, 0, s>>>(vp);
-    else
-      attn_varlen_kernel<64, 1><<<grid, block, 0, s>>>(vp);
-  } else {
-    if (head_dim == 128)
-      attn_varlen_kernel<128, kVarlenRT><<<grid, block, 0, s>>>(vp);
-    else
-      attn_varlen_kernel<64, kVarlenRT><<<grid, block, 0, s>>>(vp);
-  }
+  if (fp8)
+    launch_varlen<true>(rt_per_wave > 1, head_dim, grid, block, s, vp);
+  else
+    launch_varlen<false>(rt_per_wave > 1, head_dim, grid, block, s, vp);
   st = check_launch(fn);
   if (st) return st;
   const long long ctiles = tiles * num_kv_heads;
@@ -1961,6 +1972,33 @@ extern "C" int gpkv_paged_attention_varlen(
   else
     attn_varlen_combine_kernel<64><<<cgrid, cblock, 0, s>>>(vp);
   return check_launch(fn);
+}
+
+extern "C" int gpkv_paged_attention_varlen(
+    float* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens_q,
+    int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return varlen_run(false, out, query, key_cache, value_cache, nullptr, nullptr, block_tables,
+                    context_lens, cu_seqlens_q, batch, total_q, max_q_len, num_q_heads,
+                    num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                    max_context_len, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gpkv_paged_attention_varlen_fp8(
+    float* out, const void* query, const void* key_cache, const void* value_cache,
+    const float* k_scale, const float* v_scale, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* cu_seqlens_q, int32_t batch, int32_t total_q,
+    int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return varlen_run(true, out, query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                    context_lens, cu_seqlens_q, batch, total_q, max_q_len, num_q_heads,
+                    num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                    max_context_len, scale, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t gpkv_paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads,

@@ -392,3 +392,35 @@ def paged_attention_varlen(query, key_cache, value_cache, block_tables, context_
         int(block_tables.shape[1]), int(max_context_len), float(scale), _ptr(ws), ws.numel(),
         _stream(stream)))
     return out
+
+
+def paged_attention_varlen_fp8(query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                               context_lens, cu_seqlens_q, *, max_q_len: int, max_context_len: int,
+                               scale: float, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """paged_attention_varlen over E4M3 caches (uint8 codes, float32 scale per KV head);
+    returns [total_q, H_q, D] float32."""
+    _dev("query", query, torch.bfloat16, 3)
+    _dev("key_cache", key_cache, torch.uint8, 4)
+    _dev("value_cache", value_cache, torch.uint8, 4)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    _dev("cu_seqlens_q", cu_seqlens_q, torch.int32, 1)
+    NB, bs, Hkv, D = (int(x) for x in key_cache.shape)
+    _scales(k_scale, v_scale, Hkv)
+    UQ, Hq, Dq = query.shape
+    B = int(context_lens.shape[0])
+    if value_cache.shape != key_cache.shape or Dq != D or block_tables.shape[0] != B \
+            or cu_seqlens_q.shape[0] != B + 1:
+        raise ValueError("paged_attention_varlen_fp8: inconsistent shapes")
+    if out is None:
+        out = torch.empty((UQ, Hq, D), dtype=torch.float32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    need = paged_attention_varlen_workspace_bytes(B, UQ, max_q_len, Hq, Hkv, D, bs,
+                                                  max_context_len)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_paged_attention_varlen_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), _ptr(cu_seqlens_q), B, UQ, int(max_q_len), Hq,
+        Hkv, D, bs, NB, int(block_tables.shape[1]), int(max_context_len), float(scale), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return out

@@ -316,6 +316,24 @@ int gpkv_paged_attention_varlen(float* out, const void* query, const void* key_c
                                 int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* gpkv_paged_attention_varlen over E4M3 caches (KV quantisation, [TL18] 2.5 item 3
+ * and 3.1 item 4, with the varlen rows of 2.7 / 3.3): key_cache / value_cache are
+ * uint8 codes [num_blocks, block_size, num_kv_heads, head_dim] and k_scale /
+ * v_scale float32 [num_kv_heads], read as code * scale (as for
+ * gpkv_paged_attention_decode_fp8). Other arguments, the workspace size
+ * (gpkv_paged_attention_varlen_workspace_bytes) and errors as for the bf16 call;
+ * null scales give GPKV_ERR_NULL. */
+int gpkv_paged_attention_varlen_fp8(float* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const float* k_scale,
+                                    const float* v_scale, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* cu_seqlens_q,
+                                    int32_t batch, int32_t total_q, int32_t max_q_len,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    float scale, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Static description of a status code. */
 const char* gpkv_status_string(int status);
 

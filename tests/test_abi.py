@@ -28,7 +28,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(L):
     from gqa_paged_kv_amd._lib import SIGNATURES
     names = declared_symbols()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     assert sorted(SIGNATURES) == names
@@ -112,6 +112,11 @@ def test_other_entry_points_checks(L):
     assert L.gpkv_paged_attention_varlen(8, 8, 8, 8, 8, 8, 8, 2, 5, 4, 4, 1, 64, 16, 16, 5, 80,
                                          0.1, 8, 16, None) == -4
     assert L.gpkv_paged_attention_varlen_workspace_bytes(2, 5, 4, 4, 1, 64, 16, 80) > 0
+    # FP8 varlen: null scales, small workspace
+    assert L.gpkv_paged_attention_varlen_fp8(8, 8, 8, 8, None, 8, 8, 8, 8, 2, 5, 4, 4, 1, 64, 16,
+                                             16, 5, 80, 0.1, 8, 1 << 30, None) == -1
+    assert L.gpkv_paged_attention_varlen_fp8(8, 8, 8, 8, 8, 8, 8, 8, 8, 2, 5, 4, 4, 1, 64, 16, 16,
+                                             5, 80, 0.1, 8, 16, None) == -4
     # one-call Quest decode: null selection output, topk_blocks < 1, small workspace
     assert L.gpkv_quest_decode(8, None, 8, 8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 3, 0.1, 8,
                                1 << 30, None) == -1

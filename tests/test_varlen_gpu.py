@@ -113,3 +113,68 @@ def test_varlen_bad_offsets_read_as_empty():
     ref = _ref(w)
     assert max_abs(got[:4], ref[:4]) <= ATOL          # sequence 0 intact
     assert (got[4:] == 7.0).all(), "rows of the empty sequences are not written"
+
+
+# ---------------------------------------------------------------------------
+# E4M3 caches: codes made on the CPU by the oracle's encoder, the same codes in
+# both, attention compared (bar as above)
+# ---------------------------------------------------------------------------
+
+def _fp8_case(w):
+    Hkv = w.num_kv_heads
+    k = oracle.bf16_to_f64(w.key_cache)
+    v = oracle.bf16_to_f64(w.value_cache)
+    ks = (np.abs(k).max(axis=(0, 1, 3)) / 256.0).clip(min=1e-3).astype(np.float32)
+    vs = (np.abs(v).max(axis=(0, 1, 3)) / 256.0).clip(min=1e-3).astype(np.float32)
+    assert ks.shape == (Hkv,)
+    kq = oracle.quantize_fp8(w.key_cache, ks)
+    vq = oracle.quantize_fp8(w.value_cache, vs)
+    return kq, vq, ks, vs
+
+
+def _run_fp8(w, kq, vq, ks, vs):
+    qv = to_dev(w.query_varlen, BF)
+    ql = np.diff(w.cu_seqlens_q)
+    out = gp.paged_attention_varlen_fp8(
+        qv, to_dev(kq, torch.uint8), to_dev(vq, torch.uint8), to_dev(ks, torch.float32),
+        to_dev(vs, torch.float32), to_dev(w.block_tables, torch.int32),
+        to_dev(w.context_lens, torch.int32), to_dev(w.cu_seqlens_q, torch.int32),
+        max_q_len=int(ql.max()), max_context_len=w.max_context_len, scale=float(w.scale))
+    return out.cpu().numpy()
+
+
+FP8_VARLEN_CASES = [
+    # seed, Hq, Hkv, D, bs, ctx, q_lens
+    (721, 28, 4, 128, 16, [900, 33, 2500, 16, 1200, 700], [1, 7, 64, 16, 3, 1]),
+    (722, 4, 1, 64, 16, [0, 1, 15, 17, 40, 5], [3, 1, 15, 2, 40, 9]),
+    (723, 16, 1, 128, 64, [129, 2047, 4100], [16, 1, 130]),
+    (724, 14, 2, 64, 128, [250, 1, 700], [250, 1, 33]),
+]
+
+
+@pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx,ql", FP8_VARLEN_CASES)
+def test_varlen_fp8_random(seed, Hq, Hkv, D, bs, ctx, ql):
+    w = workloads.varlen_case(seed, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                              context_lens=ctx, q_lens=ql)
+    kq, vq, ks, vs = _fp8_case(w)
+    out = _run_fp8(w, kq, vq, ks, vs)
+    ref = oracle.paged_attention_varlen_fp8(w.query_varlen, kq, vq, ks, vs, w.block_tables,
+                                            w.context_lens, w.cu_seqlens_q, w.scale)
+    err = max_abs(out, ref)
+    print(f"seed {seed}: FP8 varlen max-abs {err:.3e}")
+    assert err <= ATOL
+    assert (out[np.all(ref == 0, axis=(1, 2))] == 0).all(), "rows that see nothing are zero"
+
+
+def test_varlen_fp8_single_tokens_equal_fp8_decode():
+    ctx = [900, 33, 2500, 16, 0, 700]
+    w = workloads.varlen_case(725, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
+                              context_lens=ctx, q_lens=[1] * 6)
+    kq, vq, ks, vs = _fp8_case(w)
+    out = _run_fp8(w, kq, vq, ks, vs)
+    dec = gp.paged_attention_decode_fp8(
+        to_dev(w.query_varlen, BF), to_dev(kq, torch.uint8), to_dev(vq, torch.uint8),
+        to_dev(ks, torch.float32), to_dev(vs, torch.float32), to_dev(w.block_tables, torch.int32),
+        to_dev(w.context_lens, torch.int32), max_context_len=w.max_context_len,
+        scale=float(w.scale)).cpu().numpy()
+    assert max_abs(out, dec) <= 1e-5
