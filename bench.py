@@ -91,7 +91,7 @@ def kernel_source_hash(read=None) -> str:
     """Hash of the attention kernels' code (comments and layout ignored): the
     committed counters stay valid across comment-only edits and no longer."""
     h = hashlib.sha256()
-    for f in ("paged_attention.hip", "gpkv_internal.h"):
+    for f in ("paged_attention.hip", "attention.h", "gpkv_internal.h"):
         if read is None:
             with open(os.path.join(ROOT, "gqa_paged_kv_amd", "csrc", f), encoding="utf-8") as fh:
                 text = fh.read()

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgpkv.so")
-SOURCES = ["status.cpp", "reshape_and_cache.hip", "paged_attention.hip", "quest.hip"]
+SOURCES = ["status.cpp", "reshape_and_cache.hip", "paged_attention.hip", "varlen.hip", "quest.hip",
+           "quest_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

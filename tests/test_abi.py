@@ -12,8 +12,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def L():
     from gqa_paged_kv_amd import _lib
     from gqa_paged_kv_amd import build as b
-    srcs = [os.path.join(b.CSRC, s) for s in b.SOURCES] + [os.path.join(b.CSRC, "gpkv_internal.h"),
-                                                          os.path.join(b.INCLUDE, "gpkv.h")]
+    srcs = [os.path.join(b.CSRC, s) for s in b.SOURCES] + \
+        [os.path.join(b.CSRC, h) for h in os.listdir(b.CSRC) if h.endswith(".h")] + \
+        [os.path.join(b.INCLUDE, "gpkv.h")]
     if not os.path.exists(_lib.LIB_PATH) or os.path.getmtime(_lib.LIB_PATH) < max(map(os.path.getmtime, srcs)):
         b.build()
     return _lib.lib()
