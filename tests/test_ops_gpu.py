@@ -521,3 +521,44 @@ def test_quest_topk_fused_path_ties_and_ragged():
     for K in (1, 5, 24, 300):
         _, got, exp = _topk_case(w, K)
         assert np.array_equal(got, exp), K
+
+
+def test_batch_above_balanced_table_uses_split_schedule():
+    """4200 sequences (more than the balanced schedule's 4096-sequence prefix): the
+    dense, sparse, select and one-call Quest paths fall back to their split or
+    two-kernel forms and still match the oracle; multi-token queries refuse the batch
+    with UNSUPPORTED."""
+    rng = np.random.default_rng(909)
+    B = 4200
+    ctx = rng.integers(0, 41, size=B).astype(np.int32)
+    w = workloads.random_case(909, batch=B, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                              block_size=16, context_lens=ctx)
+    d = Dev(w)
+    out = _dense(d, w).cpu().numpy()
+    seqs = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), 0, 1, 4096, 4097, B - 1})
+    ref = oracle.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                                        w.context_lens, w.scale, seqs=seqs)
+    assert max_abs(out[seqs], ref[seqs]) <= ATOL
+    assert (out[ctx == 0] == 0).all()
+    kmin, kmax = _meta(d, w)
+    K = 2
+    sel = gp.quest_select_topk(d.q, kmin, kmax, d.bt, d.ctx, block_size=16, topk_blocks=K,
+                               max_context_len=w.max_context_len)
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+    osel = oracle.quest_select_topk(w.query[seqs], omin, omax, w.block_tables[seqs],
+                                    w.context_lens[seqs], 16, K)
+    assert np.array_equal(sel.cpu().numpy()[seqs], osel)
+    sp = _sparse(d, w, sel).cpu().numpy()
+    oref = oracle.sparse_paged_attention_decode(w.query[seqs], w.key_cache, w.value_cache,
+                                                w.block_tables[seqs], w.context_lens[seqs], osel,
+                                                w.scale)
+    assert max_abs(sp[seqs], oref) <= ATOL
+    qd_out, qd_sel = gp.quest_decode(d.q, d.kc, d.vc, kmin, kmax, d.bt, d.ctx, topk_blocks=K,
+                                     max_context_len=w.max_context_len, scale=float(w.scale))
+    assert torch.equal(qd_sel, sel)
+    assert max_abs(qd_out.cpu().numpy()[seqs], oref) <= ATOL
+    cu = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(gp.GpkvError) as exc:
+        gp.paged_attention_varlen(d.q, d.kc, d.vc, d.bt, d.ctx, cu, max_q_len=1,
+                                  max_context_len=w.max_context_len, scale=float(w.scale))
+    assert exc.value.status == -3
