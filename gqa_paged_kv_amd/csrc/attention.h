@@ -394,6 +394,45 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
   }
 }
 
+// Merge of n partial rows (one float4 column of each): row k has base-2 lse
+// lse0[k * ls] and normalised output o0[k * os]; live(k) false skips a row. Returns
+// sum_k 2^(lse_k - M) O_k / sum_k 2^(lse_k - M) (zeros when no row holds a token).
+// NU rows (lse and output) are requested together, and the sum is kept relative
+// to the largest lse seen so far, so up to NU rows cost one round of loads.
+template <int NU, class Live>
+__device__ __forceinline__ f32x4 merge_rows(int n, const float* lse0, size_t ls, const float* o0,
+                                            size_t os, const Live& live) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float W = 0.f, mr = -INFINITY;   // acc and W are relative to mr (-inf: nothing yet)
+  for (int k0 = 0; k0 < n; k0 += NU) {
+    float l[NU];
+    f32x4 v[NU];
+#pragma unroll
+    for (int x = 0; x < NU; ++x) {
+      const int k = k0 + x;
+      const bool ok = k < n && live(k);
+      l[x] = ok ? lse0[(size_t)k * ls] : -INFINITY;
+      v[x] = ok ? *(const f32x4*)(o0 + (size_t)k * os) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float m = mr;
+#pragma unroll
+    for (int x = 0; x < NU; ++x) m = fmaxf(m, l[x]);
+    if (m == -INFINITY) continue;
+    const float s = __builtin_amdgcn_exp2f(mr - m);   // 0 when mr = -inf
+    W *= s;
+    acc *= s;
+    mr = m;
+#pragma unroll
+    for (int x = 0; x < NU; ++x) {
+      const float w = __builtin_amdgcn_exp2f(l[x] - m);   // 0 for skipped rows
+      W += w;
+      acc += w * v[x];
+    }
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  return acc * inv;
+}
+
 __device__ __forceinline__ int clamp_ctx(int v, int max_ctx) {
   return v < 0 ? 0 : (v > max_ctx ? max_ctx : v);
 }

@@ -434,7 +434,10 @@ __device__ __forceinline__ UnitRange unit_range(const CombineParams& p, int b, i
 
 // Few units per sequence: one workgroup per (sequence, KV head); each group of
 // D/4 threads (a "slot") owns query heads hl, hl + slots, ... of the group and
-// merges that head's units on its own, without barriers.
+// merges that head's units on its own, without barriers: up to kHeadUnits unit
+// rows in one round of loads after the prefix.
+constexpr int kHeadUnits = 12;
+
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_heads_kernel(const CombineParams p) {
   constexpr int TPU = D / 4;
@@ -443,38 +446,11 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_heads_kernel(con
   const int slot = tid / TPU, c4 = tid % TPU;
   for (int hl = slot; hl < p.G; hl += SLOTS) {
     const UnitRange r = unit_range<D>(p, b, g, hl);
-    float M = -INFINITY;
-    for (int u = r.u_begin; u < r.u_end; ++u)
-      if (r.live(u)) M = fmaxf(M, r.lse0[(size_t)u * r.lstride]);
-    const float Mr = (M == -INFINITY) ? 0.f : M;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float W = 0.f;
-    int u = r.u_begin;
-    for (; u + 3 < r.u_end; u += 4) {
-      float l[4];
-      f32x4 v[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const bool ok = r.live(u + k);
-        l[k] = ok ? r.lse0[(size_t)(u + k) * r.lstride] : -INFINITY;
-        v[k] = ok ? *(const f32x4*)(r.o0 + (size_t)(u + k) * r.ostride + 4 * c4)
-                  : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float w = __builtin_amdgcn_exp2f(l[k] - Mr);
-        W += w;
-        acc += w * v[k];
-      }
-    }
-    for (; u < r.u_end; ++u) {
-      if (!r.live(u)) continue;
-      const float w = __builtin_amdgcn_exp2f(r.lse0[(size_t)u * r.lstride] - Mr);
-      W += w;
-      acc += w * *(const f32x4*)(r.o0 + (size_t)u * r.ostride + 4 * c4);
-    }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    *(f32x4*)(p.out + ((size_t)b * p.Hq + (size_t)g * p.G + hl) * D + 4 * c4) = acc * inv;
+    const int u0 = r.u_begin;
+    const f32x4 o = merge_rows<kHeadUnits>(
+        r.u_end - u0, r.lse0 + (size_t)u0 * r.lstride, r.lstride,
+        r.o0 + (size_t)u0 * r.ostride + 4 * c4, r.ostride, [&](int k) { return r.live(u0 + k); });
+    *(f32x4*)(p.out + ((size_t)b * p.Hq + (size_t)g * p.G + hl) * D + 4 * c4) = o;
   }
 }
 
@@ -500,59 +476,59 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
   const size_t lstride = r.lstride, ostride = r.ostride;
   auto live = [&](int u) { return r.live(u); };
 
-  // Common maximum of the units' lse.
-  const int lane = tid & 63, wave = tid >> 6;
-  float M = -INFINITY;
-  for (int u = u_begin + tid; u < u_end; u += kCombineThreads)
-    if (live(u)) M = fmaxf(M, lse0[(size_t)u * lstride]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) s_red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  const float Mr = (M == -INFINITY) ? 0.f : M;
-
-  // Weighted sum: thread (unit slot us, float4 column c4) walks units us, us+UPP,
-  // ..., eight loads in flight at a time.
+  // Thread (unit slot us, float4 column c4) walks units us, us+UPP, ..., eight
+  // unit rows (lse and output) requested at once, and keeps its sum relative to
+  // the largest lse it has seen (mr, -inf while it has seen only empty units); the
+  // slots then meet in LDS under their common maximum. With up to 8*UPP units this
+  // is one round of loads after the prefix.
   constexpr int UNROLL = 8;
   const int us = tid / TPU, c4 = tid % TPU;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float W = 0.f;
-  int u = u_begin + us;
-  for (; u + (UNROLL - 1) * UPP < u_end; u += UNROLL * UPP) {
+  float W = 0.f, mr = -INFINITY;
+  for (int u = u_begin + us; u < u_end; u += UNROLL * UPP) {
     float l[UNROLL];
     f32x4 v[UNROLL];
 #pragma unroll
     for (int k = 0; k < UNROLL; ++k) {
       const int uu = u + k * UPP;
-      const bool ok = live(uu);
+      const bool ok = uu < u_end && live(uu);
       l[k] = ok ? lse0[(size_t)uu * lstride] : -INFINITY;
       v[k] = ok ? *(const f32x4*)(o0 + (size_t)uu * ostride + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    float m = mr;
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) m = fmaxf(m, l[k]);
+    if (m == -INFINITY) continue;           // nothing valid yet
+    const float s = __builtin_amdgcn_exp2f(mr - m);   // 0 when mr = -inf
+    W *= s;
+    acc *= s;
+    mr = m;
 #pragma unroll
     for (int k = 0; k < UNROLL; ++k) {
-      const float w = __builtin_amdgcn_exp2f(l[k] - Mr);
+      const float w = __builtin_amdgcn_exp2f(l[k] - m);
       W += w;
       acc += w * v[k];
     }
   }
-  for (; u < u_end; u += UPP) {
-    if (!live(u)) continue;
-    const float w = __builtin_amdgcn_exp2f(lse0[(size_t)u * lstride] - Mr);
-    W += w;
-    acc += w * *(const f32x4*)(o0 + (size_t)u * ostride + 4 * c4);
-  }
-  __syncthreads();  // s_red is reused below
   s_acc[us][c4] = acc;
-  if (c4 == 0) s_red[us] = W;
+  if (c4 == 0) {
+    s_red[us] = W;
+    s_red[UPP + us] = mr;
+  }
   __syncthreads();
   if (tid < TPU) {
-    f32x4 a = s_acc[0][tid];
-    float wt = s_red[0];
+    float M = -INFINITY;
 #pragma unroll
-    for (int k = 1; k < UPP; ++k) {
-      a += s_acc[k][tid];
-      wt += s_red[k];
+    for (int k = 0; k < UPP; ++k) M = fmaxf(M, s_red[UPP + k]);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    float wt = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < UPP; ++k) {
+        const float sk = __builtin_amdgcn_exp2f(s_red[UPP + k] - M);   // 0 for empty slots
+        a += sk * s_acc[k][tid];
+        wt += sk * s_red[k];
+      }
     }
     const float inv = wt > 0.f ? 1.f / wt : 0.f;
     *(f32x4*)(out + 4 * tid) = a * inv;

@@ -425,36 +425,9 @@ __global__ __launch_bounds__(kCombineThreads) void attn_varlen_combine_kernel(co
       const int rr = i / TPR, c4 = i - (i / TPR) * TPR;
       const float* lse0 = p.part_lse + unit0 * 16 + rr;
       const float* o0 = p.part_o + (unit0 * 16 + rr) * D + 4 * c4;
-      float M = -INFINITY;
-      for (int k = 0; k < n_units; ++k) M = fmaxf(M, lse0[(size_t)k * 16]);
-      const float Mr = (M == -INFINITY) ? 0.f : M;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      float W = 0.f;
-      int k = 0;
-      for (; k + 3 < n_units; k += 4) {   // four splits' rows in flight
-        float l[4];
-        f32x4 v[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          l[x] = lse0[(size_t)(k + x) * 16];
-          v[x] = *(const f32x4*)(o0 + (size_t)(k + x) * 16 * D);
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float w = __builtin_amdgcn_exp2f(l[x] - Mr);
-          W += w;
-          acc += w * v[x];
-        }
-      }
-      for (; k < n_units; ++k) {
-        const float w = __builtin_amdgcn_exp2f(lse0[(size_t)k * 16] - Mr);
-        W += w;
-        acc += w * *(const f32x4*)(o0 + (size_t)k * 16 * D);
-      }
-      const float inv = W > 0.f ? 1.f / W : 0.f;
+      const f32x4 o = merge_rows<8>(n_units, lse0, 16, o0, (size_t)16 * D, [](int) { return true; });
       const int m = m0 + rr, j = m / G;
-      *(f32x4*)(p.out + ((size_t)(q0 + j) * Hq + (size_t)g * G + (m - j * G)) * D + 4 * c4) =
-          acc * inv;
+      *(f32x4*)(p.out + ((size_t)(q0 + j) * Hq + (size_t)g * G + (m - j * G)) * D + 4 * c4) = o;
     }
   }
 }
