@@ -441,12 +441,7 @@ __device__ __forceinline__ int clamp_ctx(int v, int max_ctx) {
 // Exclusive prefix sum over the workgroup's 256 threads; *total gets the sum.
 __device__ __forceinline__ int wg_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
+  const int inc = (int)wave_inclusive_scan((unsigned)v);
   if (lane == 63) s_wave[wave] = inc;
   __syncthreads();
   int off = 0, tot = 0;
@@ -463,8 +458,6 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* s_wave, int* total)
 
 // Host side, defined in paged_attention.hip.
 size_t align256(size_t x);
-// Workgroups of the balanced schedule on the current device: one per compute unit.
-int balanced_capacity();
 // Argument checks every attention entry point shares (status, message set).
 int check_common(const char* fn, int B, int Hq, int Hkv, int D, int bs, long long NB,
                  int max_blocks, int max_ctx);

@@ -18,6 +18,9 @@ int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)))
 void clear_error();
 // Maps hipGetLastError() after a launch to GPKV_OK / GPKV_ERR_HIP.
 int check_launch(const char* what);
+// Compute units of the current device (defined in paged_attention.hip): the
+// balanced attention schedule runs one workgroup per CU.
+int balanced_capacity();
 
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
 inline bool supported_block_size(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
@@ -114,5 +117,39 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Cross-lane steps on DPP (a VALU operand modifier, a few cycles) rather than
+// LDS permutes: row_shr:n moves lane i - n of the same 16-lane row into lane i,
+// and a lane whose source falls outside its row reads 0 (bound_ctrl).
+template <int N>
+__device__ __forceinline__ unsigned row_shr_zero(unsigned v) {
+  static_assert(N >= 1 && N <= 15, "row_shr takes 1..15");
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x110 + N, 0xF, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active): a
+// Hillis-Steele scan inside each 16-lane row, then the totals of the rows below
+// (lanes 15, 31, 47) added from scalar registers.
+__device__ __forceinline__ unsigned wave_inclusive_scan(unsigned v) {
+  v += row_shr_zero<1>(v);
+  v += row_shr_zero<2>(v);
+  v += row_shr_zero<4>(v);
+  v += row_shr_zero<8>(v);
+  const unsigned r0 = (unsigned)__builtin_amdgcn_readlane((int)v, 15);
+  const unsigned r1 = (unsigned)__builtin_amdgcn_readlane((int)v, 31);
+  const unsigned r2 = (unsigned)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Bitwise OR over the 64 lanes of a wave (every lane active), the same in all lanes.
+__device__ __forceinline__ unsigned wave_or(unsigned v) {
+  v |= row_shr_zero<1>(v);
+  v |= row_shr_zero<2>(v);
+  v |= row_shr_zero<4>(v);
+  v |= row_shr_zero<8>(v);   // lane 15 of each row now holds the row's OR
+  return (unsigned)(__builtin_amdgcn_readlane((int)v, 15) | __builtin_amdgcn_readlane((int)v, 31) |
+                    __builtin_amdgcn_readlane((int)v, 47) | __builtin_amdgcn_readlane((int)v, 63));
+}
 
 }  // namespace gpkv

@@ -224,7 +224,7 @@ struct TopkParams {
   int Hkv, bs, max_blocks, max_ctx, K, lds_keys;
 };
 
-__global__ __launch_bounds__(kSelectThreads) void quest_topk_kernel(const TopkParams p) {
+__global__ __launch_bounds__(kMaxSelectThreads) void quest_topk_kernel(const TopkParams p) {
   extern __shared__ unsigned long long s_key[];
   __shared__ SelectShared sh;
   const int g = blockIdx.x, b = blockIdx.y;
@@ -257,14 +257,16 @@ __global__ __launch_bounds__(kFusedThreads) void quest_select_fused_kernel(const
   int ctx = p.ctx[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
   const int nb = (ctx + p.bs - 1) / p.bs;
+  // One round of loads for the query group and the block-table row up to the
+  // longest context (max_nb <= max_blocks: in bounds), issued without waiting for
+  // this sequence's length, so the metadata loads below depend on LDS only.
+  const int max_nb = (p.max_ctx + p.bs - 1) / p.bs;
+  int* s_pb = (int*)(s_key + max_nb);
+  stage_query<D>(p, b, g * p.G, p.G, s_q);
+  for (int lb = threadIdx.x; lb < max_nb; lb += blockDim.x)
+    s_pb[lb] = p.bt[(size_t)b * p.max_blocks + lb];
   int* out = p.out + ((size_t)b * p.Hkv + g) * p.K;
   if (select_all(nb, p.K, out)) return;
-  int* s_pb = (int*)(s_key + nb);
-  // One round of loads for the query group and the whole block-table row, so the
-  // metadata loads below depend on LDS only.
-  stage_query<D>(p, b, g * p.G, p.G, s_q);
-  for (int lb = threadIdx.x; lb < nb; lb += blockDim.x)
-    s_pb[lb] = p.bt[(size_t)b * p.max_blocks + lb];
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += blockDim.x)
     group_bounds<D>(s_q, p.G, c, s_pos + qb_index<D>(c), s_neg + qb_index<D>(c));
@@ -436,6 +438,13 @@ extern "C" int gpkv_quest_select_topk(int32_t* topk_indices, const void* query,
   tp.K = topk_blocks;
   tp.lds_keys = max_nb <= kMaxLdsKeys ? max_nb : 0;
   const size_t lds = (size_t)(tp.lds_keys > 0 ? tp.lds_keys : 1) * sizeof(unsigned long long);
-  quest_topk_kernel<<<dim3(num_kv_heads, batch), dim3(kSelectThreads), lds, s>>>(tp);
+  // Few (sequence, KV head) pairs leave most CUs idle: give each pair's select up
+  // to 1024 threads (about two keys each) so its radix passes are shorter.
+  int topk_threads = kSelectThreads;
+  const long long topk_pairs = (long long)batch * num_kv_heads;
+  while (topk_threads < kMaxSelectThreads && topk_pairs * 4 <= balanced_capacity() &&
+         2 * topk_threads <= max_nb)
+    topk_threads <<= 1;
+  quest_topk_kernel<<<dim3(num_kv_heads, batch), dim3(topk_threads), lds, s>>>(tp);
   return check_launch(fn);
 }

@@ -52,10 +52,13 @@ __global__ __launch_bounds__(kFusedThreads) void quest_decode_fused_kernel(const
   float* s_o = (float*)(s_pb + ((p.max_nb + 3) & ~3));
   int* out_ids = sp.out + ((size_t)b * sp.Hkv + g) * K;
 
-  // Selection (as quest_select_fused_kernel, into LDS).
-  for (int lb = tid; lb < nb; lb += kFusedThreads) s_pb[lb] = sp.bt[(size_t)b * sp.max_blocks + lb];
+  // Selection (as quest_select_fused_kernel, into LDS). The table row is staged
+  // up to the longest context and the query group unconditionally, so neither
+  // waits for this sequence's length (max_nb <= max_blocks: in bounds).
+  for (int lb = tid; lb < p.max_nb; lb += kFusedThreads)
+    s_pb[lb] = sp.bt[(size_t)b * sp.max_blocks + lb];
   const bool all = K >= nb;
-  if (!all) stage_query<D>(sp, b, g * G, G, s_q);
+  stage_query<D>(sp, b, g * G, G, s_q);
   __syncthreads();
   if (all) {
     for (int i = tid; i < K; i += kFusedThreads) {

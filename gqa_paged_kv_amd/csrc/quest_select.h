@@ -161,12 +161,7 @@ __device__ __forceinline__ void score_blocks(const ScoreParams& p, int g, int nb
 // Exclusive prefix sum of v over the workgroup's threads; *total receives the sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
+  const int inc = (int)wave_inclusive_scan((unsigned)v);
   if (lane == 63) s_wave[wave] = inc;
   __syncthreads();
   int off = 0, tot = 0;
@@ -180,11 +175,14 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
   return off + inc - v;
 }
 
+// Histogram and pass result are double-buffered: pass i uses buffer i & 1 and
+// clears the other one for pass i + 1, so a pass needs two barriers (histogram
+// complete; bucket found) and no barrier to clear or to retire what it read.
 struct SelectShared {
-  unsigned hist[256];
+  unsigned hist[2][256];
   int wave_sums[kMaxSelectThreads / 64];
-  unsigned long long red_and[kMaxSelectThreads / 64], red_or[kMaxSelectThreads / 64];
-  int digit, above, cnt;
+  unsigned long long red_or[kMaxSelectThreads / 64];
+  int digit[2], above[2], cnt[2];
 };
 
 // Writes the ascending ids of the K largest keys among key_at(0..n-1) (K < n) to
@@ -195,75 +193,58 @@ __device__ void radix_topk(int n, int K, const KeyAt& key_at, int* out, SelectSh
   const int tid = threadIdx.x, nt = blockDim.x;
   const int C = (n + nt - 1) / nt;
   const int i0 = min(n, tid * C), i1 = min(n, i0 + C);
-  if (tid == 0) {
-    sh.digit = 0;
-    sh.above = 0;
-    sh.cnt = 0;
+  for (int d = tid; d < 2 * 256; d += nt) (&sh.hist[0][0])[d] = 0;
+  if (tid < 2) {
+    sh.digit[tid] = 0;
+    sh.above[tid] = 0;
+    sh.cnt[tid] = 0;
   }
-  // Bits every key shares need no pass: start at the highest bit where keys differ.
-  unsigned long long k_and = ~0ull, k_or = 0ull;
-  for (int i = i0; i < i1; ++i) {
-    const unsigned long long key = key_at(i);
-    k_and &= key;
-    k_or |= key;
-  }
-  for (int o = 32; o >= 1; o >>= 1) {
-    const unsigned long long a = ((unsigned long long)__shfl_xor((unsigned)(k_and >> 32), o) << 32) |
-                                 (unsigned)__shfl_xor((unsigned)k_and, o);
-    const unsigned long long b = ((unsigned long long)__shfl_xor((unsigned)(k_or >> 32), o) << 32) |
-                                 (unsigned)__shfl_xor((unsigned)k_or, o);
-    k_and &= a;
-    k_or |= b;
-  }
-  if ((tid & 63) == 0) {
-    sh.red_and[tid >> 6] = k_and;
-    sh.red_or[tid >> 6] = k_or;
-  }
+  // Bits every key shares need no pass: start at the highest bit where some key
+  // differs from key 0 (so where keys differ at all).
+  const unsigned long long k_ref = key_at(0);
+  unsigned long long k_diff = 0ull;
+  for (int i = i0; i < i1; ++i) k_diff |= key_at(i) ^ k_ref;
+  k_diff = ((unsigned long long)wave_or((unsigned)(k_diff >> 32)) << 32) | wave_or((unsigned)k_diff);
+  if ((tid & 63) == 0) sh.red_or[tid >> 6] = k_diff;
   __syncthreads();
-  k_and = ~0ull;
-  k_or = 0ull;
-  for (int w = 0; w < (nt >> 6); ++w) {
-    k_and &= sh.red_and[w];
-    k_or |= sh.red_or[w];
-  }
-  const unsigned long long diff = k_and ^ k_or;
+  unsigned long long diff = 0ull;
+  for (int w = 0; w < (nt >> 6); ++w) diff |= sh.red_or[w];
   const int top = diff ? 63 - __clzll((long long)diff) : -1;   // highest differing bit
   unsigned long long mask = top >= 63 ? 0ull : (~0ull << (top + 1));
-  unsigned long long prefix = k_and & mask;
+  unsigned long long prefix = k_ref & mask;
   int need = K, shift = 0;
+  bool whole = false;   // the last bucket is taken entirely (no tie to break)
   for (int pass = 0; top >= 0 && pass < 8; ++pass) {
+    const int buf = pass & 1;
     shift = top - 7 - 8 * pass;
     if (shift < 0) shift = 0;
-    for (int d = tid; d < 256; d += nt) sh.hist[d] = 0;
-    __syncthreads();
+    // hist[buf] was cleared before the previous pass's first barrier (or before
+    // the reduction's barrier above); hist[buf ^ 1] was last read by the previous
+    // pass's bucket search, which every thread has passed.
     for (int i = i0; i < i1; ++i) {
       const unsigned long long key = key_at(i);
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255], 1u);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[buf][(key >> shift) & 255], 1u);
     }
+    for (int d = tid; d < 256; d += nt) sh.hist[buf ^ 1][d] = 0;
     __syncthreads();
     if (tid < 64) {
       // lane l owns digits 255-4l .. 252-4l (descending order of keys)
       unsigned c[4], t = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        c[k] = sh.hist[255 - 4 * tid - k];
+        c[k] = sh.hist[buf][255 - 4 * tid - k];
         t += c[k];
       }
-      unsigned inc = t;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned x = __shfl_up(inc, o);
-        if (tid >= o) inc += x;
-      }
+      const unsigned inc = wave_inclusive_scan(t);
       const unsigned excl = inc - t;
       if (excl < (unsigned)need && (unsigned)need <= inc) {
         unsigned above = excl;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           if (above + c[k] >= (unsigned)need) {
-            sh.digit = 255 - 4 * tid - k;
-            sh.above = (int)above;
-            sh.cnt = (int)c[k];
+            sh.digit[buf] = 255 - 4 * tid - k;
+            sh.above[buf] = (int)above;
+            sh.cnt[buf] = (int)c[k];
             break;
           }
           above += c[k];
@@ -271,21 +252,27 @@ __device__ void radix_topk(int n, int K, const KeyAt& key_at, int* out, SelectSh
       }
     }
     __syncthreads();
-    const int digit = sh.digit, above = sh.above, cnt = sh.cnt;
+    // The next write of this buffer's result is two passes on, after a barrier
+    // that every thread reaches only once it has read these.
+    const int digit = sh.digit[buf], above = sh.above[buf], cnt = sh.cnt[buf];
     need -= above;
     prefix |= (unsigned long long)digit << shift;
     mask |= 0xFFull << shift;
-    __syncthreads();
-    if (cnt == need || shift == 0) break;  // bucket fully selected, or every bit resolved
+    whole = cnt == need;
+    if (whole || shift == 0) break;  // bucket fully selected, or every bit resolved
   }
 
   // Selected: keys above the resolved prefix, plus the first `need` (by index)
-  // of those equal to it.
+  // of those equal to it (all of them when the bucket is taken whole: then no
+  // rank among equal keys is needed, and one scan is saved).
   const unsigned long long ref = prefix >> shift;
-  int n_eq = 0;
-  for (int i = i0; i < i1; ++i) n_eq += (key_at(i) >> shift) == ref;
-  int tot;
-  int rank = block_exclusive_scan(n_eq, sh.wave_sums, &tot);
+  int n_eq = 0, rank = 0, tot;
+  if (whole) {
+    need = n;
+  } else {
+    for (int i = i0; i < i1; ++i) n_eq += (key_at(i) >> shift) == ref;
+    rank = block_exclusive_scan(n_eq, sh.wave_sums, &tot);
+  }
   int n_sel = 0;
   for (int i = i0; i < i1; ++i) {
     const unsigned long long k = key_at(i) >> shift;
