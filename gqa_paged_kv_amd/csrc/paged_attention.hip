@@ -205,23 +205,34 @@ __global__ __launch_bounds__(kWaves * 64) void attn_balanced_kernel(const BalPar
       for (int i = tid; i < Hkv * n_ent; i += kWaves * 64) s_pb[i] = -1;
       __syncthreads();
       // Compaction of each head's list, 64 entries per step: a valid entry's
-      // position is the number of valid entries before it.
+      // position is the number of valid entries before it. Four steps' entries
+      // are requested at once, so a share deep in a long list waits for one
+      // round of list loads rather than one per 64 entries.
+      constexpr int kListSteps = 4;
       for (int g = wave; g < Hkv; g += kWaves) {
         const int* lst = p.topk + ((size_t)b * Hkv + g) * p.topk_blocks;
         int run = 0;
-        for (int c0 = 0; c0 < p.topk_blocks && run < e0 + n_ent; c0 += 64) {
-          const int e = c0 + lane;
-          const int id = e < p.topk_blocks ? lst[e] : -1;
-          const bool valid = id >= 0 && id < nb;
-          const unsigned long long m = __ballot(valid);
-          const int pos = run + __popcll(m & ((1ull << lane) - 1ull));
-          if (valid && pos >= e0 && pos < e0 + n_ent) {
-            const int pb = p.block_tables[(size_t)b * p.max_blocks + id];
-            const int i = g * n_ent + (pos - e0);
-            s_pb[i] = (pb >= 0 && pb < p.NB) ? pb : -1;
-            s_tok0[i] = id * bs;
+        for (int c0 = 0; c0 < p.topk_blocks && run < e0 + n_ent; c0 += 64 * kListSteps) {
+          int ids[kListSteps];
+#pragma unroll
+          for (int j = 0; j < kListSteps; ++j) {
+            const int e = c0 + 64 * j + lane;
+            ids[j] = e < p.topk_blocks ? lst[e] : -1;
           }
-          run += __popcll(m);
+#pragma unroll
+          for (int j = 0; j < kListSteps; ++j) {
+            const int id = ids[j];
+            const bool valid = id >= 0 && id < nb;
+            const unsigned long long m = __ballot(valid);
+            const int pos = run + __popcll(m & ((1ull << lane) - 1ull));
+            if (valid && pos >= e0 && pos < e0 + n_ent) {
+              const int pb = p.block_tables[(size_t)b * p.max_blocks + id];
+              const int i = g * n_ent + (pos - e0);
+              s_pb[i] = (pb >= 0 && pb < p.NB) ? pb : -1;
+              s_tok0[i] = id * bs;
+            }
+            run += __popcll(m);
+          }
         }
       }
     }
