@@ -310,8 +310,7 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
       float mx = sv[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_across_rows(mx);
       const float m_new = fmaxf(m_run[t], mx);
       const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_ref);
@@ -374,8 +373,7 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
   // The unit's result per row tile: normalised output and base-2 log-sum-exp.
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
-    float l_tot = l_run[t] + __shfl_xor(l_run[t], 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = sum_across_rows(l_run[t]);
     if (r < rows.n_rows[t]) {
       const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
       float* dst = rows.o[t] + (size_t)r * D + CPL * 4 * qd;

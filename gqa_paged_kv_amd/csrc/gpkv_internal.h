@@ -118,6 +118,23 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Reductions over the four 16-lane rows of a wave (lanes r, r + 16, r + 32, r + 48
+// all receive the result, bit-identical): gfx950's permlane swaps exchange rows
+// 1 and 3 of one copy with rows 0 and 2 of another (16), and the upper half of one
+// with the lower half of the other (32), in VALU with no LDS round trip.
+__device__ __forceinline__ float max_across_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_across_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Cross-lane steps on DPP (a VALU operand modifier, a few cycles) rather than
 // LDS permutes: row_shr:n moves lane i - n of the same 16-lane row into lane i,
 // and a lane whose source falls outside its row reads 0 (bound_ctrl).
