@@ -523,6 +523,28 @@ def test_quest_topk_fused_path_ties_and_ragged():
         assert np.array_equal(got, exp), K
 
 
+@pytest.mark.parametrize("ctx,Hkv", [([110000], 2), ([9000, 700, 20000], 1)])
+def test_quest_topk_few_pairs_long_tables(ctx, Hkv, monkeypatch):
+    """Few (sequence, KV head) pairs over long tables: the two-kernel select gives each
+    pair up to 1024 threads, and a table longer than the select's LDS key buffer (6144
+    keys) is ranked from the stored keys; an exact tie is planted in the first
+    sequence, and K spans one block, a few hundred and more than half the table."""
+    monkeypatch.setenv("GPKV_QUEST_SELECT_PATH", "two_kernel")
+    w = workloads.random_case(360 + len(ctx), batch=len(ctx), num_q_heads=4 * Hkv,
+                              num_kv_heads=Hkv, head_dim=128, block_size=16, context_lens=ctx)
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+    s = oracle.quest_block_scores(w.query, omin, omax, w.block_tables, w.context_lens, 16, 0, 0)
+    a = int(np.argmax(s))
+    later = int(s.size - 1 if a != s.size - 1 else s.size - 2)
+    kc = w.key_cache.copy()
+    kc[int(w.block_tables[0, later])] = kc[int(w.block_tables[0, a])]
+    w.key_cache = kc
+    nb0 = (ctx[0] + 15) // 16
+    for K in (1, 300, nb0 // 2 + 7):
+        _, got, exp = _topk_case(w, K)
+        assert np.array_equal(got, exp), K
+
+
 def test_batch_above_balanced_table_uses_split_schedule():
     """4200 sequences (more than the balanced schedule's 4096-sequence prefix): the
     dense, sparse, select and one-call Quest paths fall back to their split or
