@@ -22,7 +22,7 @@ Sources (page title, section):
   [TL18] TileLang tutorial ch. 18 (end-to-end inference serving) -- sections 2.4
          (KV cache structure), 2.6 (paged KV), 4.1 (decode attention / split-KV).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   R1 cache layout [NB, block_size, H_kv, D] for K and V ([TL18] 2.6).
   R2 query head h uses KV head h // (H_q / H_kv) (contiguous groups).
   R3 scores are scale * q.k with scale passed in (1/sqrt(D) in every workload).

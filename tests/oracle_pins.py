@@ -64,7 +64,8 @@ def pin_write_hand_worked(orc):
 
 
 def pin_write_config1(orc):
-    """Config 1: token 0 goes to (seq 0, position 36) -> logical block 2, row 4;
+    """The tiny workload (contexts 37 and 80, block size 16): token 0 goes to
+    (seq 0, position 36) -> logical block 2, row 4;
     token 1 has slot -1 and changes nothing. Every other byte is untouched."""
     w = workloads.make(1)
     k2, v2 = orc.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,

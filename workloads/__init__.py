@@ -13,11 +13,16 @@ shape: 28 query heads, 4 KV heads, head_dim 128 -- TileLang tutorial ch. 18,
 sections 2.4-2.6) and the problem statement of the Ascend kernel-to-serving write-up
 (sections "ReshapeAndCache", "GQA Paged Attention", "Quest Sparse Attention",
 "extreme sequence length"). Where the pages give no distribution, the recipe below
-is our own choice; it is fixed by the seed and documented per config.
+is our own choice; it is fixed by the seed and documented per workload.
 
-Draw order for every config (one ``numpy.random.default_rng(seed)`` stream):
+Workloads by number: 1 tiny GQA decode (B = 2, contexts 37 and 80); 2 Qwen-shaped
+dense decode (B = 32, block size 128); 3 the ~8K-average ragged batch, dense vs Quest
+(B = 64, block size 16); 4 four 40960-token sequences; 5 a ragged 256-sequence batch
+with 8 KV heads.
+
+Draw order for every workload (one ``numpy.random.default_rng(seed)`` stream):
   1. context_lens  2. block permutation  3. pool K / V  4. query
-  5. new K / V and slot_mapping  6. Quest key offsets (config 3 only)
+  5. new K / V and slot_mapping  6. Quest key offsets (the 8K-average batch only)
 """
 from __future__ import annotations
 
@@ -126,7 +131,7 @@ def _slots_at_last_position(ctx, bt, bs, skip=None) -> np.ndarray:
 
 
 def make(config: int, seed: int | None = None) -> Workload:
-    """Build config 1..5 with ``seed`` (default: the config number)."""
+    """Build workload 1..5 (see the module docstring) with ``seed`` (default: its number)."""
     if seed is None:
         seed = config
     rng = np.random.default_rng(seed)
