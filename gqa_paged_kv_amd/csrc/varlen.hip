@@ -68,7 +68,10 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
     for (int i = 0; i < PER_T; ++i) {
       const int pc = tid + i * kWaves * 64;
       const int tok = pc / PIECES, piece = pc - tok * PIECES;
-      const int u = 2 * k + (tok >> 4);
+      // The same sub-tile for every lane of the wave (see above): readfirstlane makes
+      // that visible to the compiler, so the buffer descriptor sits in scalar
+      // registers instead of a per-lane waterfall loop around each load.
+      const int u = uniform(2 * k + (tok >> 4));
       int pb = 0, row0 = 0, nv = 0;
       if (u < n_sub) desc(u, pb, row0, nv);
       const size_t base = (size_t)pb * (size_t)c.block_bytes + (size_t)row0 * c.row_bytes;
