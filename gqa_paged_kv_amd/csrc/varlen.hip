@@ -299,6 +299,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
+  const int bs_log2 = __builtin_ctz((unsigned)bs);
   const int T = p.split_tokens;
   auto n_tiles_of = [&](int qn) { return (qn * G + 15) / 16; };
   auto n_groups = [&](int qn) { return (n_tiles_of(qn) + RT - 1) / RT; };
@@ -341,8 +342,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
     tile_lim = tile_lim < 0 ? 0 : (tile_lim > ctx ? ctx : tile_lim);
     const int t0 = split * T;
     if (t0 >= tile_lim) continue;   // uniform: the combine counts only the splits a tile sees
-    const int e0 = t0 / bs;
-    const int n_ent = T / bs;
+    const int e0 = t0 >> bs_log2;
+    const int n_ent = T >> bs_log2;
     const int nb = (ctx + bs - 1) / bs;
     __syncthreads();                // the previous unit's table is no longer read
     for (int e = tid; e < n_ent; e += kWaves * 64) {
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
     const int span = tile_lim - t0 < T ? tile_lim - t0 : T;
     auto desc = [&](int uu, int& pb, int& row0, int& nv) {
       const int tok = t0 + 16 * uu;
-      const int x = s_pb[tok / bs - e0];
+      const int x = s_pb[(tok >> bs_log2) - e0];   // bs is a power of two: no division
       row0 = tok & (bs - 1);
       int n = t0 + span - tok;
       n = n < 0 ? 0 : (n > 16 ? 16 : n);
