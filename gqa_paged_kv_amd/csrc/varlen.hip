@@ -40,6 +40,10 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
   const int tid = threadIdx.x, lane = tid & 63;
   const int r = lane & 15, qd = lane >> 4;
   const bool active = rows.n_rows[0] > 0;   // the wave's second tile is empty if its first is
+  // Causal bounds grow with the row, so row 0 of the first tile (lane 0) has the
+  // smallest: a tile whose positions all lie below it, with every row of both
+  // sub-tiles valid, needs no mask.
+  const int lim_min = __builtin_amdgcn_readfirstlane(rows.limit[0]);
 
   u32x4 qf[RT][KSTEPS];
 #pragma unroll
@@ -124,18 +128,24 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
         }
       }
       u32x4 phi[RT], plo[RT];
+      const bool full = nv[0] == 16 && nv[1] == 16 && pos0 + 32 * k + 32 <= lim_min;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         float sv[8];
+        if (full) {
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+          for (int j = 0; j < 8; ++j) sv[j] = sacc[t][j >> 2][j & 3] * c.qk_scale_log2;
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = sacc[t][sub][i] * c.qk_scale_log2;
-            const bool ok = 4 * qd + i < nv[sub] &&
-                            pos0 + 16 * (2 * k + sub) + 4 * qd + i < rows.limit[t];
-            sv[sub * 4 + i] = ok ? x : -INFINITY;
-          }
+          for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = sacc[t][sub][i] * c.qk_scale_log2;
+              const bool ok = 4 * qd + i < nv[sub] &&
+                              pos0 + 16 * (2 * k + sub) + 4 * qd + i < rows.limit[t];
+              sv[sub * 4 + i] = ok ? x : -INFINITY;
+            }
+        }
         float mx = sv[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
