@@ -183,7 +183,7 @@ def cpu_baseline(w, target_s: float):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (got --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: the library runs on one GPU and has no multi-GPU path (got --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
