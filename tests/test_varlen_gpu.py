@@ -55,6 +55,22 @@ def test_varlen_random(seed, Hq, Hkv, D, bs, ctx, ql):
     assert (out[np.all(ref == 0, axis=(1, 2))] == 0).all(), "rows that see nothing are zero"
 
 
+@pytest.mark.parametrize("split", [256, 2048])
+def test_varlen_shared_tiles_at_the_causal_bound(split, monkeypatch):
+    """Chunks on the shared-LDS path (at least four row tiles) whose first row's causal
+    bound falls on a 32-position tile edge, one short of it and one past it, so that the
+    last unmasked tile and the first masked one meet exactly there."""
+    monkeypatch.setenv("GPKV_SPLIT_TOKENS", str(split))
+    ctx = [1055, 1056, 1058, 2080, 96]
+    ql = [32, 33, 31, 64, 96]          # first-row bounds 1024, 1024, 1028, 2017, 1
+    w = workloads.varlen_case(721, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
+                              context_lens=ctx, q_lens=ql)
+    _, out = _run(w)
+    err = max_abs(out, _ref(w))
+    print(f"split {split}: varlen max-abs {err:.3e}")
+    assert err <= ATOL
+
+
 @pytest.mark.parametrize("split", [128, 256, 512, 2048])
 def test_varlen_split_sizes(split, monkeypatch):
     """Chunks whose rows end in different splits of the KV range."""
