@@ -58,6 +58,7 @@ __all__ = [
     "quest_select_topk", "sparse_token_positions", "sparse_paged_attention_decode",
     "split_kv_partials", "split_kv_combine", "e4m3_to_f64", "e4m3_from_f32",
     "fp8_inverse_scale", "quantize_fp8", "reshape_and_cache_fp8", "paged_attention_decode_fp8",
+    "sparse_paged_attention_decode_fp8",
     "paged_attention_varlen", "paged_attention_varlen_fp8",
 ]
 
@@ -335,8 +336,9 @@ def sparse_paged_attention_decode(query, key_cache, value_cache, block_tables, c
     for b in (range(B) if seqs is None else seqs):
         for g in range(Hkv):
             pos = sparse_token_positions(topk_indices[b, g], ctx[b], bs)
-            k = bf16_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs))[:, g]
-            v = bf16_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs))[:, g]
+            # rows of KV head g only: [n, D]
+            k = bf16_to_f64(gather_sequence(key_cache[:, :, g], block_tables, b, pos, bs))
+            v = bf16_to_f64(gather_sequence(value_cache[:, :, g], block_tables, b, pos, bs))
             heads = slice(g * G, (g + 1) * G)
             out[b, heads] = _softmax_attention(q[b, heads], k, v, sc)
     return out
@@ -349,7 +351,7 @@ def sparse_paged_attention_decode(query, key_cache, value_cache, block_tables, c
 E4M3_MAX = 448.0
 
 
-def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+def _e4m3_closed_form(codes: np.ndarray) -> np.ndarray:
     """Closed-form decode: sign s, exponent e (4 bits, bias 7), mantissa m (3 bits);
     e = 0 is subnormal (m * 2^-9); e = 15 with m = 7 is NaN."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
@@ -359,6 +361,15 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
     mag = np.where((e == 15) & (m == 7), np.nan, mag)
     return sign * mag
+
+
+# The closed form evaluated once for all 256 codes; decoding is then a lookup.
+_E4M3_ALL = _e4m3_closed_form(np.arange(256, dtype=np.uint8))
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Value of each E4M3 code (the closed form above, looked up per code)."""
+    return _E4M3_ALL[np.asarray(codes, dtype=np.uint8)]
 
 
 # The finite non-negative values in code order (codes 0x00 .. 0x7E), increasing.
@@ -426,6 +437,32 @@ def paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_scale, 
         for g in range(Hkv):
             heads = slice(g * G, (g + 1) * G)
             out[b, heads] = _softmax_attention(q[b, heads], k[:, g], v[:, g], sc)
+    return out
+
+
+def sparse_paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_scale,
+                                      block_tables, context_lens, topk_indices, scale, seqs=None):
+    """Quest sparse attention over E4M3 caches: the definition of
+    ``sparse_paged_attention_decode`` (softmax over the tokens of the blocks that
+    topk_indices[b, g] selects, t < ctx_b) applied to K = code * k_scale[g] and
+    V = code * v_scale[g]."""
+    B, Hq, D = query.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    G = Hq // Hkv
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    _check_table(block_tables, ctx, bs, NB)
+    ks = np.asarray(k_scale, dtype=np.float32).astype(np.float64)
+    vs = np.asarray(v_scale, dtype=np.float32).astype(np.float64)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    q = bf16_to_f64(query)
+    sc = float(np.float32(scale))
+    for b in (range(B) if seqs is None else seqs):
+        for g in range(Hkv):
+            pos = sparse_token_positions(topk_indices[b, g], ctx[b], bs)
+            k_g = e4m3_to_f64(gather_sequence(key_cache[:, :, g], block_tables, b, pos, bs)) * ks[g]
+            v_g = e4m3_to_f64(gather_sequence(value_cache[:, :, g], block_tables, b, pos, bs)) * vs[g]
+            heads = slice(g * G, (g + 1) * G)
+            out[b, heads] = _softmax_attention(q[b, heads], k_g, v_g, sc)
     return out
 
 

@@ -6,6 +6,7 @@ import functools
 import numpy as np
 import torch
 
+import oracle
 import workloads
 
 BF = torch.bfloat16
@@ -41,6 +42,64 @@ class Dev:
 @functools.lru_cache(maxsize=None)
 def workload(config: int) -> workloads.Workload:
     return workloads.make(config)
+
+
+# ---------------------------------------------------------------------------
+# Oracle results over every sequence of a full-size workload, computed once per
+# test session (several tests and schedules compare against the same result).
+# ---------------------------------------------------------------------------
+
+@functools.lru_cache(maxsize=None)
+def step_caches(config: int):
+    """(key_cache, value_cache) bits after the step's write, by the oracle."""
+    w = workload(config)
+    if not w.num_tokens:
+        return w.key_cache, w.value_cache
+    return oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                    w.slot_mapping, w.block_size)
+
+
+@functools.lru_cache(maxsize=None)
+def dense_ref(config: int) -> np.ndarray:
+    """Dense attention of every sequence over the caches after the step's write."""
+    w = workload(config)
+    kc, vc = step_caches(config)
+    return oracle.paged_attention_decode(w.query, kc, vc, w.block_tables, w.context_lens,
+                                         w.scale)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_selection(config: int, K: int) -> np.ndarray:
+    """Top-K of every (sequence, KV head) from metadata over the generated pool."""
+    w = workload(config)
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens,
+                                             w.block_size)
+    return oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens,
+                                    w.block_size, K)
+
+
+@functools.lru_cache(maxsize=None)
+def sparse_ref(config: int, K: int) -> np.ndarray:
+    """Sparse attention of every sequence over the generated pool, the selection
+    fixed to the oracle's Top-K."""
+    w = workload(config)
+    return oracle.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache,
+                                                w.block_tables, w.context_lens,
+                                                oracle_selection(config, K), w.scale)
+
+
+def fp8_codes(cache_bits: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The oracle's E4M3 codes of a whole bf16 cache [..., H_kv, D]. quantize_fp8 is an
+    elementwise function of (bf16 pattern, KV head), so it is evaluated once on all
+    65536 patterns for each head and then looked up: the same codes as calling it on
+    the cache, in seconds rather than minutes at full size."""
+    Hkv = cache_bits.shape[-2]
+    allbits = np.repeat(np.arange(65536, dtype=np.uint16)[:, None, None], Hkv, axis=1)
+    table = oracle.quantize_fp8(allbits, scales)[:, :, 0]          # [65536, H_kv]
+    out = np.empty(cache_bits.shape, np.uint8)
+    for g in range(Hkv):
+        out[..., g, :] = table[:, g][cache_bits[..., g, :]]
+    return out
 
 
 def sample_seqs(w: workloads.Workload, n: int = 6, seed: int = 0) -> list[int]:

@@ -618,6 +618,46 @@ def pin_fp8_attention_equals_bf16_on_representable(orc):
     assert np.abs(got - exp).max() <= TOL
 
 
+def pin_fp8_sparse_all_blocks_equals_fp8_dense(orc):
+    """Selecting every block of every KV head is dense FP8 attention."""
+    scales_k, scales_v = [0.03, 0.07], [0.05, 0.011]
+    w = workloads.random_case(75, batch=3, num_q_heads=6, num_kv_heads=2, head_dim=64,
+                              block_size=16, context_lens=[1, 40, 70])
+    kq = orc.quantize_fp8(w.key_cache, scales_k)
+    vq = orc.quantize_fp8(w.value_cache, scales_v)
+    nb = -(-w.context_lens // 16)
+    sel = np.full((3, 2, 6), -1, np.int32)
+    for b in range(3):
+        sel[b, :, :nb[b]] = np.arange(nb[b])[::-1]          # unsorted: order is irrelevant
+    got = orc.sparse_paged_attention_decode_fp8(w.query, kq, vq, scales_k, scales_v,
+                                                w.block_tables, w.context_lens, sel, w.scale)
+    exp = orc.paged_attention_decode_fp8(w.query, kq, vq, scales_k, scales_v, w.block_tables,
+                                         w.context_lens, w.scale)
+    assert np.abs(got - exp).max() <= TOL
+
+
+def pin_fp8_sparse_equals_bf16_sparse_on_representable(orc):
+    """With exactly representable values and per-head K and V scales that differ, FP8
+    sparse attention is bf16 sparse attention, holes and unsorted ids included."""
+    scales_k, scales_v = [0.5, 4.0], [2.0, 0.25]
+    w = _representable_case(76, scales_k)
+    vcache = _representable_case(77, scales_v).value_cache
+    kq = orc.quantize_fp8(w.key_cache, scales_k)
+    vq = orc.quantize_fp8(vcache, scales_v)
+    sel = np.full((3, 2, 4), -1, np.int32)
+    sel[0, 0, 0] = 0
+    sel[1, 0] = [2, -1, 0, -1]
+    sel[1, 1] = [-1, 1, -1, -1]
+    sel[2, 0] = [4, 1, -1, 3]
+    sel[2, 1] = [0, -1, 2, -1]
+    got = orc.sparse_paged_attention_decode_fp8(w.query, kq, vq, scales_k, scales_v,
+                                                w.block_tables, w.context_lens, sel, w.scale)
+    exp = orc.sparse_paged_attention_decode(w.query, w.key_cache, vcache, w.block_tables,
+                                            w.context_lens, sel, w.scale)
+    assert np.abs(got - exp).max() <= TOL
+    assert (got[0, 3:] == 0).all(), "KV head 1 of sequence 0 selects nothing: zero rows"
+
+
 # ---------------------------------------------------------------------------
 # Multi-token queries (varlen, right-aligned causal mask)
 # ---------------------------------------------------------------------------

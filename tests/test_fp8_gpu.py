@@ -2,12 +2,13 @@
 
 Bars: cache codes bit-exact; attention within max-abs 2e-3 of the float64 oracle
 evaluated on the oracle's own codes (the error of quantising itself is not part of
-the bar; it is printed). On the full-size workloads the GPU quantises the whole
-pool with its own write call, and the oracle quantises the blocks of the sampled
-sequences independently: those blocks must agree bit for bit before attention is
-compared.
+the bar). On the full-size workloads the GPU quantises the whole pool with its own
+write call and the oracle quantises the whole pool independently; the two pools
+must agree bit for bit before attention is compared, on every sequence.
 """
 from __future__ import annotations
+
+import functools
 
 import numpy as np
 import pytest
@@ -16,7 +17,7 @@ import torch
 import gqa_paged_kv_amd as gp
 import oracle
 import workloads
-from gpu_util import BF, Dev, max_abs, sample_seqs, to_dev, workload
+from gpu_util import BF, Dev, fp8_codes, max_abs, oracle_selection, to_dev, workload
 
 pytestmark = pytest.mark.gpu
 ATOL = 2e-3
@@ -108,9 +109,10 @@ def test_fp8_write_empty_and_negative():
 
 class Fp8Case:
     """A workload's E4M3 caches: the GPU's (whole pool, written by the GPU) and the
-    oracle's (blocks of ``seqs`` only, quantised on the CPU)."""
+    oracle's (quantised on the CPU: the blocks of ``seqs``, or the whole pool when
+    ``seqs`` is None)."""
 
-    def __init__(self, w, seqs):
+    def __init__(self, w, seqs=None):
         self.w, self.seqs = w, seqs
         self.ks, self.vs = _scales(w.key_cache), _scales(w.value_cache)
         d = Dev(w)
@@ -124,7 +126,13 @@ class Fp8Case:
         gp.reshape_and_cache_fp8(d.kc.view(NB * bs, Hkv, D), d.vc.view(NB * bs, Hkv, D), self.kc,
                                  self.vc, self.d_ks, self.d_vs, all_slots)
         torch.cuda.synchronize()
-        # the oracle's codes for the blocks the sampled sequences read
+        if seqs is None:   # the whole pool, both sides
+            self.okc = fp8_codes(w.key_cache, self.ks)
+            self.ovc = fp8_codes(w.value_cache, self.vs)
+            assert np.array_equal(self.kc.cpu().numpy(), self.okc), "GPU key codes differ"
+            assert np.array_equal(self.vc.cpu().numpy(), self.ovc), "GPU value codes differ"
+            return
+        # the oracle's codes for the blocks the given sequences read
         self.okc = np.zeros((NB, bs, Hkv, D), np.uint8)
         self.ovc = np.zeros((NB, bs, Hkv, D), np.uint8)
         blocks = sorted({int(x) for b in seqs
@@ -157,18 +165,19 @@ class Fp8Case:
                                                  seqs=self.seqs)
 
 
-@pytest.mark.parametrize("config", [1, 3, 4, 5])
+@functools.lru_cache(maxsize=None)
+def _full_case(config):
+    """Whole-pool E4M3 caches of a full-size workload (GPU and oracle), built once."""
+    return Fp8Case(workload(config))
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
 def test_fp8_dense_config(config):
     w = workload(config)
-    seqs = list(range(w.batch)) if w.batch <= 4 else sample_seqs(w)
-    c = Fp8Case(w, seqs)
+    c = _full_case(config)
     out = c.dense()
-    ref = c.ref_dense()
-    err = max_abs(out[seqs], ref[seqs])
-    bf = oracle.paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
-                                       w.context_lens, w.scale, seqs=seqs)
-    print(f"config {config}: FP8 max-abs vs oracle {err:.3e}; "
-          f"quantisation effect vs bf16 attention {max_abs(ref[seqs], bf[seqs]):.3e}")
+    err = max_abs(out, c.ref_dense())
+    print(f"config {config}: FP8 max-abs vs oracle {err:.3e} over all {w.batch} sequences")
     assert err <= ATOL
 
 
@@ -198,35 +207,21 @@ def test_fp8_dense_random(seed, Hq, Hkv, D, bs, ctx, schedule, monkeypatch):
             assert (out[b] == 0).all()
 
 
+@functools.lru_cache(maxsize=None)
+def _sparse_ref(config, K):
+    w, c = workload(config), _full_case(config)
+    return oracle.sparse_paged_attention_decode_fp8(w.query, c.okc, c.ovc, c.ks, c.vs,
+                                                    w.block_tables, w.context_lens,
+                                                    oracle_selection(config, K), w.scale)
+
+
 @pytest.mark.parametrize("schedule", ["balanced", "split", "direct"])
 @pytest.mark.parametrize("config,K", [(1, 3), (3, 64), (5, 32)])
 def test_fp8_sparse_config(config, K, schedule, monkeypatch):
     monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
     w = workload(config)
-    seqs = list(range(w.batch)) if w.batch <= 4 else sample_seqs(w)
-    c = Fp8Case(w, seqs)
-    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens,
-                                             w.block_size)
-    sel = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens,
-                                   w.block_size, K)
-    out = c.sparse(sel)
-    # the oracle's FP8 sparse result: dense FP8 attention restricted to the selected
-    # blocks, via a block table listing only them
-    ref = np.zeros_like(out, dtype=np.float64)
-    G = w.num_q_heads // w.num_kv_heads
-    for b in seqs:
-        for g in range(w.num_kv_heads):
-            lbs = sorted(x for x in sel[b, g].tolist() if x >= 0)
-            if not lbs:
-                continue
-            bt1 = np.array([[int(w.block_tables[b, lb]) for lb in lbs]], np.int32)
-            ctx_b = int(w.context_lens[b])
-            last = lbs[-1]
-            n = (len(lbs) - 1) * w.block_size + min(w.block_size, ctx_b - last * w.block_size)
-            q1 = w.query[b:b + 1]
-            r = oracle.paged_attention_decode_fp8(q1, c.okc, c.ovc, c.ks, c.vs, bt1,
-                                                  np.array([n], np.int64), w.scale)
-            ref[b, g * G:(g + 1) * G] = r[0, g * G:(g + 1) * G]
-    err = max_abs(out[seqs], ref[seqs])
-    print(f"config {config} K={K}: FP8 sparse max-abs {err:.3e}")
+    c = _full_case(config)
+    out = c.sparse(oracle_selection(config, K))
+    err = max_abs(out, _sparse_ref(config, K))
+    print(f"config {config} K={K}: FP8 sparse max-abs {err:.3e} over all {w.batch} sequences")
     assert err <= ATOL

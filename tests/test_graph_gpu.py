@@ -1,23 +1,35 @@
-"""The whole decode step captured into a HIP graph: replay equals eager, bit for bit.
+"""The whole decode step captured into a HIP graph: replay equals eager, bit for bit,
+and both equal the oracle chain.
 
 [TL18] 6.2 (TileLang tutorial ch. 18, graph capture): graph mode only removes the
 host-side launch cost, so the check is that replays give exactly the eager results.
 Every call launches on torch's current stream with a grid fixed by host scalars and
 no memset, so it is capturable. Replays are interleaved with eager work and
-synchronisations, and every replay is compared with the eager result.
+synchronisations, and every replay is compared with the eager result; the eager
+result itself (caches, metadata, Top-K ids, both attention outputs) is compared
+with the CPU oracle's write -> metadata -> dense / select -> sparse chain (bits
+exact, attention within 2e-3).
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
 
 import gqa_paged_kv_amd as gp
+import oracle
 import workloads
-from gpu_util import BF, Dev, to_dev
+from gpu_util import BF, Dev, bits, max_abs, to_dev
+
+ATOL = 2e-3
 
 pytestmark = pytest.mark.gpu
 
 
 def _step_buffers(w, d, K):
+    """Workspaces and outputs, and the prefill state: this step's tokens already in
+    the cache and the metadata built over it, so that the step's write and its
+    incremental metadata update are idempotent (every run leaves the same state)."""
     B, Hq, Hkv, D, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     mcl = w.max_context_len
     buf = {
@@ -36,8 +48,59 @@ def _step_buffers(w, d, K):
         "kmin": torch.zeros((w.num_blocks, Hkv, D), dtype=BF, device="cuda"),
         "kmax": torch.zeros((w.num_blocks, Hkv, D), dtype=BF, device="cuda"),
     }
+    gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
     gp.quest_block_metadata(d.kc, d.bt, d.ctx, buf["kmin"], buf["kmax"], max_context_len=mcl)
     return buf
+
+
+def _graph_case(case):
+    if case == "random":
+        w = workloads.random_case(401, batch=6, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                                  block_size=16, context_lens=[900, 33, 2500, 16, 1200, 700],
+                                  num_tokens=6, neg_slots=1)
+        return w, 12
+    w = workloads.make(3)
+    return w, w.topk_list[0]
+
+
+@functools.lru_cache(maxsize=None)
+def _oracle_chain(case):
+    """The step on the CPU: write, metadata of the written cache, dense attention,
+    Top-K, sparse attention over the selection."""
+    w, K = _graph_case(case)
+    bs = w.block_size
+    kc, vc = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                      w.slot_mapping, bs)
+    kmin, kmax = oracle.quest_block_metadata(kc, w.block_tables, w.context_lens, bs)
+    sel = oracle.quest_select_topk(w.query, kmin, kmax, w.block_tables, w.context_lens, bs, K)
+    return {"kc": kc, "vc": vc, "kmin": kmin, "kmax": kmax, "sel": sel,
+            "out_d": oracle.paged_attention_decode(w.query, kc, vc, w.block_tables,
+                                                   w.context_lens, w.scale),
+            "out_s": oracle.sparse_paged_attention_decode(w.query, kc, vc, w.block_tables,
+                                                          w.context_lens, sel, w.scale)}
+
+
+def _meta_equal(got, exp, referenced):
+    """Bitwise on the referenced blocks, +0 and -0 counted equal."""
+    g, e = got[referenced].copy(), exp[referenced].copy()
+    g[g == 0x8000] = 0
+    e[e == 0x8000] = 0
+    return np.array_equal(g, e)
+
+
+def _check_against_oracle(case, w, snap):
+    exp = _oracle_chain(case)
+    assert np.array_equal(bits(snap["kc"]), exp["kc"]), "key cache differs from the oracle"
+    assert np.array_equal(bits(snap["vc"]), exp["vc"]), "value cache differs from the oracle"
+    referenced = np.unique(np.concatenate(
+        [w.block_tables[b, :-(-int(L) // w.block_size)] for b, L in enumerate(w.context_lens)]))
+    assert _meta_equal(bits(snap["kmin"]), exp["kmin"], referenced), "key_min differs"
+    assert _meta_equal(bits(snap["kmax"]), exp["kmax"], referenced), "key_max differs"
+    assert np.array_equal(snap["sel"].cpu().numpy(), exp["sel"]), "Top-K ids differ"
+    err_d = max_abs(snap["out_d"].cpu().numpy(), exp["out_d"])
+    err_s = max_abs(snap["out_s"].cpu().numpy(), exp["out_s"])
+    print(f"{case}: dense max-abs {err_d:.3e}, sparse max-abs {err_s:.3e}")
+    assert err_d <= ATOL and err_s <= ATOL
 
 
 def _step(w, d, buf, K, fused, one_call=False):
@@ -76,14 +139,7 @@ def _snapshot(buf, d):
 def test_graph_replay_equals_eager(case, fused, one_call, monkeypatch):
     if one_call:   # the one-launch Quest decode on both shapes
         monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "fused")
-    if case == "random":
-        w = workloads.random_case(401, batch=6, num_q_heads=28, num_kv_heads=4, head_dim=128,
-                                  block_size=16, context_lens=[900, 33, 2500, 16, 1200, 700],
-                                  num_tokens=6, neg_slots=1)
-        K = 12
-    else:
-        w = workloads.make(3)
-        K = w.topk_list[0]
+    w, K = _graph_case(case)
     d = Dev(w)
     buf = _step_buffers(w, d, K)
     side = torch.cuda.Stream()
@@ -95,6 +151,7 @@ def test_graph_replay_equals_eager(case, fused, one_call, monkeypatch):
     _step(w, d, buf, K, fused, one_call)       # eager reference (the write is idempotent)
     torch.cuda.synchronize()
     ref = _snapshot(buf, d)
+    _check_against_oracle(case, w, ref)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):

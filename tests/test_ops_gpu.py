@@ -2,9 +2,9 @@
 
 Bars: cache writes, Quest metadata and Top-K indices bit-exact; attention outputs
 within max-abs 2e-3 of the float64 oracle (bf16 inputs, fp32 accumulation).
-Full-size configs compare every output of the cheap ops and a sample of
-sequences (longest, shortest, seeded random) for attention, in the launch
-configuration the benchmark uses.
+Full-size configs compare every output -- caches, metadata, indices and the
+attention rows of every sequence -- in the launch configuration the benchmark
+uses.
 """
 from __future__ import annotations
 
@@ -15,7 +15,8 @@ import torch
 import gqa_paged_kv_amd as gp
 import oracle
 import workloads
-from gpu_util import BF, Dev, bits, max_abs, sample_seqs, to_dev, workload
+from gpu_util import (BF, Dev, bits, dense_ref, max_abs, oracle_selection, sparse_ref, to_dev,
+                      workload)
 
 pytestmark = pytest.mark.gpu
 ATOL = 2e-3
@@ -76,16 +77,9 @@ def test_dense_config(config):
     d = Dev(w)
     if w.num_tokens:   # the step writes the new token first (context_lens include it)
         gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
-        kc, vc = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
-                                          w.slot_mapping, w.block_size)
-    else:
-        kc, vc = w.key_cache, w.value_cache
     out = _dense(d, w).cpu().numpy()
-    seqs = list(range(w.batch)) if w.batch <= 4 else sample_seqs(w)
-    ref = oracle.paged_attention_decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale,
-                                        seqs=seqs)
-    err = max_abs(out[seqs], ref[seqs])
-    print(f"config {config}: dense max-abs {err:.3e} over sequences {seqs}")
+    err = max_abs(out, dense_ref(config))
+    print(f"config {config}: dense max-abs {err:.3e} over all {w.batch} sequences")
     assert err <= ATOL
     assert np.isfinite(out).all()
 
@@ -428,15 +422,10 @@ def test_sparse_config_fixed_selection(config, K, schedule, monkeypatch):
     monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
     w = workload(config)
     d = Dev(w)
-    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, w.block_size)
-    sel = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens,
-                                   w.block_size, K)
+    sel = oracle_selection(config, K)
     out = _sparse(d, w, to_dev(sel, torch.int32)).cpu().numpy()
-    seqs = list(range(w.batch)) if w.batch <= 4 else sample_seqs(w)
-    ref = oracle.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache, w.block_tables,
-                                               w.context_lens, sel, w.scale, seqs=seqs)
-    err = max_abs(out[seqs], ref[seqs])
-    print(f"config {config} K={K}: sparse max-abs {err:.3e}")
+    err = max_abs(out, sparse_ref(config, K))
+    print(f"config {config} K={K}: sparse max-abs {err:.3e} over all {w.batch} sequences")
     assert err <= ATOL
 
 

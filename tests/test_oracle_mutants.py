@@ -56,6 +56,11 @@ MUTANTS = [
      "                e4m3_to_f64(gather_sequence(value_cache, block_tables, b, pos, bs)) * ks[:, None])"),
     ("fp8 varlen: codes read as bf16", "        return (e4m3_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs)) * ks[:, None],",
      "        return (bf16_to_f64(gather_sequence(key_cache, block_tables, b, pos, bs)) * ks[:, None],"),
+    ("fp8 sparse: K scale on V", "* vs[g]", "* ks[g]"),
+    ("fp8 sparse: KV head 0's keys for every head",
+     "k_g = e4m3_to_f64(gather_sequence(key_cache[:, :, g]", "k_g = e4m3_to_f64(gather_sequence(key_cache[:, :, 0]"),
+    ("fp8 sparse: no K scale", "key_cache[:, :, g], block_tables, b, pos, bs)) * ks[g]",
+     "key_cache[:, :, g], block_tables, b, pos, bs))"),
     ("varlen: query rows shifted", "s_ = sc * (q[r0:r1, h] @ k[:, g].T)", "s_ = sc * (q[r0 + 1:r1 + 1, h] @ k[:, g].T)"),
 ]
 

@@ -97,7 +97,7 @@ def test_varlen_single_tokens_equal_decode():
 
 def test_varlen_mixed_batch_8k():
     """An 8K-average batch in which a few sequences bring prefill chunks and the rest
-    decode one token each; sampled sequences against the oracle."""
+    decode one token each; every query row against the oracle."""
     rng = np.random.default_rng(712)
     ctx = np.clip(np.round(rng.normal(8192, 2048, 64)), 2048, 16384).astype(np.int32)
     ql = np.ones(64, np.int32)
@@ -105,11 +105,8 @@ def test_varlen_mixed_batch_8k():
     w = workloads.varlen_case(712, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
                               context_lens=ctx, q_lens=ql)
     _, out = _run(w)
-    seqs = [0, 1, 3, 5, 17, 63]
-    ref = _ref(w, seqs=seqs)
-    rows = np.concatenate([np.arange(w.cu_seqlens_q[b], w.cu_seqlens_q[b + 1]) for b in seqs])
-    err = max_abs(out[rows], ref[rows])
-    print(f"mixed 8K batch: varlen max-abs {err:.3e}")
+    err = max_abs(out, _ref(w))
+    print(f"mixed 8K batch: varlen max-abs {err:.3e} over all {out.shape[0]} query rows")
     assert err <= ATOL
 
 
