@@ -16,7 +16,13 @@ is written so that no KV bytes survive in the 256 MB Infinity Cache; the
 per-call durations come from HIP events on the launch stream and exclude that
 flush. The value reported is the step's algorithmic KV/metadata bytes divided by
 the step time (GB/s). The full metadata rebuild is a prefill-time cost and is
-reported separately, outside the step.
+reported separately, outside the step. A workload without new tokens has no write
+in its step. The one-call Quest decode is also timed alone behind its own flush,
+and the Quest step is the write plus that alone-timed call.
+
+After the headline workload, a per-workload block times every call of each of the
+five workloads alone behind the flush (write, dense call, one-call Quest decode),
+with the dense and Quest step times and their fraction of peak HBM bandwidth.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
 """
@@ -59,6 +65,8 @@ def parse_args():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) cache timing")
     ap.add_argument("--no-varlen", action="store_true", help="skip the multi-token query timing")
     ap.add_argument("--details", action="store_true", help="print per-call timings to stderr")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-workload block (configs 1-5, each call timed alone)")
     return ap.parse_args()
 
 
@@ -180,6 +188,111 @@ def cpu_baseline(w, target_s: float):
                       f"sequences), {dt:.1f} s"}
 
 
+def time_alone(fn, flush, stream, steps):
+    """Mean / median / min of one call timed with HIP events on the launch stream,
+    each run behind a write of the flush buffer (after three untimed calls)."""
+    import numpy as np
+    import torch
+    for _ in range(3):
+        fn()
+    ts = []
+    for k in range(steps):
+        flush.fill_(k & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    t = np.array(ts)
+    return {"us_mean": round(float(t.mean()), 2), "us_median": round(float(np.median(t)), 2),
+            "us_min": round(float(t.min()), 2)}
+
+
+def per_config_block(cfg, flush, stream, steps):
+    """Every call of one workload's decode step, each timed alone behind the flush:
+    the write (when the workload has new tokens), the dense call and the one-call
+    Quest decode (when it sets topk_blocks). Step figures are sums of those calls."""
+    import numpy as np
+    import torch
+
+    import gqa_paged_kv_amd as gp
+    import workloads
+    from gqa_paged_kv_amd import roofline as R
+
+    w = workloads.make(cfg)
+    bf = torch.bfloat16
+
+    def dev(a, dtype):
+        a = np.ascontiguousarray(a)
+        if dtype == bf:
+            return torch.from_numpy(a.view(np.int16)).view(bf).cuda()
+        return torch.from_numpy(a).to(dtype).cuda()
+    kc, vc = dev(w.key_cache, bf), dev(w.value_cache, bf)
+    q = dev(w.query, bf)
+    bt, ctx = dev(w.block_tables, torch.int32), dev(w.context_lens, torch.int32)
+    B, Hq, Hkv, D, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    mcl, scale = w.max_context_len, float(w.scale)
+    K = w.topk_list[0] if w.topk_list else 0
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gp.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl), dtype=torch.uint8,
+                     device="cuda")
+    res = {"workload": w.name, "sum_context": int(w.context_lens.sum()), "topk_blocks": K or None}
+    write_us = 0.0
+    kmin = kmax = None
+    if w.num_tokens:
+        nk, nv = dev(w.new_key, bf), dev(w.new_value, bf)
+        slots = dev(w.slot_mapping, torch.int64)
+        if K:
+            kmin = torch.zeros((w.num_blocks, Hkv, D), dtype=bf, device="cuda")
+            kmax = torch.zeros_like(kmin)
+            gp.reshape_and_cache(nk, nv, kc, vc, slots)   # the step's tokens, then metadata:
+            gp.quest_block_metadata(kc, bt, ctx, kmin, kmax, max_context_len=mcl)   # idempotent
+            t = time_alone(lambda: gp.reshape_and_cache_quest(nk, nv, kc, vc, kmin, kmax, slots),
+                           flush, stream, steps)
+            res["write_call"] = "reshape_and_cache_quest"
+        else:
+            t = time_alone(lambda: gp.reshape_and_cache(nk, nv, kc, vc, slots), flush, stream,
+                           steps)
+            res["write_call"] = "reshape_and_cache"
+        res["write_us"] = t["us_mean"]
+        write_us = t["us_mean"]
+    t = time_alone(lambda: gp.paged_attention_decode(q, kc, vc, bt, ctx, max_context_len=mcl,
+                                                     scale=scale, out=out, workspace=ws),
+                   flush, stream, steps)
+    db = R.dense_attention_bytes(w.context_lens, Hkv, D)
+    res["dense_call_us"] = t["us_mean"]
+    res["dense_bytes"] = int(db)
+    res["dense_gbps"] = round(db / (t["us_mean"] * 1e-6) / 1e9, 1)
+    res["dense_pct_of_peak"] = round(100 * res["dense_gbps"] / R.MI355X_HBM_GBPS, 1)
+    res["dense_step_us"] = round(write_us + t["us_mean"], 2)
+    if K:
+        if kmin is None:
+            kmin = torch.zeros((w.num_blocks, Hkv, D), dtype=bf, device="cuda")
+            kmax = torch.zeros_like(kmin)
+            gp.quest_block_metadata(kc, bt, ctx, kmin, kmax, max_context_len=mcl)
+        sel = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda")
+        out_s = torch.empty_like(out)
+        wq = torch.empty(gp.quest_decode_workspace_bytes(B, Hq, Hkv, D, bs, w.max_blocks_per_seq, K),
+                         dtype=torch.uint8, device="cuda")
+        t = time_alone(lambda: gp.quest_decode(q, kc, vc, kmin, kmax, bt, ctx, topk_blocks=K,
+                                               max_context_len=mcl, scale=scale, out=out_s,
+                                               topk_out=sel, workspace=wq),
+                       flush, stream, steps)
+        qb = (R.select_bytes(w.context_lens, bs, Hkv, D)
+              + R.sparse_attention_bytes(sel.cpu().numpy(), w.context_lens, bs, D))
+        res["quest_call_us"] = t["us_mean"]
+        res["quest_bytes"] = int(qb)
+        res["quest_gbps"] = round(qb / (t["us_mean"] * 1e-6) / 1e9, 1)
+        res["quest_pct_of_peak"] = round(100 * res["quest_gbps"] / R.MI355X_HBM_GBPS, 1)
+        res["quest_step_us"] = round(write_us + t["us_mean"], 2)
+        res["quest_step_speedup_vs_dense_step"] = round(res["dense_step_us"] / res["quest_step_us"], 2)
+    del kc, vc, q, bt, ctx, out, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -247,6 +360,8 @@ def main():
                  "quest_select_topk", "sparse_paged_attention_decode"]
     else:
         calls = ["reshape_and_cache", "paged_attention_decode"]
+    if not w.num_tokens:   # a workload without new tokens has no write in its step
+        calls = [c for c in calls if not c.startswith("reshape_and_cache")]
 
     def run_call(name):
         if name == "reshape_and_cache":
@@ -349,24 +464,16 @@ def main():
     except RuntimeError as exc:   # report, do not fail the eager measurement
         print(f"[bench] graph capture unavailable: {exc}", file=sys.stderr)
 
-    # The Quest part as its two separate calls, each timed alone (same flush), beside
-    # the one-call form the step uses.
+    # The one-call Quest part timed alone behind its own flush, and as its two separate
+    # calls, each alone (same flush).
     quest_separate = None
+    quest_alone = None
     if one_call:
+        quest_alone = time_alone(lambda: run_call("quest_decode"), flush, stream, args.steps)
         quest_separate = {}
         for name in ("quest_select_topk", "sparse_paged_attention_decode"):
-            for _ in range(3):
-                run_call(name)
-            ts = []
-            for k in range(args.steps):
-                flush.fill_(k & 0xFF)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                run_call(name)
-                e1.record(stream)
-                e1.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e3)
-            quest_separate[name] = round(float(np.mean(ts)), 2)
+            quest_separate[name] = time_alone(lambda: run_call(name), flush, stream,
+                                              args.steps)["us_mean"]
         quest_separate["sum"] = round(sum(quest_separate.values()), 2)
 
     # FP8 (E4M3) KV cache on the same workload: the pool quantised once by the FP8
@@ -491,11 +598,18 @@ def main():
     dense_t = per_call["paged_attention_decode"].mean()
     achieved = by["paged_attention_decode"] / (dense_t * 1e-6) / 1e9
     traffic = committed_traffic(args.config)
-    # Both step figures include the write: dense = write + dense attention; Quest =
-    # write (+ metadata refresh) + select + sparse attention.
-    write_us = calls_out[calls[0]]["us_mean"]
-    quest_us = (sum(calls_out[n]["us_mean"] for n in calls if n != "paged_attention_decode")
-                if K else None)
+    # Both step figures include the write (when the workload has one): dense = write +
+    # dense attention; Quest = write (+ metadata refresh) + the Quest part, which for
+    # the one-call path is quest_decode timed alone behind its own flush (so it never
+    # follows the dense call's 1 GB stream).
+    write_us = sum(calls_out[n]["us_mean"] for n in calls
+                   if n.startswith("reshape_and_cache"))
+    if not K:
+        quest_us = None
+    elif one_call:
+        quest_us = write_us + quest_alone["us_mean"]
+    else:
+        quest_us = sum(calls_out[n]["us_mean"] for n in calls if n != "paged_attention_decode")
 
     line = {
         "metric": "paged decode attention KV-read HBM GB/s over one decode step (write + dense + Quest)",
@@ -525,6 +639,7 @@ def main():
         "graph_replay_us_per_step": round(graph_us, 2) if graph_us is not None else None,
         "fp8_kv": fp8,
         "varlen_mixed": varlen,
+        "quest_decode_alone": quest_alone,
         "quest_separate_calls_us": quest_separate,
         "calls": calls_out,
         "step_algorithmic_bytes": int(step_bytes),
@@ -542,6 +657,17 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
         "torch": torch.__version__, "hip": torch.version.hip,
     }
+    if not args.no_per_config:
+        del kc, vc, q, bt, ctx, nk, nv, slots, kmin, kmax, out_d, out_s, ws_d
+        if K:
+            del ws_sel, ws_sp, ws_qd, sel
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        blocks = {}
+        for cfg in (1, 2, 3, 4, 5):
+            print(f"[bench] per-workload block: config {cfg}", file=sys.stderr, flush=True)
+            blocks[str(cfg)] = per_config_block(cfg, flush, stream, args.steps)
+        line["per_config"] = blocks
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
