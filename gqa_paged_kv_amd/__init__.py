@@ -11,7 +11,8 @@ from .ops import (GpkvError, paged_attention_decode, paged_attention_workspace_b
                   sparse_paged_attention_decode, split_tokens, reshape_and_cache_fp8,
                   paged_attention_decode_fp8, sparse_paged_attention_decode_fp8,
                   paged_attention_varlen, paged_attention_varlen_workspace_bytes, quest_decode,
-                  quest_decode_workspace_bytes, paged_attention_varlen_fp8)
+                  quest_decode_workspace_bytes, paged_attention_varlen_fp8,
+                  paged_attention_decode_noalloc)
 
 __all__ = [
     "GpkvError", "reshape_and_cache", "reshape_and_cache_quest", "paged_attention_decode",
@@ -20,5 +21,5 @@ __all__ = [
     "quest_select_workspace_bytes", "sparse_attention_workspace_bytes", "split_tokens",
     "reshape_and_cache_fp8", "paged_attention_decode_fp8", "sparse_paged_attention_decode_fp8",
     "paged_attention_varlen", "paged_attention_varlen_workspace_bytes", "quest_decode",
-    "quest_decode_workspace_bytes", "paged_attention_varlen_fp8",
+    "quest_decode_workspace_bytes", "paged_attention_varlen_fp8", "paged_attention_decode_noalloc",
 ]

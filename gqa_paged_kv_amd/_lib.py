@@ -26,6 +26,9 @@ SIGNATURES = {
     "gpkv_paged_attention_decode": (c_int32, [vp, vp, vp, vp, vp, vp, c_int32, c_int32, c_int32,
                                               c_int32, c_int32, c_int64, c_int32, c_int32,
                                               c_float, vp, c_size, vp]),
+    "gpkv_paged_attention_decode_noalloc": (c_int32, [vp, vp, vp, vp, vp, vp, c_int32, c_int32,
+                                                      c_int32, c_int32, c_int32, c_int64, c_int32,
+                                                      c_int32, c_float, vp]),
     "gpkv_quest_block_metadata": (c_int32, [vp, vp, vp, vp, vp, c_int32, c_int32, c_int32,
                                             c_int32, c_int64, c_int32, c_int32, c_int32, vp]),
     "gpkv_quest_select_workspace_bytes": (c_size, [c_int32] * 3),

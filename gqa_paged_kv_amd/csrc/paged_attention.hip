@@ -862,6 +862,78 @@ extern "C" int gpkv_paged_attention_decode(float* out, const void* query, const 
                   workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+// ---------------------------------------------------------------------------
+// Dense decode without allocation: the workspace is a file-scope device array
+// ---------------------------------------------------------------------------
+
+// Each GPU the library runs on holds its own copy of this array from the first
+// launch until the process ends. In host code `scratch` names a host-side stand-in,
+// never the device copy: host code uses only the per-device address that
+// scratch_address() looks up.
+static __device__ __align__(256) unsigned char scratch[GPKV_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device: looked up with
+// hipGetSymbolAddress on the first call on that device (with it current), then
+// kept per device.
+static int scratch_address(const char* fn, void** ptr) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = -1;
+  const hipError_t ed = hipGetDevice(&dev);
+  if (ed != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return fail(GPKV_ERR_HIP, "%s: no current HIP device (%s)", fn, hipGetErrorString(ed));
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(GPKV_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn,
+                  dev, hipGetErrorString(e));
+    }
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return GPKV_OK;
+}
+
+extern "C" int gpkv_paged_attention_decode_noalloc(float* out, const void* query,
+                                                   const void* key_cache, const void* value_cache,
+                                                   const int32_t* block_tables,
+                                                   const int32_t* context_lens, int32_t batch,
+                                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t head_dim, int32_t block_size,
+                                                   int64_t num_blocks, int32_t max_blocks_per_seq,
+                                                   int32_t max_context_len, float scale,
+                                                   void* stream) {
+  clear_error();
+  const char* fn = "paged_attention_decode_noalloc";
+  int st = check_common(fn, batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        max_blocks_per_seq, max_context_len);
+  if (st) return st;
+  if (batch == 0) return GPKV_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
+  // The split-KV partial rows and the sequence prefix live in `scratch`. Nothing in
+  // it has to start at zero: every call writes what its combine reads.
+  const size_t need = gpkv_paged_attention_workspace_bytes(batch, num_q_heads, num_kv_heads,
+                                                           head_dim, block_size, max_context_len);
+  if (need > (size_t)GPKV_NOALLOC_SCRATCH_BYTES)
+    return fail(GPKV_ERR_WORKSPACE,
+                "%s: these sizes need %zu bytes of scratch, more than the library's fixed "
+                "%zu-byte device array; use gpkv_paged_attention_decode with a workspace",
+                fn, need, (size_t)GPKV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_address(fn, &ws);
+  if (st) return st;
+  return attn_run(false, false, out, query, key_cache, value_cache, nullptr, nullptr,
+                  block_tables, context_lens, nullptr, batch, num_q_heads, num_kv_heads, head_dim,
+                  block_size, num_blocks, max_blocks_per_seq, max_context_len, 0, scale, ws,
+                  (size_t)GPKV_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream);
+}
+
 extern "C" int gpkv_sparse_paged_attention_decode(
     float* out, const void* query, const void* key_cache, const void* value_cache,
     const int32_t* block_tables, const int32_t* context_lens, const int32_t* topk_indices,

@@ -160,6 +160,22 @@ def paged_attention_decode(query, key_cache, value_cache, block_tables, context_
     return out
 
 
+def paged_attention_decode_noalloc(query, key_cache, value_cache, block_tables, context_lens,
+                                   out, *, max_context_len: int, scale: float,
+                                   stream=None) -> torch.Tensor:
+    """Dense GQA paged decode attention without a workspace: the library's fixed device
+    scratch array holds the partial rows (calls overlapping on one GPU race). ``out``
+    [B, H_q, D] float32 is required, so the call allocates nothing."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks(query, key_cache, value_cache, block_tables,
+                                             context_lens)
+    _dev("out", out, torch.float32, 3)
+    _check(lib().gpkv_paged_attention_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), B, Hq, Hkv, D, bs, NB, MB, int(max_context_len), float(scale),
+        _stream(stream)))
+    return out
+
+
 def quest_block_metadata(key_cache, block_tables, context_lens, key_min, key_max, *,
                          max_context_len: int, last_block_only: bool = False,
                          stream=None) -> None:

@@ -141,6 +141,28 @@ int gpkv_paged_attention_decode(float* out, const void* query, const void* key_c
                                 float scale, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* gpkv_paged_attention_decode without allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, result and errors as gpkv_paged_attention_decode,
+ * minus the workspace: the split-KV partial rows live in a device array inside the
+ * library, GPKV_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held from the first call on
+ * that GPU until the process ends; its device address is looked up once per device
+ * on the first call. The call allocates nothing (no hipMalloc, no library
+ * allocation). Sizes whose workspace (gpkv_paged_attention_workspace_bytes) exceeds
+ * the array return GPKV_ERR_WORKSPACE and launch nothing; a failed address lookup
+ * returns GPKV_ERR_HIP. Every call on one GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (different streams, or threads) race and give
+ * unspecified results: the caller serialises them. Nothing in the array has to start
+ * at zero; its contents after a call are unspecified. */
+#define GPKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int gpkv_paged_attention_decode_noalloc(float* out, const void* query, const void* key_cache,
+                                        const void* value_cache, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t batch,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                        int32_t max_blocks_per_seq, int32_t max_context_len,
+                                        float scale, void* stream);
+
 /* Quest block metadata ([ASC] "Quest Sparse Attention": blocks are scored at low
  * cost; tokens past the context are skipped). For every sequence b and logical
  * block lb < ceil(context_lens[b] / block_size) -- only the last one when

@@ -29,7 +29,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(L):
     from gqa_paged_kv_amd._lib import SIGNATURES
     names = declared_symbols()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     assert sorted(SIGNATURES) == names
@@ -128,6 +128,26 @@ def test_other_entry_points_checks(L):
     assert L.gpkv_quest_decode_workspace_bytes(2, 4, 1, 64, 16, 5, 3) >= max(
         L.gpkv_quest_select_workspace_bytes(2, 1, 5),
         L.gpkv_sparse_attention_workspace_bytes(2, 4, 1, 64, 16, 3))
+
+
+def test_noalloc_argument_checks(L):
+    """The allocation-free dense call: null pointers, shapes, and sizes whose partial
+    rows would not fit the library's 32 MiB device array are refused on the host."""
+    a = ARGS
+    base = [8, 8, 8, 8, 8, 8, a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["mcl"],
+            0.125, None]
+    f = L.gpkv_paged_attention_decode_noalloc
+    assert f(*([None] + base[1:])) == -1
+    bad = list(base)
+    bad[13] = 81                      # max_context_len > max_blocks * block_size
+    assert f(*bad) == -2
+    big = [8, 8, 8, 8, 8, 8, 4096, 64, 8, 128, 16, 1 << 20, 2048, 32768, 0.1, None]
+    assert L.gpkv_paged_attention_workspace_bytes(4096, 64, 8, 128, 16, 32768) > 32 << 20
+    assert f(*big) == -4
+    assert b"32" in L.gpkv_last_error_message() or b"scratch" in L.gpkv_last_error_message()
+    zero = list(base)
+    zero[6] = 0                        # an empty batch is a no-op
+    assert f(*zero) == 0
 
 
 def test_workspace_queries(L):
