@@ -138,8 +138,9 @@ using namespace gpkv;
 
 // One launch for the Quest decode step when the (sequence, KV head) pairs fill
 // between half of the CUs and all of them (one 512-thread workgroup per CU: the
-// attention's registers leave room for no second one); otherwise the selection
-// and the sparse attention calls in turn, sharing the workspace.
+// attention's registers leave room for no second one), or when each pair reads
+// little; otherwise the selection and the sparse attention calls in turn, sharing
+// the workspace.
 // GPKV_QUEST_DECODE_PATH=fused|separate forces the choice (tuning and test switch).
 extern "C" size_t gpkv_quest_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                                     int32_t num_kv_heads, int32_t head_dim,
@@ -189,7 +190,16 @@ extern "C" int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* 
   const long long pairs = (long long)batch * num_kv_heads;
   const long long cus = balanced_capacity();
   const bool fits = topk_blocks <= kDirTab && max_nb <= kMaxFusedBlocks && lds <= 64 * 1024;
-  bool fused = fits && 2 * pairs > cus && pairs <= cus;
+  // One workgroup per pair does the pair's whole step serially, so it pays when
+  // the pairs fill the CUs, or when a pair's whole read (its metadata rows, then
+  // its selected K/V) is small enough that the serial chain is shorter than the
+  // two calls' four launches. Measured on MI355X: two 5-block pairs 11.7 us in one
+  // launch against 21.2 us as two calls; sixteen 2560-block pairs 111 us against
+  // 38 us.
+  const long long pair_bytes =
+      (long long)max_nb * 2 * head_dim * 2 +
+      (long long)(topk_blocks < max_nb ? topk_blocks : max_nb) * block_size * 4 * head_dim;
+  bool fused = fits && pairs <= cus && (2 * pairs > cus || pair_bytes <= 256 * 1024);
   const char* forced = getenv("GPKV_QUEST_DECODE_PATH");
   if (forced && strcmp(forced, "fused") == 0) fused = fits;
   if (forced && strcmp(forced, "separate") == 0) fused = false;

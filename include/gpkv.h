@@ -239,7 +239,8 @@ int gpkv_sparse_paged_attention_decode(float* out, const void* query, const void
  * padding), out [batch, num_q_heads, head_dim] fp32 the attention over it. key_min /
  * key_max as for gpkv_quest_select_topk, caches and scale as for the attention
  * calls. When the (sequence, KV head) pairs fill between half of the GPU's CUs
- * and all of them, one workgroup per pair selects in LDS and attends at once (one
+ * and all of them, or each pair reads little (at most 256 KB of metadata and
+ * selected K/V), one workgroup per pair selects in LDS and attends at once (one
  * launch); otherwise the two calls run in turn. The workspace (size from
  * gpkv_quest_decode_workspace_bytes) serves either. Errors: those of the two calls. */
 size_t gpkv_quest_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,

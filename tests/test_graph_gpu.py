@@ -59,6 +59,10 @@ def _graph_case(case):
                                   block_size=16, context_lens=[900, 33, 2500, 16, 1200, 700],
                                   num_tokens=6, neg_slots=1)
         return w, 12
+    if case == "long":   # few pairs, long selections
+        w = workloads.random_case(403, batch=2, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                                  block_size=16, context_lens=[20000, 9000], num_tokens=2)
+        return w, 200
     w = workloads.make(3)
     return w, w.topk_list[0]
 
@@ -135,10 +139,12 @@ def _snapshot(buf, d):
 
 @pytest.mark.parametrize("case,fused,one_call", [("random", False, False), ("config3", False, False),
                                                  ("random", True, False), ("config3", True, False),
-                                                 ("random", True, True), ("config3", True, True)])
+                                                 ("random", True, "fused"), ("config3", True, "fused"),
+                                                 ("long", True, "auto"),
+                                                 ("long", True, "fused")])
 def test_graph_replay_equals_eager(case, fused, one_call, monkeypatch):
-    if one_call:   # the one-launch Quest decode on both shapes
-        monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "fused")
+    if one_call:   # the one-call Quest decode on the path named
+        monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", one_call)
     w, K = _graph_case(case)
     d = Dev(w)
     buf = _step_buffers(w, d, K)

@@ -33,7 +33,10 @@ def _decode(d, w, kmin, kmax, K):
     return out.cpu().numpy(), sel.cpu().numpy()
 
 
-@pytest.mark.parametrize("path", ["auto", "fused", "separate"])
+PATHS = ["auto", "fused", "separate"]
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("config,K", [(1, 3), (1, 5), (3, 64), (4, 256), (5, 32)])
 def test_quest_decode_config(config, K, path, monkeypatch):
     if path != "auto":
@@ -55,40 +58,77 @@ QD_CASES = [
     (802, 16, 1, 128, 64, [129, 2047, 4100], 1),                 # G = 16, K = 1
     (803, 14, 2, 64, 128, [250, 1, 700, 3000], 5),               # D = 64, bs = 128
     (804, 12, 3, 64, 32, [513, 514, 96], 40),
+    # few pairs and long selections
+    (805, 28, 4, 128, 16, [5000, 3000, 9000, 40, 0], 100),
+    (806, 16, 2, 128, 64, [20000, 7000, 129], 40),
+    (807, 8, 1, 64, 16, [40960], 256),
 ]
 
 
 @pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx,K", QD_CASES)
-def test_quest_decode_random_fused_equals_separate(seed, Hq, Hkv, D, bs, ctx, K, monkeypatch):
+def test_quest_decode_random_paths_agree(seed, Hq, Hkv, D, bs, ctx, K, monkeypatch):
     w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv,
                               head_dim=D, block_size=bs, context_lens=ctx)
     d = Dev(w)
     kmin, kmax = _meta(d, w)
-    monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "fused")
-    out_f, sel_f = _decode(d, w, kmin, kmax, K)
-    monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "separate")
-    out_s, sel_s = _decode(d, w, kmin, kmax, K)
     omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, bs)
     exp = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens, bs, K)
-    assert np.array_equal(sel_f, exp) and np.array_equal(sel_s, exp)
     ref = oracle.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache,
                                                w.block_tables, w.context_lens, exp, w.scale)
-    assert max_abs(out_f, ref) <= ATOL and max_abs(out_s, ref) <= ATOL
-    assert max_abs(out_f, out_s) <= 1e-5
-    for b, L in enumerate(ctx):
-        if L == 0:
-            assert (out_f[b] == 0).all() and (sel_f[b] == -1).all()
+    outs = {}
+    for path in ("fused", "separate"):
+        monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", path)
+        out, sel = _decode(d, w, kmin, kmax, K)
+        assert np.array_equal(sel, exp), f"{path}: selection differs from the oracle"
+        err = max_abs(out, ref)
+        print(f"seed {seed} {path}: max-abs {err:.3e}")
+        assert err <= ATOL, path
+        for b, L in enumerate(ctx):
+            if L == 0:
+                assert (out[b] == 0).all() and (sel[b] == -1).all(), path
+        outs[path] = out
+    assert max_abs(outs["fused"], outs["separate"]) <= 1e-5
 
 
-def test_quest_decode_config3_fused_equals_separate(monkeypatch):
-    """The 8K-average batch (256 pairs: the one-launch path by default) against the
-    two separate calls, every sequence."""
-    w = workload(3)
+def test_quest_decode_workspace_reused():
+    """One workspace through calls of different shapes (one launch and two calls),
+    stale contents left in it between calls."""
+    cases = [(workloads.random_case(810 + i, batch=len(ctx), num_q_heads=28, num_kv_heads=4,
+                                    head_dim=128, block_size=16, context_lens=ctx), K)
+             for i, (ctx, K) in enumerate([([9000, 4000], 200), ([3000, 700, 6000, 33], 64),
+                                           ([12000], 300)])]
+    need = max(gp.quest_decode_workspace_bytes(w.batch, 28, 4, 128, 16, w.max_blocks_per_seq, K)
+               for w, K in cases)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for w, K in cases:
+            d = Dev(w)
+            kmin, kmax = _meta(d, w)
+            out, sel = gp.quest_decode(d.q, d.kc, d.vc, kmin, kmax, d.bt, d.ctx, topk_blocks=K,
+                                       max_context_len=w.max_context_len, scale=float(w.scale),
+                                       workspace=ws)
+            torch.cuda.synchronize()
+            omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+            exp = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens,
+                                           16, K)
+            assert np.array_equal(sel.cpu().numpy(), exp), (rep, w.batch)
+            ref = oracle.sparse_paged_attention_decode(w.query, w.key_cache, w.value_cache,
+                                                       w.block_tables, w.context_lens, exp,
+                                                       w.scale)
+            assert max_abs(out.cpu().numpy(), ref) <= ATOL, (rep, w.batch)
+
+
+@pytest.mark.parametrize("config", [3, 4])
+def test_quest_decode_paths_agree_full_size(config, monkeypatch):
+    """The 8K-average batch (256 pairs) and the 40960-token batch (16 pairs) on the
+    one-launch path, every sequence against the two separate calls."""
+    w = workload(config)
     d = Dev(w)
     kmin, kmax = _meta(d, w)
     K = w.topk_list[0]
-    out_f, sel_f = _decode(d, w, kmin, kmax, K)
     monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "separate")
     out_s, sel_s = _decode(d, w, kmin, kmax, K)
-    assert np.array_equal(sel_f, sel_s)
-    assert max_abs(out_f, out_s) <= 1e-5
+    monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "fused")
+    out, sel = _decode(d, w, kmin, kmax, K)
+    assert np.array_equal(sel, sel_s)
+    assert max_abs(out, out_s) <= 1e-5
