@@ -2,14 +2,16 @@
  * gpkv.h -- C ABI of the paged GQA decode-attention library for AMD MI355X (gfx950).
  *
  * Single-token decode attention over a paged KV cache, its write path and the
- * Quest long-context variant. Five operations:
+ * Quest long-context variant. The operations:
  *
  *   gpkv_reshape_and_cache           write new tokens' K/V rows into the cache
  *   gpkv_reshape_and_cache_quest     ... and update those blocks' Quest key min / max
  *   gpkv_paged_attention_decode      dense GQA paged attention (split-KV + combine)
+ *   gpkv_paged_attention_decode_noalloc  ... without a workspace (fixed device array)
  *   gpkv_quest_block_metadata        per-block, per-channel key min / max
  *   gpkv_quest_select_topk           Quest block scores + Top-K per KV head
  *   gpkv_sparse_paged_attention_decode  exact attention over the selected blocks
+ *   gpkv_quest_decode                selection and sparse attention in one call
  *   ..._fp8 variants of the write and both attention calls over E4M3 caches
  *   gpkv_paged_attention_varlen      multi-token queries (causal, right-aligned)
  *
