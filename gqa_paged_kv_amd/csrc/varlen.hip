@@ -233,6 +233,10 @@ struct VarlenParams {
   const int* cu;             // [B + 1] query row offsets
   long long NB;
   int max_blocks, max_ctx, num_splits, split_tokens, n_rt, total_q, B;
+  int balanced;              // 1: balanced schedule (equal shares of the tile space)
+  int slot_rows;             // balanced: row-tile rows per partial slot
+  int nwg;                   // balanced: workgroups of the split kernel
+  int share_ok, rt;          // balanced: the split kernel's shared-LDS path and row tiles per wave
 };
 
 // Partial rows of sequence b's row tiles sit at tiles tile_base(b) + rt: the
@@ -287,6 +291,49 @@ __device__ __forceinline__ int sequence_of(const int* s_pref, int B, int u) {
   return lo;
 }
 
+constexpr int kShareTiles = 2 * kWaves;   // row tiles of one shared unit
+constexpr int kShareMinTiles = 4;
+
+// A sequence's work under the balanced schedule: groups of grp_rt row tiles (a
+// shared group: one KV head per unit, so `heads` = H_kv units per group; a per-head
+// group: one unit whose waves take the KV heads), each group's unit covering the
+// 32-position tiles its last row sees. Units are ordered head-major, group minor.
+struct SeqGeom {
+  int ctx, q0, qn, rows, n_grp, grp_rt, heads;
+  bool shared;
+};
+
+// share_ok: the launched kernel has the shared-LDS path; rt: its row tiles per wave.
+__device__ __forceinline__ SeqGeom seq_geom(const VarlenParams& p, int b, bool share_ok, int rt) {
+  SeqGeom sg;
+  sg.ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+  varlen_rows(p, b, sg.q0, sg.qn);
+  sg.rows = sg.qn * p.c.G;
+  const int n_rt = (sg.rows + 15) / 16;
+  sg.shared = share_ok && n_rt >= kShareMinTiles;
+  sg.grp_rt = sg.shared ? kShareTiles : rt;
+  sg.n_grp = (sg.qn > 0 && sg.ctx > 0) ? (n_rt + sg.grp_rt - 1) / sg.grp_rt : 0;
+  sg.heads = sg.shared ? p.c.Hkv : 1;
+  return sg;
+}
+
+// Positions the last row of group grp sees (the group's other rows see fewer).
+__device__ __forceinline__ int group_limit(const SeqGeom& sg, int G, int grp) {
+  int m_last = 16 * sg.grp_rt * (grp + 1);
+  m_last = (m_last < sg.rows ? m_last : sg.rows) - 1;
+  int lim = sg.ctx - sg.qn + m_last / G + 1;
+  return lim < 0 ? 0 : (lim > sg.ctx ? sg.ctx : lim);
+}
+__device__ __forceinline__ int group_tiles(const SeqGeom& sg, int G, int grp) {
+  return (group_limit(sg, G, grp) + 31) >> 5;
+}
+// Tiles of one head's units (every head of a shared sequence has the same).
+__device__ __forceinline__ int head_tiles(const SeqGeom& sg, int G) {
+  int t = 0;
+  for (int grp = 0; grp < sg.n_grp; ++grp) t += group_tiles(sg, G, grp);
+  return t;
+}
+
 // Work units of multi-token queries: (sequence, group of RT row tiles, KV split),
 // split-major within a sequence so that the units running together read the
 // same split; a unit's waves take the KV heads. Sequences with kShareMinTiles row
@@ -296,14 +343,119 @@ __device__ __forceinline__ int sequence_of(const int* s_pref, int B, int u) {
 // launched for a sequence's missing row tiles. Two waves per SIMD (at most 256
 // registers) let one wave's MFMA work hide the other's loads; RT = 2 fits without
 // spilling at D = 128.
-constexpr int kShareTiles = 2 * kWaves;   // row tiles of one shared unit
-constexpr int kShareMinTiles = 4;
+
+// Balanced schedule: the flattened (unit, 32-position tile) space of the whole batch
+// is shared out equally, [w*W/N, (w+1)*W/N) for workgroup w of N (all resident), so
+// no workgroup waits for a last round. A workgroup runs the segments of the units
+// its share touches; each segment writes its partial rows (normalised O, base-2
+// lse) to slot w + (global index of the unit), unique because the shares are
+// ordered; the combine merges the slots of the workgroups that covered a unit.
+template <int D, int RT, bool FP8>
+__device__ __forceinline__ void attn_varlen_balanced(const VarlenParams& p, int* s_pb, int* s_pref,
+                                                     int* s_upref, int* s_wave,
+                                                     unsigned char* s_kv) {
+  constexpr bool kShared = RT > 1 && !FP8;
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
+  const int bs_log2 = __builtin_ctz((unsigned)bs);
+  const int r = tid & 15;
+  auto geom = [&](int b) { return seq_geom(p, b, kShared, RT); };
+  const int W = sequence_prefix(p.B, s_pref, s_wave, [&](int b) {
+    const SeqGeom sg = geom(b);
+    return sg.heads * head_tiles(sg, G);
+  });
+  sequence_prefix(p.B, s_upref, s_wave, [&](int b) {
+    const SeqGeom sg = geom(b);
+    return sg.heads * sg.n_grp;
+  });
+  const int N = (int)gridDim.x, w = (int)blockIdx.x;
+  const int s0 = (int)((long long)w * W / N), s1 = (int)((long long)(w + 1) * W / N);
+  if (s0 >= s1) return;
+  int b = sequence_of(s_pref, p.B, s0);
+  int pos = s0;
+  while (pos < s1) {
+    while (s_pref[b + 1] <= pos) ++b;   // skips sequences without work; pos < W
+    const SeqGeom sg = geom(b);
+    // The unit holding offset o: head h = o / (work per head), then its group.
+    const int hw = head_tiles(sg, G);
+    const int o = pos - s_pref[b];
+    const int h = o / hw;
+    int grp = 0, uoff = h * hw, wk = group_tiles(sg, G, 0);
+    while (o >= uoff + wk) {
+      uoff += wk;
+      ++grp;
+      wk = group_tiles(sg, G, grp);
+    }
+    const int ta = o - uoff;
+    const int tb = (s1 - s_pref[b] - uoff < wk) ? s1 - s_pref[b] - uoff : wk;
+    pos = s_pref[b] + uoff + tb;
+    const int slot = w + s_upref[b] + h * sg.n_grp + grp;
+    const int t0 = 32 * ta;
+    const int lim = group_limit(sg, G, grp);
+    const int span = (32 * (tb - ta) < lim - t0) ? 32 * (tb - ta) : lim - t0;
+    const int e0 = t0 >> bs_log2;
+    int n_ent = ((t0 + span - 1) >> bs_log2) - e0 + 1;
+    n_ent = n_ent < kMaxTable ? n_ent : kMaxTable;   // the host sizes shares below this
+    const int nb = (sg.ctx + bs - 1) / bs;
+    __syncthreads();   // the previous segment's table is no longer read
+    for (int e = tid; e < n_ent; e += kWaves * 64) {
+      const int lb = e0 + e;
+      const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
+      s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
+    }
+    __syncthreads();
+    auto desc = [&](int uu, int& pb, int& row0, int& nv) {
+      const int tok = t0 + 16 * uu;
+      const int ei = (tok >> bs_log2) - e0;
+      const int x = ei < n_ent ? s_pb[ei] : -1;
+      row0 = tok & (bs - 1);
+      int n = t0 + span - tok;
+      n = n < 0 ? 0 : (n > 16 ? 16 : n);
+      if (x < 0) n = 0;
+      nv = uniform(n);
+      pb = uniform(x < 0 ? 0 : x);
+    };
+    // Row tile rt of the sequence against KV head g, into slot row srow.
+    auto fill = [&](auto& tiles, int t, int rt, int g, int srow) {
+      const int m0 = 16 * rt;
+      const int n_rows = sg.rows - m0 < 0 ? 0 : (sg.rows - m0 < 16 ? sg.rows - m0 : 16);
+      const int m = m0 + r, j = m / G;
+      tiles.q[t] = r < n_rows
+                       ? p.c.q + ((size_t)(sg.q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
+                       : nullptr;
+      tiles.n_rows[t] = n_rows;
+      tiles.limit[t] = sg.ctx - sg.qn + j + 1;
+      const size_t row_blk = (size_t)slot * p.slot_rows + srow;
+      tiles.o[t] = p.part_o + row_blk * 16 * D;
+      tiles.lse[t] = p.part_lse + row_blk * 16;
+    };
+    const int n_sub = (span + 15) / 16;
+    if constexpr (kShared) {
+      if (sg.shared) {
+        RowTiles<2> tiles;
+        const int rt0 = grp * kShareTiles + 2 * wave;
+        fill(tiles, 0, rt0, h, 2 * wave);
+        fill(tiles, 1, rt0 + 1, h, 2 * wave + 1);
+        attend_shared<D>(p.c, h, n_sub, desc, t0, tiles, s_kv);
+        continue;
+      }
+    }
+    for (int g = wave; g < Hkv; g += kWaves) {
+      RowTiles<RT> tiles;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) fill(tiles, t, grp * RT + t, g, g * RT + t);
+      attend_head<D, FP8, true, RT>(p.c, g, n_sub, desc, t0, tiles);
+    }
+  }
+}
 
 template <int D, int RT, bool FP8>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 2))) void attn_varlen_kernel(const VarlenParams p) {
   constexpr bool kShared = RT > 1 && !FP8;   // E4M3 caches: per-head units only
   __shared__ int s_pb[kMaxTable];
   __shared__ int s_pref[kMaxBalBatch + 1];
+  __shared__ int s_upref[kMaxBalBatch + 1];   // balanced: unit prefix over sequences
   __shared__ int s_wave[kWaves];
   __shared__ __align__(16) unsigned char s_kv[kShared ? kShareLdsBytes(D) : 16];
   const int tid = threadIdx.x;
@@ -314,6 +466,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
   auto n_tiles_of = [&](int qn) { return (qn * G + 15) / 16; };
   auto n_groups = [&](int qn) { return (n_tiles_of(qn) + RT - 1) / RT; };
   auto shared_seq = [&](int qn) { return kShared && n_tiles_of(qn) >= kShareMinTiles; };
+  if (p.balanced) {
+    attn_varlen_balanced<D, RT, FP8>(p, s_pb, s_pref, s_upref, s_wave, s_kv);
+    return;
+  }
   const int U = sequence_prefix(p.B, s_pref, s_wave, [&](int b) {
     const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
     int q0, qn;
@@ -408,12 +564,82 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
 
 // Merge of each (sequence, row tile, KV head) over its splits, written to the
 // flattened output rows; the triples taken grid-stride.
+// Balanced schedule: a row tile's unit (its group, and its head on the shared path)
+// covers tiles [P, P + work) of the flattened space; workgroups w_a .. w_b held them
+// and left partial rows in slots w + (global unit index).
+template <int D>
+__device__ __forceinline__ void attn_varlen_combine_balanced(const VarlenParams& p, int* s_pref,
+                                                             int* s_upref, int* s_cpref,
+                                                             int* s_wave) {
+  constexpr int TPR = D / 4;
+  const int G = p.c.G, Hq = p.c.Hq, Hkv = p.c.Hkv;
+  const bool share_ok = p.share_ok != 0;
+  const long long W = sequence_prefix(p.B, s_pref, s_wave, [&](int b) {
+    const SeqGeom sg = seq_geom(p, b, share_ok, p.rt);
+    return sg.heads * head_tiles(sg, G);
+  });
+  sequence_prefix(p.B, s_upref, s_wave, [&](int b) {
+    const SeqGeom sg = seq_geom(p, b, share_ok, p.rt);
+    return sg.heads * sg.n_grp;
+  });
+  const int U = sequence_prefix(p.B, s_cpref, s_wave, [&](int b) {
+    int q0, qn;
+    varlen_rows(p, b, q0, qn);
+    return (qn * G + 15) / 16 * Hkv;
+  });
+  const long long N = p.nwg;
+  for (int u = blockIdx.x; u < U; u += gridDim.x) {
+    const int b = sequence_of(s_cpref, p.B, u);
+    const int local = u - s_cpref[b];
+    const int rt = local / Hkv, g = local - (local / Hkv) * Hkv;
+    const SeqGeom sg = seq_geom(p, b, share_ok, p.rt);
+    const int rows = sg.qn * G;
+    const int m0 = 16 * rt;
+    const int n_rows = rows - m0 < 16 ? rows - m0 : 16;
+    int n_units = 0, w_a = 0, k = 0, srow = 0;
+    if (sg.n_grp > 0) {
+      const int grp = rt / sg.grp_rt, t = rt - grp * sg.grp_rt;
+      const int hu = sg.shared ? g : 0;
+      srow = sg.shared ? t : g * sg.grp_rt + t;
+      k = hu * sg.n_grp + grp;
+      long long P = s_pref[b] + (long long)hu * head_tiles(sg, G);
+      for (int x = 0; x < grp; ++x) P += group_tiles(sg, G, x);
+      const int wk = group_tiles(sg, G, grp);
+      if (wk > 0) {
+        w_a = (int)(((P + 1) * N - 1) / W);
+        n_units = (int)(((P + wk) * N - 1) / W) - w_a + 1;
+      }
+    }
+    const size_t blk0 = ((size_t)w_a + s_upref[b] + k) * p.slot_rows + srow;
+    // A workgroup inside [w_a, w_b] with an empty share (only when W < N) wrote nothing.
+    auto live = [&](int x) {
+      const long long ww = w_a + x;
+      return ww * W / N < (ww + 1) * W / N;
+    };
+    for (int i = threadIdx.x; i < n_rows * TPR; i += kCombineThreads) {
+      const int rr = i / TPR, c4 = i - (i / TPR) * TPR;
+      const float* lse0 = p.part_lse + blk0 * 16 + rr;
+      const float* o0 = p.part_o + (blk0 * 16 + rr) * D + 4 * c4;
+      const f32x4 o = merge_rows<8>(n_units, lse0, (size_t)p.slot_rows * 16, o0,
+                                    (size_t)p.slot_rows * 16 * D, live);
+      const int m = m0 + rr, j = m / G;
+      *(f32x4*)(p.out + ((size_t)(sg.q0 + j) * Hq + (size_t)g * G + (m - j * G)) * D + 4 * c4) = o;
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void attn_varlen_combine_kernel(const VarlenParams p) {
   __shared__ int s_pref[kMaxBalBatch + 1];
   __shared__ int s_wave[kWaves];
   constexpr int TPR = D / 4;   // threads per row, 4 channels each
   const int G = p.c.G, Hq = p.c.Hq, Hkv = p.c.Hkv;
+  if (p.balanced) {
+    __shared__ int s_upref[kMaxBalBatch + 1];
+    __shared__ int s_cpref[kMaxBalBatch + 1];
+    attn_varlen_combine_balanced<D>(p, s_pref, s_upref, s_cpref, s_wave);
+    return;
+  }
   const int U = sequence_prefix(p.B, s_pref, s_wave, [&](int b) {
     int q0, qn;
     varlen_rows(p, b, q0, qn);
@@ -451,6 +677,9 @@ constexpr int kVarlenRT = 2;   // row tiles per wave when a chunk spans more tha
 struct VarlenPlan {
   int n_rt, split_tokens, num_splits;
   size_t o_bytes, lse_bytes;
+  // Balanced schedule: workgroups, row tiles per partial slot, and its workspace.
+  int rt, nwg, slot_rows;
+  size_t bal_o_bytes, bal_lse_bytes;
 };
 
 // Row tiles of the longest chunk (the grid), split size, and the workspace for at
@@ -481,7 +710,40 @@ static VarlenPlan make_varlen_plan(int B, int total_q, int max_q_len, int Hq, in
   const size_t u = (size_t)tiles * Hkv * pl.num_splits;
   pl.o_bytes = align256(u * 16 * D * sizeof(float));
   pl.lse_bytes = align256(u * 16 * sizeof(float));
+
+  // Balanced schedule. Units: at most H_kv * (ceil(rt / 8) + 1) per sequence on the
+  // shared path and ceil(rt / RT) + 1 on the per-head path, each covering at most
+  // ceil(max_ctx / 32) tiles. Workgroups: all resident at once (two per CU with
+  // row-tile pairs, three with single row tiles), and enough that no share holds
+  // more tiles than one staged block-table chunk covers.
+  pl.rt = pl.n_rt > 1 ? kVarlenRT : 1;
+  pl.slot_rows = kShareTiles > pl.rt * Hkv ? kShareTiles : pl.rt * Hkv;
+  const long long total_rt = ((long long)total_q * G + 15) / 16 + B;
+  const long long u_bound = (long long)Hkv * ((total_rt + kShareTiles - 1) / kShareTiles + B) +
+                            (total_rt + pl.rt - 1) / pl.rt + B;
+  const long long w_bound = u_bound * (((long long)max_ctx + 31) / 32);
+  const long long seg_cap = (long long)(kMaxTable - 1) * bs / 32 - 1;
+  long long nwg = (long long)(pl.rt == 1 ? 3 : 2) * balanced_capacity();
+  const long long need = (w_bound + seg_cap - 2) / (seg_cap - 1);
+  if (nwg < need) nwg = need;
+  pl.nwg = (int)(nwg < (1LL << 30) ? nwg : (1LL << 30));
+  const size_t slots = (size_t)pl.nwg + (size_t)u_bound;
+  pl.bal_o_bytes = align256(slots * pl.slot_rows * 16 * D * sizeof(float));
+  pl.bal_lse_bytes = align256(slots * pl.slot_rows * 16 * sizeof(float));
   return pl;
+}
+
+// The balanced schedule by default: on the 8K-average mixed batch (six chunks of
+// 32-512 tokens, 58 single tokens) 464 us against 502 us with fixed 2048-position
+// splits, and on eight 512-token chunks 984 against 1010 us (MI355X). Timestamps show
+// every workgroup then holds 131-132 tiles and ends between 285 and 402 us: what
+// remains is the per-tile cost, which varies with what shares the CU.
+// GPKV_VARLEN_SCHEDULE=split|balanced forces the schedule (tuning and test switch,
+// read per call); the workspace fits either.
+static bool varlen_balanced() {
+  const char* f = getenv("GPKV_VARLEN_SCHEDULE");
+  if (f && strcmp(f, "split") == 0) return false;
+  return true;
 }
 
 }  // namespace gpkv
@@ -500,7 +762,8 @@ extern "C" size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int
     return 0;
   const VarlenPlan pl = make_varlen_plan(batch, total_q, max_q_len, num_q_heads, num_kv_heads,
                                          head_dim, block_size, max_context_len);
-  return pl.o_bytes + pl.lse_bytes;
+  const size_t split = pl.o_bytes + pl.lse_bytes, bal = pl.bal_o_bytes + pl.bal_lse_bytes;
+  return split > bal ? split : bal;
 }
 
 template <bool FP8>
@@ -545,7 +808,8 @@ static int varlen_run(bool fp8, float* out, const void* query, const void* key_c
   if (pl.num_splits > 65535)
     return fail(GPKV_ERR_SHAPE, "%s: max_context_len=%d needs too many splits", fn,
                 max_context_len);
-  const size_t need = pl.o_bytes + pl.lse_bytes;
+  const bool balanced = varlen_balanced();
+  const size_t need = balanced ? pl.bal_o_bytes + pl.bal_lse_bytes : pl.o_bytes + pl.lse_bytes;
   if (!workspace || workspace_bytes < need)
     return fail(GPKV_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn,
                 workspace ? workspace_bytes : (size_t)0, need);
@@ -564,7 +828,7 @@ static int varlen_run(bool fp8, float* out, const void* query, const void* key_c
   vp.c.bs = block_size;
   vp.c.qk_scale_log2 = scale * 1.4426950408889634f;
   vp.part_o = (float*)workspace;
-  vp.part_lse = (float*)((char*)workspace + pl.o_bytes);
+  vp.part_lse = (float*)((char*)workspace + (balanced ? pl.bal_o_bytes : pl.o_bytes));
   vp.out = out;
   vp.block_tables = block_tables;
   vp.ctx = context_lens;
@@ -577,6 +841,11 @@ static int varlen_run(bool fp8, float* out, const void* query, const void* key_c
   vp.n_rt = pl.n_rt;
   vp.total_q = total_q;
   vp.B = batch;
+  vp.balanced = balanced ? 1 : 0;
+  vp.slot_rows = pl.slot_rows;
+  vp.nwg = pl.nwg;
+  vp.rt = pl.rt;
+  vp.share_ok = (pl.rt > 1 && !fp8) ? 1 : 0;
   // One row tile per wave for decode-sized chunks; otherwise kVarlenRT tiles share
   // every K / V tile a wave loads. Both kernels take their work units grid-stride
   // from a fixed grid of at most four workgroups per CU.
@@ -584,7 +853,8 @@ static int varlen_run(bool fp8, float* out, const void* query, const void* key_c
   const long long tiles = ((long long)total_q * vp.c.G + 15) / 16 + batch;
   const long long units_max = (tiles / rt_per_wave + batch) * pl.num_splits;
   const long long cap = 4LL * balanced_capacity();
-  const dim3 grid((unsigned)(units_max < cap ? units_max : cap)), block(kWaves * 64);
+  const dim3 grid(balanced ? (unsigned)pl.nwg : (unsigned)(units_max < cap ? units_max : cap)),
+      block(kWaves * 64);
   if (fp8)
     launch_varlen<true>(rt_per_wave > 1, head_dim, grid, block, s, vp);
   else

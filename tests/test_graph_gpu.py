@@ -177,9 +177,11 @@ def test_graph_replay_equals_eager(case, fused, one_call, monkeypatch):
             assert torch.equal(got[k], ref[k]), f"replay {rep}: {k} differs from eager"
 
 
-def test_graph_replay_varlen_equals_eager():
+@pytest.mark.parametrize("schedule", ["split", "balanced"])
+def test_graph_replay_varlen_equals_eager(schedule, monkeypatch):
     """The multi-token call (chunks on the LDS-shared path, single tokens on the
     per-head path, and its combine) captured and replayed: equal to eager."""
+    monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", schedule)
     w = workloads.varlen_case(402, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
                               context_lens=[900, 33, 2500, 16, 1200, 700],
                               q_lens=[1, 7, 64, 16, 3, 1])

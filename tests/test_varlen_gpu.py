@@ -43,8 +43,15 @@ VARLEN_CASES = [
 ]
 
 
+# Both schedules of the multi-token call: fixed KV splits, and equal shares of the
+# flattened (unit, tile) space over the resident workgroups.
+VARLEN_SCHEDULES = ["split", "balanced"]
+
+
+@pytest.mark.parametrize("schedule", VARLEN_SCHEDULES)
 @pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx,ql", VARLEN_CASES)
-def test_varlen_random(seed, Hq, Hkv, D, bs, ctx, ql):
+def test_varlen_random(seed, Hq, Hkv, D, bs, ctx, ql, schedule, monkeypatch):
+    monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", schedule)
     w = workloads.varlen_case(seed, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                               context_lens=ctx, q_lens=ql)
     _, out = _run(w)
@@ -55,12 +62,16 @@ def test_varlen_random(seed, Hq, Hkv, D, bs, ctx, ql):
     assert (out[np.all(ref == 0, axis=(1, 2))] == 0).all(), "rows that see nothing are zero"
 
 
-@pytest.mark.parametrize("split", [256, 2048])
+@pytest.mark.parametrize("split", [256, 2048, "balanced"])
 def test_varlen_shared_tiles_at_the_causal_bound(split, monkeypatch):
     """Chunks on the shared-LDS path (at least four row tiles) whose first row's causal
     bound falls on a 32-position tile edge, one short of it and one past it, so that the
     last unmasked tile and the first masked one meet exactly there."""
-    monkeypatch.setenv("GPKV_SPLIT_TOKENS", str(split))
+    if split == "balanced":
+        monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", "balanced")
+    else:
+        monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", "split")
+        monkeypatch.setenv("GPKV_SPLIT_TOKENS", str(split))
     ctx = [1055, 1056, 1058, 2080, 96]
     ql = [32, 33, 31, 64, 96]          # first-row bounds 1024, 1024, 1028, 2017, 1
     w = workloads.varlen_case(721, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
@@ -73,7 +84,8 @@ def test_varlen_shared_tiles_at_the_causal_bound(split, monkeypatch):
 
 @pytest.mark.parametrize("split", [128, 256, 512, 2048])
 def test_varlen_split_sizes(split, monkeypatch):
-    """Chunks whose rows end in different splits of the KV range."""
+    """Chunks whose rows end in different splits of the KV range (split schedule)."""
+    monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", "split")
     monkeypatch.setenv("GPKV_SPLIT_TOKENS", str(split))
     w = workloads.varlen_case(710, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
                               context_lens=[4000, 2500, 129, 700], q_lens=[300, 1, 129, 20])
@@ -81,8 +93,10 @@ def test_varlen_split_sizes(split, monkeypatch):
     assert max_abs(out, _ref(w)) <= ATOL
 
 
-def test_varlen_single_tokens_equal_decode():
+@pytest.mark.parametrize("schedule", VARLEN_SCHEDULES)
+def test_varlen_single_tokens_equal_decode(schedule, monkeypatch):
     """q_len = 1 everywhere: the same rows as the decode call."""
+    monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", schedule)
     ctx = [900, 33, 2500, 16, 0, 700]
     w = workloads.varlen_case(711, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
                               context_lens=ctx, q_lens=[1] * 6)
@@ -95,9 +109,11 @@ def test_varlen_single_tokens_equal_decode():
     assert max_abs(out, dec) <= 1e-5
 
 
-def test_varlen_mixed_batch_8k():
+@pytest.mark.parametrize("schedule", VARLEN_SCHEDULES)
+def test_varlen_mixed_batch_8k(schedule, monkeypatch):
     """An 8K-average batch in which a few sequences bring prefill chunks and the rest
     decode one token each; every query row against the oracle."""
+    monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", schedule)
     rng = np.random.default_rng(712)
     ctx = np.clip(np.round(rng.normal(8192, 2048, 64)), 2048, 16384).astype(np.int32)
     ql = np.ones(64, np.int32)
@@ -105,14 +121,26 @@ def test_varlen_mixed_batch_8k():
     w = workloads.varlen_case(712, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
                               context_lens=ctx, q_lens=ql)
     _, out = _run(w)
-    err = max_abs(out, _ref(w))
-    print(f"mixed 8K batch: varlen max-abs {err:.3e} over all {out.shape[0]} query rows")
+    err = max_abs(out, _mixed_ref(w))
+    print(f"mixed 8K batch ({schedule}): varlen max-abs {err:.3e} over all {out.shape[0]} query rows")
     assert err <= ATOL
 
 
-def test_varlen_bad_offsets_read_as_empty():
+_MIXED_REF = {}
+
+
+def _mixed_ref(w):
+    """The oracle over the mixed batch, computed once for both schedules."""
+    if "ref" not in _MIXED_REF:
+        _MIXED_REF["ref"] = _ref(w)
+    return _MIXED_REF["ref"]
+
+
+@pytest.mark.parametrize("schedule", VARLEN_SCHEDULES)
+def test_varlen_bad_offsets_read_as_empty(schedule, monkeypatch):
     """A decreasing cu_seqlens entry makes that sequence empty; the others are
     unaffected and nothing outside the buffers is touched."""
+    monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", schedule)
     w = workloads.varlen_case(713, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
                               context_lens=[40, 50, 60], q_lens=[4, 3, 5])
     d = Dev(w)
@@ -165,8 +193,10 @@ FP8_VARLEN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("schedule", VARLEN_SCHEDULES)
 @pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx,ql", FP8_VARLEN_CASES)
-def test_varlen_fp8_random(seed, Hq, Hkv, D, bs, ctx, ql):
+def test_varlen_fp8_random(seed, Hq, Hkv, D, bs, ctx, ql, schedule, monkeypatch):
+    monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", schedule)
     w = workloads.varlen_case(seed, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                               context_lens=ctx, q_lens=ql)
     kq, vq, ks, vs = _fp8_case(w)
