@@ -18,11 +18,57 @@ namespace gpkv {
 
 // Causal rows of one KV head shared by the whole workgroup: each wave carries two
 // row tiles, and every 32-token K / V tile is loaded once per workgroup into LDS
-// (double-buffered, loads for the next tile in flight while this one is used)
-// instead of once per wave. Same arithmetic as attend_head; every wave of the
-// workgroup must call it with the same n_sub, desc and pos0 (it has barriers).
-constexpr int kShareRowBytes(int D) { return 2 * D + 16; }   // padded LDS row
-constexpr int kShareLdsBytes(int D) { return 2 * 2 * 32 * kShareRowBytes(D); }
+// instead of once per wave. Same arithmetic as attend_head (S^T = K Q^T and
+// O^T += V^T P^T on MFMA, P as a bf16 hi + lo pair); every wave of the workgroup
+// must call it with the same n_sub, desc and pos0 (it has barriers).
+//
+// LDS holds two K and two V tiles:
+//   - K token-major, rows padded to 2D + 16 bytes: lane (r, qd) reads token r's
+//     channels 32s + 8qd .. +8 of k-step s as one 16-byte A operand;
+//   - V channel-major as token pairs: row c (64 bytes) holds the 16 words
+//     (V[2p][c], V[2p+1][c]), word p stored at position 4((p >> 1) & 3) + (p & 1) +
+//     2(p >> 3), in 16-byte chunks whose index is XORed with (c >> 2) & 3. The
+//     four words lane (r, qd) feeds to P.V tile j (channel 16j + r, contraction
+//     slots 8qd .. +8: tokens 4qd .. +4 of sub-tile 0, then of sub-tile 1) are
+//     then one aligned 16-byte chunk, and the 16 lanes of a row group hit
+//     distinct banks. The staging threads do the transpose once per workgroup
+//     instead of every wave repacking V with v_perm.
+// Pipelining: tile k + 1's q.k MFMAs are issued before tile k's softmax, so the
+// matrix cores work while the wave runs the softmax. K is staged two tiles ahead
+// and V one tile ahead, double-buffered, one barrier per tile.
+// Lazy rescale: the reference max of a row moves only when the tile's maximum
+// exceeds it by more than kRescaleSlack (log2 units), so the weights stay below
+// 2^kRescaleSlack and the rescale of O runs on few tiles; the result is the same
+// softmax, normalised by the same reference.
+constexpr int kShareKRowBytes(int D) { return 2 * D + 16; }
+constexpr int kShareKTileBytes(int D) { return 32 * kShareKRowBytes(D); }
+constexpr int kShareVTileBytes(int D) { return 64 * D; }
+constexpr int kShareLdsBytes(int D) { return 2 * (kShareKTileBytes(D) + kShareVTileBytes(D)); }
+constexpr float kRescaleSlack = 8.f;
+
+// Maxima of raw MFMA results without the quieting of signalling NaNs that fmaxf
+// adds in IEEE mode (one extra instruction per operand): a NaN score makes the
+// row's output NaN either way.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max_across_rows_raw(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+struct TileDesc {   // the two 16-token sub-tiles of one 32-token tile (wave-uniform)
+  int pb[2], row0[2], nv[2];
+};
 
 template <int D, class Desc>
 __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_sub,
@@ -30,13 +76,15 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
                                               unsigned char* s_kv) {
   constexpr int RT = 2;
   constexpr int KSTEPS = D / 32;
-  constexpr int CPL = D / 16;
-  constexpr int ROWB = kShareRowBytes(D);
-  constexpr int TILEB = 32 * ROWB;           // one 32-token K or V tile in LDS
-  constexpr int PIECES = 2 * D / 16;         // 16-byte pieces per token row
-  constexpr int PER_T = 32 * PIECES / (kWaves * 64);   // pieces per thread per tile
-  static_assert(PER_T >= 1 && 32 * PIECES == PER_T * kWaves * 64, "tile split");
-  typedef typename VecT<D>::type vvec;
+  constexpr int NJ = D / 16;                 // 16-channel tiles of O^T
+  constexpr int KROWB = kShareKRowBytes(D);
+  constexpr int KTILEB = kShareKTileBytes(D);
+  constexpr int VTILEB = kShareVTileBytes(D);
+  constexpr int KPIECES = 2 * D / 16;        // 16-byte pieces per K token row
+  constexpr int K_PER_T = 32 * KPIECES / (kWaves * 64);   // K pieces per thread per tile
+  static_assert(K_PER_T >= 1 && 32 * KPIECES == K_PER_T * kWaves * 64, "K tile split");
+  constexpr int VPAIRS = D / 2;              // channel pairs: one V staging item per (chunk, pair)
+  static_assert(4 * VPAIRS <= kWaves * 64, "V tile split");
   const int tid = threadIdx.x, lane = tid & 63;
   const int r = lane & 15, qd = lane >> 4;
   const bool active = rows.n_rows[0] > 0;   // the wave's second tile is empty if its first is
@@ -44,162 +92,219 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
   // smallest: a tile whose positions all lie below it, with every row of both
   // sub-tiles valid, needs no mask.
   const int lim_min = __builtin_amdgcn_readfirstlane(rows.limit[0]);
+  // Scores are scaled inside the exponent's FMA, by |scale|; a negative scale
+  // flips the sign of q instead (exact in bf16).
+  const float scl = fabsf(c.qk_scale_log2);
+  const unsigned qflip = c.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
+  unsigned char* const kbuf = s_kv;
+  unsigned char* const vbuf = s_kv + 2 * KTILEB;
 
   u32x4 qf[RT][KSTEPS];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
-      qf[t][s] = rows.q[t] != nullptr ? *(const u32x4*)(rows.q[t] + 32 * s + 8 * qd)
-                                      : u32x4{0u, 0u, 0u, 0u};
+      qf[t][s] = rows.q[t] != nullptr
+                     ? (*(const u32x4*)(rows.q[t] + 32 * s + 8 * qd)) ^ qflip
+                     : u32x4{0u, 0u, 0u, 0u};
   }
-  f32x4 oacc[RT][CPL];
-  float m_run[RT], l_run[RT];
+  f32x4 oacc[RT][NJ];
+  float m_run[RT], m_use[RT], l_run[RT];   // reference max (base 2), its finite stand-in, sum
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) oacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) oacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[t] = -INFINITY;
+    m_use[t] = 0.f;
     l_run[t] = 0.f;
   }
 
-  // Staging: piece i of a tile is token (tid + 256 i) / PIECES; a wave's pieces of
-  // one i lie in one 16-token sub-tile, so the descriptor is wave-uniform.
   const int n_tiles = (n_sub + 1) >> 1;
-  u32x4 gk[PER_T], gv[PER_T];
-  auto gload = [&](int k) {
+  auto tdesc = [&](int k) {
+    TileDesc d;
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
+    for (int sub = 0; sub < 2; ++sub) {
+      d.pb[sub] = 0;
+      d.row0[sub] = 0;
+      d.nv[sub] = 0;
+      if (2 * k + sub < n_sub) desc(2 * k + sub, d.pb[sub], d.row0[sub], d.nv[sub]);
+    }
+    return d;
+  };
+  // (sub is wave-uniform; selects rather than an indexed read keep TileDesc in
+  // scalar registers)
+  auto rsrc_of = [&](const unsigned char* cache, const TileDesc& d, int sub) {
+    const int pb = sub ? d.pb[1] : d.pb[0], row0 = sub ? d.row0[1] : d.row0[0];
+    const int nv = sub ? d.nv[1] : d.nv[0];
+    const size_t base = (size_t)pb * (size_t)c.block_bytes + (size_t)row0 * c.row_bytes;
+    return make_rsrc(cache + base, (unsigned)(nv * c.row_bytes));
+  };
+  // K staging: piece i of a thread is token (tid + 256 i) / KPIECES; a wave's
+  // pieces of one i lie in one sub-tile, so the descriptor is wave-uniform.
+  auto k_issue = [&](const TileDesc& d, u32x4 (&gk)[K_PER_T]) {
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
       const int pc = tid + i * kWaves * 64;
-      const int tok = pc / PIECES, piece = pc - tok * PIECES;
-      // The same sub-tile for every lane of the wave (see above): readfirstlane makes
-      // that visible to the compiler, so the buffer descriptor sits in scalar
-      // registers instead of a per-lane waterfall loop around each load.
-      const int u = uniform(2 * k + (tok >> 4));
-      int pb = 0, row0 = 0, nv = 0;
-      if (u < n_sub) desc(u, pb, row0, nv);
-      const size_t base = (size_t)pb * (size_t)c.block_bytes + (size_t)row0 * c.row_bytes;
+      const int tok = pc / KPIECES, piece = pc - tok * KPIECES;
+      // D = 128: piece i lies in sub-tile i; D = 64: waves 0-1 in sub-tile 0, 2-3 in 1.
+      const int sub = K_PER_T > 1 ? i * 16 * KPIECES / (kWaves * 64) : uniform(tid >> 7);
       const unsigned off = (unsigned)((tok & 15) * c.row_bytes + g * D * 2 + piece * 16);
-      gk[i] = buf_load16<0>(make_rsrc(c.kc + base, (unsigned)(nv * c.row_bytes)), off);
-      gv[i] = buf_load16<0>(make_rsrc(c.vc + base, (unsigned)(nv * c.row_bytes)), off);
+      gk[i] = buf_load16<0>(rsrc_of(c.kc, d, sub), off);
     }
   };
-  auto lstore = [&](int buf) {
-    unsigned char* kb = s_kv + buf * 2 * TILEB;
+  auto k_store = [&](int buf, const u32x4 (&gk)[K_PER_T]) {
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
+    for (int i = 0; i < K_PER_T; ++i) {
       const int pc = tid + i * kWaves * 64;
-      const int tok = pc / PIECES, piece = pc - tok * PIECES;
-      *(u32x4*)(kb + tok * ROWB + piece * 16) = gk[i];
-      *(u32x4*)(kb + TILEB + tok * ROWB + piece * 16) = gv[i];
+      const int tok = pc / KPIECES, piece = pc - tok * KPIECES;
+      *(u32x4*)(kbuf + buf * KTILEB + tok * KROWB + piece * 16) = gk[i];
+    }
+  };
+  // V staging: item (chunk q, channel pair cp) loads channels 2cp, 2cp + 1 of
+  // tokens 4q .. 4q + 3 of both sub-tiles (one word each) and writes the chunk
+  // q of rows 2cp and 2cp + 1.
+  const int v_item = tid < 4 * VPAIRS ? tid : 0;
+  const bool v_on = tid < 4 * VPAIRS;
+  const int vq = v_item / VPAIRS, vcp = v_item - vq * VPAIRS;
+  auto v_issue = [&](const TileDesc& d, unsigned (&gv)[8]) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const __amdgpu_buffer_rsrc_t rv = rsrc_of(c.vc, d, sub);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        gv[4 * sub + i] = buf_load4<0>(rv, (unsigned)((4 * vq + i) * c.row_bytes + g * D * 2 + vcp * 4));
+    }
+  };
+  auto v_store = [&](int buf, const unsigned (&gv)[8]) {
+    if (!v_on) return;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int ch = 2 * vcp + e;
+      u32x4 w;
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd)
+        w[dd] = e ? pack_hi16(gv[2 * dd], gv[2 * dd + 1]) : pack_lo16(gv[2 * dd], gv[2 * dd + 1]);
+      *(u32x4*)(vbuf + buf * VTILEB + ch * 64 + 16 * (vq ^ ((ch >> 2) & 3))) = w;
+    }
+  };
+  // S^T of one tile (raw q.k) from K buffer kb.
+  auto scores = [&](const unsigned char* kb, f32x4 (&sc)[RT][2]) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      u32x4 kf[KSTEPS];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        kf[s] = *(const u32x4*)(kb + (16 * sub + r) * KROWB + (32 * s + 8 * qd) * 2);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        sc[t][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) sc[t][sub] = mfma16x16x32(kf[s], qf[t][s], sc[t][sub]);
+      }
+    }
+  };
+  // Online softmax of tile k for row r of each row tile, then O^T += V^T P^T.
+  // Masked scores become -inf in place, and only tiles that need a mask pay for it.
+  auto softmax_pv = [&](int k, f32x4 (&sc)[RT][2], const TileDesc& d, const unsigned char* vb) {
+    const bool full = d.nv[0] == 16 && d.nv[1] == 16 && pos0 + 32 * k + 32 <= lim_min;
+    if (!full) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const int bound = min(rows.limit[t] - (pos0 + 32 * k + 16 * sub), d.nv[sub]);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            if (4 * qd + ii >= bound) sc[t][sub][ii] = -INFINITY;
+        }
+    }
+    u32x4 phi[RT], plo[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      float mx = max3_raw(max3_raw(sc[t][0][0], sc[t][0][1], sc[t][0][2]),
+                          max3_raw(sc[t][0][3], sc[t][1][0], sc[t][1][1]),
+                          max3_raw(sc[t][1][2], sc[t][1][3], -INFINITY));
+      mx = max_across_rows_raw(mx);
+      const float ms = mx == -INFINITY ? -INFINITY : mx * scl;   // the tile's scaled row max
+      const bool up = ms > m_run[t] + kRescaleSlack;
+      if (__any(up)) {
+        const float m_new = up ? ms : m_run[t];
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.f;   // 0 from -inf
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) oacc[t][j] *= alpha;
+        l_run[t] *= alpha;
+        m_run[t] = m_new;
+        m_use[t] = m_new == -INFINITY ? 0.f : m_new;
+      }
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][i >> 2][i & 3], scl, -m_use[t]));
+      if (!full) {   // exp2(-inf) is 0 already, unless |scale| = 0 made the FMA NaN
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = sc[t][i >> 2][i & 3] == -INFINITY ? 0.f : pv[i];
+      }
+      l_run[t] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        const unsigned a = __float_as_uint(pv[2 * dd]), b = __float_as_uint(pv[2 * dd + 1]);
+        phi[t][dd] = pack_hi16(a, b);
+        const float ra = pv[2 * dd] - __uint_as_float(a & 0xffff0000u);
+        const float rb = pv[2 * dd + 1] - __uint_as_float(b & 0xffff0000u);
+        plo[t][dd] = pack_hi16(__float_as_uint(ra), __float_as_uint(rb));
+      }
+    }
+    const unsigned vlane = (unsigned)(r * 64 + 16 * (qd ^ ((r >> 2) & 3)));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const u32x4 va = *(const u32x4*)(vb + j * 1024 + vlane);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        oacc[t][j] = mfma16x16x32(va, phi[t], oacc[t][j]);
+        oacc[t][j] = mfma16x16x32(va, plo[t], oacc[t][j]);
+      }
     }
   };
 
-  if (n_tiles > 0) {
-    gload(0);
-    lstore(0);
+  // Prologue: K and V of tile 0 and K of tile 1 in LDS, scores of tile 0.
+  TileDesc d_cur = tdesc(0), d_next = tdesc(1);
+  {
+    u32x4 gk0[K_PER_T], gk1[K_PER_T];
+    unsigned gv[8];
+    k_issue(d_cur, gk0);
+    v_issue(d_cur, gv);
+    k_issue(d_next, gk1);
+    k_store(0, gk0);
+    v_store(0, gv);
+    k_store(1, gk1);
   }
   __syncthreads();
-  for (int k = 0; k < n_tiles; ++k) {
-    const bool more = k + 1 < n_tiles;
-    if (more) gload(k + 1);
+  f32x4 sa[RT][2], sb[RT][2];
+  if (active && n_tiles > 0) scores(kbuf, sa);
+  __syncthreads();   // K buffer 0 is rewritten during tile 0
+
+  // Tile k: stage K of k + 2 and V of k + 1 (loads issued for every tile, with
+  // an empty descriptor past the end, so the wait counts are the same on every
+  // path), scores of k + 1, softmax and P.V of k.
+  auto step = [&](int k, f32x4 (&s_this)[RT][2], f32x4 (&s_next)[RT][2]) {
+    const TileDesc d_nn = tdesc(k + 2);
+    u32x4 gk[K_PER_T];
+    unsigned gv[8];
+    k_issue(d_nn, gk);
+    v_issue(d_next, gv);
     if (active) {
-      const unsigned char* kb = s_kv + (k & 1) * 2 * TILEB;
-      const unsigned char* vb = kb + TILEB;
-      int nv[2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        int pb, row0;
-        nv[sub] = 0;
-        if (2 * k + sub < n_sub) desc(2 * k + sub, pb, row0, nv[sub]);
-      }
-      f32x4 sacc[RT][2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        u32x4 kf[KSTEPS];
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-          kf[s] = *(const u32x4*)(kb + (16 * sub + r) * ROWB + (32 * s + 8 * qd) * 2);
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          sacc[t][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) sacc[t][sub] = mfma16x16x32(kf[s], qf[t][s], sacc[t][sub]);
-        }
-      }
-      u32x4 phi[RT], plo[RT];
-      const bool full = nv[0] == 16 && nv[1] == 16 && pos0 + 32 * k + 32 <= lim_min;
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        float sv[8];
-        if (full) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sv[j] = sacc[t][j >> 2][j & 3] * c.qk_scale_log2;
-        } else {
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float x = sacc[t][sub][i] * c.qk_scale_log2;
-              const bool ok = 4 * qd + i < nv[sub] &&
-                              pos0 + 16 * (2 * k + sub) + 4 * qd + i < rows.limit[t];
-              sv[sub * 4 + i] = ok ? x : -INFINITY;
-            }
-        }
-        float mx = sv[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-        mx = max_across_rows(mx);
-        const float m_new = fmaxf(m_run[t], mx);
-        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_ref);
-        float pv[8];
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
-          psum += pv[i];
-        }
-        l_run[t] = l_run[t] * alpha + psum;
-        m_run[t] = m_new;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) oacc[t][j] *= alpha;
-        }
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const unsigned a = __float_as_uint(pv[2 * d]), cc = __float_as_uint(pv[2 * d + 1]);
-          phi[t][d] = pack_hi16(a, cc);
-          const float ra = pv[2 * d] - __uint_as_float(a & 0xffff0000u);
-          const float rc = pv[2 * d + 1] - __uint_as_float(cc & 0xffff0000u);
-          plo[t][d] = pack_hi16(__float_as_uint(ra), __float_as_uint(rc));
-        }
-      }
-      // V rows 4 qd + i of each sub-tile, channels CPL r .. (as the global-load layout).
-      vvec vf[2][4];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vf[sub][i] = *(const vvec*)(vb + (16 * sub + 4 * qd + i) * ROWB + r * CPL * 2);
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        u32x4 va;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int sub = d >> 1, i0 = (d & 1) * 2;
-          const unsigned w0 = vf[sub][i0][j >> 1], w1 = vf[sub][i0 + 1][j >> 1];
-          va[d] = (j & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
-        }
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          oacc[t][j] = mfma16x16x32(va, phi[t], oacc[t][j]);
-          oacc[t][j] = mfma16x16x32(va, plo[t], oacc[t][j]);
-        }
-      }
+      if (k + 1 < n_tiles) scores(kbuf + ((k + 1) & 1) * KTILEB, s_next);
+      softmax_pv(k, s_this, d_cur, vbuf + (k & 1) * VTILEB);
     }
-    if (more) lstore((k + 1) & 1);
+    k_store(k & 1, gk);
+    v_store((k + 1) & 1, gv);
     __syncthreads();
+    d_cur = d_next;
+    d_next = d_nn;
+  };
+  for (int k = 0; k < n_tiles; k += 2) {
+    step(k, sa, sb);
+    if (k + 1 < n_tiles) step(k + 1, sb, sa);
   }
 
 #pragma unroll
@@ -207,17 +312,9 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
     const float l_tot = sum_across_rows(l_run[t]);
     if (r < rows.n_rows[t]) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float* dst = rows.o[t] + (size_t)r * D + CPL * 4 * qd;
+      float* dst = rows.o[t] + (size_t)r * D + 4 * qd;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j0 = 0; j0 < CPL; j0 += 4) {
-          f32x4 v;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) v[jj] = oacc[t][j0 + jj][i] * inv;
-          *(f32x4*)(dst + CPL * i + j0) = v;
-        }
-      }
+      for (int j = 0; j < NJ; ++j) *(f32x4*)(dst + 16 * j) = oacc[t][j] * inv;
       if (qd == 0) rows.lse[t][r] = l_tot > 0.f ? m_run[t] + log2f(l_tot) : -INFINITY;
     }
   }
