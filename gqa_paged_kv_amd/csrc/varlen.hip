@@ -334,6 +334,7 @@ struct VarlenParams {
   int slot_rows;             // balanced: row-tile rows per partial slot
   int nwg;                   // balanced: workgroups of the split kernel
   int share_ok, rt;          // balanced: the split kernel's shared-LDS path and row tiles per wave
+  int* unit_info;            // balanced: [units, 2] first workgroup covering a unit, and how many
 };
 
 // Partial rows of sequence b's row tiles sit at tiles tile_base(b) + rt: the
@@ -487,7 +488,13 @@ __device__ __forceinline__ void attn_varlen_balanced(const VarlenParams& p, int*
     const int ta = o - uoff;
     const int tb = (s1 - s_pref[b] - uoff < wk) ? s1 - s_pref[b] - uoff : wk;
     pos = s_pref[b] + uoff + tb;
-    const int slot = w + s_upref[b] + h * sg.n_grp + grp;
+    const int unit = s_upref[b] + h * sg.n_grp + grp;
+    const int slot = w + unit;
+    if (ta == 0 && tid == 0) {   // this share holds the unit's first tile: record its coverage
+      const long long last = (((long long)s_pref[b] + uoff + wk) * N - 1) / W;
+      p.unit_info[2 * unit] = w;
+      p.unit_info[2 * unit + 1] = (int)(last - w + 1);
+    }
     const int t0 = 32 * ta;
     const int lim = group_limit(sg, G, grp);
     const int span = (32 * (tb - ta) < lim - t0) ? 32 * (tb - ta) : lim - t0;
@@ -661,13 +668,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT 
 
 // Merge of each (sequence, row tile, KV head) over its splits, written to the
 // flattened output rows; the triples taken grid-stride.
-// Balanced schedule: a row tile's unit (its group, and its head on the shared path)
-// covers tiles [P, P + work) of the flattened space; workgroups w_a .. w_b held them
-// and left partial rows in slots w + (global unit index).
+// Balanced schedule: a work unit (sequence, KV head on the shared path, group of row
+// tiles) covers tiles [P, P + work) of the flattened space; workgroups w_a .. w_b
+// held them and left partial rows in slots w + (global unit index). The units are
+// taken grid-stride, each merging all of its rows.
 template <int D>
 __device__ __forceinline__ void attn_varlen_combine_balanced(const VarlenParams& p, int* s_pref,
-                                                             int* s_upref, int* s_cpref,
-                                                             int* s_wave) {
+                                                             int* s_upref, int* s_wave) {
   constexpr int TPR = D / 4;
   const int G = p.c.G, Hq = p.c.Hq, Hkv = p.c.Hkv;
   const bool share_ok = p.share_ok != 0;
@@ -675,46 +682,43 @@ __device__ __forceinline__ void attn_varlen_combine_balanced(const VarlenParams&
     const SeqGeom sg = seq_geom(p, b, share_ok, p.rt);
     return sg.heads * head_tiles(sg, G);
   });
-  sequence_prefix(p.B, s_upref, s_wave, [&](int b) {
+  const int U = sequence_prefix(p.B, s_upref, s_wave, [&](int b) {
     const SeqGeom sg = seq_geom(p, b, share_ok, p.rt);
     return sg.heads * sg.n_grp;
   });
-  const int U = sequence_prefix(p.B, s_cpref, s_wave, [&](int b) {
-    int q0, qn;
-    varlen_rows(p, b, q0, qn);
-    return (qn * G + 15) / 16 * Hkv;
-  });
   const long long N = p.nwg;
-  for (int u = blockIdx.x; u < U; u += gridDim.x) {
-    const int b = sequence_of(s_cpref, p.B, u);
-    const int local = u - s_cpref[b];
-    const int rt = local / Hkv, g = local - (local / Hkv) * Hkv;
+  const bool gaps = W < N;   // only then can a workgroup inside a unit's range hold no tile
+  // One (work unit, 16-row block) per iteration; the unit's covering workgroups come
+  // from the attention kernel, which recorded them at the unit's first tile.
+  const long long items = (long long)U * p.slot_rows;
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int k = (int)(it / p.slot_rows), rb = (int)(it - (long long)k * p.slot_rows);
+    const int b = sequence_of(s_upref, p.B, k);
     const SeqGeom sg = seq_geom(p, b, share_ok, p.rt);
+    const int local = k - s_upref[b];
+    const int hu = local / sg.n_grp, grp = local - hu * sg.n_grp;
+    const int n_heads = sg.shared ? 1 : Hkv;
+    if (rb >= n_heads * sg.grp_rt) continue;
+    const int t = rb % sg.grp_rt, hh = rb / sg.grp_rt;
+    const int m0 = 16 * (grp * sg.grp_rt + t);
     const int rows = sg.qn * G;
-    const int m0 = 16 * rt;
+    if (m0 >= rows) continue;
     const int n_rows = rows - m0 < 16 ? rows - m0 : 16;
-    int n_units = 0, w_a = 0, k = 0, srow = 0;
-    if (sg.n_grp > 0) {
-      const int grp = rt / sg.grp_rt, t = rt - grp * sg.grp_rt;
-      const int hu = sg.shared ? g : 0;
-      srow = sg.shared ? t : g * sg.grp_rt + t;
-      k = hu * sg.n_grp + grp;
-      long long P = s_pref[b] + (long long)hu * head_tiles(sg, G);
-      for (int x = 0; x < grp; ++x) P += group_tiles(sg, G, x);
-      const int wk = group_tiles(sg, G, grp);
-      if (wk > 0) {
-        w_a = (int)(((P + 1) * N - 1) / W);
-        n_units = (int)(((P + wk) * N - 1) / W) - w_a + 1;
-      }
+    int w_a = 0, n_units = 0;
+    if (group_tiles(sg, G, grp) > 0) {
+      w_a = p.unit_info[2 * k];
+      n_units = p.unit_info[2 * k + 1];
     }
-    const size_t blk0 = ((size_t)w_a + s_upref[b] + k) * p.slot_rows + srow;
-    // A workgroup inside [w_a, w_b] with an empty share (only when W < N) wrote nothing.
     auto live = [&](int x) {
+      if (!gaps) return true;
       const long long ww = w_a + x;
       return ww * W / N < (ww + 1) * W / N;
     };
+    const int g = sg.shared ? hu : hh;
+    const int srow = sg.shared ? t : hh * sg.grp_rt + t;
+    const size_t blk0 = ((size_t)w_a + k) * p.slot_rows + srow;
     for (int i = threadIdx.x; i < n_rows * TPR; i += kCombineThreads) {
-      const int rr = i / TPR, c4 = i - (i / TPR) * TPR;
+      const int rr = i / TPR, c4 = i - rr * TPR;
       const float* lse0 = p.part_lse + blk0 * 16 + rr;
       const float* o0 = p.part_o + (blk0 * 16 + rr) * D + 4 * c4;
       const f32x4 o = merge_rows<8>(n_units, lse0, (size_t)p.slot_rows * 16, o0,
@@ -722,6 +726,14 @@ __device__ __forceinline__ void attn_varlen_combine_balanced(const VarlenParams&
       const int m = m0 + rr, j = m / G;
       *(f32x4*)(p.out + ((size_t)(sg.q0 + j) * Hq + (size_t)g * G + (m - j * G)) * D + 4 * c4) = o;
     }
+  }
+  // Sequences with query rows but nothing to attend (empty context) have no unit:
+  // their rows are zeros.
+  for (int b = blockIdx.x; b < p.B; b += gridDim.x) {
+    const SeqGeom sg = seq_geom(p, b, share_ok, p.rt);
+    if (sg.n_grp > 0 || sg.qn <= 0) continue;
+    for (int i = threadIdx.x; i < sg.qn * Hq * TPR; i += kCombineThreads)
+      *(f32x4*)(p.out + (size_t)sg.q0 * Hq * D + 4 * (size_t)i) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -733,8 +745,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_varlen_combine_kernel(co
   const int G = p.c.G, Hq = p.c.Hq, Hkv = p.c.Hkv;
   if (p.balanced) {
     __shared__ int s_upref[kMaxBalBatch + 1];
-    __shared__ int s_cpref[kMaxBalBatch + 1];
-    attn_varlen_combine_balanced<D>(p, s_pref, s_upref, s_cpref, s_wave);
+    attn_varlen_combine_balanced<D>(p, s_pref, s_upref, s_wave);
     return;
   }
   const int U = sequence_prefix(p.B, s_pref, s_wave, [&](int b) {
@@ -776,7 +787,7 @@ struct VarlenPlan {
   size_t o_bytes, lse_bytes;
   // Balanced schedule: workgroups, row tiles per partial slot, and its workspace.
   int rt, nwg, slot_rows;
-  size_t bal_o_bytes, bal_lse_bytes;
+  size_t bal_o_bytes, bal_lse_bytes, bal_info_bytes;
 };
 
 // Row tiles of the longest chunk (the grid), split size, and the workspace for at
@@ -827,6 +838,7 @@ static VarlenPlan make_varlen_plan(int B, int total_q, int max_q_len, int Hq, in
   const size_t slots = (size_t)pl.nwg + (size_t)u_bound;
   pl.bal_o_bytes = align256(slots * pl.slot_rows * 16 * D * sizeof(float));
   pl.bal_lse_bytes = align256(slots * pl.slot_rows * 16 * sizeof(float));
+  pl.bal_info_bytes = align256((size_t)u_bound * 2 * sizeof(int));
   return pl;
 }
 
@@ -859,7 +871,8 @@ extern "C" size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int
     return 0;
   const VarlenPlan pl = make_varlen_plan(batch, total_q, max_q_len, num_q_heads, num_kv_heads,
                                          head_dim, block_size, max_context_len);
-  const size_t split = pl.o_bytes + pl.lse_bytes, bal = pl.bal_o_bytes + pl.bal_lse_bytes;
+  const size_t split = pl.o_bytes + pl.lse_bytes,
+               bal = pl.bal_o_bytes + pl.bal_lse_bytes + pl.bal_info_bytes;
   return split > bal ? split : bal;
 }
 
@@ -906,7 +919,8 @@ static int varlen_run(bool fp8, float* out, const void* query, const void* key_c
     return fail(GPKV_ERR_SHAPE, "%s: max_context_len=%d needs too many splits", fn,
                 max_context_len);
   const bool balanced = varlen_balanced();
-  const size_t need = balanced ? pl.bal_o_bytes + pl.bal_lse_bytes : pl.o_bytes + pl.lse_bytes;
+  const size_t need = balanced ? pl.bal_o_bytes + pl.bal_lse_bytes + pl.bal_info_bytes
+                               : pl.o_bytes + pl.lse_bytes;
   if (!workspace || workspace_bytes < need)
     return fail(GPKV_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn,
                 workspace ? workspace_bytes : (size_t)0, need);
@@ -926,6 +940,7 @@ static int varlen_run(bool fp8, float* out, const void* query, const void* key_c
   vp.c.qk_scale_log2 = scale * 1.4426950408889634f;
   vp.part_o = (float*)workspace;
   vp.part_lse = (float*)((char*)workspace + (balanced ? pl.bal_o_bytes : pl.o_bytes));
+  vp.unit_info = (int*)((char*)workspace + pl.bal_o_bytes + pl.bal_lse_bytes);   // balanced only
   vp.out = out;
   vp.block_tables = block_tables;
   vp.ctx = context_lens;
