@@ -332,7 +332,7 @@ struct VarlenParams {
   int max_blocks, max_ctx, num_splits, split_tokens, n_rt, total_q, B;
   int balanced;              // 1: balanced schedule (equal shares of the tile space)
   int slot_rows;             // balanced: row-tile rows per partial slot
-  int nwg;                   // balanced: workgroups of the split kernel
+  int nwg;                   // balanced: shares (a multiple of the split kernel's grid)
   int share_ok, rt;          // balanced: the split kernel's shared-LDS path and row tiles per wave
   int* unit_info;            // balanced: [units, 2] first workgroup covering a unit, and how many
 };
@@ -467,89 +467,93 @@ __device__ __forceinline__ void attn_varlen_balanced(const VarlenParams& p, int*
     const SeqGeom sg = geom(b);
     return sg.heads * sg.n_grp;
   });
-  const int N = (int)gridDim.x, w = (int)blockIdx.x;
-  const int s0 = (int)((long long)w * W / N), s1 = (int)((long long)(w + 1) * W / N);
-  if (s0 >= s1) return;
-  int b = sequence_of(s_pref, p.B, s0);
-  int pos = s0;
-  while (pos < s1) {
-    while (s_pref[b + 1] <= pos) ++b;   // skips sequences without work; pos < W
-    const SeqGeom sg = geom(b);
-    // The unit holding offset o: head h = o / (work per head), then its group.
-    const int hw = head_tiles(sg, G);
-    const int o = pos - s_pref[b];
-    const int h = o / hw;
-    int grp = 0, uoff = h * hw, wk = group_tiles(sg, G, 0);
-    while (o >= uoff + wk) {
-      uoff += wk;
-      ++grp;
-      wk = group_tiles(sg, G, grp);
-    }
-    const int ta = o - uoff;
-    const int tb = (s1 - s_pref[b] - uoff < wk) ? s1 - s_pref[b] - uoff : wk;
-    pos = s_pref[b] + uoff + tb;
-    const int unit = s_upref[b] + h * sg.n_grp + grp;
-    const int slot = w + unit;
-    if (ta == 0 && tid == 0) {   // this share holds the unit's first tile: record its coverage
-      const long long last = (((long long)s_pref[b] + uoff + wk) * N - 1) / W;
-      p.unit_info[2 * unit] = w;
-      p.unit_info[2 * unit + 1] = (int)(last - w + 1);
-    }
-    const int t0 = 32 * ta;
-    const int lim = group_limit(sg, G, grp);
-    const int span = (32 * (tb - ta) < lim - t0) ? 32 * (tb - ta) : lim - t0;
-    const int e0 = t0 >> bs_log2;
-    int n_ent = ((t0 + span - 1) >> bs_log2) - e0 + 1;
-    n_ent = n_ent < kMaxTable ? n_ent : kMaxTable;   // the host sizes shares below this
-    const int nb = (sg.ctx + bs - 1) / bs;
-    __syncthreads();   // the previous segment's table is no longer read
-    for (int e = tid; e < n_ent; e += kWaves * 64) {
-      const int lb = e0 + e;
-      const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
-      s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
-    }
-    __syncthreads();
-    auto desc = [&](int uu, int& pb, int& row0, int& nv) {
-      const int tok = t0 + 16 * uu;
-      const int ei = (tok >> bs_log2) - e0;
-      const int x = ei < n_ent ? s_pb[ei] : -1;
-      row0 = tok & (bs - 1);
-      int n = t0 + span - tok;
-      n = n < 0 ? 0 : (n > 16 ? 16 : n);
-      if (x < 0) n = 0;
-      nv = uniform(n);
-      pb = uniform(x < 0 ? 0 : x);
-    };
-    // Row tile rt of the sequence against KV head g, into slot row srow.
-    auto fill = [&](auto& tiles, int t, int rt, int g, int srow) {
-      const int m0 = 16 * rt;
-      const int n_rows = sg.rows - m0 < 0 ? 0 : (sg.rows - m0 < 16 ? sg.rows - m0 : 16);
-      const int m = m0 + r, j = m / G;
-      tiles.q[t] = r < n_rows
-                       ? p.c.q + ((size_t)(sg.q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
-                       : nullptr;
-      tiles.n_rows[t] = n_rows;
-      tiles.limit[t] = sg.ctx - sg.qn + j + 1;
-      const size_t row_blk = (size_t)slot * p.slot_rows + srow;
-      tiles.o[t] = p.part_o + row_blk * 16 * D;
-      tiles.lse[t] = p.part_lse + row_blk * 16;
-    };
-    const int n_sub = (span + 15) / 16;
-    if constexpr (kShared) {
-      if (sg.shared) {
-        RowTiles<2> tiles;
-        const int rt0 = grp * kShareTiles + 2 * wave;
-        fill(tiles, 0, rt0, h, 2 * wave);
-        fill(tiles, 1, rt0 + 1, h, 2 * wave + 1);
-        attend_shared<D>(p.c, h, n_sub, desc, t0, tiles, s_kv);
-        continue;
+  // N shares, V consecutive ones per workgroup (N = V * grid): each share is short
+  // enough for one staged table chunk, and every workgroup holds the same work.
+  const int N = p.nwg, V = p.nwg / (int)gridDim.x;
+  for (int w = (int)blockIdx.x * V; w < ((int)blockIdx.x + 1) * V; ++w) {
+    const int s0 = (int)((long long)w * W / N), s1 = (int)((long long)(w + 1) * W / N);
+    if (s0 >= s1) continue;
+    int b = sequence_of(s_pref, p.B, s0);
+    int pos = s0;
+    while (pos < s1) {
+      while (s_pref[b + 1] <= pos) ++b;   // skips sequences without work; pos < W
+      const SeqGeom sg = geom(b);
+      // The unit holding offset o: head h = o / (work per head), then its group.
+      const int hw = head_tiles(sg, G);
+      const int o = pos - s_pref[b];
+      const int h = o / hw;
+      int grp = 0, uoff = h * hw, wk = group_tiles(sg, G, 0);
+      while (o >= uoff + wk) {
+        uoff += wk;
+        ++grp;
+        wk = group_tiles(sg, G, grp);
       }
-    }
-    for (int g = wave; g < Hkv; g += kWaves) {
-      RowTiles<RT> tiles;
-#pragma unroll
-      for (int t = 0; t < RT; ++t) fill(tiles, t, grp * RT + t, g, g * RT + t);
-      attend_head<D, FP8, true, RT>(p.c, g, n_sub, desc, t0, tiles);
+      const int ta = o - uoff;
+      const int tb = (s1 - s_pref[b] - uoff < wk) ? s1 - s_pref[b] - uoff : wk;
+      pos = s_pref[b] + uoff + tb;
+      const int unit = s_upref[b] + h * sg.n_grp + grp;
+      const int slot = w + unit;
+      if (ta == 0 && tid == 0) {   // this share holds the unit's first tile: record its coverage
+        const long long last = (((long long)s_pref[b] + uoff + wk) * N - 1) / W;
+        p.unit_info[2 * unit] = w;
+        p.unit_info[2 * unit + 1] = (int)(last - w + 1);
+      }
+      const int t0 = 32 * ta;
+      const int lim = group_limit(sg, G, grp);
+      const int span = (32 * (tb - ta) < lim - t0) ? 32 * (tb - ta) : lim - t0;
+      const int e0 = t0 >> bs_log2;
+      int n_ent = ((t0 + span - 1) >> bs_log2) - e0 + 1;
+      n_ent = n_ent < kMaxTable ? n_ent : kMaxTable;   // the host sizes shares below this
+      const int nb = (sg.ctx + bs - 1) / bs;
+      __syncthreads();   // the previous segment's table is no longer read
+      for (int e = tid; e < n_ent; e += kWaves * 64) {
+        const int lb = e0 + e;
+        const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
+        s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
+      }
+      __syncthreads();
+      auto desc = [&](int uu, int& pb, int& row0, int& nv) {
+        const int tok = t0 + 16 * uu;
+        const int ei = (tok >> bs_log2) - e0;
+        const int x = ei < n_ent ? s_pb[ei] : -1;
+        row0 = tok & (bs - 1);
+        int n = t0 + span - tok;
+        n = n < 0 ? 0 : (n > 16 ? 16 : n);
+        if (x < 0) n = 0;
+        nv = uniform(n);
+        pb = uniform(x < 0 ? 0 : x);
+      };
+      // Row tile rt of the sequence against KV head g, into slot row srow.
+      auto fill = [&](auto& tiles, int t, int rt, int g, int srow) {
+        const int m0 = 16 * rt;
+        const int n_rows = sg.rows - m0 < 0 ? 0 : (sg.rows - m0 < 16 ? sg.rows - m0 : 16);
+        const int m = m0 + r, j = m / G;
+        tiles.q[t] = r < n_rows
+                         ? p.c.q + ((size_t)(sg.q0 + j) * p.c.Hq + (size_t)g * G + (m - j * G)) * D
+                         : nullptr;
+        tiles.n_rows[t] = n_rows;
+        tiles.limit[t] = sg.ctx - sg.qn + j + 1;
+        const size_t row_blk = (size_t)slot * p.slot_rows + srow;
+        tiles.o[t] = p.part_o + row_blk * 16 * D;
+        tiles.lse[t] = p.part_lse + row_blk * 16;
+      };
+      const int n_sub = (span + 15) / 16;
+      if constexpr (kShared) {
+        if (sg.shared) {
+          RowTiles<2> tiles;
+          const int rt0 = grp * kShareTiles + 2 * wave;
+          fill(tiles, 0, rt0, h, 2 * wave);
+          fill(tiles, 1, rt0 + 1, h, 2 * wave + 1);
+          attend_shared<D>(p.c, h, n_sub, desc, t0, tiles, s_kv);
+          continue;
+        }
+      }
+      for (int g = wave; g < Hkv; g += kWaves) {
+        RowTiles<RT> tiles;
+  #pragma unroll
+        for (int t = 0; t < RT; ++t) fill(tiles, t, grp * RT + t, g, g * RT + t);
+        attend_head<D, FP8, true, RT>(p.c, g, n_sub, desc, t0, tiles);
+      }
     }
   }
 }
@@ -786,7 +790,7 @@ struct VarlenPlan {
   int n_rt, split_tokens, num_splits;
   size_t o_bytes, lse_bytes;
   // Balanced schedule: workgroups, row tiles per partial slot, and its workspace.
-  int rt, nwg, slot_rows;
+  int rt, nwg, slot_rows, bal_grid;   // nwg shares over bal_grid workgroups
   size_t bal_o_bytes, bal_lse_bytes, bal_info_bytes;
 };
 
@@ -831,10 +835,16 @@ static VarlenPlan make_varlen_plan(int B, int total_q, int max_q_len, int Hq, in
                             (total_rt + pl.rt - 1) / pl.rt + B;
   const long long w_bound = u_bound * (((long long)max_ctx + 31) / 32);
   const long long seg_cap = (long long)(kMaxTable - 1) * bs / 32 - 1;
-  long long nwg = (long long)(pl.rt == 1 ? 3 : 2) * balanced_capacity();
+  // The grid is what fits at once (two workgroups per CU with row-tile pairs, three
+  // with single row tiles); each workgroup takes the same number of consecutive
+  // shares, enough that no share spans more tiles than one staged table chunk.
+  const long long grid = (long long)(pl.rt == 1 ? 3 : 2) * balanced_capacity();
   const long long need = (w_bound + seg_cap - 2) / (seg_cap - 1);
-  if (nwg < need) nwg = need;
-  pl.nwg = (int)(nwg < (1LL << 30) ? nwg : (1LL << 30));
+  long long per = (need + grid - 1) / grid;
+  if (per < 1) per = 1;
+  if (grid * per > (1LL << 30)) per = (1LL << 30) / grid;
+  pl.bal_grid = (int)grid;
+  pl.nwg = (int)(grid * per);
   const size_t slots = (size_t)pl.nwg + (size_t)u_bound;
   pl.bal_o_bytes = align256(slots * pl.slot_rows * 16 * D * sizeof(float));
   pl.bal_lse_bytes = align256(slots * pl.slot_rows * 16 * sizeof(float));
@@ -965,7 +975,7 @@ static int varlen_run(bool fp8, float* out, const void* query, const void* key_c
   const long long tiles = ((long long)total_q * vp.c.G + 15) / 16 + batch;
   const long long units_max = (tiles / rt_per_wave + batch) * pl.num_splits;
   const long long cap = 4LL * balanced_capacity();
-  const dim3 grid(balanced ? (unsigned)pl.nwg : (unsigned)(units_max < cap ? units_max : cap)),
+  const dim3 grid(balanced ? (unsigned)pl.bal_grid : (unsigned)(units_max < cap ? units_max : cap)),
       block(kWaves * 64);
   if (fp8)
     launch_varlen<true>(rt_per_wave > 1, head_dim, grid, block, s, vp);
