@@ -103,12 +103,14 @@ __device__ __forceinline__ unsigned e4m3_from_f32(float y) {
 }
 
 // Four E4M3 codes (one per byte of w, lowest byte first) -> four bf16 values
-// packed two per word. Every E4M3 value is exact in bf16.
+// packed two per word. Every E4M3 value is exact in bf16; gfx950 converts a code
+// pair straight to packed bf16 (scale 1: the same bits as decoding to float32 and
+// keeping the high half, on all 256 codes), one instruction per two codes.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16(unsigned w) {
-  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);   // bytes 0, 1
-  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);    // bytes 2, 3
-  return u32x2{pack_hi16(__float_as_uint(lo[0]), __float_as_uint(lo[1])),
-               pack_hi16(__float_as_uint(hi[0]), __float_as_uint(hi[1]))};
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);   // bytes 0, 1
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);    // bytes 2, 3
+  return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
