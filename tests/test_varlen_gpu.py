@@ -82,6 +82,57 @@ def test_varlen_shared_tiles_at_the_causal_bound(split, monkeypatch):
     assert err <= ATOL
 
 
+def _shares_per_workgroup(B, total_q, Hq, Hkv, bs, max_ctx, cus):
+    """The host's rule for the balanced schedule of the two-row-tile kernel: shares
+    are a multiple of the grid (two workgroups per CU), each short enough that its
+    blocks fit one staged table chunk of 2048 entries."""
+    G = Hq // Hkv
+    total_rt = (total_q * G + 15) // 16 + B
+    u_bound = Hkv * ((total_rt + 7) // 8 + B) + (total_rt + 1) // 2 + B
+    w_bound = u_bound * ((max_ctx + 31) // 32)
+    seg_cap = (2048 - 1) * bs // 32 - 1
+    need = (w_bound + seg_cap - 2) // (seg_cap - 1)
+    grid = 2 * cus
+    return max(1, -(-need // grid))
+
+
+@pytest.mark.parametrize("schedule", VARLEN_SCHEDULES)
+def test_varlen_several_shares_per_workgroup(schedule, monkeypatch):
+    """A max_context_len far above the real contexts makes the host's bound on a share's
+    table span ask for more shares than workgroups: each workgroup then takes a run of
+    consecutive shares, most of them empty (the work is smaller than the shares), and
+    the combine must skip the empty ones. Decode rows and shared-LDS chunks together."""
+    monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", schedule)
+    rng = np.random.default_rng(731)
+    B = 64
+    ctx = [int(x) for x in rng.integers(1, 900, size=B)]
+    ql = [1] * B
+    for i, q in ((3, 40), (17, 64), (40, 25)):   # >= 4 row tiles: the shared path
+        ctx[i] = max(ctx[i], q + 200)
+        ql[i] = q
+    w = workloads.varlen_case(731, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
+                              context_lens=ctx, q_lens=ql)
+    max_ctx = 40960
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    per = _shares_per_workgroup(B, int(sum(ql)), 28, 4, 16, max_ctx, cus)
+    print(f"shares per workgroup: {per}")
+    if schedule == "balanced":
+        assert per >= 2, "the shape no longer reaches several shares per workgroup"
+    d = Dev(w)
+    # a block table wide enough for max_context_len; entries past a sequence's blocks
+    # are never read
+    bt = np.full((B, max_ctx // 16), -1, dtype=np.int32)
+    bt[:, : w.block_tables.shape[1]] = w.block_tables
+    qv = to_dev(w.query_varlen, BF)
+    cu = to_dev(w.cu_seqlens_q, torch.int32)
+    out = gp.paged_attention_varlen(qv, d.kc, d.vc, to_dev(bt, torch.int32), d.ctx, cu,
+                                    max_q_len=max(ql), max_context_len=max_ctx,
+                                    scale=float(w.scale))
+    err = max_abs(out.cpu().numpy(), _ref(w))
+    print(f"{schedule}: varlen max-abs {err:.3e}")
+    assert err <= ATOL
+
+
 @pytest.mark.parametrize("split", [128, 256, 512, 2048])
 def test_varlen_split_sizes(split, monkeypatch):
     """Chunks whose rows end in different splits of the KV range (split schedule)."""
