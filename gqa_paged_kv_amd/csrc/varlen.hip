@@ -438,9 +438,9 @@ __device__ __forceinline__ int head_tiles(const SeqGeom& sg, int G) {
 // tiles or more (chunks, RT > 1) instead take units of (sequence, KV head, group
 // of kShareTiles row tiles, split): the four waves share that head's K / V through
 // LDS (attend_shared). A fixed grid takes the units grid-stride: no workgroup is
-// launched for a sequence's missing row tiles. Two waves per SIMD (at most 256
-// registers) let one wave's MFMA work hide the other's loads; RT = 2 fits without
-// spilling at D = 128.
+// launched for a sequence's missing row tiles. At most 256 registers (two waves per
+// SIMD): with row-tile pairs one wave's MFMA work hides the other's loads, and RT = 2
+// fits without spilling at D = 128; single row tiles run one workgroup per CU.
 
 // Balanced schedule: the flattened (unit, 32-position tile) space of the whole batch
 // is shared out equally, [w*W/N, (w+1)*W/N) for workgroup w of N (all resident), so
@@ -559,7 +559,7 @@ __device__ __forceinline__ void attn_varlen_balanced(const VarlenParams& p, int*
 }
 
 template <int D, int RT, bool FP8>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 2))) void attn_varlen_kernel(const VarlenParams p) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_varlen_kernel(const VarlenParams p) {
   constexpr bool kShared = RT > 1 && !FP8;   // E4M3 caches: per-head units only
   __shared__ int s_pb[kMaxTable];
   __shared__ int s_pref[kMaxBalBatch + 1];
@@ -835,10 +835,12 @@ static VarlenPlan make_varlen_plan(int B, int total_q, int max_q_len, int Hq, in
                             (total_rt + pl.rt - 1) / pl.rt + B;
   const long long w_bound = u_bound * (((long long)max_ctx + 31) / 32);
   const long long seg_cap = (long long)(kMaxTable - 1) * bs / 32 - 1;
-  // The grid is what fits at once (two workgroups per CU with row-tile pairs, three
-  // with single row tiles); each workgroup takes the same number of consecutive
-  // shares, enough that no share spans more tiles than one staged table chunk.
-  const long long grid = (long long)(pl.rt == 1 ? 3 : 2) * balanced_capacity();
+  // The grid: two workgroups per CU with row-tile pairs (one wave's MFMA work hides
+  // the other's loads); one with single row tiles, which stream K / V like decode
+  // (58 single-token rows on 8K contexts: 162 us at one per CU, 175 at two, 192 at
+  // three). Each workgroup takes the same number of consecutive shares, enough that
+  // no share spans more tiles than one staged table chunk.
+  const long long grid = (long long)(pl.rt == 1 ? 1 : 2) * balanced_capacity();
   const long long need = (w_bound + seg_cap - 2) / (seg_cap - 1);
   long long per = (need + grid - 1) / grid;
   if (per < 1) per = 1;
