@@ -155,23 +155,34 @@ __global__ __launch_bounds__(kSelectThreads) void quest_score_rows_kernel(const 
   constexpr int NV = D / 64;
   const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int Hkv = p.Hkv;
-  int ctx = p.ctx[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
-  const int nb = (ctx + p.bs - 1) / p.bs;
   const int bpp = (kSelectThreads / 8) / Hkv;        // blocks per pass
   const int lb0 = chunk * bpp * kRowScoreUnroll;
-  if (lb0 >= nb || p.K >= nb) return;  // nothing to rank: every block is selected
-  unsigned short* s_q = (unsigned short*)(s_qb + (size_t)Hkv * 2 * (D + kQbPad));   // [H_q][D] bf16
-  stage_query<D>(p, b, 0, p.Hq, s_q);
   const int sub = tid & 7, pair = tid >> 3;
   const int blk = pair / Hkv, g = pair % Hkv;
   const bool active = blk < bpp;
+  // The chunk's table entries are requested together with the sequence's length
+  // rather than after it (one dependent round trip fewer before the metadata
+  // loads): the grid spans the longest context, whose entries the table holds, and
+  // entries past this sequence's blocks are dropped once its length is known.
+  const int max_nb = (p.max_ctx + p.bs - 1) / p.bs;
+  int pbs[kRowScoreUnroll];
+#pragma unroll
+  for (int u = 0; u < kRowScoreUnroll; ++u) {
+    const int lb = lb0 + u * bpp + blk;
+    pbs[u] = (active && lb < max_nb) ? p.bt[(size_t)b * p.max_blocks + lb] : -1;
+  }
+  int ctx = p.ctx[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  const int nb = (ctx + p.bs - 1) / p.bs;
+  if (lb0 >= nb || p.K >= nb) return;  // nothing to rank: every block is selected
+  unsigned short* s_q = (unsigned short*)(s_qb + (size_t)Hkv * 2 * (D + kQbPad));   // [H_q][D] bf16
+  stage_query<D>(p, b, 0, p.Hq, s_q);
   u32x4 mn[kRowScoreUnroll][NV], mx[kRowScoreUnroll][NV];
   bool ok[kRowScoreUnroll];
 #pragma unroll
   for (int u = 0; u < kRowScoreUnroll; ++u) {
     const int lb = lb0 + u * bpp + blk;
-    const int pb = (active && lb < nb) ? p.bt[(size_t)b * p.max_blocks + lb] : -1;
+    const int pb = lb < nb ? pbs[u] : -1;
     ok[u] = pb >= 0 && pb < p.NB;
     const size_t o = ((size_t)(ok[u] ? pb : 0) * Hkv + g) * D + (size_t)sub * 8;
 #pragma unroll
@@ -228,14 +239,17 @@ __global__ __launch_bounds__(kMaxSelectThreads) void quest_topk_kernel(const Top
   extern __shared__ unsigned long long s_key[];
   __shared__ SelectShared sh;
   const int g = blockIdx.x, b = blockIdx.y;
+  const unsigned long long* keys = p.keys + ((size_t)b * p.Hkv + g) * p.max_blocks;
+  // With keys in LDS, the keys of the longest context (lds_keys of them, at most
+  // max_blocks) are requested together with the sequence's length rather than
+  // after it; only the first n are ranked, the rest were not written by this step.
+  for (int i = threadIdx.x; i < p.lds_keys; i += blockDim.x) s_key[i] = keys[i];
   int ctx = p.ctx[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
   const int n = (ctx + p.bs - 1) / p.bs;
   int* out = p.out + ((size_t)b * p.Hkv + g) * p.K;
   if (select_all(n, p.K, out)) return;
-  const unsigned long long* keys = p.keys + ((size_t)b * p.Hkv + g) * p.max_blocks;
   if (n <= p.lds_keys) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) s_key[i] = keys[i];
     __syncthreads();
     radix_topk(n, p.K, [&](int i) { return s_key[i]; }, out, sh);
   } else {
