@@ -792,6 +792,7 @@ struct VarlenPlan {
   // Balanced schedule: workgroups, row tiles per partial slot, and its workspace.
   int rt, nwg, slot_rows, bal_grid;   // nwg shares over bal_grid workgroups
   size_t bal_o_bytes, bal_lse_bytes, bal_info_bytes;
+  bool bal_ok;   // the flattened tile space fits the kernel's 32-bit prefix sums
 };
 
 // Row tiles of the longest chunk (the grid), split size, and the workspace for at
@@ -834,6 +835,7 @@ static VarlenPlan make_varlen_plan(int B, int total_q, int max_q_len, int Hq, in
   const long long u_bound = (long long)Hkv * ((total_rt + kShareTiles - 1) / kShareTiles + B) +
                             (total_rt + pl.rt - 1) / pl.rt + B;
   const long long w_bound = u_bound * (((long long)max_ctx + 31) / 32);
+  pl.bal_ok = w_bound < (1LL << 31);
   const long long seg_cap = (long long)(kMaxTable - 1) * bs / 32 - 1;
   // The grid: two workgroups per CU with row-tile pairs (one wave's MFMA work hides
   // the other's loads); one with single row tiles, which stream K / V like decode
@@ -860,7 +862,7 @@ static VarlenPlan make_varlen_plan(int B, int total_q, int max_q_len, int Hq, in
 // every workgroup then holds 131-132 tiles and ends between 285 and 402 us: what
 // remains is the per-tile cost, which varies with what shares the CU.
 // GPKV_VARLEN_SCHEDULE=split|balanced forces the schedule (tuning and test switch,
-// read per call); the workspace fits either.
+// read per call); the workspace fits either wherever the balanced one can run.
 static bool varlen_balanced() {
   const char* f = getenv("GPKV_VARLEN_SCHEDULE");
   if (f && strcmp(f, "split") == 0) return false;
@@ -884,7 +886,7 @@ extern "C" size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int
   const VarlenPlan pl = make_varlen_plan(batch, total_q, max_q_len, num_q_heads, num_kv_heads,
                                          head_dim, block_size, max_context_len);
   const size_t split = pl.o_bytes + pl.lse_bytes,
-               bal = pl.bal_o_bytes + pl.bal_lse_bytes + pl.bal_info_bytes;
+               bal = pl.bal_ok ? pl.bal_o_bytes + pl.bal_lse_bytes + pl.bal_info_bytes : 0;
   return split > bal ? split : bal;
 }
 
@@ -930,7 +932,9 @@ static int varlen_run(bool fp8, float* out, const void* query, const void* key_c
   if (pl.num_splits > 65535)
     return fail(GPKV_ERR_SHAPE, "%s: max_context_len=%d needs too many splits", fn,
                 max_context_len);
-  const bool balanced = varlen_balanced();
+  // Batches whose (unit, tile) space would overflow the balanced kernel's 32-bit
+  // prefix sums (very long contexts times long chunks) take the fixed splits.
+  const bool balanced = varlen_balanced() && pl.bal_ok;
   const size_t need = balanced ? pl.bal_o_bytes + pl.bal_lse_bytes + pl.bal_info_bytes
                                : pl.o_bytes + pl.lse_bytes;
   if (!workspace || workspace_bytes < need)
