@@ -266,6 +266,11 @@ def per_config_block(cfg, flush, stream, steps):
     res["dense_gbps"] = round(db / (t["us_mean"] * 1e-6) / 1e9, 1)
     res["dense_pct_of_peak"] = round(100 * res["dense_gbps"] / R.MI355X_HBM_GBPS, 1)
     res["dense_step_us"] = round(write_us + t["us_mean"], 2)
+    if w.num_tokens and w.num_tokens == B:   # the same dense step as one call (decode append)
+        t = time_alone(lambda: gp.paged_attention_decode_append(
+            q, nk, nv, kc, vc, slots, bt, ctx, max_context_len=mcl, scale=scale, key_min=kmin,
+            key_max=kmax, out=out, workspace=ws), flush, stream, steps)
+        res["dense_step_append_us"] = t["us_mean"]
     if K:
         if kmin is None:
             kmin = torch.zeros((w.num_blocks, Hkv, D), dtype=bf, device="cuda")
@@ -476,6 +481,16 @@ def main():
                                               args.steps)["us_mean"]
         quest_separate["sum"] = round(sum(quest_separate.values()), 2)
 
+    # The dense step as one call: the write (with the metadata fold when the step
+    # keeps Quest metadata) merged into the dense decode call, timed alone behind the
+    # flush. Idempotent like the step's own write.
+    append_alone = None
+    if w.num_tokens and w.num_tokens == B:
+        append_alone = time_alone(lambda: gp.paged_attention_decode_append(
+            q, nk, nv, kc, vc, slots, bt, ctx, max_context_len=mcl, scale=scale,
+            key_min=kmin if fused else None, key_max=kmax if fused else None, out=out_d,
+            workspace=ws_d), flush, stream, args.steps)
+
     # FP8 (E4M3) KV cache on the same workload: the pool quantised once by the FP8
     # write (every slot), then its write and dense calls timed like the bf16 ones.
     fp8 = None
@@ -634,6 +649,7 @@ def main():
         "us_per_step": round(mean_step, 2),
         "us_per_step_median": round(float(np.median(step_us)), 2),
         "dense_step_us": round(write_us + calls_out["paged_attention_decode"]["us_mean"], 2),
+        "dense_step_one_call": append_alone,
         "quest_step_us": round(quest_us, 2) if quest_us is not None else None,
         "quest_full_metadata_rebuild_us": round(t_full, 2) if t_full is not None else None,
         "graph_replay_us_per_step": round(graph_us, 2) if graph_us is not None else None,

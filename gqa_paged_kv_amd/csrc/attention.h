@@ -394,14 +394,39 @@ __device__ __forceinline__ void attend_head(const AttnCommon& c, int g, int n_su
   }
 }
 
+// A merge of partial rows in progress: acc and W are relative to mr (-inf: nothing
+// merged yet).
+struct MergeState {
+  f32x4 acc;
+  float W, mr;
+};
+
+// One more row (base-2 lse l, normalised values v) into a merge.
+__device__ __forceinline__ void merge_one(MergeState& st, float l, const f32x4& v) {
+  const float m = fmaxf(st.mr, l);
+  if (m == -INFINITY) return;
+  const float s = __builtin_amdgcn_exp2f(st.mr - m);   // 0 when mr = -inf
+  const float w = __builtin_amdgcn_exp2f(l - m);
+  st.W = st.W * s + w;
+  st.acc = st.acc * s + w * v;
+  st.mr = m;
+}
+
+__device__ __forceinline__ f32x4 merge_finish(const MergeState& st) {
+  const float inv = st.W > 0.f ? 1.f / st.W : 0.f;
+  return st.acc * inv;
+}
+
 // Merge of n partial rows (one float4 column of each): row k has base-2 lse
-// lse0[k * ls] and normalised output o0[k * os]; live(k) false skips a row. Returns
-// sum_k 2^(lse_k - M) O_k / sum_k 2^(lse_k - M) (zeros when no row holds a token).
-// NU rows (lse and output) are requested together, and the sum is kept relative
-// to the largest lse seen so far, so up to NU rows cost one round of loads.
+// lse0[k * ls] and normalised output o0[k * os]; live(k) false skips a row.
+// merge_rows returns sum_k 2^(lse_k - M) O_k / sum_k 2^(lse_k - M) (zeros when no
+// row holds a token). NU rows (lse and output) are requested together, and the sum
+// is kept relative to the largest lse seen so far, so up to NU rows cost one round
+// of loads.
 template <int NU, class Live>
-__device__ __forceinline__ f32x4 merge_rows(int n, const float* lse0, size_t ls, const float* o0,
-                                            size_t os, const Live& live) {
+__device__ __forceinline__ MergeState merge_rows_state(int n, const float* lse0, size_t ls,
+                                                       const float* o0, size_t os,
+                                                       const Live& live) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f, mr = -INFINITY;   // acc and W are relative to mr (-inf: nothing yet)
   for (int k0 = 0; k0 < n; k0 += NU) {
@@ -429,12 +454,39 @@ __device__ __forceinline__ f32x4 merge_rows(int n, const float* lse0, size_t ls,
       acc += w * v[x];
     }
   }
-  const float inv = W > 0.f ? 1.f / W : 0.f;
-  return acc * inv;
+  return MergeState{acc, W, mr};
+}
+
+template <int NU, class Live>
+__device__ __forceinline__ f32x4 merge_rows(int n, const float* lse0, size_t ls, const float* o0,
+                                            size_t os, const Live& live) {
+  return merge_finish(merge_rows_state<NU>(n, lse0, ls, o0, os, live));
 }
 
 __device__ __forceinline__ int clamp_ctx(int v, int max_ctx) {
   return v < 0 ? 0 : (v > max_ctx ? max_ctx : v);
+}
+
+// Decode append (the step's cache write merged into the decode call): sequence b's
+// newest token, at position ctx - 1, comes from the call's key / value inputs when
+// its slot lies in the pool and the context holds it. The split phase then stops
+// one position short and the combine merges the token as one more unit.
+// The slot is requested together with the context length (not after it), so that
+// neither load waits for the other.
+__device__ __forceinline__ bool append_token(const long long* slots, long long num_slots, int b,
+                                             const int* ctx, int max_ctx) {
+  if (slots == nullptr) return false;
+  const long long s = slots[b];
+  const int c = clamp_ctx(ctx[b], max_ctx);
+  return c >= 1 && s >= 0 && s < num_slots;
+}
+// Positions of sequence b the split phase reads: its clamped context, less the
+// appended token.
+__device__ __forceinline__ int split_ctx(const int* ctx, const long long* slots,
+                                         long long num_slots, int b, int max_ctx) {
+  const long long s = slots != nullptr ? slots[b] : -1;
+  const int c = clamp_ctx(ctx[b], max_ctx);
+  return c - ((c >= 1 && s >= 0 && s < num_slots) ? 1 : 0);
 }
 
 

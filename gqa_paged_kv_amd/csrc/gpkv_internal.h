@@ -72,6 +72,21 @@ __device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Quest key min / max of a block after one more row k (eight bf16 channels per
+// vector): the element-wise min and max of the block's current metadata and k,
+// bf16 values compared as float (exact: each result is one of the inputs).
+__device__ __forceinline__ void fold_min_max(const u32x4& k, const u32x4& om, const u32x4& ox,
+                                             u32x4& mn, u32x4& mx) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float klo = bf16_lo(k[w]), khi = bf16_hi(k[w]);
+    mn[w] = (__float_as_uint(fminf(bf16_lo(om[w]), klo)) >> 16) |
+            (__float_as_uint(fminf(bf16_hi(om[w]), khi)) & 0xffff0000u);
+    mx[w] = (__float_as_uint(fmaxf(bf16_lo(ox[w]), klo)) >> 16) |
+            (__float_as_uint(fmaxf(bf16_hi(ox[w]), khi)) & 0xffff0000u);
+  }
+}
+
 // v_perm_b32 helpers: pack the low (or high) 16-bit halves of a and b as (a | b << 16).
 __device__ __forceinline__ unsigned pack_lo16(unsigned a, unsigned b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

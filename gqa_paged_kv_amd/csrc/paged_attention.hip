@@ -46,6 +46,7 @@ struct SplitParams {
   const int* block_tables;   // [B, max_blocks]
   const int* ctx;            // [B]
   const int* topk;           // [B, H_kv, K] (sparse only)
+  const long long* slots;    // decode append: [B] slot of each sequence's new token, or null
   long long NB;              // pool size; block ids outside [0, NB) select nothing
   int max_blocks, max_ctx, num_splits, split_tokens, topk_blocks;
 };
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);  // tell the compiler the tile loop is wave-uniform
   const int bs = p.c.bs, Hkv = p.c.Hkv;
-  const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+  const int ctx = split_ctx(p.ctx, p.slots, p.NB * bs, b, p.max_ctx);
   const int nb = (ctx + bs - 1) / bs;
   const int T = p.split_tokens;
   const int span = SPARSE ? p.topk_blocks * bs : ctx;
@@ -127,6 +128,7 @@ struct BalParams {
   const int* block_tables;
   const int* ctx;
   const int* topk;           // [B, H_kv, K] logical block ids (sparse only)
+  const long long* slots;    // decode append: [B] slot of each sequence's new token, or null
   long long NB;
   int B, max_blocks, max_ctx, nwg, topk_blocks;
 };
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const int bb = base + tid;
     int n = 0;
     if (bb < B) {
-      const int ctx = clamp_ctx(p.ctx[bb], p.max_ctx);
+      const int ctx = split_ctx(p.ctx, p.slots, p.NB * bs, bb, p.max_ctx);
       if (SPARSE) {
         const int nb = (ctx + bs - 1) / bs;
         n = (nb < p.topk_blocks ? nb : p.topk_blocks) * spb;
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const int ub = (s0 > s_pref[b] ? s0 : s_pref[b]) - s_pref[b];
     const int ue = (s1 < s_pref[b + 1] ? s1 : s_pref[b + 1]) - s_pref[b];
     if (ue <= ub) continue;  // empty sequence
-    const int ctx = clamp_ctx(p.ctx[b], p.max_ctx);
+    const int ctx = split_ctx(p.ctx, p.slots, p.NB * bs, b, p.max_ctx);
     const int nb = (ctx + bs - 1) / bs;
     // Table entries (blocks) the share touches: dense, logical blocks e0 ..;
     // sparse, positions e0 .. of each KV head's list with the invalid ids removed.
@@ -390,10 +392,72 @@ struct CombineParams {
   float* out;               // [B, H_q, D]
   const float* part_o;
   const float* part_lse;
-  const int* ctx;           // split path
+  const int* ctx;
   const int* prefix;        // balanced path
   int Hq, Hkv, G, max_ctx, num_splits, split_tokens, sparse, balanced, B, nwg;
+  // Decode append (slots non-null): sequence b's new token (row b of knew / vnew)
+  // joins the merge as one more unit, and the combine writes it into the cache at
+  // its slot (and folds it into the Quest key min / max when kmin is non-null).
+  const long long* slots;      // [B]
+  long long num_slots;         // NB * bs
+  const unsigned short* q;     // [B, H_q, D] bf16
+  const unsigned short* knew;  // [B, H_kv, D] bf16
+  const unsigned short* vnew;
+  unsigned short* kc;          // [NB, bs, H_kv, D] bf16
+  unsigned short* vc;
+  unsigned short* kmin;        // [NB, H_kv, D] bf16, or null
+  unsigned short* kmax;
+  int bs;
+  float qk_scale_log2;
 };
+
+// Decode append: the new token's unit for query head g G + hl of sequence b, as
+// thread c4 of the D / 4 threads holding the row's float4 columns sees it: base-2
+// lse q . k_new * scale * log2(e) (the exact bf16 products summed in float32 over
+// those threads, consecutive lanes of one wave that all call this) and the token's
+// values.
+template <int D>
+__device__ __forceinline__ void append_unit(const CombineParams& p, int b, int g, int hl, int c4,
+                                            float& lse, f32x4& v) {
+  constexpr int TPU = D / 4;
+  const uint2 qq = *(const uint2*)(p.q + ((size_t)b * p.Hq + (size_t)g * p.G + hl) * D + 4 * c4);
+  const size_t row = ((size_t)b * p.Hkv + g) * D + 4 * c4;
+  const uint2 kk = *(const uint2*)(p.knew + row);
+  const uint2 vv = *(const uint2*)(p.vnew + row);
+  float dot = bf16_lo(qq.x) * bf16_lo(kk.x);
+  dot = __builtin_fmaf(bf16_hi(qq.x), bf16_hi(kk.x), dot);
+  dot = __builtin_fmaf(bf16_lo(qq.y), bf16_lo(kk.y), dot);
+  dot = __builtin_fmaf(bf16_hi(qq.y), bf16_hi(kk.y), dot);
+#pragma unroll
+  for (int o = TPU / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+  lse = dot * p.qk_scale_log2;
+  v = f32x4{bf16_lo(vv.x), bf16_hi(vv.x), bf16_lo(vv.y), bf16_hi(vv.y)};
+}
+
+// Decode append: KV head g's part of sequence b's new token written into the cache
+// at its slot (a slot outside the pool writes nothing, as reshape_and_cache), and
+// folded into its block's Quest key min / max (row 0 of a block starts it afresh).
+template <int D>
+__device__ __forceinline__ void append_write(const CombineParams& p, int b, int g) {
+  const long long s = p.slots[b];
+  if (s < 0 || s >= p.num_slots) return;
+  const long long blk = s / p.bs, off = s - blk * p.bs;
+  const size_t row = (size_t)p.Hkv * D;   // bf16 per cache row
+  for (int c = threadIdx.x; c < D / 8; c += blockDim.x) {
+    const size_t src = ((size_t)b * p.Hkv + g) * D + 8 * c;
+    const size_t dst = (size_t)s * row + (size_t)g * D + 8 * c;
+    const u32x4 k = *(const u32x4*)(p.knew + src);
+    *(u32x4*)(p.kc + dst) = k;
+    *(u32x4*)(p.vc + dst) = *(const u32x4*)(p.vnew + src);
+    if (p.kmin != nullptr) {
+      const size_t meta = (size_t)blk * row + (size_t)g * D + 8 * c;
+      u32x4 mn = k, mx = k;
+      if (off > 0) fold_min_max(k, *(const u32x4*)(p.kmin + meta), *(const u32x4*)(p.kmax + meta), mn, mx);
+      *(u32x4*)(p.kmin + meta) = mn;
+      *(u32x4*)(p.kmax + meta) = mx;
+    }
+  }
+}
 
 
 // Units of (sequence b, KV head g, query head hl of the group) are u in
@@ -434,7 +498,7 @@ __device__ __forceinline__ UnitRange unit_range(const CombineParams& p, int b, i
     r.lse0 = p.part_lse + ((size_t)b * p.Hkv + g) * G + hl;
     r.o0 = p.part_o + (((size_t)b * p.Hkv + g) * G + hl) * D;
   } else {
-    const int ctx = p.ctx[b] < 0 ? 0 : (p.ctx[b] > p.max_ctx ? p.max_ctx : p.ctx[b]);
+    const int ctx = split_ctx(p.ctx, p.slots, p.num_slots, b, p.max_ctx);
     r.u_begin = 0;
     r.u_end = p.sparse ? p.num_splits : (ctx + p.split_tokens - 1) / p.split_tokens;
     const size_t unit0 = ((size_t)b * p.Hkv + g) * p.num_splits;
@@ -453,23 +517,33 @@ __device__ __forceinline__ UnitRange unit_range(const CombineParams& p, int b, i
 // rows in one round of loads after the prefix.
 constexpr int kHeadUnits = 12;
 
-template <int D>
+template <int D, bool APPEND>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_heads_kernel(const CombineParams p) {
   constexpr int TPU = D / 4;
   constexpr int SLOTS = kCombineThreads / TPU;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int slot = tid / TPU, c4 = tid % TPU;
+  const bool append = APPEND && append_token(p.slots, p.num_slots, b, p.ctx, p.max_ctx);
   for (int hl = slot; hl < p.G; hl += SLOTS) {
     const UnitRange r = unit_range<D>(p, b, g, hl);
     const int u0 = r.u_begin;
-    const f32x4 o = merge_rows<kHeadUnits>(
+    // (the append instance requests eight unit rows at once, so that its new-token
+    // unit fits the same four waves per SIMD)
+    MergeState st = merge_rows_state<APPEND ? 8 : kHeadUnits>(
         r.u_end - u0, r.lse0 + (size_t)u0 * r.lstride, r.lstride,
         r.o0 + (size_t)u0 * r.ostride + 4 * c4, r.ostride, [&](int k) { return r.live(u0 + k); });
-    *(f32x4*)(p.out + ((size_t)b * p.Hq + (size_t)g * p.G + hl) * D + 4 * c4) = o;
+    if (append) {
+      float l;
+      f32x4 v;
+      append_unit<D>(p, b, g, hl, c4, l, v);
+      merge_one(st, l, v);
+    }
+    *(f32x4*)(p.out + ((size_t)b * p.Hq + (size_t)g * p.G + hl) * D + 4 * c4) = merge_finish(st);
   }
+  if (APPEND) append_write<D>(p, b, g);
 }
 
-template <int D>
+template <int D, bool APPEND>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const CombineParams p) {
   constexpr int TPU = D / 4;                       // threads per unit row
   constexpr int UPP = kCombineThreads / TPU;       // units per pass
@@ -480,9 +554,20 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
   const int g = h / G, hl = h - g * G;
   float* out = p.out + ((size_t)b * p.Hq + h) * D;
 
+  const bool append = APPEND && append_token(p.slots, p.num_slots, b, p.ctx, p.max_ctx);
+  if (APPEND && hl == 0) append_write<D>(p, b, g);
   const UnitRange r = unit_range<D>(p, b, g, hl);
-  if (r.u_end <= r.u_begin) {
-    for (int c = tid; c < D; c += kCombineThreads) out[c] = 0.f;
+  if (r.u_end <= r.u_begin) {   // no unit: the appended token alone, or nothing
+    if (tid < TPU) {
+      MergeState st{f32x4{0.f, 0.f, 0.f, 0.f}, 0.f, -INFINITY};
+      if (append) {
+        float l;
+        f32x4 v;
+        append_unit<D>(p, b, g, hl, tid, l, v);
+        merge_one(st, l, v);
+      }
+      *(f32x4*)(out + 4 * tid) = merge_finish(st);
+    }
     return;
   }
   const int u_begin = r.u_begin, u_end = r.u_end;
@@ -545,8 +630,14 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
         wt += sk * s_red[k];
       }
     }
-    const float inv = wt > 0.f ? 1.f / wt : 0.f;
-    *(f32x4*)(out + 4 * tid) = a * inv;
+    MergeState st{a, wt, M};
+    if (append) {
+      float l;
+      f32x4 v;
+      append_unit<D>(p, b, g, hl, tid, l, v);
+      merge_one(st, l, v);
+    }
+    *(f32x4*)(out + 4 * tid) = merge_finish(st);
   }
 }
 
@@ -675,19 +766,31 @@ static void launch_attention(bool balanced, const BalParams& bp, const SplitPara
     attn_split_kernel<D, SPARSE, FP8><<<dim3(num_splits, B), block, 0, stream>>>(sp);
 }
 
+// Decode append inputs (gpkv_paged_attention_decode_append): the new tokens' rows,
+// their slots and the Quest metadata to fold them into (null: none).
+struct AppendArgs {
+  const void* key;
+  const void* value;
+  void* key_min;
+  void* key_max;
+  const int64_t* slots;
+};
+
 static int attn_run(bool sparse, bool fp8, float* out, const void* query, const void* kc,
                     const void* vc, const float* k_scale, const float* v_scale, const int* bt,
                     const int* ctx, const int* topk, int B, int Hq, int Hkv, int D, int bs,
                     long long NB, int max_blocks, int max_ctx, int K, float scale, void* ws,
-                    size_t ws_bytes, hipStream_t stream) {
-  const char* fn = sparse ? (fp8 ? "sparse_paged_attention_decode_fp8" : "sparse_paged_attention_decode")
-                          : (fp8 ? "paged_attention_decode_fp8" : "paged_attention_decode");
+                    size_t ws_bytes, hipStream_t stream, const AppendArgs* app = nullptr) {
+  const char* fn = app ? "paged_attention_decode_append"
+                : sparse ? (fp8 ? "sparse_paged_attention_decode_fp8" : "sparse_paged_attention_decode")
+                         : (fp8 ? "paged_attention_decode_fp8" : "paged_attention_decode");
   int st = check_common(fn, B, Hq, Hkv, D, bs, NB, max_blocks, max_ctx);
   if (st) return st;
   if (sparse && K < 1) return fail(GPKV_ERR_SHAPE, "%s: topk_blocks=%d < 1", fn, K);
   if (B == 0) return GPKV_OK;
   if (!out || !query || !kc || !vc || !bt || !ctx || (sparse && !topk) ||
-      (fp8 && (!k_scale || !v_scale)))
+      (fp8 && (!k_scale || !v_scale)) ||
+      (app && (!app->key || !app->value || !app->slots || (!app->key_min != !app->key_max))))
     return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
   const long long span_ll = sparse ? (long long)K * bs : (long long)max_ctx;
   if (span_ll > (1LL << 30)) return fail(GPKV_ERR_SHAPE, "%s: token span too large", fn);
@@ -753,6 +856,7 @@ static int attn_run(bool sparse, bool fp8, float* out, const void* query, const 
   bp.block_tables = bt;
   bp.ctx = ctx;
   bp.topk = topk;
+  bp.slots = app ? (const long long*)app->slots : nullptr;
   bp.NB = NB;
   bp.B = B;
   bp.max_blocks = max_blocks;
@@ -766,6 +870,7 @@ static int attn_run(bool sparse, bool fp8, float* out, const void* query, const 
   sp.block_tables = bt;
   sp.ctx = ctx;
   sp.topk = topk;
+  sp.slots = bp.slots;
   sp.NB = NB;
   sp.max_blocks = max_blocks;
   sp.max_ctx = max_ctx;
@@ -802,23 +907,51 @@ static int attn_run(bool sparse, bool fp8, float* out, const void* query, const 
   cp.balanced = pl.balanced ? 1 : 0;
   cp.B = B;
   cp.nwg = pl.nwg;
+  cp.slots = bp.slots;
+  cp.num_slots = NB * bs;
+  cp.q = (const unsigned short*)query;
+  cp.knew = app ? (const unsigned short*)app->key : nullptr;
+  cp.vnew = app ? (const unsigned short*)app->value : nullptr;
+  cp.kc = (unsigned short*)kc;   // written only by the append call, whose caches are writable
+  cp.vc = (unsigned short*)vc;
+  cp.kmin = app ? (unsigned short*)app->key_min : nullptr;
+  cp.kmax = app ? (unsigned short*)app->key_max : nullptr;
+  cp.bs = bs;
+  cp.qk_scale_log2 = c.qk_scale_log2;
   // Many units per sequence (long sequences over many workgroups or splits): one
   // workgroup per query head, its threads spread over the units. Few units: one
   // workgroup per KV head, a slot of threads per query head.
   const long long units_per_seq = pl.balanced ? (long long)pl.nwg / B + 1 : pl.num_splits;
   const dim3 cblock(kCombineThreads);
+  // The append call's combine is its own instance: its extra registers (the new
+  // token's unit) stay out of the plain combine.
+  const bool app_on = cp.slots != nullptr;
   if (units_per_seq >= 6) {
     const dim3 cgrid(Hq, B);
-    if (D == 128)
-      attn_combine_kernel<128><<<cgrid, cblock, 0, stream>>>(cp);
-    else
-      attn_combine_kernel<64><<<cgrid, cblock, 0, stream>>>(cp);
+    if (D == 128) {
+      if (app_on)
+        attn_combine_kernel<128, true><<<cgrid, cblock, 0, stream>>>(cp);
+      else
+        attn_combine_kernel<128, false><<<cgrid, cblock, 0, stream>>>(cp);
+    } else {
+      if (app_on)
+        attn_combine_kernel<64, true><<<cgrid, cblock, 0, stream>>>(cp);
+      else
+        attn_combine_kernel<64, false><<<cgrid, cblock, 0, stream>>>(cp);
+    }
   } else {
     const dim3 cgrid(Hkv, B);
-    if (D == 128)
-      attn_combine_heads_kernel<128><<<cgrid, cblock, 0, stream>>>(cp);
-    else
-      attn_combine_heads_kernel<64><<<cgrid, cblock, 0, stream>>>(cp);
+    if (D == 128) {
+      if (app_on)
+        attn_combine_heads_kernel<128, true><<<cgrid, cblock, 0, stream>>>(cp);
+      else
+        attn_combine_heads_kernel<128, false><<<cgrid, cblock, 0, stream>>>(cp);
+    } else {
+      if (app_on)
+        attn_combine_heads_kernel<64, true><<<cgrid, cblock, 0, stream>>>(cp);
+      else
+        attn_combine_heads_kernel<64, false><<<cgrid, cblock, 0, stream>>>(cp);
+    }
   }
   return check_launch(fn);
 }
@@ -864,6 +997,21 @@ extern "C" int gpkv_paged_attention_decode(float* out, const void* query, const 
                   block_tables, context_lens, nullptr, batch, num_q_heads, num_kv_heads, head_dim,
                   block_size, num_blocks, max_blocks_per_seq, max_context_len, 0, scale,
                   workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" int gpkv_paged_attention_decode_append(
+    float* out, const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, void* key_min, void* key_max, const int64_t* slot_mapping,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  clear_error();
+  AppendArgs app{key, value, key_min, key_max, slot_mapping};
+  return attn_run(false, false, out, query, key_cache, value_cache, nullptr, nullptr,
+                  block_tables, context_lens, nullptr, batch, num_q_heads, num_kv_heads, head_dim,
+                  block_size, num_blocks, max_blocks_per_seq, max_context_len, 0, scale,
+                  workspace, workspace_bytes, (hipStream_t)stream, &app);
 }
 
 // ---------------------------------------------------------------------------

@@ -53,17 +53,7 @@ __global__ __launch_bounds__(64) void reshape_and_cache_quest_kernel(
     key_cache[dst + c] = k;
     value_cache[dst + c] = value[src + c];
     u32x4 mn = k, mx = k;
-    if (off > 0) {
-      const u32x4 om = key_min[meta + c], ox = key_max[meta + c];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float klo = bf16_lo(k[w]), khi = bf16_hi(k[w]);
-        mn[w] = (__float_as_uint(fminf(bf16_lo(om[w]), klo)) >> 16) |
-                (__float_as_uint(fminf(bf16_hi(om[w]), khi)) & 0xffff0000u);
-        mx[w] = (__float_as_uint(fmaxf(bf16_lo(ox[w]), klo)) >> 16) |
-                (__float_as_uint(fmaxf(bf16_hi(ox[w]), khi)) & 0xffff0000u);
-      }
-    }
+    if (off > 0) fold_min_max(k, key_min[meta + c], key_max[meta + c], mn, mx);
     key_min[meta + c] = mn;
     key_max[meta + c] = mx;
   }

@@ -13,7 +13,7 @@ from ._lib import lib
 
 __all__ = [
     "GpkvError", "reshape_and_cache", "reshape_and_cache_quest", "paged_attention_decode",
-    "quest_block_metadata",
+    "paged_attention_decode_append", "quest_block_metadata",
     "quest_select_topk", "sparse_paged_attention_decode", "paged_attention_workspace_bytes",
     "quest_select_workspace_bytes", "sparse_attention_workspace_bytes", "split_tokens",
     "reshape_and_cache_fp8", "paged_attention_decode_fp8", "sparse_paged_attention_decode_fp8",
@@ -155,6 +155,43 @@ def paged_attention_decode(query, key_cache, value_cache, block_tables, context_
     ws = _workspace(need, query.device, workspace)
     _check(lib().gpkv_paged_attention_decode(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), B, Hq, Hkv, D, bs, NB, MB, int(max_context_len), float(scale),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def paged_attention_decode_append(query, key, value, key_cache, value_cache, slot_mapping,
+                                  block_tables, context_lens, *, max_context_len: int,
+                                  scale: float, key_min=None, key_max=None, out=None,
+                                  workspace=None, stream=None) -> torch.Tensor:
+    """Decode append: writes token b of key / value (sequence b's newest token, at
+    position context_lens[b] - 1) to slot_mapping[b] (with the Quest key min / max
+    fold when key_min / key_max are given) and returns the dense attention over the
+    contexts including it, out [B, H_q, D] float32 -- one call, two launches."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks(query, key_cache, value_cache, block_tables,
+                                             context_lens)
+    _dev("key", key, torch.bfloat16, 3)
+    _dev("value", value, torch.bfloat16, 3)
+    _dev("slot_mapping", slot_mapping, torch.int64, 1)
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape[0] != B:
+        raise ValueError("paged_attention_decode_append: key / value / slot_mapping must hold "
+                         "one token per sequence")
+    if (key_min is None) != (key_max is None):
+        raise ValueError("paged_attention_decode_append: key_min and key_max go together")
+    if key_min is not None:
+        _dev("key_min", key_min, torch.bfloat16, 3)
+        _dev("key_max", key_max, torch.bfloat16, 3)
+        if key_min.shape != (NB, Hkv, D) or key_max.shape != (NB, Hkv, D):
+            raise ValueError("paged_attention_decode_append: inconsistent metadata shapes")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    need = paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_paged_attention_decode_append(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+        _ptr(key_min) if key_min is not None else None,
+        _ptr(key_max) if key_max is not None else None, _ptr(slot_mapping), _ptr(block_tables),
         _ptr(context_lens), B, Hq, Hkv, D, bs, NB, MB, int(max_context_len), float(scale),
         _ptr(ws), ws.numel(), _stream(stream)))
     return out

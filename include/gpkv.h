@@ -7,6 +7,7 @@
  *   gpkv_reshape_and_cache           write new tokens' K/V rows into the cache
  *   gpkv_reshape_and_cache_quest     ... and update those blocks' Quest key min / max
  *   gpkv_paged_attention_decode      dense GQA paged attention (split-KV + combine)
+ *   gpkv_paged_attention_decode_append   ... with the step's cache write (decode append)
  *   gpkv_paged_attention_decode_noalloc  ... without a workspace (fixed device array)
  *   gpkv_quest_block_metadata        per-block, per-channel key min / max
  *   gpkv_quest_select_topk           Quest block scores + Top-K per KV head
@@ -142,6 +143,45 @@ int gpkv_paged_attention_decode(float* out, const void* query, const void* key_c
                                 int32_t max_blocks_per_seq, int32_t max_context_len,
                                 float scale, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* The step's cache write merged into the dense decode call (the KV-cache update
+ * sharing the decode kernel's launch, [DSA] items 2-3; the per-step KV write is a
+ * real cost, [TL18] 8 item (2)): one call, two launches, for the decode-append case
+ * where token b of key / value is sequence b's newest token, at position
+ * context_lens[b] - 1. With s = slot_mapping[b]:
+ *   0 <= s < num_blocks * block_size: key[b] / value[b] are written to slot s as
+ *     gpkv_reshape_and_cache writes them and, when key_min / key_max are given,
+ *     folded into that block's Quest metadata as gpkv_reshape_and_cache_quest does;
+ *     the attention of sequence b takes its position context_lens[b] - 1 from
+ *     key[b] / value[b] (when context_lens[b] >= 1);
+ *   otherwise: nothing is written and the attention reads the cache as
+ *     gpkv_paged_attention_decode does.
+ * The result equals gpkv_reshape_and_cache(_quest) over the batch's tokens followed
+ * by gpkv_paged_attention_decode (attention within the same tolerance, caches and
+ * metadata bit for bit) under the precondition of the decode-append case: every
+ * in-pool slot_mapping[b] is the slot of sequence b's position context_lens[b] - 1
+ * (block_tables[b, (context_lens[b] - 1) / block_size], row
+ * (context_lens[b] - 1) % block_size), and no other sequence reads that slot. The
+ * split phase reads the cache up to position context_lens[b] - 2 of such a sequence;
+ * the combine merges the new token as one more unit and writes it into the cache.
+ * key, value: [batch, num_kv_heads, head_dim] bf16. slot_mapping: [batch] int64.
+ * key_min, key_max: [num_blocks, num_kv_heads, head_dim] bf16, both null (no
+ *   metadata) or both given. key_cache, value_cache (and the metadata) are modified
+ *   in place at the written slots only.
+ * Everything else (out, query, tables, sizes, scale, workspace of
+ * gpkv_paged_attention_workspace_bytes, errors) as gpkv_paged_attention_decode;
+ * one of key_min / key_max null without the other is GPKV_ERR_NULL. */
+int gpkv_paged_attention_decode_append(float* out, const void* query, const void* key,
+                                       const void* value, void* key_cache, void* value_cache,
+                                       void* key_min, void* key_max,
+                                       const int64_t* slot_mapping,
+                                       const int32_t* block_tables,
+                                       const int32_t* context_lens, int32_t batch,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /* gpkv_paged_attention_decode without allocation, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses that

@@ -117,3 +117,32 @@ def sample_seqs(w: workloads.Workload, n: int = 6, seed: int = 0) -> list[int]:
 
 def max_abs(a, b) -> float:
     return float(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64)).max())
+
+
+# ---------------------------------------------------------------------------
+# The write path: metadata comparisons and the pre-write context
+# ---------------------------------------------------------------------------
+
+SENTINEL = 0x1234   # fills metadata rows no call should touch
+
+
+def meta_equal(got, exp) -> bool:
+    """Bitwise, except +0 and -0 count as equal."""
+    g = got.copy()
+    e = exp.copy()
+    g[g == 0x8000] = 0
+    e[e == 0x8000] = 0
+    return np.array_equal(g, e)
+
+
+def before_write_lens(w: workloads.Workload) -> np.ndarray:
+    """Context lengths before this step's write: ctx - 1 for a sequence whose
+    newest slot (position ctx - 1) is written by a valid slot of slot_mapping."""
+    ctx, bt, bs = w.context_lens.astype(np.int64), w.block_tables, w.block_size
+    valid = set(int(s) for s in w.slot_mapping if 0 <= s < w.num_blocks * bs)
+    before = ctx.copy()
+    for b in np.nonzero(ctx > 0)[0]:
+        pos = ctx[b] - 1
+        if int(bt[b, pos // bs]) * bs + int(pos % bs) in valid:
+            before[b] -= 1
+    return before.astype(np.int32)

@@ -29,7 +29,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(L):
     from gqa_paged_kv_amd._lib import SIGNATURES
     names = declared_symbols()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     assert sorted(SIGNATURES) == names
@@ -128,6 +128,26 @@ def test_other_entry_points_checks(L):
     assert L.gpkv_quest_decode_workspace_bytes(2, 4, 1, 64, 16, 5, 3) >= max(
         L.gpkv_quest_select_workspace_bytes(2, 1, 5),
         L.gpkv_sparse_attention_workspace_bytes(2, 4, 1, 64, 16, 3))
+
+
+def test_append_argument_checks(L):
+    """The dense call with the step's cache write: its own pointers (new rows, slots,
+    metadata given as a pair) and the dense call's checks, all refused on the host
+    (no call here launches anything)."""
+    a = ARGS
+    f = L.gpkv_paged_attention_decode_append
+
+    def call(key=8, kmin=None, kmax=None, slots=8, ws=1 << 40, D=a["D"], B=a["B"], wsp=8):
+        return f(8, 8, key, 8, 8, 8, kmin, kmax, slots, 8, 8, B, a["Hq"], a["Hkv"], D, a["bs"],
+                 a["NB"], a["MB"], a["mcl"], 0.125, wsp, ws, None)
+
+    assert call(key=None) == -1
+    assert call(slots=None) == -1
+    assert call(kmin=8) == -1          # key_min without key_max
+    assert call(kmax=8) == -1
+    assert call(D=96) == -3
+    assert call(ws=16) == -4
+    assert call(B=0, key=None, slots=None) == 0   # an empty batch launches nothing
 
 
 def test_noalloc_argument_checks(L):

@@ -108,13 +108,21 @@ def _check_against_oracle(case, w, snap):
 
 
 def _step(w, d, buf, K, fused, one_call=False):
+    """fused: False (write, dense, metadata refresh), True (write with the metadata
+    fold, dense) or "append" (write, fold and dense attention in one call)."""
     mcl, bs, scale = w.max_context_len, w.block_size, float(w.scale)
-    if fused:   # write + incremental metadata in one launch (both idempotent)
-        gp.reshape_and_cache_quest(d.nk, d.nv, d.kc, d.vc, buf["kmin"], buf["kmax"], d.slots)
+    if fused == "append":
+        gp.paged_attention_decode_append(d.q, d.nk, d.nv, d.kc, d.vc, d.slots, d.bt, d.ctx,
+                                         max_context_len=mcl, scale=scale, key_min=buf["kmin"],
+                                         key_max=buf["kmax"], out=buf["out_d"],
+                                         workspace=buf["ws_d"])
     else:
-        gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
-    gp.paged_attention_decode(d.q, d.kc, d.vc, d.bt, d.ctx, max_context_len=mcl, scale=scale,
-                              out=buf["out_d"], workspace=buf["ws_d"])
+        if fused:   # write + incremental metadata in one launch (both idempotent)
+            gp.reshape_and_cache_quest(d.nk, d.nv, d.kc, d.vc, buf["kmin"], buf["kmax"], d.slots)
+        else:
+            gp.reshape_and_cache(d.nk, d.nv, d.kc, d.vc, d.slots)
+        gp.paged_attention_decode(d.q, d.kc, d.vc, d.bt, d.ctx, max_context_len=mcl, scale=scale,
+                                  out=buf["out_d"], workspace=buf["ws_d"])
     if not fused:
         gp.quest_block_metadata(d.kc, d.bt, d.ctx, buf["kmin"], buf["kmax"],
                                 max_context_len=mcl, last_block_only=True)
@@ -141,7 +149,10 @@ def _snapshot(buf, d):
                                                  ("random", True, False), ("config3", True, False),
                                                  ("random", True, "fused"), ("config3", True, "fused"),
                                                  ("long", True, "auto"),
-                                                 ("long", True, "fused")])
+                                                 ("long", True, "fused"),
+                                                 ("random", "append", False),
+                                                 ("config3", "append", "fused"),
+                                                 ("long", "append", "auto")])
 def test_graph_replay_equals_eager(case, fused, one_call, monkeypatch):
     if one_call:   # the one-call Quest decode on the path named
         monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", one_call)

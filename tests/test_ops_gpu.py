@@ -15,8 +15,10 @@ import torch
 import gqa_paged_kv_amd as gp
 import oracle
 import workloads
-from gpu_util import (BF, Dev, bits, dense_ref, max_abs, oracle_selection, sparse_ref, to_dev,
-                      workload)
+from gpu_util import (BF, SENTINEL, Dev, bits, dense_ref, max_abs, oracle_selection, sparse_ref,
+                      to_dev, workload)
+from gpu_util import before_write_lens as _before_write_lens
+from gpu_util import meta_equal as _meta_equal
 
 pytestmark = pytest.mark.gpu
 ATOL = 2e-3
@@ -209,9 +211,6 @@ def test_dense_invariants_permuted_poison_deterministic():
 # Quest metadata, Top-K, sparse attention
 # ---------------------------------------------------------------------------
 
-SENTINEL = 0x1234
-
-
 def _meta(d, w, last_only=False, kmin=None, kmax=None):
     if kmin is None:
         kmin = to_dev(np.full((w.num_blocks, w.num_kv_heads, w.head_dim), SENTINEL, np.uint16), BF)
@@ -219,15 +218,6 @@ def _meta(d, w, last_only=False, kmin=None, kmax=None):
     gp.quest_block_metadata(d.kc, d.bt, d.ctx, kmin, kmax, max_context_len=w.max_context_len,
                             last_block_only=last_only)
     return kmin, kmax
-
-
-def _meta_equal(got, exp):
-    """Bitwise, except +0 and -0 count as equal."""
-    g = got.copy()
-    e = exp.copy()
-    g[g == 0x8000] = 0
-    e[e == 0x8000] = 0
-    return np.array_equal(g, e)
 
 
 @pytest.mark.parametrize("config", [1, 3, 4, 5])
@@ -258,19 +248,6 @@ def test_quest_metadata_step_after_write():
     emin, emax = oracle.quest_block_metadata(kc, w.block_tables, w.context_lens, w.block_size,
                                              last_block_only=True, key_min=base, key_max=base)
     assert _meta_equal(bits(kmin), emin) and _meta_equal(bits(kmax), emax)
-
-
-def _before_write_lens(w):
-    """Context lengths before this step's write: ctx - 1 for a sequence whose
-    newest slot (position ctx - 1) is written by a valid slot of slot_mapping."""
-    ctx, bt, bs = w.context_lens.astype(np.int64), w.block_tables, w.block_size
-    valid = set(int(s) for s in w.slot_mapping if 0 <= s < w.num_blocks * bs)
-    before = ctx.copy()
-    for b in np.nonzero(ctx > 0)[0]:
-        pos = ctx[b] - 1
-        if int(bt[b, pos // bs]) * bs + int(pos % bs) in valid:
-            before[b] -= 1
-    return before.astype(np.int32)
 
 
 def _check_fused_write(w):
