@@ -286,6 +286,11 @@ def per_config_block(cfg, flush, stream, steps):
                        flush, stream, steps)
         qb = (R.select_bytes(w.context_lens, bs, Hkv, D)
               + R.sparse_attention_bytes(sel.cpu().numpy(), w.context_lens, bs, D))
+        if w.num_tokens and w.num_tokens == B:   # the Quest step as one call (decode append)
+            ta = time_alone(lambda: gp.quest_decode_append(
+                q, nk, nv, kc, vc, kmin, kmax, slots, bt, ctx, topk_blocks=K, max_context_len=mcl,
+                scale=scale, out=out_s, topk_out=sel, workspace=wq), flush, stream, steps)
+            res["quest_step_append_us"] = ta["us_mean"]
         res["quest_call_us"] = t["us_mean"]
         res["quest_bytes"] = int(qb)
         res["quest_gbps"] = round(qb / (t["us_mean"] * 1e-6) / 1e9, 1)
@@ -484,12 +489,16 @@ def main():
     # The dense step as one call: the write (with the metadata fold when the step
     # keeps Quest metadata) merged into the dense decode call, timed alone behind the
     # flush. Idempotent like the step's own write.
-    append_alone = None
+    append_alone = quest_append_alone = None
     if w.num_tokens and w.num_tokens == B:
         append_alone = time_alone(lambda: gp.paged_attention_decode_append(
             q, nk, nv, kc, vc, slots, bt, ctx, max_context_len=mcl, scale=scale,
             key_min=kmin if fused else None, key_max=kmax if fused else None, out=out_d,
             workspace=ws_d), flush, stream, args.steps)
+        if K:   # the Quest step as one call: the write folded into quest_decode
+            quest_append_alone = time_alone(lambda: gp.quest_decode_append(
+                q, nk, nv, kc, vc, kmin, kmax, slots, bt, ctx, topk_blocks=K, max_context_len=mcl,
+                scale=scale, out=out_s, topk_out=sel, workspace=ws_qd), flush, stream, args.steps)
 
     # FP8 (E4M3) KV cache on the same workload: the pool quantised once by the FP8
     # write (every slot), then its write and dense calls timed like the bf16 ones.
@@ -650,6 +659,7 @@ def main():
         "us_per_step_median": round(float(np.median(step_us)), 2),
         "dense_step_us": round(write_us + calls_out["paged_attention_decode"]["us_mean"], 2),
         "dense_step_one_call": append_alone,
+        "quest_step_one_call": quest_append_alone,
         "quest_step_us": round(quest_us, 2) if quest_us is not None else None,
         "quest_full_metadata_rebuild_us": round(t_full, 2) if t_full is not None else None,
         "graph_replay_us_per_step": round(graph_us, 2) if graph_us is not None else None,

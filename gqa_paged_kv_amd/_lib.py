@@ -48,6 +48,9 @@ SIGNATURES = {
     "gpkv_quest_decode": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int32, c_int32,
                                     c_int32, c_int32, c_int32, c_int64, c_int32, c_int32,
                                     c_int32, c_float, vp, c_size, vp]),
+    "gpkv_quest_decode_append": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           c_int32, c_int32, c_int32, c_int32, c_int32, c_int64,
+                                           c_int32, c_int32, c_int32, c_float, vp, c_size, vp]),
     "gpkv_reshape_and_cache_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, vp, c_int32, c_int32,
                                              c_int32, c_int32, c_int64, vp]),
     "gpkv_paged_attention_decode_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, c_int32,

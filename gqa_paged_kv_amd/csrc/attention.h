@@ -480,6 +480,34 @@ __device__ __forceinline__ bool append_token(const long long* slots, long long n
   const int c = clamp_ctx(ctx[b], max_ctx);
   return c >= 1 && s >= 0 && s < num_slots;
 }
+// Decode append: KV head g's part of sequence b's new token written into the cache at
+// slot s (0 <= s < NB * bs) and, when kmin is non-null, folded into its block's Quest
+// key min / max (row 0 of a block starts it afresh), as the write path does. The
+// calling threads split the D / 8 16-byte vectors of the row.
+template <int D>
+__device__ __forceinline__ void store_new_token(const unsigned short* knew,
+                                                const unsigned short* vnew, unsigned short* kc,
+                                                unsigned short* vc, unsigned short* kmin,
+                                                unsigned short* kmax, long long s, int bs, int Hkv,
+                                                int b, int g, int t, int nt) {
+  const long long blk = s / bs, off = s - blk * bs;
+  const size_t row = (size_t)Hkv * D;   // bf16 per cache row
+  for (int c = t; c < D / 8; c += nt) {
+    const size_t src = ((size_t)b * Hkv + g) * D + 8 * c;
+    const size_t dst = (size_t)s * row + (size_t)g * D + 8 * c;
+    const u32x4 k = *(const u32x4*)(knew + src);
+    *(u32x4*)(kc + dst) = k;
+    *(u32x4*)(vc + dst) = *(const u32x4*)(vnew + src);
+    if (kmin != nullptr) {
+      const size_t meta = (size_t)blk * row + (size_t)g * D + 8 * c;
+      u32x4 mn = k, mx = k;
+      if (off > 0) fold_min_max(k, *(const u32x4*)(kmin + meta), *(const u32x4*)(kmax + meta), mn, mx);
+      *(u32x4*)(kmin + meta) = mn;
+      *(u32x4*)(kmax + meta) = mx;
+    }
+  }
+}
+
 // Positions of sequence b the split phase reads: its clamped context, less the
 // appended token.
 __device__ __forceinline__ int split_ctx(const int* ctx, const long long* slots,

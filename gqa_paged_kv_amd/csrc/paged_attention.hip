@@ -434,29 +434,15 @@ __device__ __forceinline__ void append_unit(const CombineParams& p, int b, int g
   v = f32x4{bf16_lo(vv.x), bf16_hi(vv.x), bf16_lo(vv.y), bf16_hi(vv.y)};
 }
 
-// Decode append: KV head g's part of sequence b's new token written into the cache
-// at its slot (a slot outside the pool writes nothing, as reshape_and_cache), and
-// folded into its block's Quest key min / max (row 0 of a block starts it afresh).
+// Decode append: KV head g's part of sequence b's new token written into the cache at
+// its slot (a slot outside the pool writes nothing, as reshape_and_cache), with the
+// Quest fold when the metadata is given.
 template <int D>
 __device__ __forceinline__ void append_write(const CombineParams& p, int b, int g) {
   const long long s = p.slots[b];
   if (s < 0 || s >= p.num_slots) return;
-  const long long blk = s / p.bs, off = s - blk * p.bs;
-  const size_t row = (size_t)p.Hkv * D;   // bf16 per cache row
-  for (int c = threadIdx.x; c < D / 8; c += blockDim.x) {
-    const size_t src = ((size_t)b * p.Hkv + g) * D + 8 * c;
-    const size_t dst = (size_t)s * row + (size_t)g * D + 8 * c;
-    const u32x4 k = *(const u32x4*)(p.knew + src);
-    *(u32x4*)(p.kc + dst) = k;
-    *(u32x4*)(p.vc + dst) = *(const u32x4*)(p.vnew + src);
-    if (p.kmin != nullptr) {
-      const size_t meta = (size_t)blk * row + (size_t)g * D + 8 * c;
-      u32x4 mn = k, mx = k;
-      if (off > 0) fold_min_max(k, *(const u32x4*)(p.kmin + meta), *(const u32x4*)(p.kmax + meta), mn, mx);
-      *(u32x4*)(p.kmin + meta) = mn;
-      *(u32x4*)(p.kmax + meta) = mx;
-    }
-  }
+  store_new_token<D>(p.knew, p.vnew, p.kc, p.vc, p.kmin, p.kmax, s, p.bs, p.Hkv, b, g,
+                     threadIdx.x, blockDim.x);
 }
 
 

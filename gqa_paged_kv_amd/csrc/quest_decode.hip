@@ -28,6 +28,18 @@ struct QuestDecodeParams {
   AttnCommon c;
   float* out;                // [B, H_q, D] fp32
   int max_nb;                // table entries the dynamic LDS holds
+  // Decode append (slots non-null): the workgroup of (b, g) first writes KV head g's
+  // part of sequence b's new token into the cache and folds it into the block's key
+  // min / max, so that its scores and its attention see the written cache. Only
+  // that workgroup touches head g's part of the row and of the metadata.
+  const long long* slots;    // [B]
+  long long num_slots;       // NB * bs
+  const unsigned short* knew;   // [B, H_kv, D] bf16
+  const unsigned short* vnew;
+  unsigned short* kc_w;
+  unsigned short* vc_w;
+  unsigned short* kmin_w;
+  unsigned short* kmax_w;
 };
 
 template <int D>
@@ -59,7 +71,13 @@ __global__ __launch_bounds__(kFusedThreads) void quest_decode_fused_kernel(const
     s_pb[lb] = sp.bt[(size_t)b * sp.max_blocks + lb];
   const bool all = K >= nb;
   stage_query<D>(sp, b, g * G, G, s_q);
-  __syncthreads();
+  if (p.slots != nullptr) {
+    const long long s = p.slots[b];
+    if (s >= 0 && s < p.num_slots)
+      store_new_token<D>(p.knew, p.vnew, p.kc_w, p.vc_w, p.kmin_w, p.kmax_w, s, bs, sp.Hkv, b, g,
+                         tid, kFusedThreads);
+  }
+  __syncthreads();   // (the barrier also orders the new token's stores before every read)
   if (all) {
     for (int i = tid; i < K; i += kFusedThreads) {
       out_ids[i] = i < nb ? i : -1;
@@ -154,17 +172,23 @@ extern "C" size_t gpkv_quest_decode_workspace_bytes(int32_t batch, int32_t num_q
   return a > b ? a : b;
 }
 
-extern "C" int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* query,
-                                 const void* key_cache, const void* value_cache,
-                                 const void* key_min, const void* key_max,
-                                 const int32_t* block_tables, const int32_t* context_lens,
-                                 int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                 int32_t max_blocks_per_seq, int32_t max_context_len,
-                                 int32_t topk_blocks, float scale, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  clear_error();
-  const char* fn = "quest_decode";
+// Decode append inputs of gpkv_quest_decode_append.
+struct QuestAppend {
+  const void* key;
+  const void* value;
+  const int64_t* slots;
+};
+
+static int quest_decode_run(float* out, int32_t* topk_indices, const void* query,
+                            const void* key_cache, const void* value_cache, const void* key_min,
+                            const void* key_max, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, int32_t topk_blocks, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            const QuestAppend* app) {
+  const char* fn = app ? "quest_decode_append" : "quest_decode";
   int st = check_common(fn, batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                         max_blocks_per_seq, max_context_len);
   if (st) return st;
@@ -173,7 +197,7 @@ extern "C" int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* 
     return fail(GPKV_ERR_SHAPE, "%s: token span too large", fn);
   if (batch == 0) return GPKV_OK;
   if (!out || !topk_indices || !query || !key_cache || !value_cache || !key_min || !key_max ||
-      !block_tables || !context_lens)
+      !block_tables || !context_lens || (app && (!app->key || !app->value || !app->slots)))
     return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
   const size_t need = gpkv_quest_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
                                                         block_size, max_blocks_per_seq,
@@ -204,6 +228,12 @@ extern "C" int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* 
   if (forced && strcmp(forced, "fused") == 0) fused = fits;
   if (forced && strcmp(forced, "separate") == 0) fused = false;
   if (!fused) {
+    if (app) {   // the write (and metadata fold) first, then the two calls
+      st = gpkv_reshape_and_cache_quest(app->key, app->value, (void*)key_cache, (void*)value_cache,
+                                        (void*)key_min, (void*)key_max, app->slots, batch,
+                                        num_kv_heads, head_dim, block_size, num_blocks, stream);
+      if (st) return st;
+    }
     st = gpkv_quest_select_topk(topk_indices, query, key_min, key_max, block_tables,
                                 context_lens, batch, num_q_heads, num_kv_heads, head_dim,
                                 block_size, num_blocks, max_blocks_per_seq, max_context_len,
@@ -247,6 +277,14 @@ extern "C" int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* 
   c.qk_scale_log2 = scale * 1.4426950408889634f;
   qp.out = out;
   qp.max_nb = max_nb;
+  qp.slots = app ? (const long long*)app->slots : nullptr;
+  qp.num_slots = (long long)num_blocks * block_size;
+  qp.knew = app ? (const unsigned short*)app->key : nullptr;
+  qp.vnew = app ? (const unsigned short*)app->value : nullptr;
+  qp.kc_w = (unsigned short*)key_cache;   // written only by the append call
+  qp.vc_w = (unsigned short*)value_cache;
+  qp.kmin_w = (unsigned short*)key_min;
+  qp.kmax_w = (unsigned short*)key_max;
   const dim3 grid(num_kv_heads, batch), block(kFusedThreads);
   hipStream_t s = (hipStream_t)stream;
   if (head_dim == 128)
@@ -254,4 +292,38 @@ extern "C" int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* 
   else
     quest_decode_fused_kernel<64><<<grid, block, lds, s>>>(qp);
   return check_launch(fn);
+}
+
+extern "C" int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* query,
+                                 const void* key_cache, const void* value_cache,
+                                 const void* key_min, const void* key_max,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 int32_t topk_blocks, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  clear_error();
+  return quest_decode_run(out, topk_indices, query, key_cache, value_cache, key_min, key_max,
+                          block_tables, context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                          topk_blocks, scale, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int gpkv_quest_decode_append(float* out, int32_t* topk_indices, const void* query,
+                                        const void* key, const void* value, void* key_cache,
+                                        void* value_cache, void* key_min, void* key_max,
+                                        const int64_t* slot_mapping, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t batch,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                        int32_t max_blocks_per_seq, int32_t max_context_len,
+                                        int32_t topk_blocks, float scale, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  clear_error();
+  QuestAppend app{key, value, slot_mapping};
+  return quest_decode_run(out, topk_indices, query, key_cache, value_cache, key_min, key_max,
+                          block_tables, context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                          topk_blocks, scale, workspace, workspace_bytes, stream, &app);
 }

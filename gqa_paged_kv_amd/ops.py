@@ -13,7 +13,7 @@ from ._lib import lib
 
 __all__ = [
     "GpkvError", "reshape_and_cache", "reshape_and_cache_quest", "paged_attention_decode",
-    "paged_attention_decode_append", "quest_block_metadata",
+    "paged_attention_decode_append", "quest_decode_append", "quest_block_metadata",
     "quest_select_topk", "sparse_paged_attention_decode", "paged_attention_workspace_bytes",
     "quest_select_workspace_bytes", "sparse_attention_workspace_bytes", "split_tokens",
     "reshape_and_cache_fp8", "paged_attention_decode_fp8", "sparse_paged_attention_decode_fp8",
@@ -315,6 +315,44 @@ def quest_decode(query, key_cache, value_cache, key_min, key_max, block_tables, 
         _ptr(out), _ptr(topk_out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
         _ptr(key_min), _ptr(key_max), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs,
         NB, MB, int(max_context_len), K, float(scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, topk_out
+
+
+def quest_decode_append(query, key, value, key_cache, value_cache, key_min, key_max,
+                        slot_mapping, block_tables, context_lens, *, topk_blocks: int,
+                        max_context_len: int, scale: float, out=None, topk_out=None,
+                        workspace=None, stream=None):
+    """The Quest step with its cache write: reshape_and_cache_quest of token b of key /
+    value (sequence b's newest token) at slot_mapping[b], then quest_decode over the
+    written cache; returns (out, topk_indices) as quest_decode."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks(query, key_cache, value_cache, block_tables,
+                                             context_lens)
+    _dev("key", key, torch.bfloat16, 3)
+    _dev("value", value, torch.bfloat16, 3)
+    _dev("slot_mapping", slot_mapping, torch.int64, 1)
+    _dev("key_min", key_min, torch.bfloat16, 3)
+    _dev("key_max", key_max, torch.bfloat16, 3)
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape[0] != B:
+        raise ValueError("quest_decode_append: key / value / slot_mapping must hold one token "
+                         "per sequence")
+    if key_min.shape != key_max.shape or tuple(key_min.shape) != (NB, Hkv, D):
+        raise ValueError("quest_decode_append: key_min / key_max must be [num_blocks, H_kv, D]")
+    K = int(topk_blocks)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+    if topk_out is None:
+        topk_out = torch.empty((B, Hkv, K), dtype=torch.int32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    _dev("topk_out", topk_out, torch.int32, 3)
+    if tuple(topk_out.shape) != (B, Hkv, K):
+        raise ValueError("quest_decode_append: topk_out must be [B, H_kv, topk_blocks]")
+    need = quest_decode_workspace_bytes(B, Hq, Hkv, D, bs, MB, K)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_quest_decode_append(
+        _ptr(out), _ptr(topk_out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache),
+        _ptr(value_cache), _ptr(key_min), _ptr(key_max), _ptr(slot_mapping), _ptr(block_tables),
+        _ptr(context_lens), B, Hq, Hkv, D, bs, NB, MB, int(max_context_len), K, float(scale),
+        _ptr(ws), ws.numel(), _stream(stream)))
     return out, topk_out
 
 

@@ -13,6 +13,7 @@
  *   gpkv_quest_select_topk           Quest block scores + Top-K per KV head
  *   gpkv_sparse_paged_attention_decode  exact attention over the selected blocks
  *   gpkv_quest_decode                selection and sparse attention in one call
+ *   gpkv_quest_decode_append         ... with the step's cache write (decode append)
  *   ..._fp8 variants of the write and both attention calls over E4M3 caches
  *   gpkv_paged_attention_varlen      multi-token queries (causal, right-aligned)
  *
@@ -297,6 +298,30 @@ int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* query,
                       int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                       int32_t topk_blocks, float scale, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* The Quest step with its cache write in one call (the KV-cache update sharing the
+ * decode kernel's launch, [DSA] items 2-3): gpkv_reshape_and_cache_quest over the
+ * batch's new tokens, then gpkv_quest_decode, for the decode-append case of
+ * gpkv_paged_attention_decode_append (token b of key / value is sequence b's newest
+ * token, at position context_lens[b] - 1; an in-pool slot_mapping[b] is that
+ * position's slot; a slot outside the pool writes nothing). On the one-launch path
+ * the workgroup of each (sequence, KV head) pair writes its head's part of the row
+ * and folds it into the block's key min / max before it scores, selects and
+ * attends; on the other path the write kernel runs first. The caches and the
+ * metadata (modified in place at the written slots and their blocks) end bit for
+ * bit as after the two calls, and topk_indices / out are those of gpkv_quest_decode
+ * over them. The metadata must cover each sequence's earlier rows (the fold's
+ * decode-append contract). key, value: [batch, num_kv_heads, head_dim] bf16;
+ * slot_mapping: [batch] int64. Everything else as gpkv_quest_decode. */
+int gpkv_quest_decode_append(float* out, int32_t* topk_indices, const void* query,
+                             const void* key, const void* value, void* key_cache,
+                             void* value_cache, void* key_min, void* key_max,
+                             const int64_t* slot_mapping, const int32_t* block_tables,
+                             const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int64_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_context_len, int32_t topk_blocks, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * FP8 KV cache. The pages name KV quantisation as the lever for long-context

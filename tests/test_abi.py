@@ -29,7 +29,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(L):
     from gqa_paged_kv_amd._lib import SIGNATURES
     names = declared_symbols()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
     assert sorted(SIGNATURES) == names
@@ -148,6 +148,22 @@ def test_append_argument_checks(L):
     assert call(D=96) == -3
     assert call(ws=16) == -4
     assert call(B=0, key=None, slots=None) == 0   # an empty batch launches nothing
+
+
+def test_quest_append_argument_checks(L):
+    """The Quest step with its cache write: new rows and slots required, topk_blocks
+    and the workspace checked like quest_decode, all refused on the host."""
+    f = L.gpkv_quest_decode_append
+
+    def call(key=8, slots=8, K=3, ws=1 << 30, B=2):
+        return f(8, 8, 8, key, 8, 8, 8, 8, 8, slots, 8, 8, B, 4, 1, 64, 16, 16, 5, 80, K, 0.1, 8,
+                 ws, None)
+
+    assert call(key=None) == -1
+    assert call(slots=None) == -1
+    assert call(K=0) == -2
+    assert call(ws=16) == -4
+    assert call(B=0, key=None, slots=None) == 0
 
 
 def test_noalloc_argument_checks(L):

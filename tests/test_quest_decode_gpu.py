@@ -13,7 +13,8 @@ import torch
 import gqa_paged_kv_amd as gp
 import oracle
 import workloads
-from gpu_util import BF, Dev, max_abs, oracle_selection, sparse_ref, workload
+from gpu_util import (BF, Dev, before_write_lens, bits, max_abs, meta_equal, oracle_selection,
+                      sparse_ref, to_dev, workload)
 
 pytestmark = pytest.mark.gpu
 ATOL = 2e-3
@@ -132,3 +133,66 @@ def test_quest_decode_paths_agree_full_size(config, monkeypatch):
     out, sel = _decode(d, w, kmin, kmax, K)
     assert np.array_equal(sel, sel_s)
     assert max_abs(out, out_s) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# The Quest step with its cache write in one call (decode append)
+# ---------------------------------------------------------------------------
+
+def _append_case_check(w, K, path, monkeypatch):
+    """quest_decode_append against the oracle chain: write, metadata of the written
+    cache, Top-K, sparse attention. The GPU metadata starts as the prefill build over
+    the pre-write contexts, the decode-append starting point of the fold."""
+    if path != "auto":
+        monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", path)
+    assert w.num_tokens == w.batch, "decode append writes token b for sequence b"
+    bs = w.block_size
+    d = Dev(w)
+    kmin = torch.zeros((w.num_blocks, w.num_kv_heads, w.head_dim), dtype=BF, device="cuda")
+    kmax = torch.zeros_like(kmin)
+    gp.quest_block_metadata(d.kc, d.bt, to_dev(before_write_lens(w), torch.int32), kmin, kmax,
+                            max_context_len=w.max_context_len)
+    out, sel = gp.quest_decode_append(d.q, d.nk, d.nv, d.kc, d.vc, kmin, kmax, d.slots, d.bt,
+                                      d.ctx, topk_blocks=K, max_context_len=w.max_context_len,
+                                      scale=float(w.scale))
+    torch.cuda.synchronize()
+    ek, ev = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                      w.slot_mapping, bs)
+    assert np.array_equal(bits(d.kc), ek), "key cache differs from the oracle"
+    assert np.array_equal(bits(d.vc), ev), "value cache differs from the oracle"
+    omin, omax = oracle.quest_block_metadata(ek, w.block_tables, w.context_lens, bs)
+    referenced = np.unique(np.concatenate(
+        [w.block_tables[b, :-(-int(L) // bs)] for b, L in enumerate(w.context_lens) if L > 0]))
+    assert meta_equal(bits(kmin)[referenced], omin[referenced]), "key_min differs"
+    assert meta_equal(bits(kmax)[referenced], omax[referenced]), "key_max differs"
+    osel = oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens, bs, K)
+    assert np.array_equal(sel.cpu().numpy(), osel), "selection differs from the oracle"
+    ref = oracle.sparse_paged_attention_decode(w.query, ek, ev, w.block_tables, w.context_lens,
+                                               osel, w.scale)
+    err = max_abs(out.cpu().numpy(), ref)
+    print(f"{w.name} K={K} path={path}: max-abs {err:.3e} over all {w.batch} sequences")
+    assert err <= ATOL
+
+
+@pytest.mark.parametrize("config,K,path", [(1, 3, "auto"), (1, 5, "separate"), (3, 64, "auto"),
+                                           (3, 64, "separate"), (5, 32, "auto")])
+def test_quest_decode_append_config(config, K, path, monkeypatch):
+    _append_case_check(workload(config), K, path, monkeypatch)
+
+
+APPEND_CASES = [
+    # seed, Hq, Hkv, D, bs, ctx, K, slots set to -1 (new tokens at row 0, at the last row,
+    # and in between; contexts of 1; few pairs with long tables)
+    (821, 28, 4, 128, 16, [900, 33, 2500, 17, 1, 700], 12, 1),
+    (822, 16, 1, 128, 64, [129, 2048, 4097], 1, 0),
+    (823, 14, 2, 64, 128, [257, 1, 700, 3000], 5, 1),
+    (824, 8, 1, 64, 16, [40961, 16], 256, 0),
+]
+
+
+@pytest.mark.parametrize("path", ["fused", "separate"])
+@pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx,K,neg", APPEND_CASES)
+def test_quest_decode_append_random(seed, Hq, Hkv, D, bs, ctx, K, neg, path, monkeypatch):
+    w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                              block_size=bs, context_lens=ctx, num_tokens=len(ctx), neg_slots=neg)
+    _append_case_check(w, K, path, monkeypatch)
