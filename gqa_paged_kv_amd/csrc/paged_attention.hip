@@ -510,6 +510,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_heads_kernel(con
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int slot = tid / TPU, c4 = tid % TPU;
   const bool append = APPEND && append_token(p.slots, p.num_slots, b, p.ctx, p.max_ctx);
+  if (APPEND) append_write<D>(p, b, g);   // first, so that its loads overlap the merge's
   for (int hl = slot; hl < p.G; hl += SLOTS) {
     const UnitRange r = unit_range<D>(p, b, g, hl);
     const int u0 = r.u_begin;
@@ -526,7 +527,6 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_heads_kernel(con
     }
     *(f32x4*)(p.out + ((size_t)b * p.Hq + (size_t)g * p.G + hl) * D + 4 * c4) = merge_finish(st);
   }
-  if (APPEND) append_write<D>(p, b, g);
 }
 
 template <int D, bool APPEND>
