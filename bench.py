@@ -523,6 +523,12 @@ def main():
         fbytes = {"reshape_and_cache_fp8": R.write_bytes(w.slot_mapping, w.num_blocks, bs, Hkv, D)
                   * 3 // 4,
                   "paged_attention_decode_fp8": R.dense_attention_bytes_fp8(w.context_lens, Hkv, D)}
+        if w.num_tokens and w.num_tokens == B:   # the FP8 dense step as one call
+            fcalls["paged_attention_decode_fp8_append"] = lambda: gp.paged_attention_decode_fp8_append(
+                q, nk, nv, kc8, vc8, ks8, vs8, slots, bt, ctx, max_context_len=mcl, scale=scale,
+                out=out8, workspace=ws_d)
+            fbytes["paged_attention_decode_fp8_append"] = (fbytes["reshape_and_cache_fp8"]
+                                                           + fbytes["paged_attention_decode_fp8"])
         fp8 = {}
         for name, f in fcalls.items():
             for _ in range(3):

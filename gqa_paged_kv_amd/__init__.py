@@ -13,7 +13,7 @@ from .ops import (GpkvError, paged_attention_decode, paged_attention_workspace_b
                   paged_attention_varlen, paged_attention_varlen_workspace_bytes, quest_decode,
                   quest_decode_workspace_bytes, paged_attention_varlen_fp8,
                   paged_attention_decode_noalloc, paged_attention_decode_append,
-                  quest_decode_append)
+                  quest_decode_append, paged_attention_decode_fp8_append)
 
 __all__ = [
     "GpkvError", "reshape_and_cache", "reshape_and_cache_quest", "paged_attention_decode",
@@ -23,5 +23,5 @@ __all__ = [
     "reshape_and_cache_fp8", "paged_attention_decode_fp8", "sparse_paged_attention_decode_fp8",
     "paged_attention_varlen", "paged_attention_varlen_workspace_bytes", "quest_decode",
     "quest_decode_workspace_bytes", "paged_attention_varlen_fp8", "paged_attention_decode_noalloc",
-    "paged_attention_decode_append", "quest_decode_append",
+    "paged_attention_decode_append", "quest_decode_append", "paged_attention_decode_fp8_append",
 ]

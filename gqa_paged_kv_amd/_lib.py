@@ -56,6 +56,10 @@ SIGNATURES = {
     "gpkv_paged_attention_decode_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, c_int32,
                                                   c_int32, c_int32, c_int32, c_int32, c_int64,
                                                   c_int32, c_int32, c_float, vp, c_size, vp]),
+    "gpkv_paged_attention_decode_fp8_append": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                         vp, c_int32, c_int32, c_int32, c_int32,
+                                                         c_int32, c_int64, c_int32, c_int32,
+                                                         c_float, vp, c_size, vp]),
     "gpkv_sparse_paged_attention_decode_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                          c_int32, c_int32, c_int32, c_int32,
                                                          c_int32, c_int64, c_int32, c_int32,

@@ -128,6 +128,22 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(unsigned w) {
   return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
+// Sixteen bf16 values (a: the first eight, b: the next eight) as OCP E4M3 codes of
+// x * inv, one byte each in order (the FP8 write path's quantisation).
+__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv) {
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4& src = j < 2 ? a : b;
+    const unsigned w0 = src[(2 * j) & 3], w1 = src[(2 * j + 1) & 3];
+    const float y0 = bf16_lo(w0) * inv, y1 = bf16_hi(w0) * inv;
+    const float y2 = bf16_lo(w1) * inv, y3 = bf16_hi(w1) * inv;
+    out[j] = e4m3_from_f32(y0) | (e4m3_from_f32(y1) << 8) | (e4m3_from_f32(y2) << 16) |
+             (e4m3_from_f32(y3) << 24);
+  }
+  return out;
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -407,42 +407,80 @@ struct CombineParams {
   unsigned short* vc;
   unsigned short* kmin;        // [NB, H_kv, D] bf16, or null
   unsigned short* kmax;
+  const float* k_scale;        // E4M3 caches: [H_kv] (codes = e4m3(x / scale))
+  const float* v_scale;
   int bs;
   float qk_scale_log2;
 };
 
+// Four bf16 values (channels in order) as the E4M3 codes of x * inv, one byte each
+// (the FP8 write path's quantisation).
+__device__ __forceinline__ unsigned e4m3_codes4(uint2 x, float inv) {
+  return e4m3_from_f32(bf16_lo(x.x) * inv) | (e4m3_from_f32(bf16_hi(x.x) * inv) << 8) |
+         (e4m3_from_f32(bf16_lo(x.y) * inv) << 16) | (e4m3_from_f32(bf16_hi(x.y) * inv) << 24);
+}
+
+// Which new-token merge a combine instance does.
+enum AppendMode { kNoAppend = 0, kAppendBf16 = 1, kAppendFp8 = 2 };
+
 // Decode append: the new token's unit for query head g G + hl of sequence b, as
 // thread c4 of the D / 4 threads holding the row's float4 columns sees it: base-2
-// lse q . k_new * scale * log2(e) (the exact bf16 products summed in float32 over
-// those threads, consecutive lanes of one wave that all call this) and the token's
-// values.
-template <int D>
+// lse q . k_new * scale * log2(e) (the exact products summed in float32 over those
+// threads, consecutive lanes of one wave that all call this) and the token's values.
+// E4M3 caches: k_new and v_new are the values the cache will hold, code * scale of
+// the codes the write stores.
+template <int D, int MODE>
 __device__ __forceinline__ void append_unit(const CombineParams& p, int b, int g, int hl, int c4,
                                             float& lse, f32x4& v) {
   constexpr int TPU = D / 4;
   const uint2 qq = *(const uint2*)(p.q + ((size_t)b * p.Hq + (size_t)g * p.G + hl) * D + 4 * c4);
   const size_t row = ((size_t)b * p.Hkv + g) * D + 4 * c4;
-  const uint2 kk = *(const uint2*)(p.knew + row);
-  const uint2 vv = *(const uint2*)(p.vnew + row);
+  uint2 kk = *(const uint2*)(p.knew + row);
+  uint2 vv = *(const uint2*)(p.vnew + row);
+  float kf = 1.f, vf = 1.f;
+  if constexpr (MODE == kAppendFp8) {
+    const float ks = p.k_scale[g], vs = p.v_scale[g];
+    const float kinv = 1.0f / ks, vinv = 1.0f / vs;
+    const u32x2 kd = e4m3x4_to_bf16(e4m3_codes4(kk, kinv));
+    const u32x2 vd = e4m3x4_to_bf16(e4m3_codes4(vv, vinv));
+    kk = uint2{kd[0], kd[1]};
+    vv = uint2{vd[0], vd[1]};
+    kf = ks;
+    vf = vs;
+  }
   float dot = bf16_lo(qq.x) * bf16_lo(kk.x);
   dot = __builtin_fmaf(bf16_hi(qq.x), bf16_hi(kk.x), dot);
   dot = __builtin_fmaf(bf16_lo(qq.y), bf16_lo(kk.y), dot);
   dot = __builtin_fmaf(bf16_hi(qq.y), bf16_hi(kk.y), dot);
 #pragma unroll
   for (int o = TPU / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-  lse = dot * p.qk_scale_log2;
-  v = f32x4{bf16_lo(vv.x), bf16_hi(vv.x), bf16_lo(vv.y), bf16_hi(vv.y)};
+  lse = dot * (p.qk_scale_log2 * kf);   // the split kernels' scale for this KV head
+  v = f32x4{bf16_lo(vv.x), bf16_hi(vv.x), bf16_lo(vv.y), bf16_hi(vv.y)} * vf;
 }
 
 // Decode append: KV head g's part of sequence b's new token written into the cache at
-// its slot (a slot outside the pool writes nothing, as reshape_and_cache), with the
-// Quest fold when the metadata is given.
-template <int D>
+// its slot (a slot outside the pool writes nothing, as the write path), with the
+// Quest fold when the metadata is given; E4M3 caches take its codes.
+template <int D, int MODE>
 __device__ __forceinline__ void append_write(const CombineParams& p, int b, int g) {
   const long long s = p.slots[b];
   if (s < 0 || s >= p.num_slots) return;
-  store_new_token<D>(p.knew, p.vnew, p.kc, p.vc, p.kmin, p.kmax, s, p.bs, p.Hkv, b, g,
-                     threadIdx.x, blockDim.x);
+  if constexpr (MODE == kAppendFp8) {
+    // four channels per thread (D / 4 threads), so that the integer-arithmetic
+    // encoding of the row's codes is spread wide
+    const float kinv = 1.0f / p.k_scale[g], vinv = 1.0f / p.v_scale[g];
+    const size_t src = ((size_t)b * p.Hkv + g) * D;
+    const size_t dst = ((size_t)s * p.Hkv + g) * D;   // bytes
+    for (int c = threadIdx.x; c < D / 4; c += blockDim.x) {
+      const uint2 kk = *(const uint2*)(p.knew + src + 4 * c);
+      const uint2 vv = *(const uint2*)(p.vnew + src + 4 * c);
+      *(unsigned*)((unsigned char*)p.kc + dst + 4 * c) = e4m3_codes4(kk, kinv);
+      *(unsigned*)((unsigned char*)p.vc + dst + 4 * c) = e4m3_codes4(vv, vinv);
+    }
+  } else {
+    store_new_token<D>(p.knew, p.vnew, p.kc, p.vc, p.kmin, p.kmax, s, p.bs, p.Hkv, b, g,
+                       threadIdx.x, blockDim.x);
+  }
 }
 
 
@@ -503,14 +541,15 @@ __device__ __forceinline__ UnitRange unit_range(const CombineParams& p, int b, i
 // rows in one round of loads after the prefix.
 constexpr int kHeadUnits = 12;
 
-template <int D, bool APPEND>
+template <int D, int MODE>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_heads_kernel(const CombineParams p) {
   constexpr int TPU = D / 4;
   constexpr int SLOTS = kCombineThreads / TPU;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int slot = tid / TPU, c4 = tid % TPU;
+  constexpr bool APPEND = MODE != kNoAppend;
   const bool append = APPEND && append_token(p.slots, p.num_slots, b, p.ctx, p.max_ctx);
-  if (APPEND) append_write<D>(p, b, g);   // first, so that its loads overlap the merge's
+  if (APPEND) append_write<D, MODE>(p, b, g);   // first, so that its loads overlap the merge's
   for (int hl = slot; hl < p.G; hl += SLOTS) {
     const UnitRange r = unit_range<D>(p, b, g, hl);
     const int u0 = r.u_begin;
@@ -522,14 +561,14 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_heads_kernel(con
     if (append) {
       float l;
       f32x4 v;
-      append_unit<D>(p, b, g, hl, c4, l, v);
+      append_unit<D, MODE>(p, b, g, hl, c4, l, v);
       merge_one(st, l, v);
     }
     *(f32x4*)(p.out + ((size_t)b * p.Hq + (size_t)g * p.G + hl) * D + 4 * c4) = merge_finish(st);
   }
 }
 
-template <int D, bool APPEND>
+template <int D, int MODE>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const CombineParams p) {
   constexpr int TPU = D / 4;                       // threads per unit row
   constexpr int UPP = kCombineThreads / TPU;       // units per pass
@@ -540,8 +579,9 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
   const int g = h / G, hl = h - g * G;
   float* out = p.out + ((size_t)b * p.Hq + h) * D;
 
+  constexpr bool APPEND = MODE != kNoAppend;
   const bool append = APPEND && append_token(p.slots, p.num_slots, b, p.ctx, p.max_ctx);
-  if (APPEND && hl == 0) append_write<D>(p, b, g);
+  if (APPEND && hl == 0) append_write<D, MODE>(p, b, g);
   const UnitRange r = unit_range<D>(p, b, g, hl);
   if (r.u_end <= r.u_begin) {   // no unit: the appended token alone, or nothing
     if (tid < TPU) {
@@ -549,7 +589,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
       if (append) {
         float l;
         f32x4 v;
-        append_unit<D>(p, b, g, hl, tid, l, v);
+        append_unit<D, MODE>(p, b, g, hl, tid, l, v);
         merge_one(st, l, v);
       }
       *(f32x4*)(out + 4 * tid) = merge_finish(st);
@@ -620,7 +660,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
     if (append) {
       float l;
       f32x4 v;
-      append_unit<D>(p, b, g, hl, tid, l, v);
+      append_unit<D, MODE>(p, b, g, hl, tid, l, v);
       merge_one(st, l, v);
     }
     *(f32x4*)(out + 4 * tid) = merge_finish(st);
@@ -742,6 +782,29 @@ int check_common(const char* fn, int B, int Hq, int Hkv, int D, int bs, long lon
   return GPKV_OK;
 }
 
+// Many units per sequence (per_head): one workgroup per query head, its threads spread
+// over the units. Few units: one workgroup per KV head, a slot of threads per query head.
+template <int D, int MODE>
+static void launch_combine_mode(bool per_head, int B, int Hq, int Hkv, hipStream_t stream,
+                                const CombineParams& cp) {
+  const dim3 cblock(kCombineThreads);
+  if (per_head)
+    attn_combine_kernel<D, MODE><<<dim3(Hq, B), cblock, 0, stream>>>(cp);
+  else
+    attn_combine_heads_kernel<D, MODE><<<dim3(Hkv, B), cblock, 0, stream>>>(cp);
+}
+
+template <int D>
+static void launch_combine(bool per_head, int mode, int B, int Hq, int Hkv, hipStream_t stream,
+                           const CombineParams& cp) {
+  if (mode == kAppendFp8)
+    launch_combine_mode<D, kAppendFp8>(per_head, B, Hq, Hkv, stream, cp);
+  else if (mode == kAppendBf16)
+    launch_combine_mode<D, kAppendBf16>(per_head, B, Hq, Hkv, stream, cp);
+  else
+    launch_combine_mode<D, kNoAppend>(per_head, B, Hq, Hkv, stream, cp);
+}
+
 template <int D, bool SPARSE, bool FP8>
 static void launch_attention(bool balanced, const BalParams& bp, const SplitParams& sp, int nwg,
                              int num_splits, int B, hipStream_t stream) {
@@ -767,7 +830,7 @@ static int attn_run(bool sparse, bool fp8, float* out, const void* query, const 
                     const int* ctx, const int* topk, int B, int Hq, int Hkv, int D, int bs,
                     long long NB, int max_blocks, int max_ctx, int K, float scale, void* ws,
                     size_t ws_bytes, hipStream_t stream, const AppendArgs* app = nullptr) {
-  const char* fn = app ? "paged_attention_decode_append"
+  const char* fn = app ? (fp8 ? "paged_attention_decode_fp8_append" : "paged_attention_decode_append")
                 : sparse ? (fp8 ? "sparse_paged_attention_decode_fp8" : "sparse_paged_attention_decode")
                          : (fp8 ? "paged_attention_decode_fp8" : "paged_attention_decode");
   int st = check_common(fn, B, Hq, Hkv, D, bs, NB, max_blocks, max_ctx);
@@ -902,43 +965,21 @@ static int attn_run(bool sparse, bool fp8, float* out, const void* query, const 
   cp.vc = (unsigned short*)vc;
   cp.kmin = app ? (unsigned short*)app->key_min : nullptr;
   cp.kmax = app ? (unsigned short*)app->key_max : nullptr;
+  cp.k_scale = k_scale;
+  cp.v_scale = v_scale;
   cp.bs = bs;
   cp.qk_scale_log2 = c.qk_scale_log2;
   // Many units per sequence (long sequences over many workgroups or splits): one
   // workgroup per query head, its threads spread over the units. Few units: one
   // workgroup per KV head, a slot of threads per query head.
   const long long units_per_seq = pl.balanced ? (long long)pl.nwg / B + 1 : pl.num_splits;
-  const dim3 cblock(kCombineThreads);
-  // The append call's combine is its own instance: its extra registers (the new
+  // The append calls' combine is its own instance: its extra registers (the new
   // token's unit) stay out of the plain combine.
-  const bool app_on = cp.slots != nullptr;
-  if (units_per_seq >= 6) {
-    const dim3 cgrid(Hq, B);
-    if (D == 128) {
-      if (app_on)
-        attn_combine_kernel<128, true><<<cgrid, cblock, 0, stream>>>(cp);
-      else
-        attn_combine_kernel<128, false><<<cgrid, cblock, 0, stream>>>(cp);
-    } else {
-      if (app_on)
-        attn_combine_kernel<64, true><<<cgrid, cblock, 0, stream>>>(cp);
-      else
-        attn_combine_kernel<64, false><<<cgrid, cblock, 0, stream>>>(cp);
-    }
-  } else {
-    const dim3 cgrid(Hkv, B);
-    if (D == 128) {
-      if (app_on)
-        attn_combine_heads_kernel<128, true><<<cgrid, cblock, 0, stream>>>(cp);
-      else
-        attn_combine_heads_kernel<128, false><<<cgrid, cblock, 0, stream>>>(cp);
-    } else {
-      if (app_on)
-        attn_combine_heads_kernel<64, true><<<cgrid, cblock, 0, stream>>>(cp);
-      else
-        attn_combine_heads_kernel<64, false><<<cgrid, cblock, 0, stream>>>(cp);
-    }
-  }
+  const int mode = cp.slots == nullptr ? kNoAppend : (fp8 ? kAppendFp8 : kAppendBf16);
+  if (D == 128)
+    launch_combine<128>(units_per_seq >= 6, mode, B, Hq, Hkv, stream, cp);
+  else
+    launch_combine<64>(units_per_seq >= 6, mode, B, Hq, Hkv, stream, cp);
   return check_launch(fn);
 }
 
@@ -995,6 +1036,21 @@ extern "C" int gpkv_paged_attention_decode_append(
   clear_error();
   AppendArgs app{key, value, key_min, key_max, slot_mapping};
   return attn_run(false, false, out, query, key_cache, value_cache, nullptr, nullptr,
+                  block_tables, context_lens, nullptr, batch, num_q_heads, num_kv_heads, head_dim,
+                  block_size, num_blocks, max_blocks_per_seq, max_context_len, 0, scale,
+                  workspace, workspace_bytes, (hipStream_t)stream, &app);
+}
+
+extern "C" int gpkv_paged_attention_decode_fp8_append(
+    float* out, const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, const float* k_scale, const float* v_scale, const int64_t* slot_mapping,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  clear_error();
+  AppendArgs app{key, value, nullptr, nullptr, slot_mapping};
+  return attn_run(false, true, out, query, key_cache, value_cache, k_scale, v_scale,
                   block_tables, context_lens, nullptr, batch, num_q_heads, num_kv_heads, head_dim,
                   block_size, num_blocks, max_blocks_per_seq, max_context_len, 0, scale,
                   workspace, workspace_bytes, (hipStream_t)stream, &app);

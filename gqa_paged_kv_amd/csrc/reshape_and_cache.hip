@@ -61,22 +61,8 @@ __global__ __launch_bounds__(64) void reshape_and_cache_quest_kernel(
 
 
 // FP8 write path: the same slot rule; each row is quantised to OCP E4M3 with its
-// KV head's scale: code = e4m3(x * (1 / scale)), both float32 operations (the
-// reciprocal is a correctly rounded division). 16 bf16 in, 16 bytes out per lane.
-__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv) {
-  u32x4 out;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u32x4& src = j < 2 ? a : b;
-    const unsigned w0 = src[(2 * j) & 3], w1 = src[(2 * j + 1) & 3];
-    const float y0 = bf16_lo(w0) * inv, y1 = bf16_hi(w0) * inv;
-    const float y2 = bf16_lo(w1) * inv, y3 = bf16_hi(w1) * inv;
-    out[j] = e4m3_from_f32(y0) | (e4m3_from_f32(y1) << 8) | (e4m3_from_f32(y2) << 16) |
-             (e4m3_from_f32(y3) << 24);
-  }
-  return out;
-}
-
+// KV head's scale (quantize16: code = e4m3(x * (1 / scale)), both float32 operations,
+// the reciprocal a correctly rounded division). 16 bf16 in, 16 bytes out per lane.
 __global__ __launch_bounds__(64) void reshape_and_cache_fp8_kernel(
     const u32x4* __restrict__ key, const u32x4* __restrict__ value, u32x4* __restrict__ key_cache,
     u32x4* __restrict__ value_cache, const float* __restrict__ k_scale,

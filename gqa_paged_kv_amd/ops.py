@@ -17,7 +17,8 @@ __all__ = [
     "quest_select_topk", "sparse_paged_attention_decode", "paged_attention_workspace_bytes",
     "quest_select_workspace_bytes", "sparse_attention_workspace_bytes", "split_tokens",
     "reshape_and_cache_fp8", "paged_attention_decode_fp8", "sparse_paged_attention_decode_fp8",
-    "paged_attention_varlen", "paged_attention_varlen_workspace_bytes",
+    "paged_attention_decode_fp8_append", "paged_attention_varlen",
+    "paged_attention_varlen_workspace_bytes",
 ]
 
 
@@ -416,6 +417,34 @@ def paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_scale, 
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs, NB, MB, int(max_context_len),
         float(scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def paged_attention_decode_fp8_append(query, key, value, key_cache, value_cache, k_scale,
+                                      v_scale, slot_mapping, block_tables, context_lens, *,
+                                      max_context_len: int, scale: float, out=None,
+                                      workspace=None, stream=None) -> torch.Tensor:
+    """The FP8 dense step in one call: token b of key / value (bf16, sequence b's newest
+    token) quantised into the E4M3 caches at slot_mapping[b], and the dense attention
+    over the written caches; returns [B, H_q, D] float32."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks_fp8(query, key_cache, value_cache, k_scale, v_scale,
+                                                 block_tables, context_lens)
+    _dev("key", key, torch.bfloat16, 3)
+    _dev("value", value, torch.bfloat16, 3)
+    _dev("slot_mapping", slot_mapping, torch.int64, 1)
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape[0] != B:
+        raise ValueError("paged_attention_decode_fp8_append: key / value / slot_mapping must hold "
+                         "one token per sequence")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    need = paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len)
+    ws = _workspace(need, query.device, workspace)
+    _check(lib().gpkv_paged_attention_decode_fp8_append(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens),
+        B, Hq, Hkv, D, bs, NB, MB, int(max_context_len), float(scale), _ptr(ws), ws.numel(),
+        _stream(stream)))
     return out
 
 

@@ -14,7 +14,8 @@
  *   gpkv_sparse_paged_attention_decode  exact attention over the selected blocks
  *   gpkv_quest_decode                selection and sparse attention in one call
  *   gpkv_quest_decode_append         ... with the step's cache write (decode append)
- *   ..._fp8 variants of the write and both attention calls over E4M3 caches
+ *   ..._fp8 variants of the write and both attention calls over E4M3 caches,
+ *   and gpkv_paged_attention_decode_fp8_append (the FP8 dense step in one call)
  *   gpkv_paged_attention_varlen      multi-token queries (causal, right-aligned)
  *
  * Sources, by page title and section:
@@ -359,6 +360,27 @@ int gpkv_paged_attention_decode_fp8(float* out, const void* query, const void* k
                                     int32_t max_blocks_per_seq, int32_t max_context_len,
                                     float scale, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/* The FP8 dense step in one call: gpkv_reshape_and_cache_fp8 over the batch's new
+ * tokens followed by gpkv_paged_attention_decode_fp8, for the decode-append case of
+ * gpkv_paged_attention_decode_append (token b of key / value is sequence b's newest
+ * token, at position context_lens[b] - 1, and an in-pool slot_mapping[b] is that
+ * position's slot). The combine kernel writes the token's codes (the FP8 write's
+ * quantisation) and merges the token as one more unit with the values the cache then
+ * holds, code * scale; the caches end bit for bit as after the two calls, attention
+ * within the same tolerance. key, value: [batch, num_kv_heads, head_dim] bf16;
+ * slot_mapping: [batch] int64; everything else as gpkv_paged_attention_decode_fp8. */
+int gpkv_paged_attention_decode_fp8_append(float* out, const void* query, const void* key,
+                                           const void* value, void* key_cache, void* value_cache,
+                                           const float* k_scale, const float* v_scale,
+                                           const int64_t* slot_mapping,
+                                           const int32_t* block_tables,
+                                           const int32_t* context_lens, int32_t batch,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int64_t num_blocks, int32_t max_blocks_per_seq,
+                                           int32_t max_context_len, float scale, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /* gpkv_sparse_paged_attention_decode over E4M3 caches (values as above). */
 int gpkv_sparse_paged_attention_decode_fp8(float* out, const void* query, const void* key_cache,

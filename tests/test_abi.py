@@ -29,7 +29,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(L):
     from gqa_paged_kv_amd._lib import SIGNATURES
     names = declared_symbols()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
     assert sorted(SIGNATURES) == names
@@ -148,6 +148,17 @@ def test_append_argument_checks(L):
     assert call(D=96) == -3
     assert call(ws=16) == -4
     assert call(B=0, key=None, slots=None) == 0   # an empty batch launches nothing
+    # the FP8 form: scales required as for the FP8 dense call
+    g = L.gpkv_paged_attention_decode_fp8_append
+    base = [8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"],
+            a["MB"], a["mcl"], 0.125, 8, 1 << 40, None]
+    for i in (2, 3, 6, 7, 8):   # key, value, k_scale, v_scale, slot_mapping
+        args = list(base)
+        args[i] = None
+        assert g(*args) == -1, i
+    args = list(base)
+    args[21] = 16
+    assert g(*args) == -4
 
 
 def test_quest_append_argument_checks(L):

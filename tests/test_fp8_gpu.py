@@ -225,3 +225,55 @@ def test_fp8_sparse_config(config, K, schedule, monkeypatch):
     err = max_abs(out, _sparse_ref(config, K))
     print(f"config {config} K={K}: FP8 sparse max-abs {err:.3e} over all {w.batch} sequences")
     assert err <= ATOL
+
+
+# ---------------------------------------------------------------------------
+# The FP8 dense step in one call (decode append)
+# ---------------------------------------------------------------------------
+
+def _fp8_append_check(w, c):
+    """paged_attention_decode_fp8_append on copies of the case's E4M3 caches against
+    the oracle chain: the FP8 write of the new tokens, then FP8 dense attention."""
+    assert w.num_tokens == w.batch, "decode append writes token b for sequence b"
+    d = c.d
+    kc, vc = c.kc.clone(), c.vc.clone()
+    out = gp.paged_attention_decode_fp8_append(d.q, d.nk, d.nv, kc, vc, c.d_ks, c.d_vs, d.slots,
+                                               d.bt, d.ctx, max_context_len=w.max_context_len,
+                                               scale=float(w.scale))
+    torch.cuda.synchronize()
+    ek, ev = oracle.reshape_and_cache_fp8(c.okc, c.ovc, w.new_key, w.new_value, w.slot_mapping,
+                                          w.block_size, c.ks, c.vs)
+    seqs = c.seqs
+    if seqs is None:
+        assert np.array_equal(kc.cpu().numpy(), ek), "key codes differ from the oracle"
+        assert np.array_equal(vc.cpu().numpy(), ev), "value codes differ from the oracle"
+    else:   # the oracle holds codes for the blocks the sequences read
+        blocks = sorted({int(x) for b in seqs
+                         for x in w.block_tables[b, :-(-int(w.context_lens[b]) // w.block_size)]})
+        assert np.array_equal(kc.cpu().numpy()[blocks], ek[blocks]), "key codes differ"
+        assert np.array_equal(vc.cpu().numpy()[blocks], ev[blocks]), "value codes differ"
+    ref = oracle.paged_attention_decode_fp8(w.query, ek, ev, c.ks, c.vs, w.block_tables,
+                                            w.context_lens, w.scale, seqs=seqs)
+    err = max_abs(out.cpu().numpy(), ref)
+    print(f"{w.name}: FP8 append max-abs vs oracle {err:.3e}")
+    assert err <= ATOL
+
+
+@pytest.mark.parametrize("schedule", ["balanced", "split"])
+@pytest.mark.parametrize("config", [1, 2, 5])
+def test_fp8_append_config(config, schedule, monkeypatch):
+    monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
+    _fp8_append_check(workload(config), _full_case(config))
+
+
+@pytest.mark.parametrize("schedule", ["balanced", "split"])
+@pytest.mark.parametrize("seed,Hq,Hkv,D,bs,ctx", [
+    (631, 4, 1, 64, 16, [1, 2, 16, 17, 33]),
+    (632, 28, 4, 128, 16, [31, 32, 5000, 1025]),
+    (633, 64, 8, 128, 128, [1, 128, 129, 3000]),
+])
+def test_fp8_append_random(seed, Hq, Hkv, D, bs, ctx, schedule, monkeypatch):
+    monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
+    w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                              block_size=bs, context_lens=ctx, num_tokens=len(ctx), neg_slots=1)
+    _fp8_append_check(w, Fp8Case(w, list(range(w.batch))))
