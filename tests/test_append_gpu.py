@@ -159,3 +159,31 @@ def test_append_equals_write_then_decode_on_the_gpu(monkeypatch):
     torch.cuda.synchronize()
     assert torch.equal(a.kc, b.kc) and torch.equal(a.vc, b.vc)
     assert float((out_a - out_b).abs().max()) <= 1e-4
+
+
+def _spiked(seed, ctx, D=128, H=4, bs=16):
+    """One query head per KV head and each new key along its head's query, sized so that
+    the new token's score is the log of the other tokens' summed weight: it carries
+    about half of its sequence's softmax, so a slip in its unit (left out, its scale,
+    its lse, its values) moves the output by O(0.1)."""
+    w = workloads.random_case(seed, batch=len(ctx), num_q_heads=H, num_kv_heads=H, head_dim=D,
+                              block_size=bs, context_lens=ctx, num_tokens=len(ctx))
+    w.new_key[...] = spike_keys(w)
+    return w
+
+
+def spike_keys(w):
+    """k_new[b, h] = a q[b, h] with a chosen so that scale * q . k_new equals
+    ln(sum over the other tokens of exp(score)), about ln(ctx - 1) + 1/2 for random
+    keys (their scores are close to standard normal)."""
+    q = oracle.bf16_to_f64(w.query)                       # [B, H, D]
+    s = float(w.scale)
+    target = np.log(np.maximum(w.context_lens.astype(np.float64) - 1, 1)) + 0.5
+    a = target[:, None] / (s * (q * q).sum(axis=-1))      # [B, H]
+    return workloads.bf16_bits((a[..., None] * q).astype(np.float32))
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_append_spiked_new_token(schedule, monkeypatch):
+    w = _spiked(611, [9000, 3000, 2])
+    _check_random(w, schedule, monkeypatch, with_meta=True)

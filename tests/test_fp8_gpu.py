@@ -277,3 +277,16 @@ def test_fp8_append_random(seed, Hq, Hkv, D, bs, ctx, schedule, monkeypatch):
     w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                               block_size=bs, context_lens=ctx, num_tokens=len(ctx), neg_slots=1)
     _fp8_append_check(w, Fp8Case(w, list(range(w.batch))))
+
+
+@pytest.mark.parametrize("schedule", ["balanced", "split"])
+def test_fp8_append_spiked_new_token(schedule, monkeypatch):
+    """The new key along each head's query (one query head per KV head), sized to carry
+    about half of its sequence's softmax: its codes' scale and its unit's lse are
+    checked at O(0.1) sensitivity."""
+    from test_append_gpu import spike_keys
+    monkeypatch.setenv("GPKV_ATTN_SCHEDULE", schedule)
+    w = workloads.random_case(641, batch=3, num_q_heads=4, num_kv_heads=4, head_dim=128,
+                              block_size=16, context_lens=[9000, 3000, 2], num_tokens=3)
+    w.new_key[...] = spike_keys(w)
+    _fp8_append_check(w, Fp8Case(w, list(range(w.batch))))

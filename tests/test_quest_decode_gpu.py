@@ -196,3 +196,15 @@ def test_quest_decode_append_random(seed, Hq, Hkv, D, bs, ctx, K, neg, path, mon
     w = workloads.random_case(seed, batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                               block_size=bs, context_lens=ctx, num_tokens=len(ctx), neg_slots=neg)
     _append_case_check(w, K, path, monkeypatch)
+
+
+@pytest.mark.parametrize("path", ["fused", "separate"])
+def test_quest_decode_append_spiked_new_token(path, monkeypatch):
+    """New keys along their heads' queries: the fold moves each last block's bound far
+    up (a missing or stale fold changes the selection) and the new token carries about
+    half of its sequence's softmax over the selected blocks."""
+    from test_append_gpu import spike_keys
+    w = workloads.random_case(825, batch=3, num_q_heads=4, num_kv_heads=4, head_dim=128,
+                              block_size=16, context_lens=[9000, 3001, 17], num_tokens=3)
+    w.new_key[...] = spike_keys(w)
+    _append_case_check(w, 24, path, monkeypatch)
