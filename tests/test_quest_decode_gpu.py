@@ -200,11 +200,19 @@ def test_quest_decode_append_random(seed, Hq, Hkv, D, bs, ctx, K, neg, path, mon
 
 @pytest.mark.parametrize("path", ["fused", "separate"])
 def test_quest_decode_append_spiked_new_token(path, monkeypatch):
-    """New keys along their heads' queries: the fold moves each last block's bound far
-    up (a missing or stale fold changes the selection) and the new token carries about
-    half of its sequence's softmax over the selected blocks."""
-    from test_append_gpu import spike_keys
+    """New keys three times their heads' queries: the fold lifts each last block's bound
+    into the Top-K (on the two long sequences, selecting from metadata without the
+    fold gives other ids: checked below on the oracle), and the new token dominates
+    its softmax over the selected blocks."""
     w = workloads.random_case(825, batch=3, num_q_heads=4, num_kv_heads=4, head_dim=128,
                               block_size=16, context_lens=[9000, 3001, 17], num_tokens=3)
-    w.new_key[...] = spike_keys(w)
+    q = oracle.bf16_to_f64(w.query)
+    w.new_key[...] = workloads.bf16_bits((3.0 * q).astype(np.float32))
+    ek, _ = oracle.reshape_and_cache(w.key_cache, w.value_cache, w.new_key, w.new_value,
+                                     w.slot_mapping, 16)
+    good = oracle.quest_select_topk(w.query, *oracle.quest_block_metadata(
+        ek, w.block_tables, w.context_lens, 16), w.block_tables, w.context_lens, 16, 24)
+    stale = oracle.quest_select_topk(w.query, *oracle.quest_block_metadata(
+        w.key_cache, w.block_tables, w.context_lens, 16), w.block_tables, w.context_lens, 16, 24)
+    assert (good[:2] != stale[:2]).any(axis=-1).all(), "the case must depend on the fold"
     _append_case_check(w, 24, path, monkeypatch)
