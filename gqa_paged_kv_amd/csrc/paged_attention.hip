@@ -24,6 +24,10 @@
 //  - Sparse, and dense batches too large for the balanced table: a workgroup per
 //    (sequence, split of `split_tokens` virtual tokens), the split's block-table
 //    entries (per KV head when sparse) staged in LDS.
+//  - Decode append (the step's cache write in the same call, dense only): the split
+//    phase stops one position short of each appending sequence's context, and the
+//    combine merges that token from the call's inputs as one more unit and writes
+//    it into the cache (after every read of the cache in the call).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdlib.h>
