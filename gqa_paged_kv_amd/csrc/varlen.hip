@@ -558,7 +558,7 @@ __device__ __forceinline__ void attn_varlen_balanced(const VarlenParams& p, int*
   }
 }
 
-template <int D, int RT, bool FP8>
+template <int D, int RT, bool FP8, bool BAL>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_varlen_kernel(const VarlenParams p) {
   constexpr bool kShared = RT > 1 && !FP8;   // E4M3 caches: per-head units only
   __shared__ int s_pb[kMaxTable];
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   auto n_tiles_of = [&](int qn) { return (qn * G + 15) / 16; };
   auto n_groups = [&](int qn) { return (n_tiles_of(qn) + RT - 1) / RT; };
   auto shared_seq = [&](int qn) { return kShared && n_tiles_of(qn) >= kShareMinTiles; };
-  if (p.balanced) {
+  if constexpr (BAL) {
     attn_varlen_balanced<D, RT, FP8>(p, s_pb, s_pref, s_upref, s_wave, s_kv);
     return;
   }
@@ -890,20 +890,32 @@ extern "C" size_t gpkv_paged_attention_varlen_workspace_bytes(int32_t batch, int
   return split > bal ? split : bal;
 }
 
+template <bool FP8, bool BAL>
+static void launch_varlen_sched(bool multi, int head_dim, dim3 grid, dim3 block, hipStream_t s,
+                                const VarlenParams& vp) {
+  if (!multi) {
+    if (head_dim == 128)
+      attn_varlen_kernel<128, 1, FP8, BAL><<<grid, block, 0, s>>>(vp);
+    else
+      attn_varlen_kernel<64, 1, FP8, BAL><<<grid, block, 0, s>>>(vp);
+  } else {
+    if (head_dim == 128)
+      attn_varlen_kernel<128, kVarlenRT, FP8, BAL><<<grid, block, 0, s>>>(vp);
+    else
+      attn_varlen_kernel<64, kVarlenRT, FP8, BAL><<<grid, block, 0, s>>>(vp);
+  }
+}
+
+// One kernel instance per schedule: the schedule's outer loop is all that surrounds
+// the tile loop in each (the tile loop runs at the register limit, so the outer
+// code's live state shapes its code).
 template <bool FP8>
 static void launch_varlen(bool multi, int head_dim, dim3 grid, dim3 block, hipStream_t s,
                           const VarlenParams& vp) {
-  if (!multi) {
-    if (head_dim == 128)
-      attn_varlen_kernel<128, 1, FP8><<<grid, block, 0, s>>>(vp);
-    else
-      attn_varlen_kernel<64, 1, FP8><<<grid, block, 0, s>>>(vp);
-  } else {
-    if (head_dim == 128)
-      attn_varlen_kernel<128, kVarlenRT, FP8><<<grid, block, 0, s>>>(vp);
-    else
-      attn_varlen_kernel<64, kVarlenRT, FP8><<<grid, block, 0, s>>>(vp);
-  }
+  if (vp.balanced)
+    launch_varlen_sched<FP8, true>(multi, head_dim, grid, block, s, vp);
+  else
+    launch_varlen_sched<FP8, false>(multi, head_dim, grid, block, s, vp);
 }
 
 static int varlen_run(bool fp8, float* out, const void* query, const void* key_cache,
