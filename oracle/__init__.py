@@ -36,6 +36,12 @@ Readings where the pages are silent:
      sequence b are its newest q_len_b positions, already in the cache; row j
      (0-based) sees positions t <= ctx_b - q_len_b + j (a causal mask aligned to
      the right); a row that sees no position gets a zero output.
+  R9 Quest over E4M3 caches: the metadata holds the codes of each channel's
+     smallest and largest key code value over a block's valid rows (one byte per
+     channel; the keys are code * k_scale[g] with a positive per-head scale, so
+     their extremes are the scale times these); the block score is the R5 bound
+     on the code values, the scale left out: it multiplies every score of a KV
+     head by the same positive factor, and only the order within a head is used.
   R7 FP8 KV cache (the KV-quantisation lever of [TL18] 2.5 and 3.1): codes are
      OCP FP8 E4M3 (bias 7, no infinities, largest finite 448); K and V each carry
      one float32 scale per KV head. Stored code = the E4M3 value nearest to
@@ -60,6 +66,7 @@ __all__ = [
     "fp8_inverse_scale", "quantize_fp8", "reshape_and_cache_fp8", "paged_attention_decode_fp8",
     "sparse_paged_attention_decode_fp8",
     "paged_attention_varlen", "paged_attention_varlen_fp8",
+    "e4m3_code_of", "quest_block_metadata_fp8", "quest_block_scores_fp8", "quest_select_topk_fp8",
 ]
 
 
@@ -286,15 +293,20 @@ def quest_select_topk(query, key_min, key_max, block_tables, context_lens, block
     Order by score descending, equal scores by lower logical index; the kept ids
     are returned ascending and padded with -1.
     """
+    return _topk_of_scores(
+        lambda b, g: quest_block_scores(query, key_min, key_max, block_tables, context_lens,
+                                        block_size, b, g),
+        query.shape[0], key_min.shape[1], topk)
+
+
+def _topk_of_scores(scores_of, B, Hkv, topk):
+    """The Top-K rule over the scores ``scores_of(b, g)`` of each (sequence, KV head)."""
     if topk < 1:
         raise ValueError("topk_blocks must be >= 1")
-    B = query.shape[0]
-    Hkv = key_min.shape[1]
     out = np.full((B, Hkv, topk), -1, dtype=np.int32)
     for b in range(B):
         for g in range(Hkv):
-            s = quest_block_scores(query, key_min, key_max, block_tables, context_lens,
-                                   block_size, b, g)
+            s = scores_of(b, g)
             order = sorted(range(s.size), key=lambda lb: (-s[lb], lb))
             keep = sorted(order[:min(topk, s.size)])
             out[b, g, :len(keep)] = keep
@@ -464,6 +476,63 @@ def sparse_paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_
             heads = slice(g * G, (g + 1) * G)
             out[b, heads] = _softmax_attention(q[b, heads], k_g, v_g, sc)
     return out
+
+
+# ---------------------------------------------------------------------------
+# C9 -- Quest over E4M3 caches  (R9)
+# ---------------------------------------------------------------------------
+
+def e4m3_code_of(values: np.ndarray) -> np.ndarray:
+    """The E4M3 code of values that are E4M3 values (exact; -0 gives 0x80)."""
+    return e4m3_from_f32(np.asarray(values, dtype=np.float64).astype(np.float32))
+
+
+def quest_block_metadata_fp8(key_cache, block_tables, context_lens, block_size,
+                             last_block_only=False, key_min=None, key_max=None):
+    """Quest metadata of an E4M3 key cache: the codes of the smallest and largest key
+    code value per (referenced block, KV head, channel) over the block's valid rows,
+    as ``quest_block_metadata`` takes them over bf16 keys. uint8 [NB, H_kv, D]."""
+    NB, bs, Hkv, D = key_cache.shape
+    assert bs == block_size
+    kmin = np.zeros((NB, Hkv, D), np.uint8) if key_min is None else np.array(key_min, copy=True)
+    kmax = np.zeros((NB, Hkv, D), np.uint8) if key_max is None else np.array(key_max, copy=True)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    _check_table(block_tables, ctx, bs, NB)
+    for b, L in enumerate(ctx.tolist()):
+        nb = -(-L // bs)
+        blocks = [nb - 1] if (last_block_only and nb > 0) else range(nb)
+        for lb in blocks:
+            pb = int(block_tables[b, lb])
+            n = min(bs, L - lb * bs)
+            k = e4m3_to_f64(key_cache[pb, :n])           # [n, H_kv, D]
+            kmin[pb] = e4m3_code_of(k.min(axis=0))
+            kmax[pb] = e4m3_code_of(k.max(axis=0))
+    return kmin, kmax
+
+
+def quest_block_scores_fp8(query, key_min, key_max, block_tables, context_lens, block_size,
+                           b, g):
+    """``quest_block_scores`` over E4M3 metadata: the bound on the key code values.
+    bf16 x E4M3 products are exact in float64; math.fsum rounds each sum once."""
+    Hq = query.shape[1]
+    Hkv = key_min.shape[1]
+    G = Hq // Hkv
+    L = int(context_lens[b])
+    nb = -(-L // block_size)
+    q = bf16_to_f64(query[b, g * G:(g + 1) * G])             # [G, D]
+    pbs = np.asarray(block_tables[b, :nb], dtype=np.int64)
+    lo = e4m3_to_f64(key_min[pbs, g])                        # [nb, D]
+    hi = e4m3_to_f64(key_max[pbs, g])
+    terms = np.maximum(q[None, :, :] * lo[:, None, :], q[None, :, :] * hi[:, None, :])
+    return np.array([math.fsum(t.ravel().tolist()) for t in terms], dtype=np.float64)
+
+
+def quest_select_topk_fp8(query, key_min, key_max, block_tables, context_lens, block_size, topk):
+    """``quest_select_topk`` with the scores of ``quest_block_scores_fp8``."""
+    return _topk_of_scores(
+        lambda b, g: quest_block_scores_fp8(query, key_min, key_max, block_tables,
+                                            context_lens, block_size, b, g),
+        query.shape[0], key_min.shape[1], topk)
 
 
 # ---------------------------------------------------------------------------

@@ -659,6 +659,127 @@ def pin_fp8_sparse_equals_bf16_sparse_on_representable(orc):
 
 
 # ---------------------------------------------------------------------------
+# Quest over E4M3 caches
+# ---------------------------------------------------------------------------
+
+def _fp8_code_case(seed):
+    """Random finite E4M3 codes (both zeros included) in a paged key cache; the rows
+    past each sequence's context hold +-448, which the metadata must not see."""
+    w = workloads.random_case(seed, batch=3, num_q_heads=6, num_kv_heads=2, head_dim=64,
+                              block_size=16, context_lens=[1, 40, 70])
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    kc = rng.choice(finite, size=w.key_cache.shape).astype(np.uint8)
+    for b in range(3):
+        L = int(w.context_lens[b])
+        pb = int(w.block_tables[b, (L - 1) // 16])
+        kc[pb, L % 16 or 16:, :, ::2] = 0x7E       # +448
+        kc[pb, L % 16 or 16:, :, 1::2] = 0xFE      # -448
+    return w, kc
+
+
+def pin_fp8_meta_brute_force(orc):
+    """Per channel, the decoded codes are the smallest and largest code value over the
+    block's valid rows, from a decoder written from the E4M3 definition; step mode
+    writes only each sequence's last block."""
+    w, kc = _fp8_code_case(81)
+    kmin, kmax = orc.quest_block_metadata_fp8(kc, w.block_tables, w.context_lens, 16)
+    assert kmin.dtype == np.uint8 and kmin.shape == (w.num_blocks, 2, 64)
+    val = {c: _e4m3_value_py(c) for c in range(256) if c not in (0x7F, 0xFF)}
+    for b in range(3):
+        L = int(w.context_lens[b])
+        for lb in range(-(-L // 16)):
+            pb = int(w.block_tables[b, lb])
+            n = min(16, L - lb * 16)
+            for g in range(2):
+                for c in range(64):
+                    vals = [val[int(kc[pb, t, g, c])] for t in range(n)]
+                    assert val[int(kmin[pb, g, c])] == min(vals), (pb, g, c)
+                    assert val[int(kmax[pb, g, c])] == max(vals), (pb, g, c)
+    base = np.full_like(kmin, 0x35)
+    smin, smax = orc.quest_block_metadata_fp8(kc, w.block_tables, w.context_lens, 16,
+                                              last_block_only=True, key_min=base, key_max=base)
+    last = {int(w.block_tables[b, (int(w.context_lens[b]) - 1) // 16]) for b in range(3)}
+    for pb in range(w.num_blocks):
+        if pb in last:
+            assert np.array_equal(smin[pb], kmin[pb]) and np.array_equal(smax[pb], kmax[pb])
+        else:
+            assert (smin[pb] == 0x35).all() and (smax[pb] == 0x35).all()
+
+
+def pin_fp8_scores_exact_rational(orc):
+    """Each FP8 block score is the exact rational bound on the decoded codes, rounded once."""
+    w, kc = _fp8_code_case(82)
+    kmin, kmax = orc.quest_block_metadata_fp8(kc, w.block_tables, w.context_lens, 16)
+    G = w.group
+    for b in range(3):
+        nb = -(-int(w.context_lens[b]) // 16)
+        for g in range(2):
+            s = orc.quest_block_scores_fp8(w.query, kmin, kmax, w.block_tables, w.context_lens,
+                                           16, b, g)
+            assert s.size == nb
+            for lb in range(nb):
+                pb = int(w.block_tables[b, lb])
+                tot = Fraction(0)
+                for h in range(g * G, (g + 1) * G):
+                    q = _dec(w.query[b, h])
+                    for c in range(64):
+                        qc = Fraction(float(q[c]))
+                        tot += max(qc * _e4m3_value_py(int(kmin[pb, g, c])),
+                                   qc * _e4m3_value_py(int(kmax[pb, g, c])))
+                assert s[lb] == float(tot), (b, g, lb)
+
+
+def pin_fp8_quest_is_bf16_quest_over_the_scale(orc):
+    """On keys that are E4M3 values times a power-of-two scale per KV head, quantising
+    commutes with the per-channel min and max, so the FP8 scores are the bf16 scores
+    divided by the head's scale (exactly) and both select the same blocks, ties
+    included; the selection is the rank rule on the FP8 scores."""
+    scales = [0.5, 4.0]
+    w = _representable_case(83, scales)
+    kq = orc.quantize_fp8(w.key_cache, scales)
+    fmin, fmax = orc.quest_block_metadata_fp8(kq, w.block_tables, w.context_lens, 16)
+    bmin, bmax = orc.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, 16)
+    for g in range(2):
+        assert np.array_equal(_e4m3_f64_ref(fmin[:, g]) * scales[g], _dec(bmin[:, g]))
+        assert np.array_equal(_e4m3_f64_ref(fmax[:, g]) * scales[g], _dec(bmax[:, g]))
+    for b in range(3):
+        for g in range(2):
+            sf = orc.quest_block_scores_fp8(w.query, fmin, fmax, w.block_tables, w.context_lens,
+                                            16, b, g)
+            sb = orc.quest_block_scores(w.query, bmin, bmax, w.block_tables, w.context_lens,
+                                        16, b, g)
+            assert np.array_equal(sf * scales[g], sb), (b, g)
+    for K in (1, 2, 4, 6):
+        sel = orc.quest_select_topk_fp8(w.query, fmin, fmax, w.block_tables, w.context_lens, 16, K)
+        ref = orc.quest_select_topk(w.query, bmin, bmax, w.block_tables, w.context_lens, 16, K)
+        assert sel.shape == (3, 2, K) and sel.dtype == np.int32 and np.array_equal(sel, ref), K
+        for b in range(3):
+            for g in range(2):
+                s = orc.quest_block_scores_fp8(w.query, fmin, fmax, w.block_tables,
+                                               w.context_lens, 16, b, g)
+                exp = _rank_select(s.tolist(), K)
+                row = sel[b, g].tolist()
+                assert row[:len(exp)] == exp and all(x == -1 for x in row[len(exp):])
+
+
+def pin_fp8_topk_tie_lower_index(orc):
+    """Two blocks with the same codes tie; with room for one the lower index wins."""
+    w, kc = _fp8_code_case(84)
+    kmin, kmax = orc.quest_block_metadata_fp8(kc, w.block_tables, w.context_lens, 16)
+    s = orc.quest_block_scores_fp8(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, 2, 1)
+    best = int(np.argmax(s[:4]))                    # full blocks only: no poisoned rows
+    later = max(lb for lb in range(4) if lb != best)
+    kc[int(w.block_tables[2, later])] = kc[int(w.block_tables[2, best])]
+    kmin, kmax = orc.quest_block_metadata_fp8(kc, w.block_tables, w.context_lens, 16)
+    s2 = orc.quest_block_scores_fp8(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, 2, 1)
+    a, c = min(best, later), max(best, later)
+    assert s2[a] == s2[c] and s2[a] == s2.max()
+    sel = orc.quest_select_topk_fp8(w.query, kmin, kmax, w.block_tables, w.context_lens, 16, 1)
+    assert sel[2, 1, 0] == a, "tie goes to the lower logical block"
+
+
+# ---------------------------------------------------------------------------
 # Multi-token queries (varlen, right-aligned causal mask)
 # ---------------------------------------------------------------------------
 

@@ -61,6 +61,22 @@ MUTANTS = [
      "k_g = e4m3_to_f64(gather_sequence(key_cache[:, :, g]", "k_g = e4m3_to_f64(gather_sequence(key_cache[:, :, 0]"),
     ("fp8 sparse: no K scale", "key_cache[:, :, g], block_tables, b, pos, bs)) * ks[g]",
      "key_cache[:, :, g], block_tables, b, pos, bs))"),
+    ("fp8 meta: invalid rows included", "n = min(bs, L - lb * bs)\n            k = e4m3_to_f64",
+     "n = bs\n            k = e4m3_to_f64"),
+    ("fp8 meta: min and max swapped", "kmin[pb] = e4m3_code_of(k.min(axis=0))",
+     "kmin[pb] = e4m3_code_of(k.max(axis=0))"),
+    ("fp8 meta: step mode updates block 0",
+     "blocks = [nb - 1] if (last_block_only and nb > 0) else range(nb)\n        for lb in blocks:\n"
+     "            pb = int(block_tables[b, lb])\n            n = min(bs, L - lb * bs)\n            k = e4m3_to_f64",
+     "blocks = [0] if (last_block_only and nb > 0) else range(nb)\n        for lb in blocks:\n"
+     "            pb = int(block_tables[b, lb])\n            n = min(bs, L - lb * bs)\n            k = e4m3_to_f64"),
+    ("fp8 meta: code of the magnitude", "return e4m3_from_f32(np.asarray(values, dtype=np.float64).astype(np.float32))",
+     "return e4m3_from_f32(np.abs(np.asarray(values, dtype=np.float64)).astype(np.float32))"),
+    ("fp8 score: kmin used for both bounds", "hi = e4m3_to_f64(key_max[pbs, g])", "hi = e4m3_to_f64(key_min[pbs, g])"),
+    ("fp8 score: codes taken as integers", "lo = e4m3_to_f64(key_min[pbs, g])",
+     "lo = key_min[pbs, g].astype(np.float64)"),
+    ("fp8 topk: bf16 scores on the codes", "lambda b, g: quest_block_scores_fp8(",
+     "lambda b, g: quest_block_scores("),
     ("varlen: query rows shifted", "s_ = sc * (q[r0:r1, h] @ k[:, g].T)", "s_ = sc * (q[r0 + 1:r1 + 1, h] @ k[:, g].T)"),
 ]
 
