@@ -13,7 +13,9 @@ from .ops import (GpkvError, paged_attention_decode, paged_attention_workspace_b
                   paged_attention_varlen, paged_attention_varlen_workspace_bytes, quest_decode,
                   quest_decode_workspace_bytes, paged_attention_varlen_fp8,
                   paged_attention_decode_noalloc, paged_attention_decode_append,
-                  quest_decode_append, paged_attention_decode_fp8_append)
+                  quest_decode_append, paged_attention_decode_fp8_append,
+                  quest_block_metadata_fp8, reshape_and_cache_fp8_quest, quest_select_topk_fp8,
+                  quest_decode_fp8, quest_decode_fp8_append)
 
 __all__ = [
     "GpkvError", "reshape_and_cache", "reshape_and_cache_quest", "paged_attention_decode",
@@ -24,4 +26,6 @@ __all__ = [
     "paged_attention_varlen", "paged_attention_varlen_workspace_bytes", "quest_decode",
     "quest_decode_workspace_bytes", "paged_attention_varlen_fp8", "paged_attention_decode_noalloc",
     "paged_attention_decode_append", "quest_decode_append", "paged_attention_decode_fp8_append",
+    "quest_block_metadata_fp8", "reshape_and_cache_fp8_quest", "quest_select_topk_fp8",
+    "quest_decode_fp8", "quest_decode_fp8_append",
 ]

@@ -64,6 +64,20 @@ SIGNATURES = {
                                                          c_int32, c_int32, c_int32, c_int32,
                                                          c_int32, c_int64, c_int32, c_int32,
                                                          c_int32, c_float, vp, c_size, vp]),
+    "gpkv_quest_block_metadata_fp8": (c_int32, [vp, vp, vp, vp, vp, c_int32, c_int32, c_int32,
+                                                c_int32, c_int64, c_int32, c_int32, c_int32, vp]),
+    "gpkv_reshape_and_cache_fp8_quest": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int32,
+                                                   c_int32, c_int32, c_int32, c_int64, vp]),
+    "gpkv_quest_select_topk_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, c_int32, c_int32, c_int32,
+                                             c_int32, c_int32, c_int64, c_int32, c_int32, c_int32,
+                                             vp, c_size, vp]),
+    "gpkv_quest_decode_fp8": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int32,
+                                        c_int32, c_int32, c_int32, c_int32, c_int64, c_int32,
+                                        c_int32, c_int32, c_float, vp, c_size, vp]),
+    "gpkv_quest_decode_fp8_append": (c_int32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                               c_int64, c_int32, c_int32, c_int32, c_float, vp,
+                                               c_size, vp]),
     "gpkv_paged_attention_varlen_workspace_bytes": (c_size, [c_int32] * 8),
     "gpkv_paged_attention_varlen": (c_int32, [vp, vp, vp, vp, vp, vp, vp, c_int32, c_int32,
                                               c_int32, c_int32, c_int32, c_int32, c_int32,

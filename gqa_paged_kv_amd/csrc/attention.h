@@ -508,6 +508,37 @@ __device__ __forceinline__ void store_new_token(const unsigned short* knew,
   }
 }
 
+// store_new_token for E4M3 caches: KV head g's part of the token quantised as the
+// FP8 write path quantises it (code = e4m3(x * (1 / scale[g]))), and its key codes
+// folded into E4M3 metadata. The calling threads split the D / 16 16-byte code
+// vectors of the row.
+template <int D>
+__device__ __forceinline__ void store_new_token_fp8(const unsigned short* knew,
+                                                    const unsigned short* vnew, unsigned char* kc,
+                                                    unsigned char* vc, unsigned char* kmin,
+                                                    unsigned char* kmax, const float* k_scale,
+                                                    const float* v_scale, long long s, int bs,
+                                                    int Hkv, int b, int g, int t, int nt) {
+  const long long blk = s / bs, off = s - blk * bs;
+  const size_t row = (size_t)Hkv * D;   // bytes per cache row
+  const float kinv = 1.0f / k_scale[g], vinv = 1.0f / v_scale[g];
+  for (int c = t; c < D / 16; c += nt) {
+    const u32x4* ks = (const u32x4*)(knew + ((size_t)b * Hkv + g) * D + 16 * c);
+    const u32x4* vs = (const u32x4*)(vnew + ((size_t)b * Hkv + g) * D + 16 * c);
+    const size_t dst = (size_t)s * row + (size_t)g * D + 16 * c;
+    const u32x4 k = quantize16(ks[0], ks[1], kinv);
+    *(u32x4*)(kc + dst) = k;
+    *(u32x4*)(vc + dst) = quantize16(vs[0], vs[1], vinv);
+    if (kmin != nullptr) {
+      const size_t meta = (size_t)blk * row + (size_t)g * D + 16 * c;
+      u32x4 mn = k, mx = k;
+      if (off > 0) fold_min_max_e4m3(k, *(const u32x4*)(kmin + meta), *(const u32x4*)(kmax + meta), mn, mx);
+      *(u32x4*)(kmin + meta) = mn;
+      *(u32x4*)(kmax + meta) = mx;
+    }
+  }
+}
+
 // Positions of sequence b the split phase reads: its clamped context, less the
 // appended token.
 __device__ __forceinline__ int split_ctx(const int* ctx, const long long* slots,

@@ -144,6 +144,46 @@ __device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv) {
   return out;
 }
 
+// E4M3 codes are sign-magnitude, and among the finite codes of one sign a larger
+// magnitude field is a larger magnitude. Flipping the sign bit of a non-negative
+// code and every bit of a negative one gives bytes whose unsigned order is the
+// order of the values (-448 -> 0x01 ... -0 -> 0x7F, +0 -> 0x80 ... 448 -> 0xFE;
+// the two zeros stay distinct but adjacent). Four codes per word, one per byte.
+__device__ __forceinline__ unsigned e4m3_order_bytes(unsigned w) {
+  const unsigned neg = (w >> 7) & 0x01010101u;
+  return w ^ (neg * 0x7Fu) ^ 0x80808080u;
+}
+__device__ __forceinline__ unsigned e4m3_from_order_bytes(unsigned k) {
+  const unsigned t = k ^ 0x80808080u;
+  return t ^ (((t >> 7) & 0x01010101u) * 0x7Fu);
+}
+// Per-byte unsigned min / max of two words.
+__device__ __forceinline__ unsigned bytes_min(unsigned a, unsigned b) {
+  unsigned r = 0;
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) r |= min((a >> i) & 0xFFu, (b >> i) & 0xFFu) << i;
+  return r;
+}
+__device__ __forceinline__ unsigned bytes_max(unsigned a, unsigned b) {
+  unsigned r = 0;
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) r |= max((a >> i) & 0xFFu, (b >> i) & 0xFFu) << i;
+  return r;
+}
+
+// fold_min_max over sixteen E4M3 codes: the codes of the element-wise smaller and
+// larger value of the block's current metadata (om, ox) and the new row k. Each
+// result is one of the inputs (a zero extreme may come out as either zero code).
+__device__ __forceinline__ void fold_min_max_e4m3(const u32x4& k, const u32x4& om,
+                                                  const u32x4& ox, u32x4& mn, u32x4& mx) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const unsigned kk = e4m3_order_bytes(k[w]);
+    mn[w] = e4m3_from_order_bytes(bytes_min(e4m3_order_bytes(om[w]), kk));
+    mx[w] = e4m3_from_order_bytes(bytes_max(e4m3_order_bytes(ox[w]), kk));
+  }
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -27,14 +27,14 @@ namespace gpkv {
 // ---------------------------------------------------------------------------
 
 struct MetaParams {
-  unsigned short* kmin;      // [NB, H_kv, D] bf16
-  unsigned short* kmax;
-  const unsigned char* kc;   // [NB, bs, H_kv, D] bf16
+  void* kmin;                // [NB, H_kv, D] bf16 (E4M3 codes: the FP8 kernel)
+  void* kmax;
+  const unsigned char* kc;   // [NB, bs, H_kv, D] bf16 (E4M3 codes)
   const int* bt;
   const int* ctx;
   long long NB;
   long long block_bytes;
-  int row_bytes;             // H_kv * D * 2
+  int row_bytes;             // H_kv * D * bytes per element
   int bs, max_blocks, max_ctx, last_only;
 };
 
@@ -111,15 +111,75 @@ __global__ __launch_bounds__(256) void quest_meta_kernel(const MetaParams p) {
         px[k] = pack_bf16_pair(mx[2 * k], mx[2 * k + 1]);
       }
       const size_t o = (size_t)pb * (p.row_bytes / 2) + (size_t)c * 8;
-      *(u32x4*)(p.kmin + o) = pm;
-      *(u32x4*)(p.kmax + o) = px;
+      *(u32x4*)((unsigned short*)p.kmin + o) = pm;
+      *(u32x4*)((unsigned short*)p.kmax + o) = px;
+    }
+  }
+}
+
+// The same over an E4M3 key cache: a 16-byte chunk holds sixteen codes, compared
+// as order bytes (e4m3_order_bytes: unsigned byte order is value order) and
+// stored back as the codes of the extremes.
+__global__ __launch_bounds__(256) void quest_meta_fp8_kernel(const MetaParams p) {
+  __shared__ u32x4 red_min[256];
+  __shared__ u32x4 red_max[256];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  int ctx = p.ctx[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  const int nb = (ctx + p.bs - 1) / p.bs;
+  const int lb = p.last_only ? nb - 1 : (int)blockIdx.x;
+  if (lb < 0 || lb >= nb) return;
+  const int pb = p.bt[(size_t)b * p.max_blocks + lb];
+  if (pb < 0 || pb >= p.NB) return;
+  const int n = min(p.bs, ctx - lb * p.bs);
+  const unsigned char* blk = p.kc + (size_t)pb * (size_t)p.block_bytes;
+  const int chunks = p.row_bytes / 16;
+  const int cpp = chunks < 256 ? chunks : 256;
+  const int groups = 256 / cpp;
+  const int c_local = tid % cpp, tg = tid / cpp;
+
+  for (int c0 = 0; c0 < chunks; c0 += cpp) {
+    const int c = c0 + c_local;
+    u32x4 mn = u32x4{~0u, ~0u, ~0u, ~0u}, mx = u32x4{0u, 0u, 0u, 0u};   // identities
+    if (tg < groups && c < chunks) {
+      for (int t = tg; t < n; t += groups) {
+        const u32x4 v = *(const u32x4*)(blk + (size_t)t * p.row_bytes + (size_t)c * 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const unsigned o = e4m3_order_bytes(v[k]);
+          mn[k] = bytes_min(mn[k], o);
+          mx[k] = bytes_max(mx[k], o);
+        }
+      }
+    }
+    __syncthreads();
+    red_min[tid] = mn;
+    red_max[tid] = mx;
+    __syncthreads();
+    if (tg == 0 && c < chunks) {   // group 0 holds row 0: every lane has a real extreme
+      for (int gi = 1; gi < groups; ++gi) {
+        const u32x4 om = red_min[gi * cpp + c_local], ox = red_max[gi * cpp + c_local];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          mn[k] = bytes_min(mn[k], om[k]);
+          mx[k] = bytes_max(mx[k], ox[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        mn[k] = e4m3_from_order_bytes(mn[k]);
+        mx[k] = e4m3_from_order_bytes(mx[k]);
+      }
+      const size_t o = (size_t)pb * p.row_bytes + (size_t)c * 16;
+      *(u32x4*)((unsigned char*)p.kmin + o) = mn;
+      *(u32x4*)((unsigned char*)p.kmax + o) = mx;
     }
   }
 }
 
 // Two-kernel path, scoring: a workgroup covers kScoreBlocksPerWG consecutive logical
 // blocks of one (b, g) and writes float64 scores (as their order-preserving keys).
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(kSelectThreads) void quest_score_kernel(const ScoreParams p) {
   __shared__ double s_pos[D];
   __shared__ double s_neg[D];
@@ -132,7 +192,7 @@ __global__ __launch_bounds__(kSelectThreads) void quest_score_kernel(const Score
   if (lb0 >= nb || p.K >= nb) return;  // nothing to rank: every block is selected
   query_bounds<D>(p, b, g, s_q, s_pos, s_neg);
   unsigned long long* keys = (unsigned long long*)p.scores + ((size_t)b * p.Hkv + g) * p.max_blocks;
-  score_blocks<D, kScoreUnroll>(p, g, nb, lb0,
+  score_blocks<D, FP8, kScoreUnroll>(p, g, nb, lb0,
                                [&](int lb) { return p.bt[(size_t)b * p.max_blocks + lb]; },
                                s_pos, s_neg,
                                 [&](int lb, unsigned long long key) { keys[lb] = key; });
@@ -149,7 +209,7 @@ __global__ __launch_bounds__(kSelectThreads) void quest_score_kernel(const Score
 constexpr int kRowScoreUnroll = 2;
 constexpr int kMaxRowHeads = 32;
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(kSelectThreads) void quest_score_rows_kernel(const ScoreParams p) {
   extern __shared__ double s_qb[];   // [H_kv][2][D + kQbPad]: positive / negative query sums
   constexpr int NV = D / 64;
@@ -187,8 +247,8 @@ __global__ __launch_bounds__(kSelectThreads) void quest_score_rows_kernel(const 
     const size_t o = ((size_t)(ok[u] ? pb : 0) * Hkv + g) * D + (size_t)sub * 8;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      mn[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmin + o + 64 * v)) : u32x4{0, 0, 0, 0};
-      mx[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmax + o + 64 * v)) : u32x4{0, 0, 0, 0};
+      mn[u][v] = ok[u] ? meta_load8<FP8>(p.kmin, o + 64 * v) : u32x4{0, 0, 0, 0};
+      mx[u][v] = ok[u] ? meta_load8<FP8>(p.kmax, o + 64 * v) : u32x4{0, 0, 0, 0};
     }
   }
   __syncthreads();
@@ -204,20 +264,7 @@ __global__ __launch_bounds__(kSelectThreads) void quest_score_rows_kernel(const 
   unsigned long long* keys = (unsigned long long*)p.scores + ((size_t)b * Hkv + g) * p.max_blocks;
 #pragma unroll
   for (int u = 0; u < kRowScoreUnroll; ++u) {
-    double acc = 0.0;
-    if (active) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int j = (v * 8 + 2 * k) * 8 + sub;   // qb_index of channel 64v + 8 sub + 2k
-          acc = fma((double)bf16_lo(mx[u][v][k]), s_pos[j], acc);
-          acc = fma((double)bf16_lo(mn[u][v][k]), s_neg[j], acc);
-          acc = fma((double)bf16_hi(mx[u][v][k]), s_pos[j + 8], acc);
-          acc = fma((double)bf16_hi(mn[u][v][k]), s_neg[j + 8], acc);
-        }
-      }
-    }
+    double acc = active ? bound_lane<D, FP8>(mn[u], mx[u], s_pos, s_neg, sub) : 0.0;
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 4);
@@ -259,7 +306,7 @@ __global__ __launch_bounds__(kMaxSelectThreads) void quest_topk_kernel(const Top
 
 // Fused path: one workgroup per (b, g) scores all its blocks into LDS keys and
 // selects from them -- one launch, and the keys never leave the CU.
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(kFusedThreads) void quest_select_fused_kernel(const ScoreParams p) {
   // Dynamic LDS: the keys of the sequence's blocks, then its block-table row.
   extern __shared__ unsigned long long s_key[];
@@ -286,8 +333,8 @@ __global__ __launch_bounds__(kFusedThreads) void quest_select_fused_kernel(const
     group_bounds<D>(s_q, p.G, c, s_pos + qb_index<D>(c), s_neg + qb_index<D>(c));
   __syncthreads();
   for (int lb0 = 0; lb0 < nb; lb0 += (int)(blockDim.x >> 3) * kFusedUnroll)
-    score_blocks<D, kFusedUnroll>(p, g, nb, lb0, [&](int lb) { return s_pb[lb]; }, s_pos, s_neg,
-                                  [&](int lb, unsigned long long key) { s_key[lb] = key; });
+    score_blocks<D, FP8, kFusedUnroll>(p, g, nb, lb0, [&](int lb) { return s_pb[lb]; }, s_pos,
+                                       s_neg, [&](int lb, unsigned long long key) { s_key[lb] = key; });
   __syncthreads();
   radix_topk(nb, p.K, [&](int i) { return s_key[i]; }, out, sh);
 }
@@ -311,32 +358,26 @@ static int check_quest(const char* fn, int B, int Hkv, int D, int bs, long long 
   return GPKV_OK;
 }
 
-}  // namespace gpkv
-
-using namespace gpkv;
-
-extern "C" int gpkv_quest_block_metadata(void* key_min, void* key_max, const void* key_cache,
-                                         const int32_t* block_tables,
-                                         const int32_t* context_lens, int32_t batch,
-                                         int32_t num_kv_heads, int32_t head_dim,
-                                         int32_t block_size, int64_t num_blocks,
-                                         int32_t max_blocks_per_seq, int32_t max_context_len,
-                                         int32_t last_block_only, void* stream) {
-  clear_error();
-  int st = check_quest("quest_block_metadata", batch, num_kv_heads, head_dim, block_size,
-                       num_blocks, max_blocks_per_seq, max_context_len);
+static int meta_run(const char* fn, bool fp8, void* key_min, void* key_max,
+                    const void* key_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t batch, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t last_block_only,
+                    void* stream) {
+  int st = check_quest(fn, batch, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len);
   if (st) return st;
   if (batch == 0 || max_context_len == 0) return GPKV_OK;
   if (!key_min || !key_max || !key_cache || !block_tables || !context_lens)
-    return fail(GPKV_ERR_NULL, "quest_block_metadata: null pointer argument");
+    return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
   MetaParams mp;
-  mp.kmin = (unsigned short*)key_min;
-  mp.kmax = (unsigned short*)key_max;
+  mp.kmin = key_min;
+  mp.kmax = key_max;
   mp.kc = (const unsigned char*)key_cache;
   mp.bt = block_tables;
   mp.ctx = context_lens;
   mp.NB = num_blocks;
-  mp.row_bytes = num_kv_heads * head_dim * 2;
+  mp.row_bytes = num_kv_heads * head_dim * (fp8 ? 1 : 2);
   mp.block_bytes = (long long)block_size * mp.row_bytes;
   mp.bs = block_size;
   mp.max_blocks = max_blocks_per_seq;
@@ -344,26 +385,21 @@ extern "C" int gpkv_quest_block_metadata(void* key_min, void* key_max, const voi
   mp.last_only = last_block_only ? 1 : 0;
   const int max_nb = (max_context_len + block_size - 1) / block_size;
   const dim3 grid(last_block_only ? 1 : max_nb, batch);
-  quest_meta_kernel<<<grid, dim3(256), 0, (hipStream_t)stream>>>(mp);
-  return check_launch("quest_block_metadata");
+  if (fp8)
+    quest_meta_fp8_kernel<<<grid, dim3(256), 0, (hipStream_t)stream>>>(mp);
+  else
+    quest_meta_kernel<<<grid, dim3(256), 0, (hipStream_t)stream>>>(mp);
+  return check_launch(fn);
 }
 
-extern "C" size_t gpkv_quest_select_workspace_bytes(int32_t batch, int32_t num_kv_heads,
-                                                    int32_t max_blocks_per_seq) {
-  if (batch < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 0;
-  return (size_t)batch * num_kv_heads * max_blocks_per_seq * sizeof(double);
-}
-
-extern "C" int gpkv_quest_select_topk(int32_t* topk_indices, const void* query,
-                                      const void* key_min, const void* key_max,
-                                      const int32_t* block_tables, const int32_t* context_lens,
-                                      int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                      int32_t max_blocks_per_seq, int32_t max_context_len,
-                                      int32_t topk_blocks, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
-  clear_error();
-  const char* fn = "quest_select_topk";
+template <bool FP8>
+static int select_run(const char* fn, int32_t* topk_indices, const void* query,
+                      const void* key_min, const void* key_max, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                      int32_t topk_blocks, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   int st = check_quest(fn, batch, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, max_context_len);
   if (st) return st;
@@ -387,8 +423,8 @@ extern "C" int gpkv_quest_select_topk(int32_t* topk_indices, const void* query,
   sp.scores = (double*)workspace;
   sp.out = topk_indices;
   sp.q = (const unsigned short*)query;
-  sp.kmin = (const unsigned short*)key_min;
-  sp.kmax = (const unsigned short*)key_max;
+  sp.kmin = key_min;
+  sp.kmax = key_max;
   sp.bt = block_tables;
   sp.ctx = context_lens;
   sp.NB = num_blocks;
@@ -416,9 +452,9 @@ extern "C" int gpkv_quest_select_topk(int32_t* topk_indices, const void* query,
     while (threads < kFusedThreads && threads / 8 * kFusedUnroll < max_nb) threads <<= 1;
     const dim3 grid(num_kv_heads, batch);
     if (head_dim == 128)
-      quest_select_fused_kernel<128><<<grid, dim3(threads), lds, s>>>(sp);
+      quest_select_fused_kernel<128, FP8><<<grid, dim3(threads), lds, s>>>(sp);
     else
-      quest_select_fused_kernel<64><<<grid, dim3(threads), lds, s>>>(sp);
+      quest_select_fused_kernel<64, FP8><<<grid, dim3(threads), lds, s>>>(sp);
     return check_launch(fn);
   }
   const size_t row_lds = (size_t)num_kv_heads * 2 * (head_dim + kQbPad) * sizeof(double) +
@@ -427,17 +463,17 @@ extern "C" int gpkv_quest_select_topk(int32_t* topk_indices, const void* query,
     const int per_wg = (kSelectThreads / 8) / num_kv_heads * kRowScoreUnroll;
     const dim3 grid((max_nb + per_wg - 1) / per_wg, batch);
     if (head_dim == 128)
-      quest_score_rows_kernel<128><<<grid, dim3(kSelectThreads), row_lds, s>>>(sp);
+      quest_score_rows_kernel<128, FP8><<<grid, dim3(kSelectThreads), row_lds, s>>>(sp);
     else
-      quest_score_rows_kernel<64><<<grid, dim3(kSelectThreads), row_lds, s>>>(sp);
+      quest_score_rows_kernel<64, FP8><<<grid, dim3(kSelectThreads), row_lds, s>>>(sp);
     st = check_launch(fn);
     if (st) return st;
   } else if (max_nb > 0) {
     const dim3 grid((max_nb + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG, num_kv_heads, batch);
     if (head_dim == 128)
-      quest_score_kernel<128><<<grid, dim3(kSelectThreads), 0, s>>>(sp);
+      quest_score_kernel<128, FP8><<<grid, dim3(kSelectThreads), 0, s>>>(sp);
     else
-      quest_score_kernel<64><<<grid, dim3(kSelectThreads), 0, s>>>(sp);
+      quest_score_kernel<64, FP8><<<grid, dim3(kSelectThreads), 0, s>>>(sp);
     st = check_launch(fn);
     if (st) return st;
   }
@@ -461,4 +497,71 @@ extern "C" int gpkv_quest_select_topk(int32_t* topk_indices, const void* query,
     topk_threads <<= 1;
   quest_topk_kernel<<<dim3(num_kv_heads, batch), dim3(topk_threads), lds, s>>>(tp);
   return check_launch(fn);
+}
+
+}  // namespace gpkv
+
+using namespace gpkv;
+
+extern "C" int gpkv_quest_block_metadata(void* key_min, void* key_max, const void* key_cache,
+                                         const int32_t* block_tables,
+                                         const int32_t* context_lens, int32_t batch,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int64_t num_blocks,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         int32_t last_block_only, void* stream) {
+  clear_error();
+  return meta_run("quest_block_metadata", false, key_min, key_max, key_cache, block_tables,
+                  context_lens, batch, num_kv_heads, head_dim, block_size, num_blocks,
+                  max_blocks_per_seq, max_context_len, last_block_only, stream);
+}
+
+extern "C" int gpkv_quest_block_metadata_fp8(void* key_min, void* key_max, const void* key_cache,
+                                             const int32_t* block_tables,
+                                             const int32_t* context_lens, int32_t batch,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int64_t num_blocks,
+                                             int32_t max_blocks_per_seq, int32_t max_context_len,
+                                             int32_t last_block_only, void* stream) {
+  clear_error();
+  return meta_run("quest_block_metadata_fp8", true, key_min, key_max, key_cache, block_tables,
+                  context_lens, batch, num_kv_heads, head_dim, block_size, num_blocks,
+                  max_blocks_per_seq, max_context_len, last_block_only, stream);
+}
+
+extern "C" size_t gpkv_quest_select_workspace_bytes(int32_t batch, int32_t num_kv_heads,
+                                                    int32_t max_blocks_per_seq) {
+  if (batch < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 0;
+  return (size_t)batch * num_kv_heads * max_blocks_per_seq * sizeof(double);
+}
+
+extern "C" int gpkv_quest_select_topk(int32_t* topk_indices, const void* query,
+                                      const void* key_min, const void* key_max,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      int32_t topk_blocks, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  clear_error();
+  return select_run<false>("quest_select_topk", topk_indices, query, key_min, key_max,
+                           block_tables, context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                           block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                           topk_blocks, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gpkv_quest_select_topk_fp8(int32_t* topk_indices, const void* query,
+                                          const void* key_min, const void* key_max,
+                                          const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t batch,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size,
+                                          int64_t num_blocks, int32_t max_blocks_per_seq,
+                                          int32_t max_context_len, int32_t topk_blocks,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return select_run<true>("quest_select_topk_fp8", topk_indices, query, key_min, key_max,
+                          block_tables, context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_blocks_per_seq, max_context_len, topk_blocks,
+                          workspace, workspace_bytes, stream);
 }

@@ -36,13 +36,15 @@ struct QuestDecodeParams {
   long long num_slots;       // NB * bs
   const unsigned short* knew;   // [B, H_kv, D] bf16
   const unsigned short* vnew;
-  unsigned short* kc_w;
-  unsigned short* vc_w;
-  unsigned short* kmin_w;
-  unsigned short* kmax_w;
+  void* kc_w;                // the caches and metadata (bf16, or E4M3 codes)
+  void* vc_w;
+  void* kmin_w;
+  void* kmax_w;
 };
 
-template <int D>
+// FP8: E4M3 caches with per-KV-head scales (c.k_scale, c.v_scale) and E4M3
+// metadata; the new token is quantised as the FP8 write path does it.
+template <int D, bool FP8>
 __global__ __launch_bounds__(kFusedThreads) void quest_decode_fused_kernel(const QuestDecodeParams p) {
   // Dynamic LDS: keys [max_nb, padded to 2], block-table row [max_nb, padded to 4],
   // then the waves' partial rows [kQuestWaves][G][D] (16-byte aligned).
@@ -73,9 +75,16 @@ __global__ __launch_bounds__(kFusedThreads) void quest_decode_fused_kernel(const
   stage_query<D>(sp, b, g * G, G, s_q);
   if (p.slots != nullptr) {
     const long long s = p.slots[b];
-    if (s >= 0 && s < p.num_slots)
-      store_new_token<D>(p.knew, p.vnew, p.kc_w, p.vc_w, p.kmin_w, p.kmax_w, s, bs, sp.Hkv, b, g,
-                         tid, kFusedThreads);
+    if (s >= 0 && s < p.num_slots) {
+      if constexpr (FP8)
+        store_new_token_fp8<D>(p.knew, p.vnew, (unsigned char*)p.kc_w, (unsigned char*)p.vc_w,
+                               (unsigned char*)p.kmin_w, (unsigned char*)p.kmax_w, p.c.k_scale,
+                               p.c.v_scale, s, bs, sp.Hkv, b, g, tid, kFusedThreads);
+      else
+        store_new_token<D>(p.knew, p.vnew, (unsigned short*)p.kc_w, (unsigned short*)p.vc_w,
+                           (unsigned short*)p.kmin_w, (unsigned short*)p.kmax_w, s, bs, sp.Hkv, b,
+                           g, tid, kFusedThreads);
+    }
   }
   __syncthreads();   // (the barrier also orders the new token's stores before every read)
   if (all) {
@@ -88,8 +97,8 @@ __global__ __launch_bounds__(kFusedThreads) void quest_decode_fused_kernel(const
       group_bounds<D>(s_q, G, c, s_pos + qb_index<D>(c), s_neg + qb_index<D>(c));
     __syncthreads();
     for (int lb0 = 0; lb0 < nb; lb0 += (kFusedThreads >> 3) * kFusedUnroll)
-      score_blocks<D, kFusedUnroll>(sp, g, nb, lb0, [&](int lb) { return s_pb[lb]; }, s_pos, s_neg,
-                                    [&](int lb, unsigned long long key) { s_key[lb] = key; });
+      score_blocks<D, FP8, kFusedUnroll>(sp, g, nb, lb0, [&](int lb) { return s_pb[lb]; }, s_pos,
+                                         s_neg, [&](int lb, unsigned long long key) { s_key[lb] = key; });
     __syncthreads();
     radix_topk(nb, K, [&](int i) { return s_key[i]; }, s_sel, sh);
     __syncthreads();
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(kFusedThreads) void quest_decode_fused_kernel(const
   rows.limit[0] = 0;
   rows.o[0] = s_o + wave * G * D;
   rows.lse[0] = s_lse + wave * kMaxGroup;
-  attend_head<D, false, false, 1>(p.c, g, ue > ub ? ue - ub : 0, desc, 0, rows);
+  attend_head<D, FP8, false, 1>(p.c, g, ue > ub ? ue - ub : 0, desc, 0, rows);
   __syncthreads();
 
   // out = sum_w 2^(lse_w - M) O_w / sum_w 2^(lse_w - M); no valid token: zeros.
@@ -172,14 +181,20 @@ extern "C" size_t gpkv_quest_decode_workspace_bytes(int32_t batch, int32_t num_q
   return a > b ? a : b;
 }
 
-// Decode append inputs of gpkv_quest_decode_append.
+// Decode append inputs of gpkv_quest_decode_append and its FP8 variant.
 struct QuestAppend {
   const void* key;
   const void* value;
   const int64_t* slots;
 };
 
-static int quest_decode_run(float* out, int32_t* topk_indices, const void* query,
+// FP8 caches and metadata (E4M3) with their per-KV-head scales.
+struct QuestFp8 {
+  const float* k_scale;
+  const float* v_scale;
+};
+
+static int quest_decode_run(const char* fn, float* out, int32_t* topk_indices, const void* query,
                             const void* key_cache, const void* value_cache, const void* key_min,
                             const void* key_max, const int32_t* block_tables,
                             const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
@@ -187,8 +202,7 @@ static int quest_decode_run(float* out, int32_t* topk_indices, const void* query
                             int64_t num_blocks, int32_t max_blocks_per_seq,
                             int32_t max_context_len, int32_t topk_blocks, float scale,
                             void* workspace, size_t workspace_bytes, void* stream,
-                            const QuestAppend* app) {
-  const char* fn = app ? "quest_decode_append" : "quest_decode";
+                            const QuestAppend* app, const QuestFp8* fp8) {
   int st = check_common(fn, batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                         max_blocks_per_seq, max_context_len);
   if (st) return st;
@@ -197,7 +211,8 @@ static int quest_decode_run(float* out, int32_t* topk_indices, const void* query
     return fail(GPKV_ERR_SHAPE, "%s: token span too large", fn);
   if (batch == 0) return GPKV_OK;
   if (!out || !topk_indices || !query || !key_cache || !value_cache || !key_min || !key_max ||
-      !block_tables || !context_lens || (app && (!app->key || !app->value || !app->slots)))
+      !block_tables || !context_lens || (app && (!app->key || !app->value || !app->slots)) ||
+      (fp8 && (!fp8->k_scale || !fp8->v_scale)))
     return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
   const size_t need = gpkv_quest_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
                                                         block_size, max_blocks_per_seq,
@@ -220,13 +235,33 @@ static int quest_decode_run(float* out, int32_t* topk_indices, const void* query
   // two calls' four launches. Measured on MI355X: two 5-block pairs 11.7 us in one
   // launch against 21.2 us as two calls; sixteen 2560-block pairs 111 us against
   // 38 us.
+  const int eb = fp8 ? 1 : 2;   // bytes per cached element and per metadata channel
   const long long pair_bytes =
-      (long long)max_nb * 2 * head_dim * 2 +
-      (long long)(topk_blocks < max_nb ? topk_blocks : max_nb) * block_size * 4 * head_dim;
+      (long long)max_nb * 2 * head_dim * eb +
+      (long long)(topk_blocks < max_nb ? topk_blocks : max_nb) * block_size * 2 * head_dim * eb;
   bool fused = fits && pairs <= cus && (2 * pairs > cus || pair_bytes <= 256 * 1024);
   const char* forced = getenv("GPKV_QUEST_DECODE_PATH");
   if (forced && strcmp(forced, "fused") == 0) fused = fits;
   if (forced && strcmp(forced, "separate") == 0) fused = false;
+  if (!fused && fp8) {
+    if (app) {   // the write (and metadata fold) first, then the two calls
+      st = gpkv_reshape_and_cache_fp8_quest(app->key, app->value, (void*)key_cache,
+                                            (void*)value_cache, fp8->k_scale, fp8->v_scale,
+                                            (void*)key_min, (void*)key_max, app->slots, batch,
+                                            num_kv_heads, head_dim, block_size, num_blocks, stream);
+      if (st) return st;
+    }
+    st = gpkv_quest_select_topk_fp8(topk_indices, query, key_min, key_max, block_tables,
+                                    context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                    block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                                    topk_blocks, workspace, workspace_bytes, stream);
+    if (st) return st;
+    return gpkv_sparse_paged_attention_decode_fp8(
+        out, query, key_cache, value_cache, fp8->k_scale, fp8->v_scale, block_tables,
+        context_lens, topk_indices, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+        num_blocks, max_blocks_per_seq, max_context_len, topk_blocks, scale, workspace,
+        workspace_bytes, stream);
+  }
   if (!fused) {
     if (app) {   // the write (and metadata fold) first, then the two calls
       st = gpkv_reshape_and_cache_quest(app->key, app->value, (void*)key_cache, (void*)value_cache,
@@ -250,8 +285,8 @@ static int quest_decode_run(float* out, int32_t* topk_indices, const void* query
   sp.scores = nullptr;
   sp.out = topk_indices;
   sp.q = (const unsigned short*)query;
-  sp.kmin = (const unsigned short*)key_min;
-  sp.kmax = (const unsigned short*)key_max;
+  sp.kmin = key_min;
+  sp.kmax = key_max;
   sp.bt = block_tables;
   sp.ctx = context_lens;
   sp.NB = num_blocks;
@@ -266,9 +301,9 @@ static int quest_decode_run(float* out, int32_t* topk_indices, const void* query
   c.q = (const unsigned short*)query;
   c.kc = (const unsigned char*)key_cache;
   c.vc = (const unsigned char*)value_cache;
-  c.k_scale = nullptr;
-  c.v_scale = nullptr;
-  c.row_bytes = num_kv_heads * head_dim * 2;
+  c.k_scale = fp8 ? fp8->k_scale : nullptr;
+  c.v_scale = fp8 ? fp8->v_scale : nullptr;
+  c.row_bytes = num_kv_heads * head_dim * eb;
   c.block_bytes = (long long)block_size * c.row_bytes;
   c.Hq = num_q_heads;
   c.Hkv = num_kv_heads;
@@ -281,16 +316,20 @@ static int quest_decode_run(float* out, int32_t* topk_indices, const void* query
   qp.num_slots = (long long)num_blocks * block_size;
   qp.knew = app ? (const unsigned short*)app->key : nullptr;
   qp.vnew = app ? (const unsigned short*)app->value : nullptr;
-  qp.kc_w = (unsigned short*)key_cache;   // written only by the append call
-  qp.vc_w = (unsigned short*)value_cache;
-  qp.kmin_w = (unsigned short*)key_min;
-  qp.kmax_w = (unsigned short*)key_max;
+  qp.kc_w = (void*)key_cache;   // written only by the append calls
+  qp.vc_w = (void*)value_cache;
+  qp.kmin_w = (void*)key_min;
+  qp.kmax_w = (void*)key_max;
   const dim3 grid(num_kv_heads, batch), block(kFusedThreads);
   hipStream_t s = (hipStream_t)stream;
-  if (head_dim == 128)
-    quest_decode_fused_kernel<128><<<grid, block, lds, s>>>(qp);
+  if (head_dim == 128 && fp8)
+    quest_decode_fused_kernel<128, true><<<grid, block, lds, s>>>(qp);
+  else if (head_dim == 128)
+    quest_decode_fused_kernel<128, false><<<grid, block, lds, s>>>(qp);
+  else if (fp8)
+    quest_decode_fused_kernel<64, true><<<grid, block, lds, s>>>(qp);
   else
-    quest_decode_fused_kernel<64><<<grid, block, lds, s>>>(qp);
+    quest_decode_fused_kernel<64, false><<<grid, block, lds, s>>>(qp);
   return check_launch(fn);
 }
 
@@ -304,10 +343,11 @@ extern "C" int gpkv_quest_decode(float* out, int32_t* topk_indices, const void* 
                                  int32_t topk_blocks, float scale, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   clear_error();
-  return quest_decode_run(out, topk_indices, query, key_cache, value_cache, key_min, key_max,
-                          block_tables, context_lens, batch, num_q_heads, num_kv_heads, head_dim,
-                          block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                          topk_blocks, scale, workspace, workspace_bytes, stream, nullptr);
+  return quest_decode_run("quest_decode", out, topk_indices, query, key_cache, value_cache,
+                          key_min, key_max, block_tables, context_lens, batch, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                          max_context_len, topk_blocks, scale, workspace, workspace_bytes, stream,
+                          nullptr, nullptr);
 }
 
 extern "C" int gpkv_quest_decode_append(float* out, int32_t* topk_indices, const void* query,
@@ -322,8 +362,51 @@ extern "C" int gpkv_quest_decode_append(float* out, int32_t* topk_indices, const
                                         size_t workspace_bytes, void* stream) {
   clear_error();
   QuestAppend app{key, value, slot_mapping};
-  return quest_decode_run(out, topk_indices, query, key_cache, value_cache, key_min, key_max,
-                          block_tables, context_lens, batch, num_q_heads, num_kv_heads, head_dim,
-                          block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                          topk_blocks, scale, workspace, workspace_bytes, stream, &app);
+  return quest_decode_run("quest_decode_append", out, topk_indices, query, key_cache,
+                          value_cache, key_min, key_max, block_tables, context_lens, batch,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, max_context_len, topk_blocks, scale, workspace,
+                          workspace_bytes, stream, &app, nullptr);
+}
+
+extern "C" int gpkv_quest_decode_fp8(float* out, int32_t* topk_indices, const void* query,
+                                     const void* key_cache, const void* value_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const void* key_min, const void* key_max,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     int32_t topk_blocks, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  clear_error();
+  QuestFp8 f{k_scale, v_scale};
+  return quest_decode_run("quest_decode_fp8", out, topk_indices, query, key_cache, value_cache,
+                          key_min, key_max, block_tables, context_lens, batch, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                          max_context_len, topk_blocks, scale, workspace, workspace_bytes, stream,
+                          nullptr, &f);
+}
+
+extern "C" int gpkv_quest_decode_fp8_append(float* out, int32_t* topk_indices, const void* query,
+                                            const void* key, const void* value, void* key_cache,
+                                            void* value_cache, const float* k_scale,
+                                            const float* v_scale, void* key_min, void* key_max,
+                                            const int64_t* slot_mapping,
+                                            const int32_t* block_tables,
+                                            const int32_t* context_lens, int32_t batch,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t block_size,
+                                            int64_t num_blocks, int32_t max_blocks_per_seq,
+                                            int32_t max_context_len, int32_t topk_blocks,
+                                            float scale, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  clear_error();
+  QuestAppend app{key, value, slot_mapping};
+  QuestFp8 f{k_scale, v_scale};
+  return quest_decode_run("quest_decode_fp8_append", out, topk_indices, query, key_cache,
+                          value_cache, key_min, key_max, block_tables, context_lens, batch,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, max_context_len, topk_blocks, scale, workspace,
+                          workspace_bytes, stream, &app, &f);
 }

@@ -21,6 +21,53 @@ namespace gpkv {
 // non-temporal loads measured faster than default-policy ones here too.
 __device__ __forceinline__ u32x4 meta_load(const u32x4* ptr) { return __builtin_nontemporal_load(ptr); }
 
+// Eight channels of a metadata row starting at element `elem` (a multiple of 8):
+// 16 bytes of bf16, or 8 bytes of E4M3 codes in words 0 and 1.
+template <bool FP8>
+__device__ __forceinline__ u32x4 meta_load8(const void* base, size_t elem) {
+  if constexpr (FP8) {
+    const u32x2 x = __builtin_nontemporal_load((const u32x2*)((const unsigned char*)base + elem));
+    return u32x4{x[0], x[1], 0u, 0u};
+  } else {
+    return meta_load((const u32x4*)((const unsigned short*)base + elem));
+  }
+}
+
+// A block's bound over the lane's D / 8 channels (64v + 8 sub .. + 8 for v < D / 64):
+// kmax against the positive query sums, kmin against the negative ones.
+template <int D, bool FP8>
+__device__ __forceinline__ double bound_lane(const u32x4 (&mn)[D / 64], const u32x4 (&mx)[D / 64],
+                                             const double* s_pos, const double* s_neg, int sub) {
+  double acc = 0.0;
+#pragma unroll
+  for (int v = 0; v < D / 64; ++v) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {   // word h: channels 4h .. 4h + 3, as bf16 pairs
+        const u32x2 lo = e4m3x4_to_bf16(mn[v][h]), hi = e4m3x4_to_bf16(mx[v][h]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int j = (v * 8 + 4 * h + 2 * k) * 8 + sub;   // qb_index of channel 64v + 8 sub + 4h + 2k
+          acc = fma((double)bf16_lo(hi[k]), s_pos[j], acc);
+          acc = fma((double)bf16_lo(lo[k]), s_neg[j], acc);
+          acc = fma((double)bf16_hi(hi[k]), s_pos[j + 8], acc);
+          acc = fma((double)bf16_hi(lo[k]), s_neg[j + 8], acc);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = (v * 8 + 2 * k) * 8 + sub;   // qb_index of channel 64v + 8 sub + 2k
+        acc = fma((double)bf16_lo(mx[v][k]), s_pos[j], acc);
+        acc = fma((double)bf16_lo(mn[v][k]), s_neg[j], acc);
+        acc = fma((double)bf16_hi(mx[v][k]), s_pos[j + 8], acc);
+        acc = fma((double)bf16_hi(mn[v][k]), s_neg[j + 8], acc);
+      }
+    }
+  }
+  return acc;
+}
+
 // ---------------------------------------------------------------------------
 // Scores: one float64 per (sequence, KV head, logical block)
 // ---------------------------------------------------------------------------
@@ -38,8 +85,8 @@ struct ScoreParams {
   double* scores;              // [B, H_kv, max_blocks] (two-kernel path)
   int* out;                    // [B, H_kv, K] (fused path)
   const unsigned short* q;     // [B, H_q, D]
-  const unsigned short* kmin;  // [NB, H_kv, D]
-  const unsigned short* kmax;
+  const void* kmin;            // [NB, H_kv, D] bf16, or E4M3 codes (the FP8 kernels)
+  const void* kmax;
   const int* bt;
   const int* ctx;
   long long NB;
@@ -110,8 +157,8 @@ __device__ __forceinline__ void query_bounds(const ScoreParams& p, int b, int g,
 // merge the eight partial sums. pb_at(lb) gives the physical block of lb < nb (any
 // value outside [0, NB) scores as -inf). Calls emit(lb, key) from the sub == 0 lane
 // of every block lb < nb. Every lane of the workgroup must call this with the same
-// lb0.
-template <int D, int UNROLL, class PbAt, class Emit>
+// lb0. FP8: the metadata holds E4M3 codes and the bound is taken on their values.
+template <int D, bool FP8, int UNROLL, class PbAt, class Emit>
 __device__ __forceinline__ void score_blocks(const ScoreParams& p, int g, int nb, int lb0,
                                              const PbAt& pb_at, const double* s_pos,
                                              const double* s_neg, const Emit& emit) {
@@ -128,24 +175,13 @@ __device__ __forceinline__ void score_blocks(const ScoreParams& p, int g, int nb
     const size_t o = ((size_t)(ok[u] ? pb : 0) * p.Hkv + g) * D + (size_t)sub * 8;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      mn[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmin + o + 64 * v)) : u32x4{0, 0, 0, 0};
-      mx[u][v] = ok[u] ? meta_load((const u32x4*)(p.kmax + o + 64 * v)) : u32x4{0, 0, 0, 0};
+      mn[u][v] = ok[u] ? meta_load8<FP8>(p.kmin, o + 64 * v) : u32x4{0, 0, 0, 0};
+      mx[u][v] = ok[u] ? meta_load8<FP8>(p.kmax, o + 64 * v) : u32x4{0, 0, 0, 0};
     }
   }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    double acc = 0.0;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = (v * 8 + 2 * k) * 8 + sub;   // qb_index of channel 64v + 8 sub + 2k
-        acc = fma((double)bf16_lo(mx[u][v][k]), s_pos[j], acc);
-        acc = fma((double)bf16_lo(mn[u][v][k]), s_neg[j], acc);
-        acc = fma((double)bf16_hi(mx[u][v][k]), s_pos[j + 8], acc);
-        acc = fma((double)bf16_hi(mn[u][v][k]), s_neg[j + 8], acc);
-      }
-    }
+    double acc = bound_lane<D, FP8>(mn[u], mx[u], s_pos, s_neg, sub);
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 4);

@@ -82,6 +82,37 @@ __global__ __launch_bounds__(64) void reshape_and_cache_fp8_kernel(
   }
 }
 
+// FP8 write path with the Quest fold: each row is quantised as above and its codes
+// fold into the block's E4M3 key min / max (fold_min_max_e4m3: row 0 starts the
+// block's metadata afresh, a later row takes the min / max of values).
+__global__ __launch_bounds__(64) void reshape_and_cache_fp8_quest_kernel(
+    const u32x4* __restrict__ key, const u32x4* __restrict__ value, u32x4* __restrict__ key_cache,
+    u32x4* __restrict__ value_cache, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, u32x4* __restrict__ key_min, u32x4* __restrict__ key_max,
+    const int64_t* __restrict__ slot_mapping, int row_vec8, int head_dim, int block_size,
+    long long num_slots) {
+  const int i = blockIdx.x;
+  const long long s = slot_mapping[i];
+  if (s < 0 || s >= num_slots) return;
+  const long long blk = s / block_size;
+  const long long off = s - blk * block_size;
+  const int row_vec = row_vec8 / 2;
+  const size_t dst = (size_t)s * (size_t)row_vec;
+  const size_t src = (size_t)i * (size_t)row_vec8;
+  const size_t meta = (size_t)blk * (size_t)row_vec;
+  for (int c = threadIdx.x; c < row_vec; c += 64) {
+    const int g = (16 * c) / head_dim;
+    const float kinv = 1.0f / k_scale[g], vinv = 1.0f / v_scale[g];
+    const u32x4 k = quantize16(key[src + 2 * c], key[src + 2 * c + 1], kinv);
+    key_cache[dst + c] = k;
+    value_cache[dst + c] = quantize16(value[src + 2 * c], value[src + 2 * c + 1], vinv);
+    u32x4 mn = k, mx = k;
+    if (off > 0) fold_min_max_e4m3(k, key_min[meta + c], key_max[meta + c], mn, mx);
+    key_min[meta + c] = mn;
+    key_max[meta + c] = mx;
+  }
+}
+
 }  // namespace gpkv
 
 extern "C" int gpkv_reshape_and_cache(const void* key, const void* value, void* key_cache,
@@ -159,4 +190,34 @@ extern "C" int gpkv_reshape_and_cache_fp8(const void* key, const void* value, vo
       (const u32x4*)key, (const u32x4*)value, (u32x4*)key_cache, (u32x4*)value_cache, k_scale,
       v_scale, slot_mapping, row_vec8, head_dim, block_size, (long long)num_blocks * block_size);
   return check_launch("reshape_and_cache_fp8");
+}
+
+extern "C" int gpkv_reshape_and_cache_fp8_quest(const void* key, const void* value,
+                                                void* key_cache, void* value_cache,
+                                                const float* k_scale, const float* v_scale,
+                                                void* key_min, void* key_max,
+                                                const int64_t* slot_mapping, int32_t num_tokens,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int64_t num_blocks,
+                                                void* stream) {
+  using namespace gpkv;
+  clear_error();
+  const char* fn = "reshape_and_cache_fp8_quest";
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
+    return fail(GPKV_ERR_SHAPE, "%s: num_tokens=%d num_kv_heads=%d num_blocks=%lld", fn,
+                num_tokens, num_kv_heads, (long long)num_blocks);
+  if (!supported_head_dim(head_dim))
+    return fail(GPKV_ERR_UNSUPPORTED, "%s: head_dim=%d (64 or 128)", fn, head_dim);
+  if (!supported_block_size(block_size))
+    return fail(GPKV_ERR_UNSUPPORTED, "%s: block_size=%d (16/32/64/128)", fn, block_size);
+  if (num_tokens == 0) return GPKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !k_scale || !v_scale || !key_min ||
+      !key_max || !slot_mapping)
+    return fail(GPKV_ERR_NULL, "%s: null pointer argument", fn);
+  const int row_vec8 = num_kv_heads * head_dim / 8;
+  reshape_and_cache_fp8_quest_kernel<<<dim3(num_tokens), dim3(64), 0, (hipStream_t)stream>>>(
+      (const u32x4*)key, (const u32x4*)value, (u32x4*)key_cache, (u32x4*)value_cache, k_scale,
+      v_scale, (u32x4*)key_min, (u32x4*)key_max, slot_mapping, row_vec8, head_dim, block_size,
+      (long long)num_blocks * block_size);
+  return check_launch(fn);
 }

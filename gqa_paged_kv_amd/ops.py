@@ -472,6 +472,141 @@ def sparse_paged_attention_decode_fp8(query, key_cache, value_cache, k_scale, v_
 
 
 # ---------------------------------------------------------------------------
+# Quest over E4M3 caches: the metadata holds uint8 codes of the key code extremes
+# ---------------------------------------------------------------------------
+
+def _meta_fp8(fn, key_min, key_max, NB, Hkv, D):
+    _dev("key_min", key_min, torch.uint8, 3)
+    _dev("key_max", key_max, torch.uint8, 3)
+    if key_min.shape != key_max.shape or tuple(key_min.shape) != (NB, Hkv, D):
+        raise ValueError(f"{fn}: key_min / key_max must be [num_blocks, H_kv, D] uint8")
+
+
+def quest_block_metadata_fp8(key_cache, block_tables, context_lens, key_min, key_max, *,
+                             max_context_len: int, last_block_only: bool = False,
+                             stream=None) -> None:
+    """quest_block_metadata over an E4M3 key cache: codes of each channel's extremes."""
+    _dev("key_cache", key_cache, torch.uint8, 4)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    NB, bs, Hkv, D = _cache_dims(key_cache)
+    _meta_fp8("quest_block_metadata_fp8", key_min, key_max, NB, Hkv, D)
+    B = int(context_lens.shape[0])
+    if block_tables.shape[0] != B:
+        raise ValueError("quest_block_metadata_fp8: inconsistent shapes")
+    _check(lib().gpkv_quest_block_metadata_fp8(
+        _ptr(key_min), _ptr(key_max), _ptr(key_cache), _ptr(block_tables), _ptr(context_lens), B,
+        Hkv, D, bs, NB, int(block_tables.shape[1]), int(max_context_len),
+        1 if last_block_only else 0, _stream(stream)))
+
+
+def reshape_and_cache_fp8_quest(key, value, key_cache, value_cache, k_scale, v_scale, key_min,
+                                key_max, slot_mapping, *, stream=None) -> None:
+    """reshape_and_cache_fp8 plus the fold of each written key row's codes into its
+    block's code metadata."""
+    _dev("key_cache", key_cache, torch.uint8, 4)
+    _dev("value_cache", value_cache, torch.uint8, 4)
+    _dev("key", key, torch.bfloat16, 3)
+    _dev("value", value, torch.bfloat16, 3)
+    _dev("slot_mapping", slot_mapping, torch.int64, 1)
+    NB, bs, Hkv, D = _cache_dims(key_cache)
+    _scales(k_scale, v_scale, Hkv)
+    _meta_fp8("reshape_and_cache_fp8_quest", key_min, key_max, NB, Hkv, D)
+    T = key.shape[0]
+    if value_cache.shape != key_cache.shape or key.shape != (T, Hkv, D) or value.shape != key.shape \
+            or slot_mapping.shape[0] != T:
+        raise ValueError("reshape_and_cache_fp8_quest: inconsistent shapes")
+    _check(lib().gpkv_reshape_and_cache_fp8_quest(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(key_min), _ptr(key_max), _ptr(slot_mapping), T, Hkv, D, bs, NB, _stream(stream)))
+
+
+def quest_select_topk_fp8(query, key_min, key_max, block_tables, context_lens, *, block_size: int,
+                          topk_blocks: int, max_context_len: int, out=None, workspace=None,
+                          stream=None) -> torch.Tensor:
+    """quest_select_topk over E4M3 code metadata; returns [B, H_kv, topk_blocks] int32."""
+    _dev("query", query, torch.bfloat16, 3)
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("context_lens", context_lens, torch.int32, 1)
+    NB, Hkv, D = (int(x) for x in key_min.shape)
+    _meta_fp8("quest_select_topk_fp8", key_min, key_max, NB, Hkv, D)
+    B, Hq, Dq = query.shape
+    MB = int(block_tables.shape[1])
+    if Dq != D or block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("quest_select_topk_fp8: inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, Hkv, int(topk_blocks)), dtype=torch.int32, device=query.device)
+    _dev("out", out, torch.int32, 3)
+    ws = _workspace(quest_select_workspace_bytes(B, Hkv, MB), query.device, workspace)
+    _check(lib().gpkv_quest_select_topk_fp8(
+        _ptr(out), _ptr(query), _ptr(key_min), _ptr(key_max), _ptr(block_tables),
+        _ptr(context_lens), B, Hq, Hkv, D, int(block_size), NB, MB, int(max_context_len),
+        int(topk_blocks), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def _quest_outputs(fn, query, B, Hq, Hkv, D, K, out, topk_out):
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=query.device)
+    if topk_out is None:
+        topk_out = torch.empty((B, Hkv, K), dtype=torch.int32, device=query.device)
+    _dev("out", out, torch.float32, 3)
+    _dev("topk_out", topk_out, torch.int32, 3)
+    if tuple(topk_out.shape) != (B, Hkv, K):
+        raise ValueError(f"{fn}: topk_out must be [B, H_kv, topk_blocks]")
+    return out, topk_out
+
+
+def quest_decode_fp8(query, key_cache, value_cache, k_scale, v_scale, key_min, key_max,
+                     block_tables, context_lens, *, topk_blocks: int, max_context_len: int,
+                     scale: float, out=None, topk_out=None, workspace=None, stream=None):
+    """quest_decode over E4M3 caches and code metadata; returns (out, topk_indices) as
+    quest_select_topk_fp8 followed by sparse_paged_attention_decode_fp8."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks_fp8(query, key_cache, value_cache, k_scale, v_scale,
+                                                 block_tables, context_lens)
+    _meta_fp8("quest_decode_fp8", key_min, key_max, NB, Hkv, D)
+    K = int(topk_blocks)
+    out, topk_out = _quest_outputs("quest_decode_fp8", query, B, Hq, Hkv, D, K, out, topk_out)
+    ws = _workspace(quest_decode_workspace_bytes(B, Hq, Hkv, D, bs, MB, K), query.device,
+                    workspace)
+    _check(lib().gpkv_quest_decode_fp8(
+        _ptr(out), _ptr(topk_out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(key_min), _ptr(key_max), _ptr(block_tables), _ptr(context_lens), B,
+        Hq, Hkv, D, bs, NB, MB, int(max_context_len), K, float(scale), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return out, topk_out
+
+
+def quest_decode_fp8_append(query, key, value, key_cache, value_cache, k_scale, v_scale, key_min,
+                            key_max, slot_mapping, block_tables, context_lens, *,
+                            topk_blocks: int, max_context_len: int, scale: float, out=None,
+                            topk_out=None, workspace=None, stream=None):
+    """The FP8 Quest step with its cache write: reshape_and_cache_fp8_quest of token b of
+    key / value (bf16, sequence b's newest token) at slot_mapping[b], then
+    quest_decode_fp8 over the written caches; returns (out, topk_indices)."""
+    B, Hq, Hkv, D, bs, NB, MB = _attn_checks_fp8(query, key_cache, value_cache, k_scale, v_scale,
+                                                 block_tables, context_lens)
+    _dev("key", key, torch.bfloat16, 3)
+    _dev("value", value, torch.bfloat16, 3)
+    _dev("slot_mapping", slot_mapping, torch.int64, 1)
+    _meta_fp8("quest_decode_fp8_append", key_min, key_max, NB, Hkv, D)
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape[0] != B:
+        raise ValueError("quest_decode_fp8_append: key / value / slot_mapping must hold one "
+                         "token per sequence")
+    K = int(topk_blocks)
+    out, topk_out = _quest_outputs("quest_decode_fp8_append", query, B, Hq, Hkv, D, K, out,
+                                   topk_out)
+    ws = _workspace(quest_decode_workspace_bytes(B, Hq, Hkv, D, bs, MB, K), query.device,
+                    workspace)
+    _check(lib().gpkv_quest_decode_fp8_append(
+        _ptr(out), _ptr(topk_out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache),
+        _ptr(value_cache), _ptr(k_scale), _ptr(v_scale), _ptr(key_min), _ptr(key_max),
+        _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs, NB, MB,
+        int(max_context_len), K, float(scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, topk_out
+
+
+# ---------------------------------------------------------------------------
 # Multi-token queries (varlen, causal mask aligned to the right)
 # ---------------------------------------------------------------------------
 

@@ -395,6 +395,81 @@ int gpkv_sparse_paged_attention_decode_fp8(float* out, const void* query, const 
                                            float scale, void* workspace,
                                            size_t workspace_bytes, void* stream);
 
+/* Quest over E4M3 caches ([ASC] "Quest Sparse Attention" with the FP8 cache above).
+ * The pages give the metadata and the bound for one key format; for E4M3 keys this
+ * library keeps, per (physical block, KV head, channel), the CODES of the smallest
+ * and largest key code value over the block's valid rows (one byte each, half the
+ * bf16 metadata's bytes). A key is code * k_scale[g] with k_scale[g] > 0, so these
+ * are the keys' extremes divided by the scale. The block score is the Quest bound
+ * over the code values:
+ *   score(lb) = sum over h in group g, c of max(q[b,h,c] * val(key_min[pb,g,c]),
+ *                                               q[b,h,c] * val(key_max[pb,g,c]))
+ * in float64: the bound on the keys divided by k_scale[g], one positive factor for
+ * every block of a KV head, so the selection (per KV head) is the same. A zero
+ * extreme may be stored as either zero code (0x00 or 0x80); NaN codes are not
+ * supported in the caches (they would order past +-448).
+ * key_min, key_max: [num_blocks, num_kv_heads, head_dim] uint8 E4M3 codes.
+ *
+ * gpkv_quest_block_metadata_fp8: gpkv_quest_block_metadata over an E4M3 key_cache
+ *   [num_blocks, block_size, num_kv_heads, head_dim] uint8, writing code metadata. */
+int gpkv_quest_block_metadata_fp8(void* key_min, void* key_max, const void* key_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t batch, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  int32_t last_block_only, void* stream);
+
+/* gpkv_reshape_and_cache_fp8 plus the fold of each written key row's codes into its
+ * block's code metadata, as gpkv_reshape_and_cache_quest folds bf16 rows (row 0 of
+ * a block starts its metadata afresh; a later row takes the min / max by value). */
+int gpkv_reshape_and_cache_fp8_quest(const void* key, const void* value, void* key_cache,
+                                     void* value_cache, const float* k_scale,
+                                     const float* v_scale, void* key_min, void* key_max,
+                                     const int64_t* slot_mapping, int32_t num_tokens,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int64_t num_blocks, void* stream);
+
+/* gpkv_quest_select_topk over code metadata (the score above); the same workspace
+ * (gpkv_quest_select_workspace_bytes), tie rule, output and errors. */
+int gpkv_quest_select_topk_fp8(int32_t* topk_indices, const void* query, const void* key_min,
+                               const void* key_max, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, int32_t topk_blocks, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* gpkv_quest_decode over E4M3 caches and code metadata: the result of
+ * gpkv_quest_select_topk_fp8 followed by gpkv_sparse_paged_attention_decode_fp8, in
+ * one launch under the same rule as gpkv_quest_decode (with the pair's bytes at one
+ * byte per element), else those two calls. Workspace from
+ * gpkv_quest_decode_workspace_bytes. */
+int gpkv_quest_decode_fp8(float* out, int32_t* topk_indices, const void* query,
+                          const void* key_cache, const void* value_cache, const float* k_scale,
+                          const float* v_scale, const void* key_min, const void* key_max,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                          int32_t topk_blocks, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* gpkv_quest_decode_append over E4M3 caches: gpkv_reshape_and_cache_fp8_quest over the
+ * batch's new tokens (key, value bf16 as there), then gpkv_quest_decode_fp8; on the
+ * one-launch path each (sequence, KV head) workgroup quantises and writes its head's
+ * part of the row and folds its codes before it scores. The caches end bit for bit
+ * as after the two calls, the metadata equal by value. */
+int gpkv_quest_decode_fp8_append(float* out, int32_t* topk_indices, const void* query,
+                                 const void* key, const void* value, void* key_cache,
+                                 void* value_cache, const float* k_scale, const float* v_scale,
+                                 void* key_min, void* key_max, const int64_t* slot_mapping,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 int32_t topk_blocks, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Multi-token queries (varlen batches: [TL18] 2.7 continuous batching with
  * ragged lengths; 3.3 flattened queries with cu_seqlens and the causal mask

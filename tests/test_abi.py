@@ -29,7 +29,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(L):
     from gqa_paged_kv_amd._lib import SIGNATURES
     names = declared_symbols()
-    assert len(names) == 24
+    assert len(names) == 29
     for n in names:
         assert hasattr(L, n), n
     assert sorted(SIGNATURES) == names
@@ -175,6 +175,51 @@ def test_quest_append_argument_checks(L):
     assert call(K=0) == -2
     assert call(ws=16) == -4
     assert call(B=0, key=None, slots=None) == 0
+
+
+def test_quest_fp8_argument_checks(L):
+    """Quest over E4M3 caches: scales and metadata required, shapes and sizes checked as
+    for the bf16 calls, all refused on the host (an empty batch launches nothing)."""
+    m = L.gpkv_quest_block_metadata_fp8
+    assert m(None, 8, 8, 8, 8, 2, 1, 64, 16, 16, 5, 80, 0, None) == -1
+    assert m(8, 8, 8, 8, 8, 2, 1, 96, 16, 16, 5, 80, 0, None) == -3
+    assert m(8, 8, 8, 8, 8, 2, 1, 64, 16, 16, 5, 81, 0, None) == -2    # past the table
+    assert m(None, None, None, None, None, 0, 1, 64, 16, 16, 5, 80, 0, None) == 0
+    w = L.gpkv_reshape_and_cache_fp8_quest
+    assert w(8, 8, 8, 8, None, 8, 8, 8, 8, 2, 1, 64, 16, 16, None) == -1    # k_scale
+    assert w(8, 8, 8, 8, 8, 8, None, 8, 8, 2, 1, 64, 16, 16, None) == -1    # key_min
+    assert w(8, 8, 8, 8, 8, 8, 8, 8, 8, 2, 1, 64, 24, 16, None) == -3
+    assert w(None, None, None, None, None, None, None, None, None, 0, 1, 64, 16, 16, None) == 0
+    t = L.gpkv_quest_select_topk_fp8
+    assert t(8, 8, None, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 3, 8, 1 << 30, None) == -1
+    assert t(8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 0, 8, 1 << 30, None) == -2
+    assert t(8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 3, 8, 8, None) == -4
+    d = L.gpkv_quest_decode_fp8
+    base = [8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 3, 0.1, 8, 1 << 30, None]
+    for i in (1, 5, 6, 7, 8):          # topk_out, k_scale, v_scale, key_min, key_max
+        args = list(base)
+        args[i] = None
+        assert d(*args) == -1, i
+    args = list(base)
+    args[19] = 0
+    assert d(*args) == -2
+    args = list(base)
+    args[22] = 16
+    assert d(*args) == -4
+    a = L.gpkv_quest_decode_fp8_append
+    base = [8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 2, 4, 1, 64, 16, 16, 5, 80, 3, 0.1, 8,
+            1 << 30, None]
+    for i in (3, 4, 7, 8, 11):         # key, value, k_scale, v_scale, slot_mapping
+        args = list(base)
+        args[i] = None
+        assert a(*args) == -1, i
+    args = list(base)
+    args[25] = 16
+    assert a(*args) == -4
+    args = list(base)
+    args[14] = 0
+    args[3] = args[11] = None
+    assert a(*args) == 0
 
 
 def test_noalloc_argument_checks(L):
