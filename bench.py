@@ -297,10 +297,40 @@ def per_config_block(cfg, flush, stream, steps):
         res["quest_pct_of_peak"] = round(100 * res["quest_gbps"] / R.MI355X_HBM_GBPS, 1)
         res["quest_step_us"] = round(write_us + t["us_mean"], 2)
         res["quest_step_speedup_vs_dense_step"] = round(res["dense_step_us"] / res["quest_step_us"], 2)
+        # The same Quest call over E4M3 copies of the caches and their code metadata.
+        kc8, vc8, ks8, vs8 = fp8_copy(gp, kc, vc)
+        kmin8 = torch.empty(kmin.shape, dtype=torch.uint8, device="cuda")
+        kmax8 = torch.empty_like(kmin8)
+        gp.quest_block_metadata_fp8(kc8, bt, ctx, kmin8, kmax8, max_context_len=mcl)
+        t = time_alone(lambda: gp.quest_decode_fp8(q, kc8, vc8, ks8, vs8, kmin8, kmax8, bt, ctx,
+                                                   topk_blocks=K, max_context_len=mcl,
+                                                   scale=scale, out=out_s, topk_out=sel,
+                                                   workspace=wq), flush, stream, steps)
+        qb8 = (R.select_bytes(w.context_lens, bs, Hkv, D, elem_bytes=1)
+               + R.sparse_attention_bytes(sel.cpu().numpy(), w.context_lens, bs, D, elem_bytes=1))
+        res["quest_fp8_call_us"] = t["us_mean"]
+        res["quest_fp8_gbps"] = round(qb8 / (t["us_mean"] * 1e-6) / 1e9, 1)
+        del kc8, vc8, kmin8, kmax8
     del kc, vc, q, bt, ctx, out, ws
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def fp8_copy(gp, kc, vc):
+    """E4M3 copies of bf16 caches written by the FP8 write call over every slot, with
+    per-KV-head scales amax / 256 (the largest values land near 256 of E4M3's 448)."""
+    import torch
+    NB, bs, Hkv, D = kc.shape
+
+    def amax_scale(t):
+        return (t.float().abs().amax(dim=(0, 1, 3)) / 256.0).clamp_min(1e-3).contiguous()
+    ks8, vs8 = amax_scale(kc), amax_scale(vc)
+    kc8 = torch.empty(kc.shape, dtype=torch.uint8, device="cuda")
+    vc8 = torch.empty_like(kc8)
+    gp.reshape_and_cache_fp8(kc.view(NB * bs, Hkv, D), vc.view(NB * bs, Hkv, D), kc8, vc8, ks8,
+                             vs8, torch.arange(NB * bs, dtype=torch.int64, device="cuda"))
+    return kc8, vc8, ks8, vs8
 
 
 def main():
@@ -504,14 +534,7 @@ def main():
     # write (every slot), then its write and dense calls timed like the bf16 ones.
     fp8 = None
     if not args.no_fp8:
-        kc8 = torch.empty(kc.shape, dtype=torch.uint8, device="cuda")
-        vc8 = torch.empty_like(kc8)
-        def amax_scale(t):
-            return (t.float().abs().amax(dim=(0, 1, 3)) / 256.0).clamp_min(1e-3).contiguous()
-        ks8, vs8 = amax_scale(kc), amax_scale(vc)
-        NBs = kc.shape[0] * kc.shape[1]
-        gp.reshape_and_cache_fp8(kc.view(NBs, Hkv, D), vc.view(NBs, Hkv, D), kc8, vc8, ks8, vs8,
-                                 torch.arange(NBs, dtype=torch.int64, device="cuda"))
+        kc8, vc8, ks8, vs8 = fp8_copy(gp, kc, vc)
         out8 = torch.empty_like(out_d)
         fcalls = {
             "reshape_and_cache_fp8": lambda: gp.reshape_and_cache_fp8(nk, nv, kc8, vc8, ks8, vs8,
@@ -529,6 +552,25 @@ def main():
                 out=out8, workspace=ws_d)
             fbytes["paged_attention_decode_fp8_append"] = (fbytes["reshape_and_cache_fp8"]
                                                            + fbytes["paged_attention_decode_fp8"])
+        if K:   # Quest over the E4M3 caches: code metadata built once (prefill work)
+            kmin8 = torch.empty(kmin.shape, dtype=torch.uint8, device="cuda")
+            kmax8 = torch.empty_like(kmin8)
+            gp.quest_block_metadata_fp8(kc8, bt, ctx, kmin8, kmax8, max_context_len=mcl)
+            sel8, out8s = torch.empty_like(sel), torch.empty_like(out_s)
+            fcalls["quest_decode_fp8"] = lambda: gp.quest_decode_fp8(
+                q, kc8, vc8, ks8, vs8, kmin8, kmax8, bt, ctx, topk_blocks=K, max_context_len=mcl,
+                scale=scale, out=out8s, topk_out=sel8, workspace=ws_qd)
+            fcalls["quest_decode_fp8"]()
+            q8 = (R.select_bytes(w.context_lens, bs, Hkv, D, elem_bytes=1)
+                  + R.sparse_attention_bytes(sel8.cpu().numpy(), w.context_lens, bs, D,
+                                             elem_bytes=1))
+            fbytes["quest_decode_fp8"] = q8
+            if w.num_tokens and w.num_tokens == B:   # the FP8 Quest step as one call
+                fcalls["quest_decode_fp8_append"] = lambda: gp.quest_decode_fp8_append(
+                    q, nk, nv, kc8, vc8, ks8, vs8, kmin8, kmax8, slots, bt, ctx, topk_blocks=K,
+                    max_context_len=mcl, scale=scale, out=out8s, topk_out=sel8, workspace=ws_qd)
+                fbytes["quest_decode_fp8_append"] = q8 + R.fused_write_bytes_fp8(
+                    w.slot_mapping, w.num_blocks, bs, Hkv, D)
         fp8 = {}
         for name, f in fcalls.items():
             for _ in range(3):
@@ -548,6 +590,8 @@ def main():
                          "pct_of_peak": round(100 * fbytes[name] / (t * 1e-6) / 1e9
                                               / R.MI355X_HBM_GBPS, 1)}
         del kc8, vc8
+        if K:
+            del kmin8, kmax8
 
     # Multi-token queries on the same caches: a mixed batch in which six sequences
     # bring prefill chunks (the newest positions of their contexts) and the rest

@@ -73,19 +73,35 @@ def metadata_full_bytes(context_lens, block_size: int, num_kv_heads: int, head_d
     return int(ctx.sum()) * row + int(nb.sum()) * 2 * row
 
 
-def select_bytes(context_lens, block_size: int, num_kv_heads: int, head_dim: int) -> int:
-    """Scan the key min/max of every valid block of every (sequence, KV head)."""
+def select_bytes(context_lens, block_size: int, num_kv_heads: int, head_dim: int,
+                 elem_bytes: int = BF16) -> int:
+    """Scan the key min/max of every valid block of every (sequence, KV head)
+    (elem_bytes 1: E4M3 code metadata)."""
     ctx = np.asarray(context_lens, dtype=np.int64)
     nb = (ctx + block_size - 1) // block_size
-    return int(nb.sum()) * num_kv_heads * 2 * head_dim * BF16
+    return int(nb.sum()) * num_kv_heads * 2 * head_dim * elem_bytes
 
 
-def sparse_attention_bytes(topk_indices, context_lens, block_size: int, head_dim: int) -> int:
-    """K + V of the valid tokens of every selected block, per KV head."""
+def fused_write_bytes_fp8(slot_mapping, num_blocks: int, block_size: int, num_kv_heads: int,
+                          head_dim: int) -> int:
+    """The FP8 write (bf16 rows in, E4M3 codes out) with the code metadata fold: per
+    written token its block's min / max code rows, read when the token is not at row 0
+    of its block, always written."""
+    s = np.asarray(slot_mapping, dtype=np.int64)
+    s = s[(s >= 0) & (s < num_blocks * block_size)]
+    row = num_kv_heads * head_dim          # bytes of one code row
+    folded = int((s % block_size != 0).sum())
+    return int(s.size) * (2 * row * BF16 + 2 * row) + folded * 2 * row + int(s.size) * 2 * row
+
+
+def sparse_attention_bytes(topk_indices, context_lens, block_size: int, head_dim: int,
+                           elem_bytes: int = BF16) -> int:
+    """K + V of the valid tokens of every selected block, per KV head (elem_bytes 1:
+    E4M3 caches)."""
     sel = np.asarray(topk_indices, dtype=np.int64)
     ctx = np.asarray(context_lens, dtype=np.int64)[:, None, None]
     nb = (ctx + block_size - 1) // block_size
     ok = (sel >= 0) & (sel < nb)
     valid = np.clip(ctx - sel * block_size, 0, block_size)
     tokens = int(np.where(ok, valid, 0).sum())
-    return tokens * 2 * head_dim * BF16
+    return tokens * 2 * head_dim * elem_bytes

@@ -34,3 +34,14 @@ def test_sparse_and_metadata_accounting_by_hand():
     assert R.write_bytes([5, -1, 10**9], 16, 16, 1, 64) == 1 * 2 * 64 * 2 * 2
     # slot 5 folds into its block (row 5), slot 32 starts a block (row 0)
     assert R.fused_write_bytes([5, 32, -1], 16, 16, 1, 64) == 2 * 4 * 128 + 1 * 2 * 128 + 2 * 2 * 128
+
+
+def test_fp8_quest_accounting_by_hand():
+    # one byte per element: the selection's metadata scan and the sparse K / V halve
+    sel = np.array([[[0, 2, -1]]])
+    assert R.sparse_attention_bytes(sel, [37], 16, 64, elem_bytes=1) == (16 + 5) * 2 * 64
+    assert R.select_bytes([37, 32], 16, 1, 64, elem_bytes=1) == (3 + 2) * 2 * 64
+    # H_kv 1, D 64: per token bf16 K and V in (2 * 128 bytes), codes out (2 * 64);
+    # slot 5 folds (reads its block's two 64-byte code rows), both write two
+    assert R.fused_write_bytes_fp8([5, 32, -1], 16, 16, 1, 64) == \
+        2 * (2 * 128 + 2 * 64) + 1 * 2 * 64 + 2 * 2 * 64
