@@ -230,3 +230,125 @@ def test_graph_replay_varlen_equals_eager(schedule, monkeypatch):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {rep} differs from eager"
+
+
+# ---------------------------------------------------------------------------
+# The step over E4M3 caches (Quest with code metadata)
+# ---------------------------------------------------------------------------
+
+def _fp8_step(w, c, buf, K, one_call):
+    """The FP8 step: one_call -- quest_decode_fp8_append (write, code fold, selection,
+    sparse attention) then the FP8 dense call; else the write with the code fold, the
+    FP8 dense call, the FP8 selection and FP8 sparse attention."""
+    d, mcl, bs, scale = c.d, w.max_context_len, w.block_size, float(w.scale)
+    if one_call:
+        gp.quest_decode_fp8_append(d.q, d.nk, d.nv, c.kc, c.vc, c.d_ks, c.d_vs, buf["kmin"],
+                                   buf["kmax"], d.slots, d.bt, d.ctx, topk_blocks=K,
+                                   max_context_len=mcl, scale=scale, out=buf["out_s"],
+                                   topk_out=buf["sel"], workspace=buf["ws_qd"])
+        gp.paged_attention_decode_fp8(d.q, c.kc, c.vc, c.d_ks, c.d_vs, d.bt, d.ctx,
+                                      max_context_len=mcl, scale=scale, out=buf["out_d"],
+                                      workspace=buf["ws_d"])
+        return
+    gp.reshape_and_cache_fp8_quest(d.nk, d.nv, c.kc, c.vc, c.d_ks, c.d_vs, buf["kmin"],
+                                   buf["kmax"], d.slots)
+    gp.paged_attention_decode_fp8(d.q, c.kc, c.vc, c.d_ks, c.d_vs, d.bt, d.ctx,
+                                  max_context_len=mcl, scale=scale, out=buf["out_d"],
+                                  workspace=buf["ws_d"])
+    gp.quest_select_topk_fp8(d.q, buf["kmin"], buf["kmax"], d.bt, d.ctx, block_size=bs,
+                             topk_blocks=K, max_context_len=mcl, out=buf["sel"],
+                             workspace=buf["ws_sel"])
+    gp.sparse_paged_attention_decode_fp8(d.q, c.kc, c.vc, c.d_ks, c.d_vs, d.bt, d.ctx,
+                                         buf["sel"], max_context_len=mcl, scale=scale,
+                                         out=buf["out_s"], workspace=buf["ws_sp"])
+
+
+@pytest.mark.parametrize("case,one_call", [("random", False), ("random", True), ("long", True)])
+def test_graph_replay_fp8_equals_eager(case, one_call):
+    """The FP8 step captured and replayed four times between eager work: every output,
+    cache and code-metadata buffer equals eager bit for bit, and eager equals the
+    oracle's FP8 chain (write, code metadata, Top-K, dense and sparse attention)."""
+    from test_fp8_gpu import Fp8Case
+    w, K = _graph_case(case)
+    c = Fp8Case(w, list(range(w.batch)))
+    d = c.d
+    buf = _step_buffers_fp8(w, c, K)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _fp8_step(w, c, buf, K, one_call)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    _fp8_step(w, c, buf, K, one_call)
+    torch.cuda.synchronize()
+    snap = lambda: {k: v.clone() for k, v in (("out_d", buf["out_d"]), ("out_s", buf["out_s"]),
+                                               ("sel", buf["sel"]), ("kmin", buf["kmin"]),
+                                               ("kmax", buf["kmax"]), ("kc", c.kc), ("vc", c.vc))}
+    ref = snap()
+
+    bs = w.block_size
+    ek, ev = oracle.reshape_and_cache_fp8(c.okc, c.ovc, w.new_key, w.new_value, w.slot_mapping,
+                                          bs, c.ks, c.vs)
+    omin, omax = oracle.quest_block_metadata_fp8(ek, w.block_tables, w.context_lens, bs)
+    osel = oracle.quest_select_topk_fp8(w.query, omin, omax, w.block_tables, w.context_lens, bs, K)
+    referenced = np.unique(np.concatenate(
+        [w.block_tables[b, :-(-int(L) // bs)] for b, L in enumerate(w.context_lens)]))
+    for name, exp in (("kc", ek), ("vc", ev)):
+        assert np.array_equal(ref[name].cpu().numpy()[referenced], exp[referenced]), name
+    for name, exp in (("kmin", omin), ("kmax", omax)):
+        g, e = ref[name].cpu().numpy()[referenced], exp[referenced].copy()
+        g[g == 0x80] = 0
+        e[e == 0x80] = 0
+        assert np.array_equal(g, e), name
+    assert np.array_equal(ref["sel"].cpu().numpy(), osel), "Top-K ids differ"
+    err_d = max_abs(ref["out_d"].cpu().numpy(),
+                    oracle.paged_attention_decode_fp8(w.query, ek, ev, c.ks, c.vs, w.block_tables,
+                                                      w.context_lens, w.scale))
+    err_s = max_abs(ref["out_s"].cpu().numpy(),
+                    oracle.sparse_paged_attention_decode_fp8(w.query, ek, ev, c.ks, c.vs,
+                                                             w.block_tables, w.context_lens, osel,
+                                                             w.scale))
+    print(f"{case} FP8: dense max-abs {err_d:.3e}, sparse max-abs {err_s:.3e}")
+    assert err_d <= ATOL and err_s <= ATOL
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _fp8_step(w, c, buf, K, one_call)
+    scratch = torch.empty(1 << 20, device="cuda")
+    for rep in range(4):
+        buf["out_d"].fill_(float("nan"))
+        buf["out_s"].fill_(float("nan"))
+        buf["sel"].fill_(-7)
+        scratch.normal_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snap()
+        for k in ref:
+            assert torch.equal(got[k], ref[k]), f"replay {rep}: {k} differs from eager"
+
+
+def _step_buffers_fp8(w, c, K):
+    """The FP8 step's buffers and its prefill state: this step's tokens already in the
+    E4M3 caches and the code metadata built over them (the step is then idempotent)."""
+    B, Hq, Hkv, D, bs = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    d, mcl = c.d, w.max_context_len
+    buf = {
+        "out_d": torch.empty((B, Hq, D), dtype=torch.float32, device="cuda"),
+        "out_s": torch.empty((B, Hq, D), dtype=torch.float32, device="cuda"),
+        "ws_d": torch.zeros(gp.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl),
+                            dtype=torch.uint8, device="cuda"),
+        "ws_sel": torch.empty(gp.quest_select_workspace_bytes(B, Hkv, w.max_blocks_per_seq),
+                              dtype=torch.uint8, device="cuda"),
+        "ws_sp": torch.zeros(gp.sparse_attention_workspace_bytes(B, Hq, Hkv, D, bs, K),
+                             dtype=torch.uint8, device="cuda"),
+        "ws_qd": torch.zeros(gp.quest_decode_workspace_bytes(B, Hq, Hkv, D, bs,
+                                                             w.max_blocks_per_seq, K),
+                             dtype=torch.uint8, device="cuda"),
+        "sel": torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda"),
+        "kmin": torch.zeros((w.num_blocks, Hkv, D), dtype=torch.uint8, device="cuda"),
+        "kmax": torch.zeros((w.num_blocks, Hkv, D), dtype=torch.uint8, device="cuda"),
+    }
+    gp.reshape_and_cache_fp8(d.nk, d.nv, c.kc, c.vc, c.d_ks, c.d_vs, d.slots)
+    gp.quest_block_metadata_fp8(c.kc, d.bt, d.ctx, buf["kmin"], buf["kmax"], max_context_len=mcl)
+    return buf
