@@ -614,18 +614,15 @@ def main():
         fv = lambda: gp.paged_attention_varlen(qv, kc, vc, bt, ctx, cu_d, max_q_len=int(ql.max()),
                                                max_context_len=mcl, scale=scale, out=out_v,
                                                workspace=ws_v)
-        for _ in range(3):
-            fv()
-        ts = []
-        for k in range(args.steps):
-            flush.fill_(k & 0xFF)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fv()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        t = float(np.mean(ts))
+        t = time_alone(fv, flush, stream, args.steps)["us_mean"]
+        t8 = None
+        if not args.no_fp8:   # the same batch over E4M3 copies of the caches
+            kc8, vc8, ks8, vs8 = fp8_copy(gp, kc, vc)
+            t8 = time_alone(lambda: gp.paged_attention_varlen_fp8(
+                qv, kc8, vc8, ks8, vs8, bt, ctx, cu_d, max_q_len=int(ql.max()),
+                max_context_len=mcl, scale=scale, out=out_v, workspace=ws_v),
+                flush, stream, args.steps)["us_mean"]
+            del kc8, vc8
         kv_bytes = R.dense_attention_bytes(w.context_lens, Hkv, D)
         ctx64 = w.context_lens.astype(np.int64)
         visible = int(sum(int((ctx64[b] - ql[b] + 1 + np.arange(ql[b])).sum()) for b in range(B)))
@@ -636,7 +633,8 @@ def main():
                   "gbps_kv_once": round(kv_bytes / (t * 1e-6) / 1e9, 1),
                   "tflops": round(flops / (t * 1e-6) / 1e12, 2),
                   "pct_of_8tbps": round(100 * kv_bytes / (t * 1e-6) / 1e9 / R.MI355X_HBM_GBPS, 1),
-                  "pct_of_bf16_mfma_2500tflops": round(100 * flops / (t * 1e-6) / 1e12 / 2500.0, 2)}
+                  "pct_of_bf16_mfma_2500tflops": round(100 * flops / (t * 1e-6) / 1e12 / 2500.0, 2),
+                  "fp8_kv_us_mean": round(t8, 2) if t8 else None}
         del qv, ws_v, out_v
 
     per_call = {name: np.array([evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)])

@@ -20,7 +20,10 @@ namespace gpkv {
 // row tiles, and every 32-token K / V tile is loaded once per workgroup into LDS
 // instead of once per wave. Same arithmetic as attend_head (S^T = K Q^T and
 // O^T += V^T P^T on MFMA, P as a bf16 hi + lo pair); every wave of the workgroup
-// must call it with the same n_sub, desc and pos0 (it has barriers).
+// must call it with the same n_sub, desc and pos0 (it has barriers). E4M3 caches
+// (FP8): the staging threads load codes (half the bytes) and widen them to bf16
+// (exact) as they store, so LDS holds the same bf16 tiles; K's scale joins the
+// softmax scale and V's the final normalisation, as in attend_head.
 //
 // LDS holds two K and two V tiles:
 //   - K token-major, rows padded to 2D + 16 bytes: lane (r, qd) reads token r's
@@ -70,7 +73,7 @@ struct TileDesc {   // the two 16-token sub-tiles of one 32-token tile (wave-uni
   int pb[2], row0[2], nv[2];
 };
 
-template <int D, class Desc>
+template <int D, bool FP8, class Desc>
 __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_sub,
                                               const Desc& desc, int pos0, const RowTiles<2>& rows,
                                               unsigned char* s_kv) {
@@ -85,6 +88,9 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
   static_assert(K_PER_T >= 1 && 32 * KPIECES == K_PER_T * kWaves * 64, "K tile split");
   constexpr int VPAIRS = D / 2;              // channel pairs: one V staging item per (chunk, pair)
   static_assert(4 * VPAIRS <= kWaves * 64, "V tile split");
+  // V staging columns: channel pairs (bf16, 4 bytes per token) or channel quads (E4M3)
+  constexpr int VCOLS = FP8 ? D / 4 : VPAIRS;
+  constexpr int EB = FP8 ? 1 : 2;            // bytes per cached element
   const int tid = threadIdx.x, lane = tid & 63;
   const int r = lane & 15, qd = lane >> 4;
   const bool active = rows.n_rows[0] > 0;   // the wave's second tile is empty if its first is
@@ -94,8 +100,10 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
   const int lim_min = __builtin_amdgcn_readfirstlane(rows.limit[0]);
   // Scores are scaled inside the exponent's FMA, by |scale|; a negative scale
   // flips the sign of q instead (exact in bf16).
-  const float scl = fabsf(c.qk_scale_log2);
-  const unsigned qflip = c.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
+  float qks = c.qk_scale_log2;
+  if constexpr (FP8) qks *= c.k_scale[g];
+  const float scl = fabsf(qks);
+  const unsigned qflip = qks < 0.f ? 0x80008000u : 0u;
   unsigned char* const kbuf = s_kv;
   unsigned char* const vbuf = s_kv + 2 * KTILEB;
 
@@ -148,8 +156,14 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
       const int tok = pc / KPIECES, piece = pc - tok * KPIECES;
       // D = 128: piece i lies in sub-tile i; D = 64: waves 0-1 in sub-tile 0, 2-3 in 1.
       const int sub = K_PER_T > 1 ? i * 16 * KPIECES / (kWaves * 64) : uniform(tid >> 7);
-      const unsigned off = (unsigned)((tok & 15) * c.row_bytes + g * D * 2 + piece * 16);
-      gk[i] = buf_load16<0>(rsrc_of(c.kc, d, sub), off);
+      if constexpr (FP8) {   // the piece's 8 channels as 8 codes
+        const unsigned off = (unsigned)((tok & 15) * c.row_bytes + g * D + piece * 8);
+        const u32x2 x = buf_load8<0>(rsrc_of(c.kc, d, sub), off);
+        gk[i] = u32x4{x[0], x[1], 0u, 0u};
+      } else {
+        const unsigned off = (unsigned)((tok & 15) * c.row_bytes + g * D * 2 + piece * 16);
+        gk[i] = buf_load16<0>(rsrc_of(c.kc, d, sub), off);
+      }
     }
   };
   auto k_store = [&](int buf, const u32x4 (&gk)[K_PER_T]) {
@@ -157,34 +171,55 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
     for (int i = 0; i < K_PER_T; ++i) {
       const int pc = tid + i * kWaves * 64;
       const int tok = pc / KPIECES, piece = pc - tok * KPIECES;
-      *(u32x4*)(kbuf + buf * KTILEB + tok * KROWB + piece * 16) = gk[i];
+      u32x4 v = gk[i];
+      if constexpr (FP8) {
+        const u32x2 lo = e4m3x4_to_bf16(gk[i][0]), hi = e4m3x4_to_bf16(gk[i][1]);
+        v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+      *(u32x4*)(kbuf + buf * KTILEB + tok * KROWB + piece * 16) = v;
     }
   };
-  // V staging: item (chunk q, channel pair cp) loads channels 2cp, 2cp + 1 of
-  // tokens 4q .. 4q + 3 of both sub-tiles (one word each) and writes the chunk
-  // q of rows 2cp and 2cp + 1.
-  const int v_item = tid < 4 * VPAIRS ? tid : 0;
-  const bool v_on = tid < 4 * VPAIRS;
-  const int vq = v_item / VPAIRS, vcp = v_item - vq * VPAIRS;
+  // V staging: item (chunk q, column cp) loads one word of tokens 4q .. 4q + 3 of
+  // both sub-tiles -- channels 2cp, 2cp + 1 (bf16) or 4cp .. 4cp + 3 (E4M3 codes) --
+  // and writes the chunk q of those channels' rows.
+  const int v_item = tid < 4 * VCOLS ? tid : 0;
+  const bool v_on = tid < 4 * VCOLS;
+  const int vq = v_item / VCOLS, vcp = v_item - vq * VCOLS;
   auto v_issue = [&](const TileDesc& d, unsigned (&gv)[8]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const __amdgpu_buffer_rsrc_t rv = rsrc_of(c.vc, d, sub);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        gv[4 * sub + i] = buf_load4<0>(rv, (unsigned)((4 * vq + i) * c.row_bytes + g * D * 2 + vcp * 4));
+        gv[4 * sub + i] = buf_load4<0>(rv, (unsigned)((4 * vq + i) * c.row_bytes + g * D * EB + vcp * 4));
     }
   };
   auto v_store = [&](int buf, const unsigned (&gv)[8]) {
     if (!v_on) return;
+    if constexpr (FP8) {
+      u32x2 cv[8];   // per token: channels (4cp, 4cp + 1) and (4cp + 2, 4cp + 3) as bf16 pairs
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int ch = 2 * vcp + e;
-      u32x4 w;
+      for (int i = 0; i < 8; ++i) cv[i] = e4m3x4_to_bf16(gv[i]);
 #pragma unroll
-      for (int dd = 0; dd < 4; ++dd)
-        w[dd] = e ? pack_hi16(gv[2 * dd], gv[2 * dd + 1]) : pack_lo16(gv[2 * dd], gv[2 * dd + 1]);
-      *(u32x4*)(vbuf + buf * VTILEB + ch * 64 + 16 * (vq ^ ((ch >> 2) & 3))) = w;
+      for (int e = 0; e < 4; ++e) {
+        const int ch = 4 * vcp + e;
+        u32x4 w;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd)
+          w[dd] = (e & 1) ? pack_hi16(cv[2 * dd][e >> 1], cv[2 * dd + 1][e >> 1])
+                          : pack_lo16(cv[2 * dd][e >> 1], cv[2 * dd + 1][e >> 1]);
+        *(u32x4*)(vbuf + buf * VTILEB + ch * 64 + 16 * (vq ^ ((ch >> 2) & 3))) = w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int ch = 2 * vcp + e;
+        u32x4 w;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd)
+          w[dd] = e ? pack_hi16(gv[2 * dd], gv[2 * dd + 1]) : pack_lo16(gv[2 * dd], gv[2 * dd + 1]);
+        *(u32x4*)(vbuf + buf * VTILEB + ch * 64 + 16 * (vq ^ ((ch >> 2) & 3))) = w;
+      }
     }
   };
   // S^T of one tile (raw q.k) from K buffer kb.
@@ -307,11 +342,13 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
     if (k + 1 < n_tiles) step(k + 1, sb, sa);
   }
 
+  float vsc = 1.f;
+  if constexpr (FP8) vsc = c.v_scale[g];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const float l_tot = sum_across_rows(l_run[t]);
     if (r < rows.n_rows[t]) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float inv = l_tot > 0.f ? vsc / l_tot : 0.f;
       float* dst = rows.o[t] + (size_t)r * D + 4 * qd;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) *(f32x4*)(dst + 16 * j) = oacc[t][j] * inv;
@@ -452,7 +489,7 @@ template <int D, int RT, bool FP8>
 __device__ __forceinline__ void attn_varlen_balanced(const VarlenParams& p, int* s_pb, int* s_pref,
                                                      int* s_upref, int* s_wave,
                                                      unsigned char* s_kv) {
-  constexpr bool kShared = RT > 1 && !FP8;
+  constexpr bool kShared = RT > 1;
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
@@ -544,7 +581,7 @@ __device__ __forceinline__ void attn_varlen_balanced(const VarlenParams& p, int*
           const int rt0 = grp * kShareTiles + 2 * wave;
           fill(tiles, 0, rt0, h, 2 * wave);
           fill(tiles, 1, rt0 + 1, h, 2 * wave + 1);
-          attend_shared<D>(p.c, h, n_sub, desc, t0, tiles, s_kv);
+          attend_shared<D, FP8>(p.c, h, n_sub, desc, t0, tiles, s_kv);
           continue;
         }
       }
@@ -560,7 +597,7 @@ __device__ __forceinline__ void attn_varlen_balanced(const VarlenParams& p, int*
 
 template <int D, int RT, bool FP8, bool BAL>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_varlen_kernel(const VarlenParams p) {
-  constexpr bool kShared = RT > 1 && !FP8;   // E4M3 caches: per-head units only
+  constexpr bool kShared = RT > 1;
   __shared__ int s_pb[kMaxTable];
   __shared__ int s_pref[kMaxBalBatch + 1];
   __shared__ int s_upref[kMaxBalBatch + 1];   // balanced: unit prefix over sequences
@@ -657,7 +694,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         RowTiles<2> tiles;
         fill(tiles, 0, m_first / 16 + 2 * wave, g_sh);
         fill(tiles, 1, m_first / 16 + 2 * wave + 1, g_sh);
-        attend_shared<D>(p.c, g_sh, (span + 15) / 16, desc, t0, tiles, s_kv);
+        attend_shared<D, FP8>(p.c, g_sh, (span + 15) / 16, desc, t0, tiles, s_kv);
         continue;
       }
     }
@@ -985,7 +1022,7 @@ static int varlen_run(bool fp8, float* out, const void* query, const void* key_c
   vp.slot_rows = pl.slot_rows;
   vp.nwg = pl.nwg;
   vp.rt = pl.rt;
-  vp.share_ok = (pl.rt > 1 && !fp8) ? 1 : 0;
+  vp.share_ok = pl.rt > 1 ? 1 : 0;
   // One row tile per wave for decode-sized chunks; otherwise kVarlenRT tiles share
   // every K / V tile a wave loads. Both kernels take their work units grid-stride
   // from a fixed grid of at most four workgroups per CU.

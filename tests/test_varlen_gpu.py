@@ -9,7 +9,7 @@ import torch
 import gqa_paged_kv_amd as gp
 import oracle
 import workloads
-from gpu_util import BF, Dev, max_abs, to_dev
+from gpu_util import BF, Dev, fp8_codes, max_abs, to_dev
 
 pytestmark = pytest.mark.gpu
 ATOL = 2e-3
@@ -272,3 +272,56 @@ def test_varlen_fp8_single_tokens_equal_fp8_decode():
         to_dev(w.context_lens, torch.int32), max_context_len=w.max_context_len,
         scale=float(w.scale)).cpu().numpy()
     assert max_abs(out, dec) <= 1e-5
+
+
+@pytest.mark.parametrize("split", [256, 2048, "balanced"])
+def test_varlen_fp8_shared_tiles_at_the_causal_bound(split, monkeypatch):
+    """E4M3 chunks on the shared-LDS path (codes widened to bf16 as they are staged),
+    with first-row causal bounds on, one short of and one past a 32-position tile edge."""
+    if split == "balanced":
+        monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", "balanced")
+    else:
+        monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", "split")
+        monkeypatch.setenv("GPKV_SPLIT_TOKENS", str(split))
+    w = workloads.varlen_case(726, num_q_heads=28, num_kv_heads=4, head_dim=128, block_size=16,
+                              context_lens=[1055, 1056, 1058, 2080, 96],
+                              q_lens=[32, 33, 31, 64, 96])
+    kq, vq, ks, vs = _fp8_case(w)
+    out = _run_fp8(w, kq, vq, ks, vs)
+    ref = oracle.paged_attention_varlen_fp8(w.query_varlen, kq, vq, ks, vs, w.block_tables,
+                                            w.context_lens, w.cu_seqlens_q, w.scale)
+    err = max_abs(out, ref)
+    print(f"split {split}: FP8 varlen max-abs {err:.3e}")
+    assert err <= ATOL
+
+
+_MIXED_FP8 = {}
+
+
+@pytest.mark.parametrize("schedule", VARLEN_SCHEDULES)
+def test_varlen_fp8_mixed_batch_8k(schedule, monkeypatch):
+    """The 8K-average mixed batch over E4M3 caches (per-head scales amax / 256): the six
+    chunks take the shared-LDS path, the single tokens the per-head one; every query row
+    against the oracle on the same codes."""
+    monkeypatch.setenv("GPKV_VARLEN_SCHEDULE", schedule)
+    if "case" not in _MIXED_FP8:
+        rng = np.random.default_rng(714)
+        ctx = np.clip(np.round(rng.normal(8192, 2048, 64)), 2048, 16384).astype(np.int32)
+        ql = np.ones(64, np.int32)
+        ql[:6] = [128, 256, 64, 512, 32, 128]
+        w = workloads.varlen_case(714, num_q_heads=28, num_kv_heads=4, head_dim=128,
+                                  block_size=16, context_lens=ctx, q_lens=ql)
+        k = (w.key_cache.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        v = (w.value_cache.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        ks = np.maximum(np.abs(k).max(axis=(0, 1, 3)) / 256.0, 1e-3).astype(np.float32)
+        vs = np.maximum(np.abs(v).max(axis=(0, 1, 3)) / 256.0, 1e-3).astype(np.float32)
+        del k, v
+        kq, vq = fp8_codes(w.key_cache, ks), fp8_codes(w.value_cache, vs)
+        ref = oracle.paged_attention_varlen_fp8(w.query_varlen, kq, vq, ks, vs, w.block_tables,
+                                                w.context_lens, w.cu_seqlens_q, w.scale)
+        _MIXED_FP8["case"] = (w, kq, vq, ks, vs, ref)
+    w, kq, vq, ks, vs, ref = _MIXED_FP8["case"]
+    out = _run_fp8(w, kq, vq, ks, vs)
+    err = max_abs(out, ref)
+    print(f"mixed 8K batch, E4M3 ({schedule}): max-abs {err:.3e} over all {out.shape[0]} rows")
+    assert err <= ATOL
