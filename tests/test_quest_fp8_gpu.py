@@ -417,3 +417,35 @@ def test_fp8_quest_append_spiked_new_token(path, monkeypatch):
     good = oracle.quest_select_topk_fp8(w.query, gmin, gmax, w.block_tables, w.context_lens, 16, 4)
     assert not np.array_equal(stale, good), "the case does not depend on the fold"
     _append_check(c, 4, path, monkeypatch)
+
+
+def test_fp8_quest_batch_above_balanced_table():
+    """4200 sequences (past the balanced schedule's 4096-sequence prefix): the FP8
+    selection and the one-call FP8 Quest step take their two-kernel and split forms and
+    match the oracle on sampled sequences (the oracle's codes cover those sequences'
+    blocks)."""
+    rng = np.random.default_rng(951)
+    B = 4200
+    ctx = rng.integers(0, 41, size=B).astype(np.int32)
+    w = workloads.random_case(951, batch=B, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                              block_size=16, context_lens=ctx)
+    seqs = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), 0, 1, 4096, 4097, B - 1})
+    c = Fp8Case(w, seqs)
+    kmin, kmax = _gpu_meta(c)
+    K = 2
+    sel = gp.quest_select_topk_fp8(c.d.q, kmin, kmax, c.d.bt, c.d.ctx, block_size=16,
+                                   topk_blocks=K, max_context_len=w.max_context_len)
+    out, qsel = gp.quest_decode_fp8(c.d.q, c.kc, c.vc, c.d_ks, c.d_vs, kmin, kmax, c.d.bt,
+                                    c.d.ctx, topk_blocks=K, max_context_len=w.max_context_len,
+                                    scale=float(w.scale))
+    torch.cuda.synchronize()
+    bt, cl = w.block_tables[seqs], w.context_lens[seqs]
+    omin, omax = oracle.quest_block_metadata_fp8(c.okc, bt, cl, 16)
+    osel = oracle.quest_select_topk_fp8(w.query[seqs], omin, omax, bt, cl, 16, K)
+    assert np.array_equal(sel.cpu().numpy()[seqs], osel), "selection differs"
+    assert torch.equal(qsel, sel), "the one-call step selected differently"
+    ref = oracle.sparse_paged_attention_decode_fp8(w.query[seqs], c.okc, c.ovc, c.ks, c.vs, bt,
+                                                   cl, osel, w.scale)
+    o = out.cpu().numpy()
+    assert max_abs(o[seqs], ref) <= ATOL
+    assert (o[ctx == 0] == 0).all()
