@@ -1,14 +1,17 @@
 """Decode-step benchmark of the paged GQA attention library on one MI355X.
 
 One step = the whole hot path once over one batch of synthetic input:
-  reshape_and_cache_quest (one new token per sequence, and the incremental Quest
-  min / max of its block, in one launch)
-  -> paged_attention_decode (dense, split-KV + combine)
+  paged_attention_decode_append (dense attention, split-KV + combine, with the
+  step's write: one new token per sequence, stored by the combine, which also folds
+  it into its block's Quest min / max)
   -> quest_decode (Quest block selection and sparse attention over the selection;
   one launch when the batch's (sequence, KV head) pairs fill the GPU).
-With --quest-path separate the last call is quest_select_topk followed by
-sparse_paged_attention_decode (the two calls are also timed on their own either
-way). With --write-path separate the first call is reshape_and_cache, a
+With --write-path fused the write is a launch of its own first
+(reshape_and_cache_quest) and the dense call is paged_attention_decode; a workload
+whose new tokens are not one per sequence takes that form, and one without new
+tokens has no write. With --quest-path separate the Quest call is quest_select_topk
+followed by sparse_paged_attention_decode (the two calls are also timed on their
+own either way). With --write-path separate the first call is reshape_and_cache, a
 quest_block_metadata refresh of each sequence's last block follows the dense call,
 and the Quest part runs as the two separate calls.
 Inputs are resident in HBM before timing. Before every timed step a 1 GiB buffer
@@ -16,9 +19,9 @@ is written so that no KV bytes survive in the 256 MB Infinity Cache; the
 per-call durations come from HIP events on the launch stream and exclude that
 flush. The value reported is the step's algorithmic KV/metadata bytes divided by
 the step time (GB/s). The full metadata rebuild is a prefill-time cost and is
-reported separately, outside the step. A workload without new tokens has no write
-in its step. The one-call Quest decode is also timed alone behind its own flush,
-and the Quest step is the write plus that alone-timed call.
+reported separately, outside the step. The one-call Quest decode is also timed
+alone behind its own flush, and the Quest step is that call with the write folded
+into it (quest_decode_append) timed alone, or the write plus quest_decode alone.
 
 After the headline workload, a per-workload block times every call of each of the
 five workloads alone behind the flush (write, dense call, one-call Quest decode),
@@ -57,9 +60,10 @@ def parse_args():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte calibration)")
-    ap.add_argument("--write-path", choices=["fused", "separate"], default="fused",
-                    help="fused: reshape_and_cache_quest; separate: reshape_and_cache + "
-                         "quest_block_metadata(last_block_only)")
+    ap.add_argument("--write-path", choices=["append", "fused", "separate"], default="append",
+                    help="append: the write (and metadata fold) inside the dense call, "
+                         "paged_attention_decode_append; fused: reshape_and_cache_quest; "
+                         "separate: reshape_and_cache + quest_block_metadata(last_block_only)")
     ap.add_argument("--quest-path", choices=["one_call", "separate"], default="one_call",
                     help="Quest part of the step: quest_decode, or select + sparse calls")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) cache timing")
@@ -388,9 +392,18 @@ def main():
     flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    fused = bool(K) and args.write_path == "fused"
+    # The one-call dense step needs one new token per sequence (token b is sequence b's
+    # newest); other workloads take the separate write kernel.
+    write_mode = args.write_path
+    if write_mode == "append" and not (w.num_tokens and w.num_tokens == B):
+        write_mode = "fused"
+    fused = bool(K) and write_mode in ("fused", "append")
     one_call = fused and args.quest_path == "one_call"
-    if one_call:
+    dense_name = "paged_attention_decode_append" if write_mode == "append" else "paged_attention_decode"
+    if write_mode == "append":
+        calls = [dense_name] + (["quest_decode"] if one_call else
+                                (["quest_select_topk", "sparse_paged_attention_decode"] if K else []))
+    elif one_call:
         calls = ["reshape_and_cache_quest", "paged_attention_decode", "quest_decode"]
     elif fused:
         calls = ["reshape_and_cache_quest", "paged_attention_decode", "quest_select_topk",
@@ -413,6 +426,12 @@ def main():
         elif name == "paged_attention_decode":
             gp.paged_attention_decode(q, kc, vc, bt, ctx, max_context_len=mcl, scale=scale,
                                       out=out_d, workspace=ws_d)
+        elif name == "paged_attention_decode_append":
+            gp.paged_attention_decode_append(q, nk, nv, kc, vc, slots, bt, ctx,
+                                             max_context_len=mcl, scale=scale,
+                                             key_min=kmin if K else None,
+                                             key_max=kmax if K else None, out=out_d,
+                                             workspace=ws_d)
         elif name == "quest_block_metadata":
             gp.quest_block_metadata(kc, bt, ctx, kmin, kmax, max_context_len=mcl, last_block_only=True)
         elif name == "quest_select_topk":
@@ -653,6 +672,10 @@ def main():
         by["quest_select_topk"] = R.select_bytes(w.context_lens, bs, Hkv, D)
         by["sparse_paged_attention_decode"] = R.sparse_attention_bytes(sel_host, w.context_lens, bs, D)
         by["quest_decode"] = by["quest_select_topk"] + by["sparse_paged_attention_decode"]
+    # The one-call dense step: K / V of every valid token plus the write (with the
+    # metadata fold when the step keeps Quest metadata).
+    by["paged_attention_decode_append"] = by["paged_attention_decode"] + (
+        by["reshape_and_cache_quest"] if K else by["reshape_and_cache"])
     step_bytes = sum(by[n] for n in calls)
     mean_step = float(step_us.mean())
     value = step_bytes / (mean_step * 1e-6) / 1e9
@@ -667,21 +690,24 @@ def main():
         }
         calls_out[name]["pct_of_peak"] = round(100 * calls_out[name]["gbps"] / R.MI355X_HBM_GBPS, 1)
 
-    dense_t = per_call["paged_attention_decode"].mean()
-    achieved = by["paged_attention_decode"] / (dense_t * 1e-6) / 1e9
+    dense_t = per_call[dense_name].mean()
+    achieved = by[dense_name] / (dense_t * 1e-6) / 1e9
     traffic = committed_traffic(args.config)
     # Both step figures include the write (when the workload has one): dense = write +
-    # dense attention; Quest = write (+ metadata refresh) + the Quest part, which for
-    # the one-call path is quest_decode timed alone behind its own flush (so it never
-    # follows the dense call's 1 GB stream).
+    # dense attention (one call on the append path); Quest = write (+ metadata refresh)
+    # + the Quest part, which for the one-call path is quest_decode timed alone behind
+    # its own flush (so it never follows the dense call's 1 GB stream), and on the
+    # append path quest_decode_append timed alone (the write folded into it).
     write_us = sum(calls_out[n]["us_mean"] for n in calls
                    if n.startswith("reshape_and_cache"))
     if not K:
         quest_us = None
+    elif one_call and write_mode == "append" and quest_append_alone:
+        quest_us = quest_append_alone["us_mean"]
     elif one_call:
         quest_us = write_us + quest_alone["us_mean"]
     else:
-        quest_us = sum(calls_out[n]["us_mean"] for n in calls if n != "paged_attention_decode")
+        quest_us = sum(calls_out[n]["us_mean"] for n in calls if n != dense_name)
 
     line = {
         "metric": "paged decode attention KV-read HBM GB/s over one decode step (write + dense + Quest)",
@@ -699,13 +725,13 @@ def main():
         "config": {"workload": w.name, "global_batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": bs, "sum_context": int(w.context_lens.sum()),
                    "max_context_len": mcl, "topk_blocks": K, "parallelism": "single-gpu",
-                   "write_path": args.write_path if K else "plain",
+                   "write_path": write_mode if (K or write_mode == "append") else "plain",
                    "quest_path": ("one_call" if one_call else "separate") if K else None,
                    "sparse_split_tokens": gp.split_tokens(B, Hkv, K * bs) if K else None},
         "pct_of_peak": round(100 * value / R.MI355X_HBM_GBPS, 1),
         "us_per_step": round(mean_step, 2),
         "us_per_step_median": round(float(np.median(step_us)), 2),
-        "dense_step_us": round(write_us + calls_out["paged_attention_decode"]["us_mean"], 2),
+        "dense_step_us": round(write_us + calls_out[dense_name]["us_mean"], 2),
         "dense_step_one_call": append_alone,
         "quest_step_one_call": quest_append_alone,
         "quest_step_us": round(quest_us, 2) if quest_us is not None else None,
@@ -721,10 +747,12 @@ def main():
         "flush_mib_between_steps": args.flush_mib,
         "roofline": {
             "bound": "hbm",
-            "kernel": f"paged_attention_decode call: {DOMINANT_KERNEL} + its combine kernel",
+            "kernel": (f"{dense_name} call: {DOMINANT_KERNEL} + its combine kernel"
+                       + (" (which also writes the new tokens and folds them into the metadata)"
+                          if dense_name.endswith("append") else "")),
             "achieved": round(achieved, 1), "peak": R.MI355X_HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved / R.MI355X_HBM_GBPS, 4), "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(by["paged_attention_decode"]),
+            "algorithmic_bytes_per_launch": int(by[dense_name]),
             "launch_us_mean": round(float(dense_t), 2),
         },
         "kernel_source_sha256_16": kernel_source_hash(),
