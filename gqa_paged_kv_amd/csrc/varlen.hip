@@ -128,15 +128,12 @@ __device__ __forceinline__ void attend_shared(const AttnCommon& c, int g, int n_
   }
 
   const int n_tiles = (n_sub + 1) >> 1;
+  // desc gives an empty sub-tile (nv = 0) past the span, so both sub-tiles are
+  // described without a branch and their two table reads are in flight together.
   auto tdesc = [&](int k) {
     TileDesc d;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      d.pb[sub] = 0;
-      d.row0[sub] = 0;
-      d.nv[sub] = 0;
-      if (2 * k + sub < n_sub) desc(2 * k + sub, d.pb[sub], d.row0[sub], d.nv[sub]);
-    }
+    for (int sub = 0; sub < 2; ++sub) desc(2 * k + sub, d.pb[sub], d.row0[sub], d.nv[sub]);
     return d;
   };
   // (sub is wave-uniform; selects rather than an indexed read keep TileDesc in
@@ -552,7 +549,8 @@ __device__ __forceinline__ void attn_varlen_balanced(const VarlenParams& p, int*
       auto desc = [&](int uu, int& pb, int& row0, int& nv) {
         const int tok = t0 + 16 * uu;
         const int ei = (tok >> bs_log2) - e0;
-        const int x = ei < n_ent ? s_pb[ei] : -1;
+        const int xr = s_pb[ei < n_ent ? ei : 0];   // read unconditionally, in bounds
+        const int x = ei < n_ent ? xr : -1;
         row0 = tok & (bs - 1);
         int n = t0 + span - tok;
         n = n < 0 ? 0 : (n > 16 ? 16 : n);
@@ -666,7 +664,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const int span = tile_lim - t0 < T ? tile_lim - t0 : T;
     auto desc = [&](int uu, int& pb, int& row0, int& nv) {
       const int tok = t0 + 16 * uu;
-      const int x = s_pb[(tok >> bs_log2) - e0];   // bs is a power of two: no division
+      const int ei = (tok >> bs_log2) - e0;        // bs is a power of two: no division
+      const int xr = s_pb[ei < n_ent ? ei : 0];    // read unconditionally, in bounds
+      const int x = ei < n_ent ? xr : -1;
       row0 = tok & (bs - 1);
       int n = t0 + span - tok;
       n = n < 0 ? 0 : (n > 16 ? 16 : n);
