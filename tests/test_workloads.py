@@ -70,3 +70,33 @@ def test_topk_has_no_near_ties(config):
     for K in w.topk_list:
         gap = _min_relative_gap(w, K)
         assert gap > 1e-9, f"config {config} K={K}: near-tie, relative gap {gap:.3e}"
+
+
+def _fp8_min_relative_gap(w, K):
+    """The same gap for Quest over E4M3 caches: codes made with the per-head scales the
+    GPU tests use (amax of a fixed subsample / 256), code metadata, scores on codes."""
+    from gpu_util import fp8_codes
+    from test_fp8_gpu import _scales
+    kc = fp8_codes(w.key_cache, _scales(w.key_cache))
+    kmin, kmax = oracle.quest_block_metadata_fp8(kc, w.block_tables, w.context_lens,
+                                                 w.block_size)
+    worst = np.inf
+    for b in range(w.batch):
+        for g in range(w.num_kv_heads):
+            s = oracle.quest_block_scores_fp8(w.query, kmin, kmax, w.block_tables,
+                                              w.context_lens, w.block_size, b, g)
+            if s.size <= K:
+                continue
+            top = np.sort(s)[::-1]
+            gap = (top[K - 1] - top[K]) / max(abs(top[K - 1]), 1e-300)
+            worst = min(worst, gap)
+    return worst
+
+
+@pytest.mark.parametrize("config", [1, 3, 4, 5])
+def test_fp8_topk_has_no_near_ties(config):
+    """The FP8 selections the GPU tests compare bit for bit are just as well separated."""
+    w = workloads.make(config)
+    for K in w.topk_list:
+        gap = _fp8_min_relative_gap(w, K)
+        assert gap > 1e-9, f"config {config} K={K}: near-tie, relative gap {gap:.3e}"
