@@ -12,6 +12,9 @@ group's summed query are planted exactly where the schedule cuts the work:
     sub-tiles of each sequence's selected blocks, in list order;
   - sparse, one workgroup per (sequence, KV head) (the 8K-average batch): its four
     waves take [w*T/4, (w+1)*T/4) of the pair's 32-token tiles;
+  - the one-launch Quest decode (the 8K-average batch): its workgroup of eight waves
+    selects the pair's blocks, then wave w takes [w*T/8, (w+1)*T/8) of the selected
+    32-token tiles;
 
 plus the first and last token of every sequence. Each spike outweighs the rest of
 its sequence many times over, so the spikes share the softmax weight among
@@ -39,6 +42,7 @@ SPIKE_SCORE = 20.0      # scale * q.k of a spike for the median head of its grou
 MAX_SUB_PER_WG = 2048   # dense balanced schedule: most sub-tiles per workgroup
 BAL_TAB = 4096          # sparse balanced schedule: table entries per workgroup
 DIRECT_WAVES = 4        # waves of the one-workgroup-per-(sequence, KV head) sparse path
+QUEST_WAVES = 8         # waves of the one-launch Quest decode's workgroup
 
 
 def _cus() -> int:
@@ -136,7 +140,7 @@ def _sparse_balanced_spikes(w, sel, K):
     return nwg, spikes
 
 
-def _direct_spikes(w, sel, K):
+def _direct_spikes(w, sel, K, waves=DIRECT_WAVES):
     bs, spb = w.block_size, w.block_size // 16
     ctx = w.context_lens.astype(np.int64)
     spikes = set()
@@ -146,8 +150,8 @@ def _direct_spikes(w, sel, K):
             continue
         n_tiles = (n * spb + 1) // 2
         for g in range(w.num_kv_heads):
-            for wave in range(1, DIRECT_WAVES):
-                u = 2 * (wave * n_tiles // DIRECT_WAVES)
+            for wave in range(1, waves):
+                u = 2 * (wave * n_tiles // waves)
                 for uu, row_in in ((u, 0), (u - 1, 15)):
                     if 0 <= uu < n * spb:
                         t = _selected_token(sel[b, g], uu // spb, (uu % spb) * 16 + row_in,
@@ -252,4 +256,41 @@ def test_sparse_spikes_at_schedule_seams(config, K):
                                            scale=float(w.scale)).cpu().numpy()
     err = max_abs(out, attend(w))
     print(f"config {config}: {len(spikes)} spikes at {where}; sparse max-abs {err:.3e}")
+    assert err <= ATOL
+
+
+def test_quest_decode_spikes_at_wave_seams(monkeypatch):
+    """The one-launch Quest decode on the 8K-average batch: one 512-thread workgroup per
+    (sequence, KV head) selects its blocks and its eight waves take [w*T/8, (w+1)*T/8) of
+    the pair's selected 32-token tiles. Spikes sit at those seams of the oracle's
+    selection and at each pair's first and last selected token; they only raise the
+    scores of selected blocks, so the selection stays the same (checked), and the
+    kernel selects and attends by itself."""
+    monkeypatch.setenv("GPKV_QUEST_DECODE_PATH", "fused")
+    config, K = 3, 64
+    w0 = workload(config)
+    sel = oracle_selection(config, K)
+    spikes = _direct_spikes(w0, sel, K, waves=QUEST_WAVES)
+    w = _plant(w0, spikes)
+    bs = w.block_size
+    omin, omax = oracle.quest_block_metadata(w.key_cache, w.block_tables, w.context_lens, bs)
+    assert np.array_equal(
+        oracle.quest_select_topk(w.query, omin, omax, w.block_tables, w.context_lens, bs, K), sel)
+
+    def attend(wx, seqs=None):
+        return oracle.sparse_paged_attention_decode(wx.query, wx.key_cache, wx.value_cache,
+                                                    wx.block_tables, wx.context_lens, sel,
+                                                    wx.scale, seqs=seqs)
+    _assert_drop_is_visible(w, spikes, attend)
+    d = Dev(w)
+    kmin = torch.zeros((w.num_blocks, w.num_kv_heads, w.head_dim), dtype=BF, device="cuda")
+    kmax = torch.zeros_like(kmin)
+    gp.quest_block_metadata(d.kc, d.bt, d.ctx, kmin, kmax, max_context_len=w.max_context_len)
+    out, gsel = gp.quest_decode(d.q, d.kc, d.vc, kmin, kmax, d.bt, d.ctx, topk_blocks=K,
+                                max_context_len=w.max_context_len, scale=float(w.scale))
+    torch.cuda.synchronize()
+    assert np.array_equal(gsel.cpu().numpy(), sel), "selection differs from the oracle"
+    err = max_abs(out.cpu().numpy(), attend(w))
+    print(f"config {config}: {len(spikes)} spikes at the eight wave seams; one-launch Quest "
+          f"max-abs {err:.3e}")
     assert err <= ATOL
