@@ -549,7 +549,8 @@ __device__ __forceinline__ int split_ctx(const int* ctx, const long long* slots,
 }
 
 
-// Exclusive prefix sum over the workgroup's 256 threads; *total gets the sum.
+// Exclusive prefix sum over the workgroup's NW * 64 threads; *total gets the sum.
+template <int NW = kWaves>
 __device__ __forceinline__ int wg_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int inc = (int)wave_inclusive_scan((unsigned)v);
@@ -557,7 +558,7 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* s_wave, int* total)
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int x = s_wave[w];
     off += w < wave ? x : 0;
     tot += x;

@@ -145,12 +145,12 @@ struct BalParams {
 // the direct sparse one: without it the compiler keeps the MFMA accumulators in AGPRs
 // and copies them to VGPRs around every softmax (72 v_accvgpr moves per 32-token tile
 // at D = 128, 242 VALU per tile against 170 with the hint).
-template <int D, bool SPARSE, bool FP8>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_balanced_kernel(const BalParams p) {
+template <int D, bool SPARSE, bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_balanced_kernel(const BalParams p) {
   __shared__ int s_pref[kMaxBalBatch + 1];
   __shared__ int s_pb[kBalTab];                  // physical block per table entry (-1: none)
   __shared__ int s_tok0[SPARSE ? kBalTab : 1];   // sparse: logical position of its row 0
-  __shared__ int s_wave[kWaves];
+  __shared__ int s_wave[NW];
   const int wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int B = p.B, bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // Sub-tile counts of every sequence, and their prefix sums (all workgroups
   // compute the same values; workgroup 0 also hands them to the combine).
   int carry = 0;
-  for (int base = 0; base < B; base += kWaves * 64) {
+  for (int base = 0; base < B; base += NW * 64) {
     const int bb = base + tid;
     int n = 0;
     if (bb < B) {
@@ -172,14 +172,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
     int tot;
-    const int ex = wg_exclusive_scan(n, s_wave, &tot);
+    const int ex = wg_exclusive_scan<NW>(n, s_wave, &tot);
     if (bb < B) s_pref[bb + 1] = carry + ex + n;
     carry += tot;
   }
   if (tid == 0) s_pref[0] = 0;
   __syncthreads();
   if (wg == 0)
-    for (int i = tid; i <= B; i += kWaves * 64) p.prefix[i] = s_pref[i];
+    for (int i = tid; i <= B; i += NW * 64) p.prefix[i] = s_pref[i];
   const long long S = s_pref[B];
   const int s0 = (int)((long long)wg * S / p.nwg);
   const int s1 = (int)((long long)(wg + 1) * S / p.nwg);
@@ -206,20 +206,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const int n_ent = (ue - 1) / spb - e0 + 1;
     __syncthreads();  // the previous sequence's table is no longer read
     if (!SPARSE) {
-      for (int e = tid; e < n_ent; e += kWaves * 64) {
+      for (int e = tid; e < n_ent; e += NW * 64) {
         const int lb = e0 + e;
         const int pb = lb < nb ? p.block_tables[(size_t)b * p.max_blocks + lb] : -1;
         s_pb[e] = (pb >= 0 && pb < p.NB) ? pb : -1;
       }
     } else {
-      for (int i = tid; i < Hkv * n_ent; i += kWaves * 64) s_pb[i] = -1;
+      for (int i = tid; i < Hkv * n_ent; i += NW * 64) s_pb[i] = -1;
       __syncthreads();
       // Compaction of each head's list, 64 entries per step: a valid entry's
       // position is the number of valid entries before it. Four steps' entries
       // are requested at once, so a share deep in a long list waits for one
       // round of list loads rather than one per 64 entries.
       constexpr int kListSteps = 4;
-      for (int g = wave; g < Hkv; g += kWaves) {
+      for (int g = wave; g < Hkv; g += NW) {
         const int* lst = p.topk + ((size_t)b * Hkv + g) * p.topk_blocks;
         int run = 0;
         for (int c0 = 0; c0 < p.topk_blocks && run < e0 + n_ent; c0 += 64 * kListSteps) {
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }
     __syncthreads();
     const size_t slot = (size_t)wg + b;
-    for (int g = wave; g < Hkv; g += kWaves) {
+    for (int g = wave; g < Hkv; g += NW) {
       const int* tab = s_pb + (SPARSE ? g * n_ent : 0);
       const int* tok = s_tok0 + (SPARSE ? g * n_ent : 0);
       auto desc = [&](int u, int& pb, int& row0, int& nv) {
@@ -809,12 +809,25 @@ static void launch_combine(bool per_head, int mode, int B, int Hq, int Hkv, hipS
     launch_combine_mode<D, kNoAppend>(per_head, B, Hq, Hkv, stream, cp);
 }
 
+// GPKV_BAL_WIDE=0 keeps four waves per balanced workgroup everywhere (tuning and test
+// switch, read per call).
+static bool getenv_wide() {
+  const char* f = getenv("GPKV_BAL_WIDE");
+  return !(f && strcmp(f, "0") == 0);
+}
+
 template <int D, bool SPARSE, bool FP8>
 static void launch_attention(bool balanced, const BalParams& bp, const SplitParams& sp, int nwg,
                              int num_splits, int B, hipStream_t stream) {
   const dim3 block(kWaves * 64);
-  if (balanced)
-    attn_balanced_kernel<D, SPARSE, FP8><<<dim3(nwg), block, 0, stream>>>(bp);
+  // Dense with 8 KV heads or a multiple: eight waves per workgroup (one per KV head of
+  // the share's tokens, two per SIMD). Measured on MI355X over the ragged 8-KV-head
+  // batch: E4M3 caches 256-263 -> 250 us (one wave's code decoding overlaps the other's
+  // loads), bf16 unchanged (441-445 us), outputs bit-identical.
+  if (balanced && !SPARSE && bp.c.Hkv % 8 == 0 && getenv_wide())
+    attn_balanced_kernel<D, SPARSE, FP8, 8><<<dim3(nwg), dim3(8 * 64), 0, stream>>>(bp);
+  else if (balanced)
+    attn_balanced_kernel<D, SPARSE, FP8, kWaves><<<dim3(nwg), block, 0, stream>>>(bp);
   else
     attn_split_kernel<D, SPARSE, FP8><<<dim3(num_splits, B), block, 0, stream>>>(sp);
 }
