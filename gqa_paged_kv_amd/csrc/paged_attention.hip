@@ -820,11 +820,12 @@ template <int D, bool SPARSE, bool FP8>
 static void launch_attention(bool balanced, const BalParams& bp, const SplitParams& sp, int nwg,
                              int num_splits, int B, hipStream_t stream) {
   const dim3 block(kWaves * 64);
-  // Dense with 8 KV heads or a multiple: eight waves per workgroup (one per KV head of
-  // the share's tokens, two per SIMD). Measured on MI355X over the ragged 8-KV-head
-  // batch: E4M3 caches 256-263 -> 250 us (one wave's code decoding overlaps the other's
-  // loads), bf16 unchanged (441-445 us), outputs bit-identical.
-  if (balanced && !SPARSE && bp.c.Hkv % 8 == 0 && getenv_wide())
+  // 8 KV heads or a multiple: eight waves per workgroup (one per KV head of the share's
+  // tokens, two per SIMD). Measured on MI355X over the ragged 8-KV-head batch, outputs
+  // bit-identical: dense over E4M3 caches 256-263 -> 250 us (one wave's code decoding
+  // overlaps the other's loads), over bf16 unchanged (441-445 us); sparse over E4M3
+  // 206-212 -> 197-198 us, over bf16 351-353 -> 345-348 us.
+  if (balanced && bp.c.Hkv % 8 == 0 && getenv_wide())
     attn_balanced_kernel<D, SPARSE, FP8, 8><<<dim3(nwg), dim3(8 * 64), 0, stream>>>(bp);
   else if (balanced)
     attn_balanced_kernel<D, SPARSE, FP8, kWaves><<<dim3(nwg), block, 0, stream>>>(bp);
