@@ -45,7 +45,10 @@ sys.path.insert(0, ROOT)
 DEFAULT_CONFIG = 3
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = "attn_balanced_dense_long8k_traffic.md"
-DOMINANT_KERNEL = "attn_balanced_kernel<128, false, false>"
+def dominant_kernel(num_kv_heads: int) -> str:
+    """The dense split kernel's instance: eight waves per workgroup with 8 KV heads or a
+    multiple, four otherwise."""
+    return f"attn_balanced_kernel<128, false, false, {8 if num_kv_heads % 8 == 0 else 4}>"
 
 
 def parse_args():
@@ -747,7 +750,7 @@ def main():
         "flush_mib_between_steps": args.flush_mib,
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"{dense_name} call: {DOMINANT_KERNEL} + its combine kernel"
+            "kernel": (f"{dense_name} call: {dominant_kernel(Hkv)} + its combine kernel"
                        + (" (which also writes the new tokens and folds them into the metadata)"
                           if dense_name.endswith("append") else "")),
             "achieved": round(achieved, 1), "peak": R.MI355X_HBM_GBPS, "unit": "GB/s",
