@@ -12,7 +12,8 @@
 //   sum_h max(q_h*kmin, q_h*kmax) = kmax * sum_{q_h>0} q_h + kmin * sum_{q_h<0} q_h,
 // so each (b, g) pre-reduces its queries once into two float64 vectors and a block
 // costs 2*D float64 FMAs. Scores stay in float64 so near-equal blocks keep their
-// exact order; ties go to the lower logical block.
+// exact order; ties go to the lower logical block. The _fp8 entry points do the same
+// over E4M3 caches with metadata of codes (quest_select.h).
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>

@@ -9,6 +9,10 @@
 //   sum_h max(q_h*kmin, q_h*kmax) = kmax * sum_{q_h>0} q_h + kmin * sum_{q_h<0} q_h,
 // so each (b, g) pre-reduces its queries once into two float64 vectors and a block
 // costs 2*D float64 FMAs. Scores stay in float64; ties go to the lower logical block.
+// Over E4M3 caches the metadata holds the codes of each channel's extremes and the
+// bound is taken on the code values (the per-KV-head key scale, one positive factor
+// for every block of a head, leaves the selection unchanged): the same kernels with
+// FP8 = true read 8 bytes of codes where they read 16 bytes of bf16.
 #pragma once
 
 #include <math.h>
