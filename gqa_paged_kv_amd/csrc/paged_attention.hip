@@ -16,9 +16,10 @@
 // HBM together.
 //  - Dense (balanced): the grid is one workgroup per compute unit. Each
 //    workgroup computes the prefix sums of the sequences' 16-token sub-tile
-//    counts and takes an equal share of the flattened (sequence, sub-tile)
-//    space, so ragged batches cost no tail: every workgroup moves the same
-//    number of KV bytes. A workgroup writes one partial per sequence it
+//    counts (each plus a fixed cost for starting the sequence) and takes an
+//    equal share of the flattened (sequence, sub-tile) space, so ragged batches
+//    cost no tail: every workgroup moves about the same number of KV bytes, a
+//    little less where it starts more sequences. A workgroup writes one partial per sequence it
 //    touches into slot (workgroup + sequence), which is unique because shares are
 //    ordered; the combine recomputes which workgroups covered a sequence.
 //  - Sparse, and dense batches too large for the balanced table: a workgroup per
@@ -128,7 +129,8 @@ struct BalParams {
   AttnCommon c;
   float* part_o;             // [N + B, H_kv, G, D] fp32, slot = workgroup + sequence
   float* part_lse;           // [N + B, H_kv, G] fp32 (base 2)
-  int* prefix;               // [B + 1] sub-tile prefix sums, written by workgroup 0
+  int* prefix;               // [B + 1] prefix sums of the sequences' costs (sub-tiles +
+                             // kSegCost each), written by workgroup 0
   const int* block_tables;
   const int* ctx;
   const int* topk;           // [B, H_kv, K] logical block ids (sparse only)
@@ -136,6 +138,15 @@ struct BalParams {
   long long NB;
   int B, max_blocks, max_ctx, nwg, topk_blocks;
 };
+
+// Cost of starting a sequence inside a share, in sub-tiles: each sequence's span of
+// the flattened space opens with this many sub-tiles of no work, so shares that
+// start many sequences (table staging, the first tile's loads, the partial row's
+// write) take fewer sub-tiles. Measured (one workgroup per CU, 0 / 1 / 2 / 3 / 4 / 6):
+// Qwen-shaped batch 59.1 / 58.0 / 57.4 / 57.6 / 57.5 / 57.7 us, 8K-average 173.8 /
+// 172.5 / 172.2 / 172.2 / 172.4 / 173.2, ragged 8-KV-head batch 443 / 441 / 438 /
+// 440 / 443 / 445; the 40960-token batch and the sparse calls did not move.
+constexpr int kSegCost = 2;
 
 // Work of a sequence, in 16-token sub-tiles: dense, its context; sparse,
 // min(K, blocks) blocks. Valid ids of one KV head's list are distinct blocks of the
@@ -156,8 +167,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int B = p.B, bs = p.c.bs, Hkv = p.c.Hkv, G = p.c.G;
   const int spb = bs >> 4;   // sub-tiles per block
 
-  // Sub-tile counts of every sequence, and their prefix sums (all workgroups
-  // compute the same values; workgroup 0 also hands them to the combine).
+  // Costs of every sequence (sub-tiles plus the start cost; an empty sequence costs
+  // nothing), and their prefix sums (all workgroups compute the same values;
+  // workgroup 0 also hands them to the combine).
   int carry = 0;
   for (int base = 0; base < B; base += NW * 64) {
     const int bb = base + tid;
@@ -171,6 +183,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         n = (ctx + 15) >> 4;
       }
     }
+    n += n > 0 ? kSegCost : 0;
     int tot;
     const int ex = wg_exclusive_scan<NW>(n, s_wave, &tot);
     if (bb < B) s_pref[bb + 1] = carry + ex + n;
@@ -195,8 +208,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       hi = mid - 1;
   }
   for (int b = lo; b < B && s_pref[b] < s1; ++b) {
-    const int ub = (s0 > s_pref[b] ? s0 : s_pref[b]) - s_pref[b];
-    const int ue = (s1 < s_pref[b + 1] ? s1 : s_pref[b + 1]) - s_pref[b];
+    const int c0 = s_pref[b] + (s_pref[b + 1] > s_pref[b] ? kSegCost : 0);  // first sub-tile
+    const int ub = (s0 > c0 ? s0 : c0) - c0;
+    const int ue = (s1 < s_pref[b + 1] ? s1 : s_pref[b + 1]) - c0;
     if (ue <= ub) continue;  // empty sequence
     const int ctx = split_ctx(p.ctx, p.slots, p.NB * bs, b, p.max_ctx);
     const int nb = (ctx + bs - 1) / bs;
@@ -512,12 +526,13 @@ __device__ __forceinline__ UnitRange unit_range(const CombineParams& p, int b, i
   r.nwg = p.nwg;
   r.S = 0;
   if (p.balanced) {
-    const long long pre0 = p.prefix[b];
+    long long pre0 = p.prefix[b];
     const long long pre1 = p.prefix[b + 1];
     r.S = p.prefix[p.B];
     if (pre1 <= pre0) {
       r.u_begin = r.u_end = 0;
     } else {
+      pre0 += kSegCost;  // the sequence's first sub-tile
       r.u_begin = (int)(((pre0 + 1) * p.nwg - 1) / r.S);  // workgroup holding sub-tile pre0
       r.u_end = (int)((pre1 * p.nwg - 1) / r.S) + 1;      // ... and sub-tile pre1 - 1
     }
@@ -745,8 +760,9 @@ static Plan make_plan(bool sparse, int B, int Hq, int Hkv, int D, int bs, int sp
     // are sub-tiles.
     const long long max_sub = sparse ? (long long)B * (span / bs) * spb : (long long)B * ((span + 15) / 16);
     const long long share_max = sparse ? (long long)(kBalTab / Hkv - 2) * spb : kMaxSubPerWG;
+    const long long max_cost = max_sub + (long long)B * kSegCost;
     long long n = balanced_capacity();
-    const long long need = (max_sub + share_max - 1) / share_max;
+    const long long need = (max_cost + share_max - 1) / share_max;
     if (n < need) n = need;
     if (n > max_sub) n = max_sub;
     if (n < 1) n = 1;

@@ -6,8 +6,10 @@ thousands carries a weight of about 1e-4. So tokens whose keys point along their
 group's summed query are planted exactly where the schedule cuts the work:
 
   - dense (balanced schedule, one workgroup per CU): the flattened space of
-    (sequence, 16-token sub-tile) is shared out as [wg*S/N, (wg+1)*S/N); a spike sits
-    on the first token of every share and on the last token of the share before it;
+    (sequence, 16-token sub-tile), where every non-empty sequence opens with
+    SEG_COST sub-tiles of no work, is shared out as [wg*S/N, (wg+1)*S/N); a spike
+    sits on the first token of every share and on the last token of the share
+    before it;
   - sparse, balanced schedule (the 8-KV-head ragged batch): the same rule over the
     sub-tiles of each sequence's selected blocks, in list order;
   - sparse, one workgroup per (sequence, KV head) (the 8K-average batch): its four
@@ -41,6 +43,7 @@ ATOL = 2e-3
 SPIKE_SCORE = 20.0      # scale * q.k of a spike for the median head of its group
 MAX_SUB_PER_WG = 2048   # dense balanced schedule: most sub-tiles per workgroup
 BAL_TAB = 4096          # sparse balanced schedule: table entries per workgroup
+SEG_COST = 2            # balanced schedules: cost of starting a sequence, in sub-tiles
 DIRECT_WAVES = 4        # waves of the one-workgroup-per-(sequence, KV head) sparse path
 QUEST_WAVES = 8         # waves of the one-launch Quest decode's workgroup
 
@@ -49,15 +52,18 @@ def _cus() -> int:
     return int(torch.cuda.get_device_properties(0).multi_processor_count)
 
 
-def _balanced_workgroups(max_sub: int, share_max: int) -> int:
-    n = max(_cus(), -(-max_sub // share_max))
+def _balanced_workgroups(max_sub: int, share_max: int, batch: int) -> int:
+    n = max(_cus(), -(-(max_sub + batch * SEG_COST) // share_max))
     return max(1, min(n, max_sub))
 
 
 def _cuts(work: np.ndarray, nwg: int):
     """(item, first sub-tile of a share inside it) for every share boundary of the
-    flattened work (sub-tiles per item), as the balanced schedule draws them."""
-    pre = np.concatenate([[0], np.cumsum(work.astype(np.int64))])
+    flattened work (sub-tiles per item, each non-empty item opening with SEG_COST
+    sub-tiles of no work), as the balanced schedule draws them."""
+    work = work.astype(np.int64)
+    cost = work + np.where(work > 0, SEG_COST, 0)
+    pre = np.concatenate([[0], np.cumsum(cost)])
     S = int(pre[-1])
     out = []
     for wg in range(1, nwg):
@@ -65,7 +71,7 @@ def _cuts(work: np.ndarray, nwg: int):
         if s0 >= S or s0 == (wg - 1) * S // nwg:
             continue
         b = int(np.searchsorted(pre, s0, side="right") - 1)
-        out.append((b, s0 - int(pre[b])))
+        out.append((b, max(0, s0 - int(pre[b]) - SEG_COST)))
     return out
 
 
@@ -103,7 +109,8 @@ def _plant(w, spikes):
 def _dense_spikes(w):
     ctx = w.context_lens.astype(np.int64)
     work = (ctx + 15) // 16
-    nwg = _balanced_workgroups(int(w.batch * ((w.max_context_len + 15) // 16)), MAX_SUB_PER_WG)
+    nwg = _balanced_workgroups(int(w.batch * ((w.max_context_len + 15) // 16)), MAX_SUB_PER_WG,
+                               w.batch)
     pos = set()
     for b, u in _cuts(work, nwg):
         pos.add((b, 16 * u))
@@ -125,7 +132,8 @@ def _sparse_balanced_spikes(w, sel, K):
     bs, spb = w.block_size, w.block_size // 16
     ctx = w.context_lens.astype(np.int64)
     nsel = np.minimum(K, -(-ctx // bs))
-    nwg = _balanced_workgroups(int(w.batch * K * spb), (BAL_TAB // w.num_kv_heads - 2) * spb)
+    nwg = _balanced_workgroups(int(w.batch * K * spb), (BAL_TAB // w.num_kv_heads - 2) * spb,
+                               w.batch)
     spikes = set()
     for b, u in _cuts(nsel * spb, nwg):
         for g in range(w.num_kv_heads):
