@@ -478,9 +478,10 @@ __device__ __forceinline__ void append_unit(const CombineParams& p, int b, int g
 
 // Decode append: KV head g's part of sequence b's new token written into the cache at
 // its slot (a slot outside the pool writes nothing, as the write path), with the
-// Quest fold when the metadata is given; E4M3 caches take its codes.
+// Quest fold when the metadata is given; E4M3 caches take its codes. Threads t of nt
+// share the row.
 template <int D, int MODE>
-__device__ __forceinline__ void append_write(const CombineParams& p, int b, int g) {
+__device__ __forceinline__ void append_write(const CombineParams& p, int b, int g, int t, int nt) {
   const long long s = p.slots[b];
   if (s < 0 || s >= p.num_slots) return;
   if constexpr (MODE == kAppendFp8) {
@@ -489,15 +490,14 @@ __device__ __forceinline__ void append_write(const CombineParams& p, int b, int 
     const float kinv = 1.0f / p.k_scale[g], vinv = 1.0f / p.v_scale[g];
     const size_t src = ((size_t)b * p.Hkv + g) * D;
     const size_t dst = ((size_t)s * p.Hkv + g) * D;   // bytes
-    for (int c = threadIdx.x; c < D / 4; c += blockDim.x) {
+    for (int c = t; c < D / 4; c += nt) {
       const uint2 kk = *(const uint2*)(p.knew + src + 4 * c);
       const uint2 vv = *(const uint2*)(p.vnew + src + 4 * c);
       *(unsigned*)((unsigned char*)p.kc + dst + 4 * c) = e4m3_codes4(kk, kinv);
       *(unsigned*)((unsigned char*)p.vc + dst + 4 * c) = e4m3_codes4(vv, vinv);
     }
   } else {
-    store_new_token<D>(p.knew, p.vnew, p.kc, p.vc, p.kmin, p.kmax, s, p.bs, p.Hkv, b, g,
-                       threadIdx.x, blockDim.x);
+    store_new_token<D>(p.knew, p.vnew, p.kc, p.vc, p.kmin, p.kmax, s, p.bs, p.Hkv, b, g, t, nt);
   }
 }
 
@@ -557,18 +557,31 @@ __device__ __forceinline__ UnitRange unit_range(const CombineParams& p, int b, i
 // Few units per sequence: one workgroup per (sequence, KV head); each group of
 // D/4 threads (a "slot") owns query heads hl, hl + slots, ... of the group and
 // merges that head's units on its own, without barriers: up to kHeadUnits unit
-// rows in one round of loads after the prefix.
+// rows in one round of loads after the prefix. Append calls whose grid stays resident
+// with one more wave per workgroup launch it (WRITE_WAVE): that wave writes the new
+// token into the cache while the others merge. Written by a merging wave, the write's
+// loads delay that wave's merge: on the 8K-average batch the call goes 171.9 -> 171.2 us
+// (bf16, with the Quest fold) and 96.4 -> 95.4 us (E4M3), medians of four runs. With
+// eight workgroups per CU (the ragged 8-KV-head batch) a fifth wave costs a second round
+// of workgroups (443 -> 449 us), so there the first wave writes before it merges.
 constexpr int kHeadUnits = 12;
 
-template <int D, int MODE>
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_heads_kernel(const CombineParams p) {
+template <int D, int MODE, bool WRITE_WAVE>
+__global__ __launch_bounds__(kCombineThreads + (WRITE_WAVE ? 64 : 0)) void attn_combine_heads_kernel(const CombineParams p) {
   constexpr int TPU = D / 4;
   constexpr int SLOTS = kCombineThreads / TPU;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int slot = tid / TPU, c4 = tid % TPU;
   constexpr bool APPEND = MODE != kNoAppend;
+  if constexpr (APPEND && WRITE_WAVE) {
+    if (tid >= kCombineThreads) {
+      append_write<D, MODE>(p, b, g, tid - kCombineThreads, 64);
+      return;
+    }
+  } else if constexpr (APPEND) {
+    append_write<D, MODE>(p, b, g, tid, kCombineThreads);
+  }
   const bool append = APPEND && append_token(p.slots, p.num_slots, b, p.ctx, p.max_ctx);
-  if (APPEND) append_write<D, MODE>(p, b, g);   // first, so that its loads overlap the merge's
   for (int hl = slot; hl < p.G; hl += SLOTS) {
     const UnitRange r = unit_range<D>(p, b, g, hl);
     const int u0 = r.u_begin;
@@ -600,7 +613,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const Com
 
   constexpr bool APPEND = MODE != kNoAppend;
   const bool append = APPEND && append_token(p.slots, p.num_slots, b, p.ctx, p.max_ctx);
-  if (APPEND && hl == 0) append_write<D, MODE>(p, b, g);
+  if (APPEND && hl == 0) append_write<D, MODE>(p, b, g, tid, kCombineThreads);
   const UnitRange r = unit_range<D>(p, b, g, hl);
   if (r.u_end <= r.u_begin) {   // no unit: the appended token alone, or nothing
     if (tid < TPU) {
@@ -808,10 +821,13 @@ template <int D, int MODE>
 static void launch_combine_mode(bool per_head, int B, int Hq, int Hkv, hipStream_t stream,
                                 const CombineParams& cp) {
   const dim3 cblock(kCombineThreads);
+  const bool write_wave = MODE != kNoAppend && (long long)B * Hkv <= 4LL * balanced_capacity();
   if (per_head)
     attn_combine_kernel<D, MODE><<<dim3(Hq, B), cblock, 0, stream>>>(cp);
+  else if (write_wave)
+    attn_combine_heads_kernel<D, MODE, true><<<dim3(Hkv, B), dim3(kCombineThreads + 64), 0, stream>>>(cp);
   else
-    attn_combine_heads_kernel<D, MODE><<<dim3(Hkv, B), cblock, 0, stream>>>(cp);
+    attn_combine_heads_kernel<D, MODE, false><<<dim3(Hkv, B), cblock, 0, stream>>>(cp);
 }
 
 template <int D>
