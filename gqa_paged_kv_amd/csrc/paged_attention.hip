@@ -19,9 +19,10 @@
 //    counts (each plus a fixed cost for starting the sequence) and takes an
 //    equal share of the flattened (sequence, sub-tile) space, so ragged batches
 //    cost no tail: every workgroup moves about the same number of KV bytes, a
-//    little less where it starts more sequences. A workgroup writes one partial per sequence it
-//    touches into slot (workgroup + sequence), which is unique because shares are
-//    ordered; the combine recomputes which workgroups covered a sequence.
+//    little less where it starts more sequences. A workgroup writes one partial
+//    per sequence it touches into slot (workgroup + sequence), which is unique
+//    because shares are ordered; the combine recomputes which workgroups covered
+//    a sequence.
 //  - Sparse, and dense batches too large for the balanced table: a workgroup per
 //    (sequence, split of `split_tokens` virtual tokens), the split's block-table
 //    entries (per KV head when sparse) staged in LDS.
