@@ -558,29 +558,37 @@ __device__ __forceinline__ UnitRange unit_range(const CombineParams& p, int b, i
 // Few units per sequence: one workgroup per (sequence, KV head); each group of
 // D/4 threads (a "slot") owns query heads hl, hl + slots, ... of the group and
 // merges that head's units on its own, without barriers: up to kHeadUnits unit
-// rows in one round of loads after the prefix. Append calls whose grid stays resident
-// with one more wave per workgroup launch it (WRITE_WAVE): that wave writes the new
-// token into the cache while the others merge. Written by a merging wave, the write's
-// loads delay that wave's merge: on the 8K-average batch the call goes 171.9 -> 171.2 us
-// (bf16, with the Quest fold) and 96.4 -> 95.4 us (E4M3), medians of four runs. With
-// eight workgroups per CU (the ragged 8-KV-head batch) a fifth wave costs a second round
-// of workgroups (443 -> 449 us), so there the first wave writes before it merges.
+// rows in one round of loads after the prefix. In the append calls no merging wave
+// writes the new token (its merge would wait for the write's loads): when the grid stays
+// resident with one more wave per workgroup (WRITER 1), that wave writes KV head g's
+// part; otherwise (WRITER 2) workgroup H_kv of each sequence writes every KV head's
+// part. 8K-average batch (WRITER 1 against the first wave writing): the call 171.9 ->
+// 171.2 us (bf16, with the Quest fold), 96.4 -> 95.4 us (E4M3); a fifth wave on the
+// ragged 8-KV-head batch's eight workgroups per CU cost a second round of them
+// (443 -> 449 us), hence WRITER 2 there (against the first wave writing: 439.4 ->
+// 437.9 us bf16, 250.9 -> 248.9 us E4M3, medians of four runs).
 constexpr int kHeadUnits = 12;
 
-template <int D, int MODE, bool WRITE_WAVE, int NU>
-__global__ __launch_bounds__(kCombineThreads + (WRITE_WAVE ? 64 : 0)) void attn_combine_heads_kernel(const CombineParams p) {
+template <int D, int MODE, int WRITER, int NU>
+__global__ __launch_bounds__(kCombineThreads + (WRITER == 1 ? 64 : 0)) void attn_combine_heads_kernel(const CombineParams p) {
   constexpr int TPU = D / 4;
   constexpr int SLOTS = kCombineThreads / TPU;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int slot = tid / TPU, c4 = tid % TPU;
   constexpr bool APPEND = MODE != kNoAppend;
-  if constexpr (APPEND && WRITE_WAVE) {
+  static_assert(APPEND == (WRITER != 0), "the append instances have a writer");
+  if constexpr (WRITER == 1) {
     if (tid >= kCombineThreads) {
       append_write<D, MODE>(p, b, g, tid - kCombineThreads, 64);
       return;
     }
-  } else if constexpr (APPEND) {
-    append_write<D, MODE>(p, b, g, tid, kCombineThreads);
+  } else if constexpr (WRITER == 2) {
+    if (g == p.Hkv) {
+      constexpr int PER = MODE == kAppendFp8 ? D / 4 : D / 8;   // threads per KV head's row
+      for (int gg = tid / PER; gg < p.Hkv; gg += kCombineThreads / PER)
+        append_write<D, MODE>(p, b, gg, tid % PER, PER);
+      return;
+    }
   }
   const bool append = APPEND && append_token(p.slots, p.num_slots, b, p.ctx, p.max_ctx);
   for (int hl = slot; hl < p.G; hl += SLOTS) {
@@ -828,7 +836,7 @@ template <int D, int MODE>
 static void launch_combine_mode(bool per_head, bool few_units, int B, int Hq, int Hkv,
                                 hipStream_t stream, const CombineParams& cp) {
   const dim3 cblock(kCombineThreads), grid(Hkv, B);
-  const bool write_wave = MODE != kNoAppend && (long long)B * Hkv <= 4LL * balanced_capacity();
+  const bool write_wave = (long long)B * Hkv <= 4LL * balanced_capacity();
   // Unit rows requested at once: kHeadUnits (eight in the append instances, so that the
   // new token's unit fits four waves per SIMD), or four when sequences hold few units:
   // 53-60 registers instead of 96-125, eight waves per SIMD instead of four or five, so
@@ -836,14 +844,22 @@ static void launch_combine_mode(bool per_head, bool few_units, int B, int Hq, in
   // (2048 workgroups, medians of four runs): dense 440.0 -> 436.1 us, sparse 347.3 ->
   // 342.7, E4M3 dense 244.5 -> 241.4, dense append 440.9 -> 439.3.
   constexpr int NU = MODE != kNoAppend ? 8 : kHeadUnits;
-  if (per_head)   // + one write workgroup per KV head in the append instances
+  if (per_head) {   // + one write workgroup per KV head in the append instances
     attn_combine_kernel<D, MODE><<<dim3(Hq + (MODE != kNoAppend ? Hkv : 0), B), cblock, 0, stream>>>(cp);
-  else if (write_wave)
-    attn_combine_heads_kernel<D, MODE, true, NU><<<grid, dim3(kCombineThreads + 64), 0, stream>>>(cp);
-  else if (few_units)
-    attn_combine_heads_kernel<D, MODE, false, 4><<<grid, cblock, 0, stream>>>(cp);
-  else
-    attn_combine_heads_kernel<D, MODE, false, NU><<<grid, cblock, 0, stream>>>(cp);
+  } else if constexpr (MODE == kNoAppend) {
+    if (few_units)
+      attn_combine_heads_kernel<D, MODE, 0, 4><<<grid, cblock, 0, stream>>>(cp);
+    else
+      attn_combine_heads_kernel<D, MODE, 0, NU><<<grid, cblock, 0, stream>>>(cp);
+  } else if (write_wave) {
+    attn_combine_heads_kernel<D, MODE, 1, NU><<<grid, dim3(kCombineThreads + 64), 0, stream>>>(cp);
+  } else {
+    const dim3 wgrid(Hkv + 1, B);   // + the writing workgroup of each sequence
+    if (few_units)
+      attn_combine_heads_kernel<D, MODE, 2, 4><<<wgrid, cblock, 0, stream>>>(cp);
+    else
+      attn_combine_heads_kernel<D, MODE, 2, NU><<<wgrid, cblock, 0, stream>>>(cp);
+  }
 }
 
 template <int D>
